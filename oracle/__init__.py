@@ -1,0 +1,13 @@
+"""fp64 CPU oracle (test infrastructure only; see attention.py)."""
+from .attention import (  # noqa: F401
+    aggregate_scores,
+    attend,
+    collected_logits,
+    default_scale,
+    kvgroup_sum,
+    select_topk,
+    select_topk_batch,
+    sparse_attention,
+    verify_attention,
+    widen_bf16,
+)

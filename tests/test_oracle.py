@@ -1,0 +1,263 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+Each test ties an oracle function to something other than its own formula:
+a library routine it must reduce to (torch CPU fp64 scaled_dot_product_attention),
+a closed form, an invariant of the definitions, or brute force over every
+subset on tiny inputs (the argmax of Vegas, "A. aggregated attention-logit
+selection", restricted by the protected sinks/window of Dustin, "1. hybrid
+attention aggregation").
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_long_amd import workloads as W
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def causal_mask(T, L):
+    """bool [T, L]: row t sees j <= L - T + t (bottom-right aligned)."""
+    j = np.arange(L)[None, :]
+    t = np.arange(T)[:, None]
+    return j <= (L - T + t)
+
+
+# ------------------------------------------------------------------ verify attention
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+def test_verify_equals_torch_sdpa_fp64(T, Hq, Hkv):
+    B, d, ctx = 3, 16, 40
+    lens = [40, 23, T]  # full, ragged, minimal (only the verify tokens)
+    q, k, v = rnd((B, Hq, T, d), 1), rnd((B, Hkv, ctx, d), 2), rnd((B, Hkv, ctx, d), 3)
+    o, lse = oracle.verify_attention(q, k, v, lens)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        qt = torch.from_numpy(q[b])
+        kt = torch.from_numpy(k[b, :, :L]).repeat_interleave(G, dim=0)
+        vt = torch.from_numpy(v[b, :, :L]).repeat_interleave(G, dim=0)
+        mask = torch.from_numpy(causal_mask(T, L))
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+        np.testing.assert_allclose(o[b], ref.numpy(), rtol=0, atol=1e-12)
+        # lse against torch.logsumexp of the library's own masked score matrix
+        s = (qt @ kt.transpose(-1, -2)) / math.sqrt(d)
+        s = s.masked_fill(~mask, float("-inf"))
+        np.testing.assert_allclose(lse[b], torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_softmax_weights_sum_to_one():
+    # V = identity rows: o[r] is the weight vector itself.
+    d, L, T = 64, 50, 5
+    q, k = rnd((1, 2, T, d), 4), rnd((1, 1, L, d), 5)
+    v = np.zeros((1, 1, L, L))
+    v[0, 0] = np.eye(L)
+    o, _ = oracle.verify_attention(q, k, v, [L], scale=0.3)
+    w = o[0].reshape(-1, L)
+    assert np.all(w >= 0)
+    assert np.max(np.abs(w.sum(axis=1) - 1.0)) < 1e-12
+    # causally hidden positions carry zero weight
+    for t in range(T):
+        assert np.all(o[0, :, t, L - T + t + 1:] == 0.0)
+
+
+def test_constant_values_and_identical_keys():
+    d, L, T = 32, 70, 3
+    q, k = rnd((2, 4, T, d), 6), rnd((2, 2, L, d), 7)
+    vrow = rnd(d, 8)
+    v = np.broadcast_to(vrow, (2, 2, L, d)).copy()
+    o, _ = oracle.verify_attention(q, k, v, [L, 41])
+    np.testing.assert_allclose(o, np.broadcast_to(vrow, o.shape), rtol=0, atol=1e-13)
+    # identical keys: uniform weights -> mean of the visible values; lse = s + ln(n)
+    k_same = np.broadcast_to(rnd(d, 9), (2, 2, L, d)).copy()
+    v2 = rnd((2, 2, L, d), 10)
+    o2, lse2 = oracle.verify_attention(q, k_same, v2, [L, 41])
+    for b, Lb in enumerate([L, 41]):
+        for h in range(4):
+            g = h // 2
+            for t in range(T):
+                n = Lb - T + t + 1
+                np.testing.assert_allclose(o2[b, h, t], v2[b, g, :n].mean(axis=0), atol=1e-12)
+                s = q[b, h, t] @ k_same[b, g, 0] / math.sqrt(d)
+                assert abs(lse2[b, h, t] - (s + math.log(n))) < 1e-12
+
+
+def test_single_visible_position():
+    # L == T: row 0 sees only position 0 -> o = v_0, lse = s_0
+    d, T = 16, 4
+    q, k, v = rnd((1, 2, T, d), 11), rnd((1, 1, T, d), 12), rnd((1, 1, T, d), 13)
+    o, lse = oracle.verify_attention(q, k, v, [T], scale=0.5)
+    np.testing.assert_array_equal(o[0, :, 0], np.broadcast_to(v[0, 0, 0], (2, d)))
+    np.testing.assert_allclose(lse[0, :, 0], 0.5 * (q[0, :, 0] @ k[0, 0, 0]), atol=1e-14)
+
+
+# ------------------------------------------------------------------ collected logits
+def test_logits_closed_form_basis_keys():
+    # k[g, j] = (g + 1) * e_{(j + g) mod d}  =>  l[c, h, j] = scale * (g+1) * q[h, r_c][(j+g) mod d]
+    B, Hq, Hkv, T, d, ctx = 2, 6, 3, 5, 8, 30
+    lens = [30, 17]
+    rows = (0, 4)
+    q = rnd((B, Hq, T, d), 14)
+    k = np.zeros((B, Hkv, ctx, d))
+    for g in range(Hkv):
+        for j in range(ctx):
+            k[:, g, j, (j + g) % d] = g + 1
+    sc = 0.25
+    l = oracle.collected_logits(q, k, lens, rows, scale=sc)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        for c, r in enumerate(rows):
+            for h in range(Hq):
+                g = h // G
+                for j in range(L):
+                    want = sc * (g + 1) * q[b, h, r, (j + g) % d] if j <= L - T + r else -np.inf
+                    assert l[b, c, h, j] == want
+            assert np.all(np.isnan(l[b, c, :, L:]))
+
+
+def test_logits_depend_only_on_collected_rows():
+    B, Hq, Hkv, T, d, L = 1, 4, 2, 5, 16, 25
+    q, k = rnd((B, Hq, T, d), 15), rnd((B, Hkv, L, d), 16)
+    l1 = oracle.collected_logits(q, k, [L], (0, 4))
+    q2 = q.copy()
+    q2[:, :, 1:4] += 3.0  # rows that are not collected
+    assert np.array_equal(l1, oracle.collected_logits(q2, k, [L], (0, 4)), equal_nan=True)
+    q3 = q.copy()
+    q3[:, :, 4] += 1.0    # the bonus row
+    l3 = oracle.collected_logits(q3, k, [L], (0, 4))
+    assert np.array_equal(l1[:, 0], l3[:, 0], equal_nan=True)
+    assert not np.allclose(l1[:, 1, :, :L - T + 4], l3[:, 1, :, :L - T + 4])
+
+
+def test_scores_per_head_equal_regrouped_sum():
+    B, Hq, Hkv, T, d, L = 2, 8, 2, 4, 16, 33
+    q, k = rnd((B, Hq, T, d), 17), rnd((B, Hkv, L, d), 18)
+    l = oracle.collected_logits(q, k, [L, L], (0, 3))
+    s1 = oracle.aggregate_scores(l)
+    s2 = oracle.aggregate_scores(oracle.kvgroup_sum(l, Hkv))
+    fin = np.isfinite(s1)
+    np.testing.assert_allclose(s1[fin], s2[fin], rtol=1e-13, atol=1e-12)
+    assert np.array_equal(np.isneginf(s1), np.isneginf(s2))
+    # linearity: the score of position j is the sum of its 2*Hq logits
+    b, j = 1, 7
+    assert abs(s1[b, j] - sum(l[b, c, h, j] for c in range(2) for h in range(Hq))) < 1e-12
+
+
+# ------------------------------------------------------------------ selection
+def brute_force_best(scores, L, k, n_sink, window):
+    forced = set(range(min(n_sink, L))) | set(range(max(0, L - window), L))
+    rest = [j for j in range(L) if j not in forced]
+    best, best_sets = -np.inf, []
+    for extra in itertools.combinations(rest, k - len(forced)):
+        tot = sum(scores[j] for j in extra)
+        if tot > best:
+            best, best_sets = tot, [set(extra) | forced]
+        elif tot == best:
+            best_sets.append(set(extra) | forced)
+    return best, best_sets, forced
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("L,k,n_sink,window", [(10, 5, 1, 2), (12, 7, 2, 3), (14, 6, 0, 0),
+                                               (13, 4, 4, 0), (11, 5, 0, 5), (9, 3, 1, 1)])
+def test_select_attains_bruteforce_argmax(seed, L, k, n_sink, window):
+    rng = np.random.default_rng(seed)
+    # integer-valued, tie-heavy scores
+    scores = rng.integers(-3, 4, size=L).astype(np.float64)
+    got = oracle.select_topk(scores, L, k, n_sink, window)
+    best, best_sets, forced = brute_force_best(scores, L, k, n_sink, window)
+    gs = set(int(x) for x in got)
+    assert gs in best_sets
+    assert forced <= gs and len(gs) == k and list(got) == sorted(gs)
+    # among equal scores the lower positions win
+    free_sel = [j for j in gs if j not in forced]
+    free_out = [j for j in range(L) if j not in gs]
+    for i in free_sel:
+        for j in free_out:
+            assert scores[i] > scores[j] or (scores[i] == scores[j] and i < j)
+
+
+def test_select_edge_cases():
+    s = np.array([5.0, -0.0, 0.0, -np.inf, 2.0, 0.0, -np.inf, 1.0])
+    # k >= L keeps everything
+    assert list(oracle.select_topk(s, 8, 8, 1, 1)) == list(range(8))
+    assert list(oracle.select_topk(s, 5, 9, 1, 1)) == list(range(5))
+    # -0.0 == +0.0: ties go to the lower position; -inf ranks last, ties by position
+    assert list(oracle.select_topk(s, 8, 3, 0, 0)) == [0, 4, 7]
+    assert list(oracle.select_topk(s, 8, 5, 0, 0)) == [0, 1, 2, 4, 7]
+    assert list(oracle.select_topk(s, 8, 7, 0, 0)) == [0, 1, 2, 3, 4, 5, 7]
+    # sinks + window == k: exactly the forced set
+    assert list(oracle.select_topk(s, 8, 4, 2, 2)) == [0, 1, 6, 7]
+    # L shorter than sinks + window (so k >= L as well): every position is kept
+    assert list(oracle.select_topk(s, 5, 6, 3, 3)) == [0, 1, 2, 3, 4]
+    # sinks and window overlapping inside L: forced set is their union
+    assert list(oracle.select_topk(s, 6, 5, 2, 3)) == [0, 1, 3, 4, 5]
+    assert list(oracle.select_topk(s, 0, 4, 1, 1)) == []
+    with pytest.raises(ValueError):
+        oracle.select_topk(s, 8, 3, 2, 2)
+
+
+def test_select_planted_positions_win_on_small_workload():
+    """Planted keys (aligned with the group's queries) must be selected: their
+    summed logit is far above the spread of the unplanted ones."""
+    w = W.WORKLOADS["ctx2k_b1_h32kv8_d128"]
+    x = W.make_layer(w)
+    l = oracle.collected_logits(x.q, x.k, x.seq_lens, w.collect_rows)
+    scores = oracle.aggregate_scores(l)
+    sel = oracle.select_topk(scores[0], int(x.seq_lens[0]), w.budget, w.n_sink, w.window)
+    assert len(sel) == w.budget
+    assert set(x.planted[0].tolist()) <= set(sel.tolist())
+
+
+# ------------------------------------------------------------------ sparse attention
+def test_sparse_with_every_position_equals_verify():
+    B, Hq, Hkv, T, d, ctx = 2, 4, 2, 3, 16, 45
+    lens = [45, 29]
+    q, k, v = rnd((B, Hq, T, d), 19), rnd((B, Hkv, ctx, d), 20), rnd((B, Hkv, ctx, d), 21)
+    o1, l1 = oracle.verify_attention(q, k, v, lens)
+    o2, l2 = oracle.sparse_attention(q, k, v, lens, [np.arange(L) for L in lens])
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_sparse_equals_torch_sdpa_on_gathered_subset():
+    B, Hq, Hkv, T, d, L = 1, 6, 3, 4, 32, 80
+    q, k, v = rnd((B, Hq, T, d), 22), rnd((B, Hkv, L, d), 23), rnd((B, Hkv, L, d), 24)
+    idx = np.sort(np.random.default_rng(25).choice(L, 20, replace=False))
+    idx[-1] = L - 1
+    o, lse = oracle.sparse_attention(q, k, v, [L], [idx])
+    G = Hq // Hkv
+    qt = torch.from_numpy(q[0])
+    kt = torch.from_numpy(k[0][:, idx]).repeat_interleave(G, dim=0)
+    vt = torch.from_numpy(v[0][:, idx]).repeat_interleave(G, dim=0)
+    mask = torch.from_numpy(idx[None, :] <= (L - T + np.arange(T))[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    np.testing.assert_allclose(o[0], ref.numpy(), atol=1e-12)
+
+
+def test_sparse_single_index_and_empty_rows():
+    d, T, L = 16, 3, 50
+    q, k, v = rnd((1, 2, T, d), 26), rnd((1, 1, L, d), 27), rnd((1, 1, L, d), 28)
+    o, lse = oracle.sparse_attention(q, k, v, [L], [np.array([17])], scale=0.5)
+    for t in range(T):
+        np.testing.assert_array_equal(o[0, :, t], np.broadcast_to(v[0, 0, 17], (2, d)))
+        np.testing.assert_allclose(lse[0, :, t], 0.5 * (q[0, :, t] @ k[0, 0, 17]), atol=1e-14)
+    # only the last position listed: rows that cannot see it get o = 0, lse = -inf
+    o, lse = oracle.sparse_attention(q, k, v, [L], [np.array([L - 1])])
+    assert np.all(o[0, :, :T - 1] == 0) and np.all(np.isneginf(lse[0, :, :T - 1]))
+    np.testing.assert_array_equal(o[0, :, T - 1], np.broadcast_to(v[0, 0, L - 1], (2, d)))
+    # empty list
+    o, lse = oracle.sparse_attention(q, k, v, [L], [np.zeros(0, dtype=np.int64)])
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+def test_widen_bf16_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
+    want = [1.0, -1.0, 0.0, -0.0, 3.3895313892515355e38, 9.183549615799121e-41, 3.140625]
+    got = oracle.widen_bf16(bits)
+    assert list(got) == want
+    assert math.copysign(1.0, got[3]) == -1.0
