@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of one per-layer decode iteration of verification-guided sparse
+attention on one MI355X.
+
+A step is the whole hot path over one batch of synthetic, HBM-resident input:
+  verify (split-KV attention of the T = gamma+1 rows + kv-group-summed
+  pre-softmax logits of the first-draft and bonus rows) -> combine ->
+  aggregate scores -> top-k select (sinks + window kept) -> sparse attention
+  over the selected positions (sparse verify over the T rows, and/or
+  single-query draft steps) -> combine.
+
+Prints one JSON line.  `value` is iterations per second; `roofline` is the
+verify kernel (the dominant one) against the 8 TB/s HBM peak, timed with HIP
+events on the stream it runs on; `cpu_baseline` is the fp64 oracle on a
+bounded sample of the same workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify+topk+sparse-attn iters/s per layer at 32K, b16; % of HBM peak BW"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(w, lens):
+    """Algorithmic HBM bytes of one iteration, by stage (what the method must
+    move: every K/V row read once, the collected logits written once, scores
+    and indices once; split partials are implementation overhead and excluded)."""
+    B, Hq, Hkv, d, T, k = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.q_len, w.budget
+    Ls = [int(L) for L in lens]
+    kv = sum(Hkv * L * d * 2 * 2 for L in Ls)
+    q_in = B * Hq * T * d * 2
+    o_out = B * Hq * T * d * 2
+    emit = sum(Hkv * L * 4 for L in Ls)
+    agg = emit + sum(L * 4 for L in Ls)
+    sel = sum(L * 4 for L in Ls) + B * k * 4
+    n_sel = [min(k, L) for L in Ls]
+    sparse = 0
+    if w.sparse_verify:
+        sparse += sum(Hkv * n * d * 2 * 2 for n in n_sel) + q_in + o_out + B * k * 4
+    for s in range(1, w.draft_steps + 1):
+        sparse += sum(Hkv * (n + s) * d * 2 * 2 for n in n_sel) + 2 * (B * Hq * d * 2) + B * k * 4
+    return {
+        "verify_kernel": kv + q_in + emit,  # the split-KV kernel: K, V, Q read; logits written
+        "verify": kv + q_in + o_out + emit,
+        "aggregate": agg,
+        "select": sel,
+        "sparse": sparse,
+        "iteration": kv + q_in + o_out + emit + agg + sel + sparse,
+        "sparse_kernel_kv": sum(Hkv * n * d * 2 * 2 for n in n_sel) + q_in if w.sparse_verify else 0,
+    }
+
+
+def cpu_baseline(w, x, seconds):
+    """The fp64 oracle, as it stands, on whole sequences of the workload until
+    `seconds` have passed; scaled to iterations/s of the full batch."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(w.batch):
+        sl = slice(b, b + 1)
+        lens = x.seq_lens[sl]
+        oracle.verify_attention(x.q[sl], x.k[sl], x.v[sl], lens)
+        lg = oracle.collected_logits(x.q[sl], x.k[sl], lens, w.collect_rows)
+        sc = oracle.aggregate_scores(oracle.kvgroup_sum(lg, w.num_kv_heads))
+        idx = oracle.select_topk(sc[0], int(lens[0]), w.budget, w.n_sink, w.window)
+        if w.sparse_verify:
+            oracle.sparse_attention(x.q[sl], x.k[sl], x.v[sl], lens, [idx])
+        for s in range(1, w.draft_steps + 1):
+            li = np.concatenate([idx, np.arange(int(lens[0]), int(lens[0]) + s)])
+            oracle.sparse_attention(x.q_draft[s - 1][sl], x.k[sl], x.v[sl], lens + s, [li])
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    per_seq = el / done
+    return {
+        "value": 1.0 / (per_seq * w.batch),
+        "unit": "iters/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.batch} sequences (full iteration each: verify, logits, scores, "
+                  f"select, sparse) in {el:.1f} s, fp64 numpy; value scaled to the whole batch",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(sequences shard across GPUs with no exchange; run one process per GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_long_amd import binding as Bn
+    from sparse_attention_long_amd import workloads as W
+
+    name = args.workload or W.HEADLINE
+    w = W.WORKLOADS[name]
+    if w.draft_steps and not hasattr(Bn, "append_positions"):
+        raise SystemExit(f"{name}: draft steps are not wired into the benchmark yet")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    Bn.load()
+
+    log(f"[bench] generating {name}")
+    t0 = time.perf_counter()
+    x = W.make_layer(w, 0)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f}s")
+
+    def d_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = d_bf16(x.q)
+    if w.paged:
+        k, v = d_bf16(x.k_pool), d_bf16(x.v_pool)
+        bt = torch.from_numpy(x.block_table).to(dev)
+    else:
+        k, v, bt = d_bf16(x.k), d_bf16(x.v), None
+    lens = torch.from_numpy(x.seq_lens).to(dev)
+    B, Hq, Hkv, T, d = w.batch, w.num_q_heads, w.num_kv_heads, w.q_len, w.head_dim
+    max_ctx = w.max_ctx()
+    desc = Bn.make_desc(q, k, bt, max_ctx)
+    ws_v = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    logits = torch.empty((B, Hkv, max_ctx), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, max_ctx), dtype=torch.float32, device=dev)
+    stride = w.budget + w.draft_steps
+    idx = torch.empty((B, stride), dtype=torch.int32, device=dev)
+    n_idx = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws_s = torch.empty(Bn.sparse_workspace_bytes(desc, stride), dtype=torch.uint8, device=dev)
+    out_s = torch.empty_like(out)
+    lse_s = torch.empty_like(lse)
+    rows = w.collect_rows
+    KV = Bn.LOGITS_KVGROUP_SUM
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
+        if ev is not None:
+            ev[1].record()
+        Bn.combine_partials(desc, max_ctx, lens, ws_v, out, lse)
+        if ev is not None:
+            ev[2].record()
+        Bn.aggregate_scores(logits, lens, Hq, Hkv, scores=scores)
+        if ev is not None:
+            ev[3].record()
+        Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+        if ev is not None:
+            ev[4].record()
+        if w.sparse_verify:
+            Bn.sparse_partials(desc, q, k, v, lens, bt, idx, n_idx, ws_s)
+            if ev is not None:
+                ev[5].record()
+            Bn.combine_partials(desc, stride, n_idx, ws_s, out_s, lse_s)
+            if ev is not None:
+                ev[6].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps; events around the verify kernel
+    K = args.steps
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(K)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    e_start.record()
+    for i in range(K):
+        a, b_ = ev_pairs[i]
+        a.record()
+        Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
+        b_.record()
+        Bn.combine_partials(desc, max_ctx, lens, ws_v, out, lse)
+        Bn.aggregate_scores(logits, lens, Hq, Hkv, scores=scores)
+        Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+        if w.sparse_verify:
+            Bn.sparse_partials(desc, q, k, v, lens, bt, idx, n_idx, ws_s)
+            Bn.combine_partials(desc, stride, n_idx, ws_s, out_s, lse_s)
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = e_start.elapsed_time(e_end)
+    verify_us = float(np.mean([a.elapsed_time(b_) for a, b_ in ev_pairs])) * 1e3
+    log(f"[bench] {K} steps: wall {wall * 1e3:.2f} ms, gpu {gpu_ms:.2f} ms, verify kernel {verify_us:.1f} us")
+
+    # ---- stage breakdown and logit-emit overhead (outside the timed region)
+    nst = 7
+    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(K)]
+    for i in range(K):
+        step(stage_ev[i])
+    torch.cuda.synchronize()
+
+    def span(i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in stage_ev])) * 1e3
+
+    stages = {"verify_partials": span(0, 1), "verify_combine": span(1, 2), "aggregate": span(2, 3),
+              "select": span(3, 4)}
+    if w.sparse_verify:
+        stages["sparse_partials"] = span(4, 5)
+        stages["sparse_combine"] = span(5, 6)
+    none_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+    for a, b_ in none_ev:
+        a.record()
+        Bn.verify_partials(desc, q, k, v, lens, bt, rows, Bn.LOGITS_NONE, None, ws_v)
+        b_.record()
+    torch.cuda.synchronize()
+    verify_none_us = float(np.mean([a.elapsed_time(b_) for a, b_ in none_ev])) * 1e3
+
+    ab = alg_bytes(w, x.seq_lens)
+    iters = K / wall
+    achieved = ab["verify_kernel"] / (verify_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": iters,
+        "unit": "iters/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "ctx": w.ctx if w.ctx else list(w.ctx_range),
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "gamma": w.gamma,
+                   "budget": w.budget, "n_sink": w.n_sink, "window": w.window,
+                   "paged": w.paged, "logits": "kvgroup_sum"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "attn_partials_kernel (verify)",
+                     "alg_bytes_per_launch": ab["verify_kernel"], "avg_launch_us": verify_us},
+        "iteration_alg_bytes": ab["iteration"],
+        "iteration_hbm_frac": ab["iteration"] * iters / (HBM_PEAK_GBS * 1e9),
+        "gpu_ms_per_step": gpu_ms / K,
+        "stages_us": stages,
+        "verify_partials_no_logits_us": verify_none_us,
+        "logit_emit_overhead": stages["verify_partials"] / verify_none_us - 1.0,
+    }
+    if w.sparse_verify and stages.get("sparse_partials"):
+        sb = ab["sparse_kernel_kv"]
+        result["sparse_roofline"] = {"achieved": sb / (stages["sparse_partials"] * 1e-6) / 1e9,
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "alg_bytes_per_launch": sb,
+                                     "avg_launch_us": stages["sparse_partials"]}
+        result["sparse_roofline"]["frac"] = result["sparse_roofline"]["achieved"] / HBM_PEAK_GBS
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

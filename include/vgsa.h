@@ -1,0 +1,227 @@
+/*
+ * vgsa.h -- C ABI of the verification-guided sparse attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode iteration of long-context self-speculative decoding, per layer:
+ *
+ *   1. vgsa_verify_attention  full attention of the T = gamma + 1 verify rows
+ *      (gamma draft tokens + the bonus token) over the whole KV cache, writing
+ *      the pre-softmax logits of two rows only: the first draft token and the
+ *      bonus token.
+ *        Vegas (gist.science 2602.07223), section 2 "core mechanism", step 1
+ *        (the verify pass computes the logits of every KV entry);
+ *        "B. Collect-2-Query" (collect the first draft and the bonus token);
+ *        section 3 "implementation" (logits before softmax normalisation are
+ *        written to HBM).
+ *   2. vgsa_aggregate_scores  one importance score per KV position: the sum of
+ *      those logits over the collected rows and all query heads.
+ *        Vegas, "A. aggregated attention-logit selection" (the summand of the
+ *        argmax over subsets of size k).
+ *   3. vgsa_select_topk  the k positions kept for the next step: a few
+ *      attention-sink prefix positions and a recent window are always kept,
+ *      the rest of the budget goes to the highest scores.
+ *        Vegas "A." (argmax of the summed logits; it is separable, so it is a
+ *        top-k of per-position sums); Dustin (gist.science 2606.24957),
+ *        "1. hybrid attention aggregation" (sinks and local window protected,
+ *        remaining budget by score).
+ *   4. vgsa_sparse_attention  attention over only the selected positions, an
+ *      index list used as a page-size-1 page table.
+ *        Vegas section 2 step 3 (drafting with the selected entries) and
+ *        section 3 (page size 1, selected token indices as page indices);
+ *        Dustin "3. verification workflow" (verify on the compressed cache).
+ *
+ * Conventions
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream).  Nothing synchronises with the host.
+ *   - Arguments are checked on the host before anything is launched; a failed
+ *     check returns VGSA_ERR_INVALID_ARG / VGSA_ERR_UNSUPPORTED /
+ *     VGSA_ERR_WORKSPACE and launches nothing.  A failed launch returns
+ *     VGSA_ERR_HIP.  Faults during execution surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - Device-side values (seq_lens, n_idx, idx, block_table) are preconditions:
+ *     q_len <= seq_lens[b] <= max_ctx; idx[b][0:n_idx[b]] ascending, distinct
+ *     and < seq_lens[b]; n_idx[b] <= idx_stride; block ids < num_blocks.  The
+ *     kernels clamp them into range so a violation gives wrong numbers, never
+ *     an out-of-bounds access.
+ *   - Row-major layouts.  GQA: q-head h reads kv-head h / (Hq / Hkv).
+ *   - No global mutable state; calls are reentrant.  Calls that share a
+ *     workspace must be ordered on one stream.
+ *   - Causality: seq_lens[b] = L counts every cached position including the
+ *     T query tokens' own K/V.  Query row t sits at absolute position L-T+t and
+ *     sees positions j <= L-T+t.  The same rule applies to the absolute
+ *     positions of an index list.
+ */
+#ifndef VGSA_H
+#define VGSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vgsa_status {
+  VGSA_OK = 0,
+  VGSA_ERR_INVALID_ARG = 1, /* a scalar, shape or pointer is invalid         */
+  VGSA_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels implement */
+  VGSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  VGSA_ERR_HIP = 4          /* a HIP launch failed                           */
+} vgsa_status;
+
+/* Layout of the collected pre-softmax logits written by the verify pass. */
+typedef enum vgsa_logit_layout {
+  VGSA_LOGITS_NONE = 0,        /* no logits are written                           */
+  VGSA_LOGITS_PER_HEAD = 1,    /* fp32 [B][2][Hq][max_ctx]; [b][c][h][j] is row c */
+  VGSA_LOGITS_KVGROUP_SUM = 2  /* fp32 [B][Hkv][max_ctx]: sum over the 2 rows and
+                                  the q-heads of kv-head g (same total as PER_HEAD
+                                  summed, 2*G times fewer bytes)                  */
+} vgsa_logit_layout;
+
+/* Shape of one attention call.  The KV cache is either contiguous,
+ * K/V [B][Hkv][max_ctx][head_dim] bf16, or a paged pool of 16-position blocks,
+ * K/V [num_blocks][Hkv][16][head_dim] bf16 addressed through
+ * block_table[B][max_blocks_per_seq] (int32 block ids). */
+typedef struct vgsa_attn_desc {
+  int32_t batch;              /* B >= 0                                          */
+  int32_t num_q_heads;        /* Hq >= 1, a multiple of num_kv_heads             */
+  int32_t num_kv_heads;       /* Hkv >= 1                                        */
+  int32_t head_dim;           /* 64 or 128                                       */
+  int32_t q_len;              /* T query rows per sequence, 1..16;
+                                 (Hq/Hkv) * T <= 64                              */
+  int32_t max_ctx;            /* logical positions per sequence (row capacity)   */
+  int32_t block_size;         /* 0: contiguous cache; 16: paged pool             */
+  int32_t max_blocks_per_seq; /* paged: block_table row stride, with
+                                 max_ctx <= 16 * max_blocks_per_seq              */
+  int32_t num_blocks;         /* paged: blocks in the pool                       */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(head_dim)                   */
+} vgsa_attn_desc;
+
+/* Human-readable name of a status code (static string). */
+const char* vgsa_status_string(vgsa_status status);
+
+/* Library version string (static). */
+const char* vgsa_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Split plan.  Attention over a span of positions (max_ctx for verify,
+ * idx_stride for sparse) is split into num_splits chunks of `chunk`
+ * positions, one workgroup per (chunk, kv-head, sequence); the partial
+ * results are merged by an exact log-sum-exp combine.  Returns
+ * VGSA_ERR_INVALID_ARG on a bad desc or span. */
+vgsa_status vgsa_split_plan(const vgsa_attn_desc* desc, int32_t span, int32_t* num_splits,
+                            int32_t* chunk);
+
+/* Workspace bytes needed by vgsa_verify_attention / vgsa_verify_partials for
+ * this desc (partial outputs of every split).  0 on an invalid desc. */
+size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc);
+
+/* Workspace bytes needed by vgsa_sparse_attention / vgsa_sparse_partials. */
+size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_stride);
+
+/* ------------------------------------------------------------------------ */
+/* 1. Verify pass: full attention of the T rows, with the Collect-2-Query
+ *    logit epilogue.
+ *    (Vegas, section 2 step 1; "B. Collect-2-Query"; section 3.)
+ *
+ * q            bf16 [B][Hq][T][d]
+ * k_cache,
+ * v_cache      bf16, contiguous or paged (see vgsa_attn_desc)
+ * block_table  int32 [B][max_blocks_per_seq]; NULL iff block_size == 0
+ * seq_lens     int32 [B]; L_b includes the T verify tokens
+ * collect_row0,
+ * collect_row1 the two rows whose logits are written, 0 <= r0 < r1 < T
+ *              (the first draft token's row 0 and the bonus row gamma); ignored
+ *              when layout == VGSA_LOGITS_NONE
+ * logits       fp32 in `layout`; NULL iff layout == NONE.  Written for
+ *              positions j < L_b only: scale * q.k for visible positions,
+ *              -inf where the row may not see j.  Entries j >= L_b untouched.
+ * out          bf16 [B][Hq][T][d]: softmax(scale * q K^T) V
+ * lse          fp32 [B][Hq][T] natural-log sum-exp of the scaled logits, or NULL
+ * workspace    >= vgsa_verify_workspace_bytes(desc) bytes of device memory;
+ *              contents on entry do not matter.
+ */
+vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t collect_row0,
+                                  int32_t collect_row1, vgsa_logit_layout layout, float* logits,
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* 2. Aggregate collected logits into one score per position.
+ *    (Vegas, "A. aggregated attention-logit selection": the sum over draft
+ *    rows t and heads h of l_ti^(h).)
+ * logits   fp32 in `layout` (PER_HEAD or KVGROUP_SUM) as written by step 1
+ * scores   fp32 [B][max_ctx]; scores[b][j] for j < L_b is the sum, in a fixed
+ *          order, over the collected rows and all q-heads (or over kv-groups).
+ *          Entries j >= L_b untouched.
+ */
+vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t max_ctx, vgsa_logit_layout layout, const float* logits,
+                                  const int32_t* seq_lens, float* scores, void* stream);
+
+/* 3. Select the positions kept for the next step.
+ *    (Vegas "A." argmax over |T| = k; Dustin "1." protected sinks and window.)
+ * scores    fp32 [B][max_ctx]
+ * k         budget >= 1, including sinks and window; n_sink + window <= k
+ * n_sink    leading positions always kept
+ * window    trailing positions always kept
+ * idx       int32 [B][idx_stride], idx_stride >= k.  Row b receives, in
+ *           ascending order, F = [0, min(n_sink, L)) U [max(0, L-window), L)
+ *           plus the k - |F| other positions of highest score (lower position
+ *           first among equal scores; -0.0 equals +0.0); every position when
+ *           k >= L.
+ * n_idx     int32 [B]: min(k, L_b)
+ */
+vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
+                             const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
+                             int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream);
+
+/* 4. Sparse attention over an index list (page size 1).
+ *    (Vegas section 2 step 3 and section 3; Dustin "3.")
+ * desc->q_len is T' (1 for a draft step, gamma + 1 for a sparse verify).
+ * idx, n_idx, idx_stride  as written by vgsa_select_topk (a caller may append
+ *          positions, e.g. freshly drafted tokens, keeping the row ascending)
+ * seq_lens L'_b for the causal rule: row t sees listed j <= L'_b - T' + t.
+ *          A row that sees no listed position gets out = 0, lse = -inf.
+ * Other arguments as in vgsa_verify_attention.
+ */
+vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const int32_t* idx,
+                                  const int32_t* n_idx, int32_t idx_stride, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Two-phase form of steps 1 and 4, for callers that time or schedule the
+ * phases separately.  vgsa_verify_attention == vgsa_verify_partials followed
+ * by vgsa_combine_partials(span = max_ctx, lengths = seq_lens);
+ * vgsa_sparse_attention == vgsa_sparse_partials followed by
+ * vgsa_combine_partials(span = idx_stride, lengths = n_idx).
+ * The partials live in the workspace between the two calls. */
+vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t collect_row0,
+                                 int32_t collect_row1, vgsa_logit_layout layout, float* logits,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* idx,
+                                 const int32_t* n_idx, int32_t idx_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Merge the split partials (exact log-sum-exp combine) into out / lse.
+ * lengths: seq_lens (verify) or n_idx (sparse): chunks at or past a
+ * sequence's length hold nothing and are skipped. */
+vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
+                                  const int32_t* lengths, const void* workspace,
+                                  size_t workspace_bytes, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VGSA_H */

@@ -1,0 +1,297 @@
+// C ABI of the library: argument validation on the host, split planning and
+// kernel launches.  Validation is pure host code and runs before any HIP call,
+// so a rejected call touches neither the device nor the stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace vgsa {
+
+namespace {
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+vgsa_status check_desc(const vgsa_attn_desc* d) {
+  if (d == nullptr) return VGSA_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1) return VGSA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return VGSA_ERR_INVALID_ARG;
+  if (d->head_dim < 1 || d->q_len < 1 || d->max_ctx < 1) return VGSA_ERR_INVALID_ARG;
+  if (!isfinite(d->softmax_scale)) return VGSA_ERR_INVALID_ARG;
+  if (d->block_size < 0) return VGSA_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return VGSA_ERR_UNSUPPORTED;
+  if (d->q_len > 16) return VGSA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)(d->num_q_heads / d->num_kv_heads) * d->q_len;
+  if (rows > kMaxRows) return VGSA_ERR_UNSUPPORTED;
+  if (d->batch > kMaxGridYZ || d->num_kv_heads > kMaxGridYZ) return VGSA_ERR_UNSUPPORTED;
+  if (d->block_size == 16) {
+    if (d->max_blocks_per_seq < 1 || d->num_blocks < 1) return VGSA_ERR_INVALID_ARG;
+    if ((int64_t)d->max_ctx > (int64_t)16 * d->max_blocks_per_seq) return VGSA_ERR_INVALID_ARG;
+  } else if (d->block_size != 0) {
+    return VGSA_ERR_UNSUPPORTED;
+  }
+  return VGSA_OK;
+}
+
+float effective_scale(const vgsa_attn_desc& d) {
+  return d.softmax_scale > 0.f ? d.softmax_scale : 1.0f / sqrtf((float)d.head_dim);
+}
+
+struct Carve {
+  float* part_o;
+  float* part_ml;
+};
+
+Carve carve(const vgsa_attn_desc& d, const SplitPlan& p, void* ws) {
+  const size_t o_bytes = (size_t)d.batch * d.num_q_heads * d.q_len * p.num_splits * d.head_dim * 4;
+  const size_t o_aligned = (o_bytes + 255) / 256 * 256;
+  Carve c;
+  c.part_o = static_cast<float*>(ws);
+  c.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + o_aligned);
+  return c;
+}
+
+vgsa_status hip_status(hipError_t e) { return e == hipSuccess ? VGSA_OK : VGSA_ERR_HIP; }
+
+AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, const void* k,
+                   const void* v, const int32_t* block_table, const int32_t* seq_lens,
+                   void* workspace) {
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.batch = d.batch;
+  a.hq = d.num_q_heads;
+  a.hkv = d.num_kv_heads;
+  a.group = d.num_q_heads / d.num_kv_heads;
+  a.q_len = d.q_len;
+  a.head_dim = d.head_dim;
+  a.max_ctx = d.max_ctx;
+  a.paged = d.block_size == 16 ? 1 : 0;
+  a.max_blocks = d.max_blocks_per_seq;
+  a.num_blocks = d.num_blocks;
+  a.num_splits = p.num_splits;
+  a.chunk = p.chunk;
+  a.scale = effective_scale(d);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  const Carve c = carve(d, p, workspace);
+  a.part_o = c.part_o;
+  a.part_ml = c.part_ml;
+  a.layout = VGSA_LOGITS_NONE;
+  a.row0 = a.row1 = -1;
+  return a;
+}
+
+vgsa_status check_attn_pointers(const vgsa_attn_desc& d, const void* q, const void* k,
+                                const void* v, const int32_t* block_table,
+                                const int32_t* seq_lens) {
+  if (q == nullptr || k == nullptr || v == nullptr || seq_lens == nullptr)
+    return VGSA_ERR_INVALID_ARG;
+  if ((d.block_size == 16) != (block_table != nullptr)) return VGSA_ERR_INVALID_ARG;
+  return VGSA_OK;
+}
+
+}  // namespace
+
+SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span) {
+  const int64_t bh = (int64_t)(batch > 0 ? batch : 1) * num_kv_heads;
+  const int64_t max_splits = ceil_div(span, kMinChunk) > 0 ? ceil_div(span, kMinChunk) : 1;
+  int64_t s = ceil_div(kTargetWorkgroups, bh);
+  if (s < 1) s = 1;
+  if (s > max_splits) s = max_splits;
+  int64_t chunk = ceil_div(ceil_div(span, s), kMinChunk) * kMinChunk;
+  s = ceil_div(span, chunk);
+  SplitPlan p;
+  p.num_splits = (int32_t)s;
+  p.chunk = (int32_t)chunk;
+  return p;
+}
+
+size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p) {
+  const size_t rows = (size_t)d.batch * d.num_q_heads * d.q_len * p.num_splits;
+  const size_t o_bytes = rows * d.head_dim * 4;
+  return (o_bytes + 255) / 256 * 256 + rows * 2 * 4;
+}
+
+}  // namespace vgsa
+
+using namespace vgsa;
+
+extern "C" {
+
+const char* vgsa_status_string(vgsa_status status) {
+  switch (status) {
+    case VGSA_OK: return "ok";
+    case VGSA_ERR_INVALID_ARG: return "invalid argument";
+    case VGSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VGSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case VGSA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* vgsa_version(void) { return "vgsa 0.1.0 gfx950"; }
+
+vgsa_status vgsa_split_plan(const vgsa_attn_desc* desc, int32_t span, int32_t* num_splits,
+                            int32_t* chunk) {
+  const vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  if (span < 1 || num_splits == nullptr || chunk == nullptr) return VGSA_ERR_INVALID_ARG;
+  const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, span);
+  *num_splits = p.num_splits;
+  *chunk = p.chunk;
+  return VGSA_OK;
+}
+
+size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc) {
+  if (check_desc(desc) != VGSA_OK) return 0;
+  return partial_bytes(*desc, make_plan(desc->batch, desc->num_kv_heads, desc->max_ctx));
+}
+
+size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_stride) {
+  if (check_desc(desc) != VGSA_OK || idx_stride < 1) return 0;
+  return partial_bytes(*desc, make_plan(desc->batch, desc->num_kv_heads, idx_stride));
+}
+
+vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t collect_row0,
+                                 int32_t collect_row1, vgsa_logit_layout layout, float* logits,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  const vgsa_attn_desc& d = *desc;
+  st = check_attn_pointers(d, q, k_cache, v_cache, block_table, seq_lens);
+  if (st != VGSA_OK) return st;
+  if (layout != VGSA_LOGITS_NONE && layout != VGSA_LOGITS_PER_HEAD &&
+      layout != VGSA_LOGITS_KVGROUP_SUM)
+    return VGSA_ERR_INVALID_ARG;
+  if (layout != VGSA_LOGITS_NONE) {
+    if (logits == nullptr) return VGSA_ERR_INVALID_ARG;
+    if (collect_row0 < 0 || collect_row1 >= d.q_len || collect_row0 >= collect_row1)
+      return VGSA_ERR_INVALID_ARG;
+  }
+  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
+  if (workspace == nullptr || workspace_bytes < partial_bytes(d, p)) return VGSA_ERR_WORKSPACE;
+  if (d.batch == 0) return VGSA_OK;
+  AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens, workspace);
+  a.layout = layout;
+  a.logits = layout == VGSA_LOGITS_NONE ? nullptr : logits;
+  a.row0 = collect_row0;
+  a.row1 = collect_row1;
+  return hip_status(launch_attention_partials(a, false, static_cast<hipStream_t>(stream)));
+}
+
+vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* idx,
+                                 const int32_t* n_idx, int32_t idx_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  const vgsa_attn_desc& d = *desc;
+  st = check_attn_pointers(d, q, k_cache, v_cache, block_table, seq_lens);
+  if (st != VGSA_OK) return st;
+  if (idx == nullptr || n_idx == nullptr || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
+  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, idx_stride);
+  if (workspace == nullptr || workspace_bytes < partial_bytes(d, p)) return VGSA_ERR_WORKSPACE;
+  if (d.batch == 0) return VGSA_OK;
+  AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens, workspace);
+  a.idx = idx;
+  a.n_idx = n_idx;
+  a.idx_stride = idx_stride;
+  return hip_status(launch_attention_partials(a, true, static_cast<hipStream_t>(stream)));
+}
+
+vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
+                                  const int32_t* lengths, const void* workspace,
+                                  size_t workspace_bytes, void* out, float* lse, void* stream) {
+  vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  const vgsa_attn_desc& d = *desc;
+  if (span < 1 || lengths == nullptr || out == nullptr) return VGSA_ERR_INVALID_ARG;
+  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, span);
+  if (workspace == nullptr || workspace_bytes < partial_bytes(d, p)) return VGSA_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)d.batch * d.num_q_heads * d.q_len;
+  if (rows > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
+  if (rows == 0) return VGSA_OK;
+  const Carve c = carve(d, p, const_cast<void*>(workspace));
+  CombineArgs a{};
+  a.part_o = c.part_o;
+  a.part_ml = c.part_ml;
+  a.lengths = lengths;
+  a.rows = (int32_t)rows;
+  a.rows_per_seq = d.num_q_heads * d.q_len;
+  a.head_dim = d.head_dim;
+  a.num_splits = p.num_splits;
+  a.chunk = p.chunk;
+  a.span = span;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return hip_status(launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t collect_row0,
+                                  int32_t collect_row1, vgsa_logit_layout layout, float* logits,
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  if (out == nullptr) return VGSA_ERR_INVALID_ARG;
+  st = vgsa_verify_partials(desc, q, k_cache, v_cache, block_table, seq_lens,
+                                        collect_row0, collect_row1, layout, logits, workspace,
+                                        workspace_bytes, stream);
+  if (st != VGSA_OK) return st;
+  return vgsa_combine_partials(desc, desc->max_ctx, seq_lens, workspace, workspace_bytes, out,
+                               lse, stream);
+}
+
+vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const int32_t* idx,
+                                  const int32_t* n_idx, int32_t idx_stride, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  if (out == nullptr) return VGSA_ERR_INVALID_ARG;
+  st = vgsa_sparse_partials(desc, q, k_cache, v_cache, block_table, seq_lens, idx,
+                                        n_idx, idx_stride, workspace, workspace_bytes, stream);
+  if (st != VGSA_OK) return st;
+  return vgsa_combine_partials(desc, idx_stride, n_idx, workspace, workspace_bytes, out, lse,
+                               stream);
+}
+
+vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t max_ctx, vgsa_logit_layout layout, const float* logits,
+                                  const int32_t* seq_lens, float* scores, void* stream) {
+  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_ctx < 1) return VGSA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return VGSA_ERR_INVALID_ARG;
+  if (layout != VGSA_LOGITS_PER_HEAD && layout != VGSA_LOGITS_KVGROUP_SUM)
+    return VGSA_ERR_INVALID_ARG;
+  if (logits == nullptr || seq_lens == nullptr || scores == nullptr) return VGSA_ERR_INVALID_ARG;
+  if (batch > kMaxGridYZ) return VGSA_ERR_UNSUPPORTED;
+  if (batch == 0) return VGSA_OK;
+  return hip_status(launch_aggregate(batch, num_q_heads, num_kv_heads, max_ctx, layout, logits,
+                                     seq_lens, scores, static_cast<hipStream_t>(stream)));
+}
+
+vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
+                             const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
+                             int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream) {
+  if (batch < 0 || max_ctx < 1 || k < 1 || n_sink < 0 || window < 0) return VGSA_ERR_INVALID_ARG;
+  if ((int64_t)n_sink + window > k) return VGSA_ERR_INVALID_ARG;
+  if (idx_stride < k) return VGSA_ERR_INVALID_ARG;
+  if (scores == nullptr || seq_lens == nullptr || idx == nullptr || n_idx == nullptr)
+    return VGSA_ERR_INVALID_ARG;
+  if (batch == 0) return VGSA_OK;
+  return hip_status(launch_select_topk(batch, max_ctx, scores, seq_lens, k, n_sink, window, idx,
+                                       idx_stride, n_idx, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal declarations shared by the HIP sources of the library (not part
+// of the C ABI).  Host-side launchers take already-validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "vgsa.h"
+
+namespace vgsa {
+
+// Positions one wavefront processes per step, waves per workgroup, and the
+// smallest chunk a workgroup is given (one step of every wave).
+constexpr int kTile = 32;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMinChunk = kTile * kWaves;
+// Workgroups aimed for per attention launch: 4 per CU on 256 CUs.
+constexpr int kTargetWorkgroups = 1024;
+// Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.
+constexpr int kMaxRows = 64;
+
+struct SplitPlan {
+  int32_t num_splits;
+  int32_t chunk;
+};
+
+SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span);
+
+// Partial results of one attention launch, carved out of the workspace:
+//   part_o  fp32 [B][Hq][T][S][d]   un-normalised sum of p * v of the split
+//   part_ml fp32 [B][Hq][T][S][2]   (running max m in log2 units, sum l)
+size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* idx;    // sparse only
+  const int32_t* n_idx;  // sparse only
+  int32_t idx_stride;
+  float* logits;         // verify only, may be null
+  int32_t layout;
+  int32_t row0, row1;
+  float* part_o;
+  float* part_ml;
+  int32_t batch, hq, hkv, group, q_len, head_dim;
+  int32_t max_ctx, paged, max_blocks, num_blocks;
+  int32_t num_splits, chunk;
+  float scale;       // natural-log softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+
+hipError_t launch_attention_partials(const AttnArgs& a, bool sparse, hipStream_t stream);
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* lengths;
+  int32_t rows;  // B * Hq * T
+  int32_t rows_per_seq;  // Hq * T
+  int32_t head_dim;
+  int32_t num_splits, chunk, span;
+  uint16_t* out;
+  float* lse;
+};
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t layout,
+                            const float* logits, const int32_t* seq_lens, float* scores,
+                            hipStream_t stream);
+
+hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
+                              const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
+                              int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                              hipStream_t stream);
+
+}  // namespace vgsa

@@ -68,6 +68,7 @@ class Workload:
     paged: bool = False
     layers: int = 1
     seed: int = 1
+    lens: Optional[Tuple[int, ...]] = None       # explicit per-sequence lengths (tests)
 
     # ---- derived sizes ----
     @property
@@ -84,6 +85,8 @@ class Workload:
         return (0, self.gamma)
 
     def max_len(self) -> int:
+        if self.lens is not None:
+            return max(self.lens)
         if self.ctx is not None:
             return self.ctx
         return self.ctx_range[1]
@@ -156,6 +159,8 @@ def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
 # ---------------------------------------------------------------- lengths
 def seq_lens(w: Workload) -> np.ndarray:
     """Verify-time context length per sequence (it counts the T verify tokens)."""
+    if w.lens is not None:
+        return np.asarray(w.lens, dtype=np.int32)
     if w.ctx is not None:
         return np.full(w.batch, w.ctx, dtype=np.int32)
     lo, hi = w.ctx_range
@@ -296,3 +301,19 @@ def small(name: str = "small", **kw) -> Workload:
                 sparse_verify=True, seed=7)
     base.update(kw)
     return Workload(name, **base)
+
+
+def index_lists(seed: int, lens, count: int, stride: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Seeded ascending index lists: for each sequence, min(count, L) distinct
+    positions drawn uniformly from [0, L), padded to `stride` with zeros.
+    Returns (idx int32 [B, stride], n_idx int32 [B])."""
+    rng = np.random.default_rng([seed, TAG_PLANT, 99])
+    B = len(lens)
+    idx = np.zeros((B, stride), dtype=np.int32)
+    n = np.zeros(B, dtype=np.int32)
+    for b, L in enumerate(lens):
+        m = min(count, int(L), stride)
+        pos = np.sort(rng.choice(int(L), size=m, replace=False)) if m > 0 else np.zeros(0, np.int64)
+        idx[b, :m] = pos
+        n[b] = m
+    return idx, n

@@ -1,0 +1,171 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+arguments on the host before anything is launched (no GPU needed: every call
+here fails validation, so no HIP call is reached)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_long_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vgsa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: each call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vgsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_attention_long_amd import build
+        build.build()
+    return B.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = declared_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.SIGNATURES)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (vgsa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_desc_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "vgsa.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu\\n\", sizeof(vgsa_attn_desc),"
+        " offsetof(vgsa_attn_desc, num_blocks), offsetof(vgsa_attn_desc, softmax_scale),"
+        " sizeof(vgsa_status));return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    size, off_nb, off_scale, st = map(int, subprocess.run([str(exe)], capture_output=True, text=True).stdout.split())
+    assert size == ctypes.sizeof(B.AttnDesc)
+    assert off_nb == B.AttnDesc.num_blocks.offset and off_scale == B.AttnDesc.softmax_scale.offset
+    assert st == 4
+
+
+def test_status_strings_and_version(lib):
+    assert B.status_string(0) == "ok"
+    assert "invalid" in B.status_string(1)
+    assert lib.vgsa_version().decode().startswith("vgsa")
+
+
+def desc(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, q_len=4, max_ctx=1000,
+                block_size=0, max_blocks_per_seq=0, num_blocks=0, softmax_scale=0.0)
+    base.update(kw)
+    return B.AttnDesc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), INVALID),
+    (dict(num_q_heads=0), INVALID),
+    (dict(num_kv_heads=0), INVALID),
+    (dict(num_q_heads=6, num_kv_heads=4), INVALID),
+    (dict(head_dim=0), INVALID),
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(q_len=0), INVALID),
+    (dict(q_len=17), UNSUPPORTED),
+    (dict(num_q_heads=64, num_kv_heads=4, q_len=5), UNSUPPORTED),  # 16 * 5 rows > 64
+    (dict(max_ctx=0), INVALID),
+    (dict(block_size=8), UNSUPPORTED),
+    (dict(block_size=-16), INVALID),
+    (dict(block_size=16, max_blocks_per_seq=0, num_blocks=4), INVALID),
+    (dict(block_size=16, max_blocks_per_seq=10, num_blocks=4, max_ctx=161), INVALID),
+    (dict(softmax_scale=float("nan")), INVALID),
+    (dict(batch=70000), UNSUPPORTED),
+])
+def test_bad_desc_rejected_everywhere(lib, kw, code):
+    d = ctypes.byref(desc(**kw))
+    assert lib.vgsa_verify_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 3, 2, FAKE, FAKE, None,
+                                     FAKE, 1 << 40, None) == code
+    assert lib.vgsa_sparse_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None,
+                                     FAKE, 1 << 40, None) == code
+    assert lib.vgsa_verify_workspace_bytes(d) == 0
+    s, c = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.vgsa_split_plan(d, 100, ctypes.byref(s), ctypes.byref(c)) == code
+
+
+def test_verify_argument_checks(lib):
+    d = desc()
+    dp = ctypes.byref(d)
+    ws = lib.vgsa_verify_workspace_bytes(dp)
+    assert ws > 0
+    V = lib.vgsa_verify_attention
+    # null q / cache / seq_lens / out
+    assert V(dp, None, FAKE, FAKE, None, FAKE, 0, 3, 0, None, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, None, 0, 3, 0, None, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 0, None, None, None, FAKE, ws, None) == INVALID
+    # block table given for a contiguous cache
+    assert V(dp, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 3, 0, None, FAKE, None, FAKE, ws, None) == INVALID
+    # logits requested but missing; collect rows out of range / equal / reversed; bad layout
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 1, None, FAKE, None, FAKE, ws, None) == INVALID
+    for r0, r1 in [(0, 4), (-1, 3), (2, 2), (3, 0)]:
+        assert V(dp, FAKE, FAKE, FAKE, None, FAKE, r0, r1, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 7, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    # workspace missing or one byte short
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, None, ws, None) == WORKSPACE
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
+    # paged cache without a block table
+    dpg = desc(block_size=16, max_blocks_per_seq=63, num_blocks=100, max_ctx=1000)
+    wsp = lib.vgsa_verify_workspace_bytes(ctypes.byref(dpg))
+    assert V(ctypes.byref(dpg), FAKE, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, FAKE, wsp,
+             None) == INVALID
+
+
+def test_sparse_and_combine_argument_checks(lib):
+    d = desc()
+    dp = ctypes.byref(d)
+    ws = lib.vgsa_sparse_workspace_bytes(dp, 64)
+    assert ws > 0 and lib.vgsa_sparse_workspace_bytes(dp, 0) == 0
+    S = lib.vgsa_sparse_attention
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 64, FAKE, None, FAKE, ws, None) == INVALID
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 64, FAKE, None, FAKE, ws, None) == INVALID
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, ws, None) == INVALID
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
+    C = lib.vgsa_combine_partials
+    assert C(dp, 0, FAKE, FAKE, ws, FAKE, None, None) == INVALID
+    assert C(dp, 64, None, FAKE, ws, FAKE, None, None) == INVALID
+    assert C(dp, 64, FAKE, FAKE, ws, None, None, None) == INVALID
+    assert C(dp, 64, FAKE, FAKE, ws - 1, FAKE, None, None) == WORKSPACE
+
+
+def test_aggregate_and_select_argument_checks(lib):
+    A = lib.vgsa_aggregate_scores
+    assert A(-1, 8, 2, 100, 2, FAKE, FAKE, FAKE, None) == INVALID
+    assert A(2, 6, 4, 100, 2, FAKE, FAKE, FAKE, None) == INVALID
+    assert A(2, 8, 2, 0, 2, FAKE, FAKE, FAKE, None) == INVALID
+    assert A(2, 8, 2, 100, 0, FAKE, FAKE, FAKE, None) == INVALID   # layout NONE has nothing to sum
+    assert A(2, 8, 2, 100, 2, None, FAKE, FAKE, None) == INVALID
+    assert A(0, 8, 2, 100, 2, FAKE, FAKE, FAKE, None) == OK        # empty batch: nothing launched
+    T = lib.vgsa_select_topk
+    assert T(2, 100, FAKE, FAKE, 0, 0, 0, FAKE, 8, FAKE, None) == INVALID     # k < 1
+    assert T(2, 100, FAKE, FAKE, 8, -1, 0, FAKE, 8, FAKE, None) == INVALID
+    assert T(2, 100, FAKE, FAKE, 8, 4, 5, FAKE, 8, FAKE, None) == INVALID     # sinks + window > k
+    assert T(2, 100, FAKE, FAKE, 8, 4, 4, FAKE, 7, FAKE, None) == INVALID     # idx_stride < k
+    assert T(2, 100, None, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == INVALID
+    assert T(2, 0, FAKE, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == INVALID
+    assert T(0, 100, FAKE, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == OK
+
+
+def test_split_plan_covers_span(lib):
+    for B_, Hkv, span in [(16, 8, 32768), (1, 8, 32768), (8, 8, 131078), (4, 8, 65536), (1, 1, 5),
+                          (16, 8, 512), (1, 8, 2049)]:
+        d = desc(batch=B_, num_kv_heads=Hkv, num_q_heads=Hkv, q_len=1, max_ctx=span)
+        s, c = B.split_plan(d, span)
+        assert s >= 1 and c % 128 == 0 and s * c >= span and (s - 1) * c < span
+    d = desc(batch=16, num_q_heads=64, num_kv_heads=8, q_len=5, max_ctx=32768)
+    assert B.split_plan(d, 32768) == (8, 4096)

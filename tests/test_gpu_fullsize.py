@@ -1,0 +1,109 @@
+"""GPU parity at the full workload sizes, on sampled outputs.
+
+Every workload runs the whole per-layer iteration on the GPU in the launch
+configuration the benchmark times (same descriptors, same split plans):
+verify with the kv-group-summed logit epilogue, aggregate, select, then the
+sparse pass (sparse verify over the T rows and/or single-query draft steps
+whose lists carry the freshly drafted positions).  The oracle checks:
+  * selection for every sequence, bit-exact on the GPU's own scores;
+  * outputs, lse, collected logits and scores on a sample of sequences
+    (first and last) and kv-heads (first and last), element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_long_amd import binding as Bn
+from sparse_attention_long_amd import workloads as W
+from tests.gpu_helpers import (assert_lse_close, assert_logits_close, assert_out_close, dev_bf16,
+                               dev_i32, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["ctx32k_b1_h32kv8_d128_draft4", "ctx32k_b16_h64kv8_d128", "ctx128k_b8_h32kv8_d128_draft6",
+        "ragged8k-64k_b4_h64kv8_d64_paged16_l24"]
+
+
+def sub(x, b):
+    return x[b:b + 1]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_sampled(name):
+    w = W.WORKLOADS[name]
+    layers = [0] if w.layers == 1 else [0, w.layers - 1]
+    for layer in layers:
+        say(f"[fullsize] {name} layer {layer}: generating")
+        x = W.make_layer(w, layer)
+        d = to_device(x)
+        say(f"[fullsize] {name} layer {layer}: gpu iteration")
+        out, lse, lg = Bn.verify_attention(d.q, d.k, d.v, d.seq_lens, block_table=d.block_table,
+                                           max_ctx=d.max_ctx, collect_rows=w.collect_rows,
+                                           layout="kvgroup_sum")
+        scores = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads)
+        stride = w.budget + w.draft_steps
+        idx, n_idx = Bn.select_topk(scores, d.seq_lens, w.budget, w.n_sink, w.window,
+                                    idx_stride=stride)
+        torch.cuda.synchronize()
+        sc = scores.cpu().numpy()
+        lens = [int(L) for L in x.seq_lens]
+        say(f"[fullsize] {name} layer {layer}: oracle selection")
+        want = oracle.select_topk_batch(sc, lens, w.budget, w.n_sink, w.window)
+        idx_h, n_h = idx.cpu().numpy(), n_idx.cpu().numpy()
+        for b in range(w.batch):
+            assert n_h[b] == len(want[b])
+            assert np.array_equal(idx_h[b, :n_h[b]], want[b]), f"{name} idx b={b}"
+            assert set(x.planted[b].tolist()) <= set(want[b].tolist()), f"planted key dropped b={b}"
+
+        bs = sorted({0, w.batch - 1})
+        gs = sorted({0, w.num_kv_heads - 1})
+        G = w.group
+        heads = [h for g in gs for h in range(g * G, (g + 1) * G)]
+        lg_h = lg.cpu().numpy()
+        for b in bs:
+            say(f"[fullsize] {name} layer {layer}: oracle b={b}")
+            qb, kb, vb = sub(x.q, b), sub(x.k, b), sub(x.v, b)
+            o_ref, lse_ref = oracle.verify_attention(qb, kb, vb, lens[b:b + 1], heads=heads)
+            assert_out_close(out[b:b + 1, heads], o_ref[:, heads], f"{name} b={b} verify out")
+            assert_lse_close(lse[b:b + 1, heads], lse_ref[:, heads], f"{name} b={b} verify lse")
+            l_ref = oracle.collected_logits(qb, kb, lens[b:b + 1], w.collect_rows)
+            absl = np.where(np.isneginf(l_ref), 0.0, np.abs(l_ref))
+            grp = oracle.kvgroup_sum(l_ref, w.num_kv_heads)
+            assert_logits_close(lg_h[b:b + 1], grp, f"{name} b={b} group logits",
+                                floor=oracle.kvgroup_sum(absl, w.num_kv_heads))
+            assert_logits_close(sc[b:b + 1], oracle.aggregate_scores(l_ref), f"{name} b={b} scores",
+                                floor=oracle.aggregate_scores(absl))
+
+        if w.sparse_verify:
+            say(f"[fullsize] {name} layer {layer}: sparse verify")
+            so, sl = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n_idx,
+                                         block_table=d.block_table, max_ctx=d.max_ctx)
+            torch.cuda.synchronize()
+            for b in bs:
+                o_ref, lse_ref = oracle.sparse_attention(sub(x.q, b), sub(x.k, b), sub(x.v, b),
+                                                         lens[b:b + 1], [want[b]], heads=heads)
+                assert_out_close(so[b:b + 1, heads], o_ref[:, heads], f"{name} b={b} sparse out")
+                assert_lse_close(sl[b:b + 1, heads], lse_ref[:, heads], f"{name} b={b} sparse lse")
+
+        for s in range(1, w.draft_steps + 1):
+            say(f"[fullsize] {name} layer {layer}: draft step {s}")
+            # step s: s freshly drafted positions L..L+s-1 are appended to the list
+            lists = [np.concatenate([want[b], np.arange(lens[b], lens[b] + s)]) for b in range(w.batch)]
+            idx_s = np.zeros((w.batch, stride), np.int32)
+            for b, li in enumerate(lists):
+                idx_s[b, :len(li)] = li
+            n_s = np.array([len(li) for li in lists], np.int32)
+            lens_s = [L + s for L in lens]
+            qd = dev_bf16(x.q_draft[s - 1])
+            so, sl = Bn.sparse_attention(qd, d.k, d.v, dev_i32(lens_s), dev_i32(idx_s), dev_i32(n_s),
+                                         block_table=d.block_table, max_ctx=d.max_ctx)
+            torch.cuda.synchronize()
+            for b in bs:
+                o_ref, lse_ref = oracle.sparse_attention(sub(x.q_draft[s - 1], b), sub(x.k, b),
+                                                         sub(x.v, b), lens_s[b:b + 1], [lists[b]],
+                                                         heads=heads)
+                assert_out_close(so[b:b + 1, heads], o_ref[:, heads], f"{name} b={b} draft {s}")
+                assert_lse_close(sl[b:b + 1, heads], lse_ref[:, heads], f"{name} b={b} draft {s} lse")
+        del d
+        torch.cuda.empty_cache()

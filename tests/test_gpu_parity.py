@@ -1,0 +1,211 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes here run the oracle in seconds but span several 32-position tiles,
+several splits, ragged tails, every MFMA row-block count (1-4 blocks of 16
+query rows), both head dims, contiguous and paged caches.  Full-size
+workloads are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_long_amd import binding as Bn
+from sparse_attention_long_amd import workloads as W
+from tests.gpu_helpers import (assert_lse_close, assert_logits_close, assert_out_close, dev_i32,
+                               say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: workload (G*T query rows -> MFMA row blocks)
+    "g4t4_d128_ragged": W.small("g4t4", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                gamma=3, lens=(301, 4, 128), budget=40, n_sink=4, window=8),
+    "g4t5_d64": W.small("g4t5", batch=2, num_q_heads=16, num_kv_heads=4, head_dim=64, gamma=4,
+                        lens=(33, 257), budget=24, n_sink=2, window=6, seed=11),
+    "g8t5_d128": W.small("g8t5", batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128, gamma=4,
+                         lens=(700, 129), budget=64, n_sink=4, window=16, seed=12),
+    "g8t8_d64": W.small("g8t8", batch=1, num_q_heads=32, num_kv_heads=4, head_dim=64, gamma=7,
+                        lens=(513,), budget=100, n_sink=4, window=32, seed=13),
+    "g1t2_d128": W.small("g1t2", batch=2, num_q_heads=4, num_kv_heads=4, head_dim=128, gamma=1,
+                         lens=(1000, 2), budget=50, n_sink=1, window=3, seed=14),
+    "paged_g8t6_d64": W.small("pg", batch=3, num_q_heads=16, num_kv_heads=2, head_dim=64, gamma=5,
+                              ctx=None, ctx_range=(40, 300), paged=True, budget=48, n_sink=4,
+                              window=12, seed=15),
+    "ctx2k_b1_h32kv8_d128": W.WORKLOADS["ctx2k_b1_h32kv8_d128"],
+}
+
+
+def run_verify(d, w, layout):
+    return Bn.verify_attention(d.q, d.k, d.v, d.seq_lens, block_table=d.block_table,
+                               max_ctx=d.max_ctx, collect_rows=w.collect_rows, layout=layout)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_verify_logits_scores_select_sparse(name):
+    w = CASES[name]
+    say(f"[verify pipeline] {name}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    o_ref, lse_ref = oracle.verify_attention(x.q, x.k, x.v, x.seq_lens)
+    l_ref = oracle.collected_logits(x.q, x.k, x.seq_lens, w.collect_rows)
+    absl = np.where(np.isneginf(l_ref), 0.0, np.abs(l_ref))
+    for layout in ("per_head", "kvgroup_sum"):
+        out, lse, logits = run_verify(d, w, layout)
+        torch.cuda.synchronize()
+        assert_out_close(out, o_ref, f"{name}/{layout} out")
+        assert_lse_close(lse, lse_ref, f"{name}/{layout} lse")
+        lg = logits.cpu().numpy()
+        if layout == "per_head":
+            assert_logits_close(lg, l_ref, f"{name} per-head logits")
+            s_floor = oracle.aggregate_scores(absl)
+        else:
+            assert_logits_close(lg, oracle.kvgroup_sum(l_ref, w.num_kv_heads), f"{name} group logits",
+                                floor=oracle.kvgroup_sum(absl, w.num_kv_heads))
+            s_floor = oracle.aggregate_scores(absl)
+        scores = Bn.aggregate_scores(logits, d.seq_lens, w.num_q_heads, w.num_kv_heads, layout=layout)
+        torch.cuda.synchronize()
+        s_ref = oracle.aggregate_scores(l_ref)
+        assert_logits_close(scores.cpu().numpy(), s_ref, f"{name}/{layout} scores", floor=s_floor)
+
+        # selection: bit-exact against the oracle run on the GPU's own scores
+        sc = scores.cpu().numpy()
+        idx, n_idx = Bn.select_topk(scores, d.seq_lens, w.budget, w.n_sink, w.window,
+                                    idx_stride=w.budget + 3)
+        torch.cuda.synchronize()
+        idx_h, n_h = idx.cpu().numpy(), n_idx.cpu().numpy()
+        want = oracle.select_topk_batch(sc, x.seq_lens, w.budget, w.n_sink, w.window)
+        for b in range(w.batch):
+            assert n_h[b] == len(want[b])
+            assert np.array_equal(idx_h[b, :n_h[b]], want[b]), f"{name}/{layout} idx b={b}"
+        for b, pos in enumerate(x.planted):
+            if w.budget < int(x.seq_lens[b]):
+                assert set(pos.tolist()) <= set(want[b].tolist()), f"planted key dropped b={b}"
+
+    # sparse verify over the selected positions (same T rows)
+    out_s, lse_s = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n_idx,
+                                       block_table=d.block_table, max_ctx=d.max_ctx)
+    torch.cuda.synchronize()
+    so_ref, slse_ref = oracle.sparse_attention(x.q, x.k, x.v, x.seq_lens, want)
+    assert_out_close(out_s, so_ref, f"{name} sparse out")
+    assert_lse_close(lse_s, slse_ref, f"{name} sparse lse")
+
+
+@pytest.mark.parametrize("name", ["g4t5_d64", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])
+def test_sparse_random_lists_and_draft_step(name):
+    """Index lists from the seeded generator; T' = 1 draft query at the newest position."""
+    w = CASES[name]
+    say(f"[sparse lists] {name}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    lens = x.seq_lens
+    idx, n = W.index_lists(w.seed, lens, count=max(1, w.budget // 2), stride=w.budget)
+    out, lse = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, dev_i32(idx), dev_i32(n),
+                                   block_table=d.block_table, max_ctx=d.max_ctx)
+    torch.cuda.synchronize()
+    lists = [idx[b, :n[b]] for b in range(w.batch)]
+    o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, lens, lists)
+    assert_out_close(out, o_ref, f"{name} sparse lists")
+    assert_lse_close(lse, lse_ref, f"{name} sparse lists lse")
+    # one query row (a draft step): q = last verify row
+    q1 = d.q[:, :, -1:, :].contiguous()
+    out1, lse1 = Bn.sparse_attention(q1, d.k, d.v, d.seq_lens, dev_i32(idx), dev_i32(n),
+                                     block_table=d.block_table, max_ctx=d.max_ctx)
+    torch.cuda.synchronize()
+    o1_ref, l1_ref = oracle.sparse_attention(x.q[:, :, -1:, :], x.k, x.v, lens, lists)
+    assert_out_close(out1, o1_ref, f"{name} sparse T'=1")
+    assert_lse_close(lse1, l1_ref, f"{name} sparse T'=1 lse")
+
+
+def test_sparse_degenerate_lists():
+    """Empty list, one listed position, and rows that see no listed position."""
+    w = CASES["g4t4_d128_ragged"]
+    x = W.make_layer(w)
+    d = to_device(x)
+    lens = [int(L) for L in x.seq_lens]
+    T = w.q_len
+    lists = [np.zeros(0, np.int64), np.array([lens[1] - 1]), np.array([5, lens[2] - 1])]
+    stride = 4
+    idx = np.zeros((3, stride), np.int32)
+    n = np.array([len(li) for li in lists], np.int32)
+    for b, li in enumerate(lists):
+        idx[b, :len(li)] = li
+    out, lse = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, dev_i32(idx), dev_i32(n))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, lens, lists)
+    assert_out_close(out, o_ref, "degenerate sparse")
+    assert_lse_close(lse, lse_ref, "degenerate sparse lse")
+    lh = lse.cpu().numpy()
+    assert np.all(np.isneginf(lh[0])) and np.all(out[0].float().cpu().numpy() == 0)
+    assert np.all(np.isneginf(lh[1, :, :T - 1]))  # rows before the last cannot see L-1
+
+
+def test_verify_no_logits_and_explicit_scale():
+    w = CASES["g8t5_d128"]
+    x = W.make_layer(w)
+    d = to_device(x)
+    out, lse, logits = Bn.verify_attention(d.q, d.k, d.v, d.seq_lens, layout="none", scale=0.05)
+    torch.cuda.synchronize()
+    assert logits is None
+    o_ref, lse_ref = oracle.verify_attention(x.q, x.k, x.v, x.seq_lens, scale=0.05)
+    assert_out_close(out, o_ref, "scale=0.05")
+    assert_lse_close(lse, lse_ref, "scale=0.05 lse")
+
+
+# ------------------------------------------------------------------ selection stress
+def _select_case(scores_h, lens, k, n_sink, window, stride=None):
+    scores = torch.from_numpy(np.ascontiguousarray(scores_h, dtype=np.float32)).cuda()
+    idx, n = Bn.select_topk(scores, dev_i32(lens), k, n_sink, window, idx_stride=stride or k)
+    torch.cuda.synchronize()
+    idx_h, n_h = idx.cpu().numpy(), n.cpu().numpy()
+    for b, L in enumerate(lens):
+        want = oracle.select_topk(scores_h[b], int(L), k, n_sink, window)
+        assert n_h[b] == len(want), (b, L, k, n_h[b], len(want))
+        assert np.array_equal(idx_h[b, :n_h[b]], want), (b, L, k, n_sink, window)
+
+
+@pytest.mark.parametrize("L", [1, 2, 7, 64, 100, 1000, 4095, 4096, 4097, 32768, 40000, 131072])
+def test_select_random_scores(L):
+    rng = np.random.default_rng(L)
+    lens = [L, max(1, L // 3), max(1, L - 1)]
+    ctx = L + 5
+    sc = rng.standard_normal((3, ctx)).astype(np.float32) * 10
+    for k, ns, win in [(1, 0, 0), (16, 4, 8), (512, 4, 64), (6554, 4, 256), (L, 0, 0)]:
+        if k < 1 or ns + win > k:
+            continue
+        _select_case(sc, lens, k, ns, win)
+
+
+def test_select_ties_zeros_and_infinities():
+    rng = np.random.default_rng(5)
+    ctx = 5000
+    sc = rng.integers(-3, 4, size=(4, ctx)).astype(np.float32)     # heavy ties
+    sc[1] = np.where(rng.random(ctx) < 0.5, 0.0, -0.0).astype(np.float32)  # only +-0
+    sc[2, ::3] = -np.inf
+    sc[3] = 1.0                                                    # all equal
+    lens = [5000, 4000, 4999, 3000]
+    for k, ns, win in [(7, 0, 0), (100, 4, 16), (1000, 10, 990), (1000, 0, 1000), (2500, 3, 5)]:
+        _select_case(sc, lens, k, ns, win, stride=k + 7)
+    # -inf must rank below every finite score
+    sc2 = np.full((1, 64), -np.inf, np.float32)
+    sc2[0, 10] = -1e30
+    _select_case(sc2, [64], 1, 0, 0)
+
+
+def test_determinism_bitwise():
+    w = CASES["g8t5_d128"]
+    x = W.make_layer(w)
+    d = to_device(x)
+    runs = []
+    for _ in range(2):
+        out, lse, lg = run_verify(d, w, "kvgroup_sum")
+        sc = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads)
+        idx, n = Bn.select_topk(sc, d.seq_lens, w.budget, w.n_sink, w.window)
+        so, sl = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n)
+        torch.cuda.synchronize()
+        L = x.seq_lens
+        lgv = np.concatenate([lg[b, :, :L[b]].cpu().numpy().ravel() for b in range(w.batch)])
+        runs.append([out.view(torch.int16).cpu().numpy(), lse.cpu().numpy(), lgv,
+                     idx.cpu().numpy(), so.view(torch.int16).cpu().numpy(), sl.cpu().numpy()])
+    for a, b in zip(*runs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
