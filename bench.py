@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain fp32 copy of this many MiB three times (a kernel of "
+                         "known traffic, for scaling HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -132,6 +135,15 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     Bn.load()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {args.copy_calibration_mib} MiB read + written")
+        del src, dst
 
     log(f"[bench] generating {name}")
     t0 = time.perf_counter()

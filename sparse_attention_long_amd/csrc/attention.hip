@@ -34,6 +34,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -54,15 +57,35 @@ __device__ __forceinline__ size_t kv_row(const AttnArgs& a, int b, int g, int po
   return (((size_t)b * a.hkv + g) * a.max_ctx + pos) * D;
 }
 
-// D: head dim (64/128); QB: 16-row query blocks (G*T <= 16*QB); SPARSE: index list.
-template <int D, int QB, bool SPARSE>
-__global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
+// Waves per SIMD the register budget is sized for: two (<= 256 registers per
+// wave) unless four query blocks of d = 128 need more.
+template <int D, int QB>
+struct Occupancy {
+  static constexpr int kWavesPerEU = (D == 128 && QB == 4) ? 1 : 2;
+};
+
+// Lazy rescaling: a row's running max is only raised (and O, l rescaled)
+// when a tile exceeds it by more than 2^kRescaleLog2; otherwise the stale max
+// is kept, so p <= 2^kRescaleLog2.  The combine uses the same (m, l, O)
+// triple, so the result is exact.
+constexpr float kRescaleLog2 = 8.0f;
+
+// D: head dim (64/128); QB: 16-row query blocks (G*T <= 16*QB); SPARSE: index
+// list; EMIT: logit layout written by the verify pass (VGSA_LOGITS_*).
+template <int D, int QB, bool SPARSE, int EMIT>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Occupancy<D, QB>::kWavesPerEU, Occupancy<D, QB>::kWavesPerEU)))
+void attn_partials_kernel(AttnArgs a) {
   constexpr int KS = D / 32;       // MFMA steps over the head dimension
   constexpr int DB = D / 16;       // 16-wide blocks of the head dimension
-  constexpr int VS = D + 4;        // padded LDS row, in elements (breaks bank aliasing)
-  // V tiles of the four wavefronts; reused at the end as the fp32 merge
-  // buffer [64][D + 4] (both are 256 * (D + 4) bytes).
+  constexpr int VS = D + 16;       // V tile row stride (elements): rows land 32 B apart in the banks
+  constexpr int OS = D + 4;        // merge-buffer row stride (floats)
+  static_assert(kWaves * kTile * VS * 2 >= kMaxRows * OS * 4, "merge buffer must fit in the V tiles");
+  // V tiles of the four wavefronts, [position][d]; reused at the end as the
+  // fp32 merge buffer [64][D + 4].
   __shared__ __align__(16) uint16_t sbuf[kWaves * kTile * VS];
+  // Query fragments, already in MFMA operand order: [qb][ks][lane] x 16 B.
+  __shared__ __align__(16) u32x4 sq[QB * KS * 64];
   __shared__ float s_m[kWaves][kMaxRows];
   __shared__ float s_l[kWaves][kMaxRows];
   __shared__ int s_idx[kWaves][kTile];
@@ -78,9 +101,21 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
   const int end = min(start + a.chunk, count);
   const int G = a.group, T = a.q_len, rows = G * T;
 
-  // Query fragments: B operand of S^T = K Q^T; lane column c16 of block qb is
-  // query row m = qb*16 + c16 = (head-in-group, t).
-  bf16x8 qf[QB][KS];
+  // Stage the query fragments (B operand of S^T = K Q^T): fragment
+  // (qb, ks, lane) holds row m = qb*16 + lane%16, d = ks*32 + (lane/16)*8 .. +8.
+  for (int f = threadIdx.x; f < QB * KS * 64; f += kThreads) {
+    const int fl = f & 63, fks = (f >> 6) % KS, fqb = (f >> 6) / KS;
+    const int m = fqb * 16 + (fl & 15);
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (m < rows) {
+      const int h = g * G + m / T, t = m % T;
+      val = *reinterpret_cast<const u32x4*>(a.q + (((size_t)b * a.hq + h) * T + t) * D +
+                                            fks * 32 + (fl >> 4) * 8);
+    }
+    sq[f] = val;
+  }
+
+  // This lane's query column c16 of block qb: causal limit and collected row.
   int lim[QB], rowc[QB], head[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -89,17 +124,9 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
     const int hh = ok ? m / T : 0, t = ok ? m % T : 0;
     head[qb] = g * G + hh;
     lim[qb] = ok ? L - T + t : 0x7fffffff;  // row t sees positions <= L - T + t
-    rowc[qb] = (!SPARSE && ok) ? (t == a.row0 ? 0 : (t == a.row1 ? 1 : -1)) : -1;
-    const uint16_t* qp = a.q + (((size_t)b * a.hq + head[qb]) * T + t) * D + kg * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ok) {
-        qf[qb][ks] = load16(qp + ks * 32);
-      } else {
-        qf[qb][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      }
-    }
+    rowc[qb] = (EMIT != VGSA_LOGITS_NONE && ok) ? (t == a.row0 ? 0 : (t == a.row1 ? 1 : -1)) : -1;
   }
+  const int lim_min = L - T;  // every row sees positions <= L - T
 
   f32x4 oacc[DB][QB];
 #pragma unroll
@@ -149,8 +176,12 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
         vv[pb][ks] = load16(a.v + roff[pb] + ks * 32 + kg * 8);
       }
   }
+  __syncthreads();  // query fragments staged
 
   for (; ts < end; ts += step) {
+    // Every entry of the tile is in range and visible to every row?
+    const int last_pos = SPARSE ? sidx[kTile - 1] : ts + kTile - 1;
+    const bool full = (ts + kTile <= end) && (last_pos <= lim_min);
     // Absolute positions of the 8 S^T entries this lane holds.
     int apos[2][4];
     bool inr[2][4];
@@ -163,29 +194,30 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
         apos[pb][r] = SPARSE ? sidx[pb * 16 + 4 * kg + r] : li;
       }
 
-    // V tile -> LDS in natural [position][d] layout (two 8-byte stores per 16 B).
+    // V tile -> LDS in [position][d] layout.
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 w = __builtin_bit_cast(u32x4, vv[pb][ks]);
-        u32x2* dst = reinterpret_cast<u32x2*>(vt + (pb * 16 + c16) * VS + ks * 32 + kg * 8);
-        dst[0] = u32x2{w[0], w[1]};
-        dst[1] = u32x2{w[2], w[3]};
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        *reinterpret_cast<u32x4*>(vt + (pb * 16 + c16) * VS + ks * 32 + kg * 8) =
+            __builtin_bit_cast(u32x4, vv[pb][ks]);
 
     // S^T = K Q^T: entry (position pb*16 + 4*kg + r, query row qb*16 + c16).
     f32x4 sacc[2][QB];
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb)
+    for (int qb = 0; qb < QB; ++qb) {
+      bf16x8 qf[KS];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, sq[(qb * KS + ks) * 64 + lane]);
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pb][ks], qf[qb][ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pb][ks], qf[ks], acc, 0, 0, 0);
         sacc[pb][qb] = acc;
       }
+    }
 
     // Prefetch the next tile's K/V rows while this one is consumed.
     const int tn = ts + step;
@@ -202,42 +234,60 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
     }
 
     // Collect-2-Query epilogue: pre-softmax logits of rows row0 / row1.
-    if (!SPARSE && a.layout != VGSA_LOGITS_NONE) {
-      if (a.layout == VGSA_LOGITS_PER_HEAD) {
+    if (EMIT == VGSA_LOGITS_PER_HEAD) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (rowc[qb] < 0) continue;
-          float* lp = a.logits + (((size_t)b * 2 + rowc[qb]) * a.hq + head[qb]) * a.max_ctx;
-#pragma unroll
-          for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (inr[pb][r])
-                lp[apos[pb][r]] = apos[pb][r] <= lim[qb] ? sacc[pb][qb][r] * a.scale : kNegInf;
-        }
-      } else {
-        float* lp = a.logits + ((size_t)b * a.hkv + g) * a.max_ctx;
+      for (int qb = 0; qb < QB; ++qb) {
+        if (rowc[qb] < 0) continue;
+        float* lp = a.logits + (((size_t)b * 2 + rowc[qb]) * a.hq + head[qb]) * a.max_ctx;
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float acc = 0.f;
+          for (int r = 0; r < 4; ++r)
+            if (inr[pb][r])
+              lp[apos[pb][r]] = (full || apos[pb][r] <= lim[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
+      }
+    } else if (EMIT == VGSA_LOGITS_KVGROUP_SUM) {
+      // v8[pb*4 + r]: this lane's collected rows summed, at position pb*16 + 4*kg + r.
+      float v8[8];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              if (rowc[qb] >= 0)
-                acc += apos[pb][r] <= lim[qb] ? sacc[pb][qb][r] * a.scale : kNegInf;
-            // sum over the 16 query-row lanes of this position (butterfly:
-            // every lane ends with the same value)
-            acc += __shfl_xor(acc, 1);
-            acc += __shfl_xor(acc, 2);
-            acc += __shfl_xor(acc, 4);
-            acc += __shfl_xor(acc, 8);
-            if (c16 == 0 && inr[pb][r]) lp[apos[pb][r]] = acc;
-          }
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float acc = 0.f;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (rowc[qb] >= 0)
+              acc += (full || apos[pb][r] <= lim[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
+          v8[pb * 4 + r] = acc;
+        }
+      // Reduce-scatter over the 16 query-row lanes: after the four steps lane
+      // c16 holds the full sum of position pb = bit 3, r = 2*bit 2 + bit 1.
+      const bool h8 = (c16 >> 3) & 1, h4 = (c16 >> 2) & 1, h2 = (c16 >> 1) & 1;
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float keep = h8 ? v8[4 + i] : v8[i];
+        const float give = h8 ? v8[i] : v8[4 + i];
+        v4[i] = keep + __shfl_xor(give, 8);
+      }
+      float v2[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float keep = h4 ? v4[2 + i] : v4[i];
+        const float give = h4 ? v4[i] : v4[2 + i];
+        v2[i] = keep + __shfl_xor(give, 4);
+      }
+      float v1 = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 2);
+      v1 += __shfl_xor(v1, 1);
+      const int li = ts + (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
+      if ((c16 & 1) == 0 && li < end) {
+        const int pos = SPARSE ? sidx[li - ts] : li;
+        a.logits[((size_t)b * a.hkv + g) * a.max_ctx + pos] = v1;
       }
     }
 
-    // Online softmax (log2 units) and the P fragments (B operand of O^T = V^T P^T).
+    // Online softmax (log2 units, lazily rescaled) and the P fragments
+    // (B operand of O^T = V^T P^T).
     bf16x8 pf[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -247,15 +297,22 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
       for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool vis = inr[pb][r] && apos[pb][r] <= lim[qb];
+          const bool vis = full || (inr[pb][r] && apos[pb][r] <= lim[qb]);
           x[pb][r] = vis ? sacc[pb][qb][r] * a.scale_log2 : kNegInf;
           mx = fmaxf(mx, x[pb][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[qb] - m_use);
+      const bool grow = mx > m_run[qb] + kRescaleLog2;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run[qb];
+        const float alpha = grow ? fast_exp2(m_run[qb] - m_new) : 1.f;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float m_use = m_run[qb] == kNegInf ? 0.f : m_run[qb];
       float psum = 0.f;
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb)
@@ -265,25 +322,25 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
           pf[qb][pb * 4 + r] = (__bf16)pv;
           psum += pv;
         }
-      l_run[qb] = l_run[qb] * alpha + psum;
-      m_run[qb] = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+      l_run[qb] += psum;
     }
 
     // O^T += V^T P^T.  A operand: row d = db*16 + c16, k slots 0..3 are
-    // positions 4*kg + j, slots 4..7 are positions 16 + 4*kg + j (the same
-    // positions the P fragment holds).
+    // positions 4*kg + j, slots 4..7 are positions 16 + 4*kg + j -- the
+    // positions the P fragment holds.  The LDS transpose read hands lane
+    // (c16 = 4*j + q) the 4 values of d = db*16 + c16 from the 4 rows whose
+    // 8-byte pieces (row 4*kg + j, d = db*16 + 4*q ..) the 16 lanes point at.
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    const int trow = 4 * kg + (c16 >> 2), tcol = 4 * (c16 & 3);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      bf16x8 vf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int pos = (j < 4) ? 4 * kg + j : 16 + 4 * kg + (j - 4);
-        vf[j] = __builtin_bit_cast(__bf16, vt[pos * VS + db * 16 + c16]);
-      }
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS s16x4*)(vt + trow * VS + db * 16 + tcol));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS s16x4*)(vt + (16 + trow) * VS + db * 16 + tcol));
+      const bf16x8 vf = __builtin_bit_cast(
+          bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], oacc[db][qb], 0, 0, 0);
@@ -324,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          f32x4* dst = reinterpret_cast<f32x4*>(obuf + (qb * 16 + c16) * VS + db * 16 + 4 * kg);
+          f32x4* dst = reinterpret_cast<f32x4*>(obuf + (qb * 16 + c16) * OS + db * 16 + 4 * kg);
           const f32x4 add = oacc[db][qb] * scl[qb];
           *dst = (w == 0) ? add : (*dst + add);
         }
@@ -337,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void attn_partials_kernel(AttnArgs a) {
     const int m = e / D, d = e % D;
     const int h = g * G + m / T, t = m % T;
     const size_t prow = (((size_t)b * a.hq + h) * T + t) * S + split;
-    a.part_o[prow * D + d] = obuf[m * VS + d];
+    a.part_o[prow * D + d] = obuf[m * OS + d];
   }
   if ((int)threadIdx.x < rows) {
     const int m = threadIdx.x;
@@ -382,27 +439,36 @@ __global__ __launch_bounds__(D) void combine_kernel(CombineArgs a) {
   if (a.lse != nullptr && d == 0) a.lse[row] = l > 0.f ? (M + __log2f(l)) * kLn2 : kNegInf;
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, int EMIT>
 hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int rows = a.group * a.q_len;
   if (rows <= 16) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 1, SPARSE>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 1, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
   } else if (rows <= 32) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 2, SPARSE>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 2, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
   } else if (rows <= 48) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 3, SPARSE>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 3, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dim(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) {
+  if (sparse) return launch_d<D, true, VGSA_LOGITS_NONE>(a, grid, s);
+  switch (a.layout) {
+    case VGSA_LOGITS_PER_HEAD: return launch_d<D, false, VGSA_LOGITS_PER_HEAD>(a, grid, s);
+    case VGSA_LOGITS_KVGROUP_SUM: return launch_d<D, false, VGSA_LOGITS_KVGROUP_SUM>(a, grid, s);
+    default: return launch_d<D, false, VGSA_LOGITS_NONE>(a, grid, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_attention_partials(const AttnArgs& a, bool sparse, hipStream_t s) {
   const dim3 grid(a.num_splits, a.hkv, a.batch);
-  if (a.head_dim == 64) return sparse ? launch_d<64, true>(a, grid, s) : launch_d<64, false>(a, grid, s);
-  return sparse ? launch_d<128, true>(a, grid, s) : launch_d<128, false>(a, grid, s);
+  return a.head_dim == 64 ? launch_dim<64>(a, sparse, grid, s) : launch_dim<128>(a, sparse, grid, s);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
