@@ -11,6 +11,7 @@ namespace vgsa {
 namespace {
 
 constexpr int64_t kMaxGridYZ = 65535;
+constexpr int64_t kMaxOffset = 0xFFFFFFFFLL;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -29,9 +30,14 @@ vgsa_status check_desc(const vgsa_attn_desc* d) {
   if (d->block_size == 16) {
     if (d->max_blocks_per_seq < 1 || d->num_blocks < 1) return VGSA_ERR_INVALID_ARG;
     if ((int64_t)d->max_ctx > (int64_t)16 * d->max_blocks_per_seq) return VGSA_ERR_INVALID_ARG;
+    // element offsets inside the pool are 32-bit
+    if ((int64_t)d->num_blocks * d->num_kv_heads * 16 * d->head_dim > kMaxOffset)
+      return VGSA_ERR_UNSUPPORTED;
   } else if (d->block_size != 0) {
     return VGSA_ERR_UNSUPPORTED;
   }
+  // element offsets inside one (sequence, kv-head) row are 32-bit
+  if ((int64_t)d->max_ctx * d->head_dim > kMaxOffset) return VGSA_ERR_UNSUPPORTED;
   return VGSA_OK;
 }
 

@@ -45,17 +45,15 @@ __device__ __forceinline__ bf16x8 load16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D>
-__device__ __forceinline__ size_t kv_row(const AttnArgs& a, int b, int g, int pos) {
-  if (a.paged) {
-    int blk = a.block_table[(size_t)b * a.max_blocks + (pos >> 4)];
-    blk = min(max(blk, 0), a.num_blocks - 1);
-    return (((size_t)blk * a.hkv + g) * 16 + (pos & 15)) * D;
-  }
-  return (((size_t)b * a.hkv + g) * a.max_ctx + pos) * D;
+// K/V rows are read once per launch: nontemporal loads stream them past the
+// caches.  Each wavefront load instruction covers whole rows (1 KB contiguous
+// per instruction for contiguous caches), the shape that streams fastest.
+__device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Waves per SIMD the register budget is sized for: two (<= 256 registers per
 // wave) unless four query blocks of d = 128 need more.
@@ -140,15 +138,30 @@ void attn_partials_kernel(AttnArgs a) {
     l_run[qb] = 0.f;
   }
 
-  uint16_t* vt = sbuf + wave * kTile * VS;
+  uint16_t* vt = sbuf + wave * kTile * VS;  // this wavefront's K/V tile
   int* sidx = s_idx[wave];
   const int step = kWaves * kTile;
 
-  // Row offsets of the two 16-position blocks this lane loads for tile ts.
-  auto rows_of = [&](int ts, size_t roff[2]) {
+  // Global -> register loads use whole rows: instruction i of a tile covers
+  // rows i*RPI + lane/CPR, 16-byte chunk lane%CPR (RPI rows of D bf16 = 1 KB).
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per load instruction
+  constexpr int NI = kTile / RPI;     // load instructions per tile (each for K and V)
+  const int lrow = lane / CPR, lchunk = lane % CPR;
+
+  // K/V of this (sequence, kv-head) for contiguous caches; the paged pool base
+  // otherwise.  Per-lane element offsets from it fit in 32 bits (checked on
+  // the host).
+  const size_t bg_off = a.paged ? 0 : ((size_t)b * a.hkv + g) * a.max_ctx * D;
+  const uint16_t* kbase = a.k + bg_off;
+  const uint16_t* vbase = a.v + bg_off;
+  const int32_t* btab = a.paged ? a.block_table + (size_t)b * a.max_blocks : nullptr;
+
+  // Issue the K/V loads of tile t0 (staging its positions first when sparse).
+  auto issue = [&](int t0, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
     if (SPARSE) {
       if (lane < kTile) {
-        const int li = ts + lane;
+        const int li = t0 + lane;
         const int p = li < end ? a.idx[(size_t)b * a.idx_stride + li] : 0;
         sidx[lane] = min(max(p, 0), max(L - 1, 0));
       }
@@ -156,95 +169,100 @@ void attn_partials_kernel(AttnArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-      const int li = min(ts + pb * 16 + c16, end - 1);
-      const int pos = SPARSE ? sidx[pb * 16 + c16] : li;
-      roff[pb] = kv_row<D>(a, b, g, pos);
+    for (int i = 0; i < NI; ++i) {
+      const int r = i * RPI + lrow;
+      const int pos = SPARSE ? sidx[r] : min(t0 + r, end - 1);
+      uint32_t off;
+      if (a.paged) {
+        const int blk = min(max(btab[pos >> 4], 0), a.num_blocks - 1);
+        off = (((uint32_t)blk * a.hkv + g) * 16u + (uint32_t)(pos & 15)) * D;
+      } else {
+        off = (uint32_t)pos * D;
+      }
+      off += lchunk * 8;
+      kr[i] = load16_stream(kbase + off);
+      vr[i] = load16_stream(vbase + off);
     }
   };
 
-  bf16x8 kf[2][KS], vv[2][KS];
+  u32x4 kraw[NI], vraw[NI];
   int ts = start + wave * kTile;
-  if (ts < end) {
-    size_t roff[2];
-    rows_of(ts, roff);
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kf[pb][ks] = load16(a.k + roff[pb] + ks * 32 + kg * 8);
-        vv[pb][ks] = load16(a.v + roff[pb] + ks * 32 + kg * 8);
-      }
-  }
+  if (ts < end) issue(ts, kraw, vraw);
   __syncthreads();  // query fragments staged
 
   for (; ts < end; ts += step) {
-    // Every entry of the tile is in range and visible to every row?
-    const int last_pos = SPARSE ? sidx[kTile - 1] : ts + kTile - 1;
-    const bool full = (ts + kTile <= end) && (last_pos <= lim_min);
-    // Absolute positions of the 8 S^T entries this lane holds.
-    int apos[2][4];
-    bool inr[2][4];
+    // Entry e of the tile (e = pb*16 + 4*kg + r for this lane's S^T values)
+    // is visible to query row qb iff e < vis[qb]: positions ascend within a
+    // tile, so each row sees a prefix.  `full`: every entry visible to all.
+    const int n_in = min(kTile, end - ts);
+    const bool full = n_in == kTile && (SPARSE ? sidx[kTile - 1] : ts + kTile - 1) <= lim_min;
+    int vis[QB];
+    if (!full) {
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int li = ts + pb * 16 + 4 * kg + r;
-        inr[pb][r] = li < end;
-        apos[pb][r] = SPARSE ? sidx[pb * 16 + 4 * kg + r] : li;
+      for (int qb = 0; qb < QB; ++qb) {
+        if (SPARSE) {
+          int lo = 0, hi = n_in;  // count of entries with position <= lim[qb]
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sidx[mid] <= lim[qb]) lo = mid + 1; else hi = mid;
+          }
+          vis[qb] = lo;
+        } else {
+          vis[qb] = max(0, min(lim[qb], ts + n_in - 1) - ts + 1);
+        }
       }
+    }
 
-    // V tile -> LDS in [position][d] layout.
+    // K tile -> LDS [position][d]; read back as A fragments of S^T = K Q^T
+    // (lane (c16, kg) of step ks holds row pb*16 + c16, d = ks*32 + kg*8 ..).
+    // Per 16-row half: read the K fragments, overwrite those rows with V (LDS
+    // executes one wavefront's operations in order), multiply.
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        *reinterpret_cast<u32x4*>(vt + (pb * 16 + c16) * VS + ks * 32 + kg * 8) =
-            __builtin_bit_cast(u32x4, vv[pb][ks]);
-
-    // S^T = K Q^T: entry (position pb*16 + 4*kg + r, query row qb*16 + c16).
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<u32x4*>(vt + (i * RPI + lrow) * VS + lchunk * 8) = kraw[i];
     f32x4 sacc[2][QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      bf16x8 qf[KS];
+    for (int pb = 0; pb < 2; ++pb) {
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      bf16x8 kf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, sq[(qb * KS + ks) * 64 + lane]);
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                vt + (pb * 16 + c16) * VS + ks * 32 + kg * 8));
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
+      for (int i = pb * (NI / 2); i < (pb + 1) * (NI / 2); ++i)
+        *reinterpret_cast<u32x4*>(vt + (i * RPI + lrow) * VS + lchunk * 8) = vraw[i];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pb][ks], qf[ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[ks], __builtin_bit_cast(bf16x8, sq[(qb * KS + ks) * 64 + lane]), acc, 0, 0, 0);
         sacc[pb][qb] = acc;
       }
     }
 
     // Prefetch the next tile's K/V rows while this one is consumed.
     const int tn = ts + step;
-    if (tn < end) {
-      size_t roff[2];
-      rows_of(tn, roff);
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          kf[pb][ks] = load16(a.k + roff[pb] + ks * 32 + kg * 8);
-          vv[pb][ks] = load16(a.v + roff[pb] + ks * 32 + kg * 8);
-        }
-    }
+    if (tn < end) issue(tn, kraw, vraw);
 
     // Collect-2-Query epilogue: pre-softmax logits of rows row0 / row1.
     if (EMIT == VGSA_LOGITS_PER_HEAD) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (rowc[qb] < 0) continue;
-        float* lp = a.logits + (((size_t)b * 2 + rowc[qb]) * a.hq + head[qb]) * a.max_ctx;
+        float* lp = a.logits + (((size_t)b * 2 + rowc[qb]) * a.hq + head[qb]) * a.max_ctx + ts;
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (inr[pb][r])
-              lp[apos[pb][r]] = (full || apos[pb][r] <= lim[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
+          for (int r = 0; r < 4; ++r) {
+            const int e = pb * 16 + 4 * kg + r;
+            if (e < n_in) lp[e] = (full || e < vis[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
+          }
       }
     } else if (EMIT == VGSA_LOGITS_KVGROUP_SUM) {
       // v8[pb*4 + r]: this lane's collected rows summed, at position pb*16 + 4*kg + r.
@@ -254,10 +272,10 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float acc = 0.f;
+          const int e = pb * 16 + 4 * kg + r;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            if (rowc[qb] >= 0)
-              acc += (full || apos[pb][r] <= lim[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
+            if (rowc[qb] >= 0) acc += (full || e < vis[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
           v8[pb * 4 + r] = acc;
         }
       // Reduce-scatter over the 16 query-row lanes: after the four steps lane
@@ -279,11 +297,8 @@ void attn_partials_kernel(AttnArgs a) {
       }
       float v1 = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 2);
       v1 += __shfl_xor(v1, 1);
-      const int li = ts + (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
-      if ((c16 & 1) == 0 && li < end) {
-        const int pos = SPARSE ? sidx[li - ts] : li;
-        a.logits[((size_t)b * a.hkv + g) * a.max_ctx + pos] = v1;
-      }
+      const int e = (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
+      if ((c16 & 1) == 0 && e < n_in) a.logits[((size_t)b * a.hkv + g) * a.max_ctx + ts + e] = v1;
     }
 
     // Online softmax (log2 units, lazily rescaled) and the P fragments
@@ -297,8 +312,8 @@ void attn_partials_kernel(AttnArgs a) {
       for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool vis = full || (inr[pb][r] && apos[pb][r] <= lim[qb]);
-          x[pb][r] = vis ? sacc[pb][qb][r] * a.scale_log2 : kNegInf;
+          const bool seen = full || (pb * 16 + 4 * kg + r) < vis[qb];
+          x[pb][r] = seen ? sacc[pb][qb][r] * a.scale_log2 : kNegInf;
           mx = fmaxf(mx, x[pb][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));

@@ -7,16 +7,25 @@
 // attention-sink prefix positions and a window of recent positions are kept
 // first and the remaining budget is filled by score.
 //
-// One workgroup of 1024 threads per sequence:
-//   1. F = [0, s_end) U [w_start, L) is forced; r = k - |F| positions are
-//      picked from the middle range M = [s_end, w_start).
-//   2. Radix select over order-preserving 32-bit keys (digits of 12, 12 and 8
-//      bits, histograms in LDS) finds the key `thr` of the r-th largest score
-//      in M and how many keys equal to `thr` are needed.
-//   3. An ordered compaction (block-wide scans) writes F, every key above thr,
-//      and the lowest-positioned keys equal to thr, in ascending position
-//      order.  Everything is integer arithmetic, so the result is exact and
-//      deterministic.
+// One workgroup of 1024 threads per sequence.
+//   * F = [0, s_end) U [w_start, L) is forced; r = k - |F| positions are
+//     picked from the middle range M = [s_end, w_start).
+//   * Scores become order-preserving 32-bit keys (larger score, larger key;
+//     -0.0 == +0.0).  Positions outside M get key 0, below every real key.
+//   * Thread t owns the contiguous run [t*run, (t+1)*run) of positions, so
+//     runs are in position order and one block-wide scan orders any subset.
+//   * Pass 1: a 4096-bin histogram of the top 12 key bits (LDS atomics)
+//     locates the bin holding the r-th largest key.
+//   * Fast path: the keys at or above that bin (typically a few hundred to a
+//     few thousand) are compacted, in position order, into an LDS list; the
+//     remaining 20 key bits are resolved by two more histogram passes over
+//     the list only, and the output is written from the list:
+//     [0, s_end) ++ selected list entries ++ [w_start, L), ascending.
+//   * If the list would overflow (massive ties in one bin) the same passes
+//     run over all keys instead.
+// All decisions are integer comparisons, so the result is exact and
+// deterministic: keys above the threshold key, then the lowest positions
+// among keys equal to it.
 #include "internal.h"
 
 namespace vgsa {
@@ -25,12 +34,17 @@ namespace {
 constexpr int kThreadsTk = 1024;
 constexpr int kWavesTk = kThreadsTk / 64;
 constexpr int kBins = 4096;
+constexpr int kRunMax = 32;      // keys a thread keeps in registers
+constexpr int kCandMax = 4096;   // LDS candidate list capacity
+constexpr int kCandPerThread = kCandMax / kThreadsTk;
 
-// Larger score -> larger key; -0.0 and +0.0 share one key.
+// Larger score -> larger key; -0.0 and +0.0 share one key; every real key >= 1
+// (only a NaN pattern would map to 0), so 0 marks positions outside M.
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
   if ((u << 1) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return key > 1u ? key : 1u;
 }
 
 // Exclusive prefix sum of v over the workgroup; `total` receives the sum.
@@ -56,97 +70,230 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t&
   return base + x - v;
 }
 
+struct Row {
+  const float* sc;
+  int L, s_end, w_start, run, j0;
+  bool vec;  // 16-byte aligned runs: float4 loads
+};
+
+// Keys of positions [j0 + base, j0 + base + n) of this thread's run, n <= kRunMax;
+// positions outside M (or past L) get key 0.
+__device__ __forceinline__ void load_keys(const Row& c, int base, uint32_t (&key)[kRunMax], int& n) {
+  n = min(kRunMax, c.run - base);
+  const int j = c.j0 + base;
+  if (c.vec) {
+#pragma unroll
+    for (int i = 0; i < kRunMax; i += 4) {
+      if (i < n) {
+        if (j + i + 3 < c.L) {
+          const float4 v = *reinterpret_cast<const float4*>(c.sc + j + i);
+          key[i] = order_key(v.x);
+          key[i + 1] = order_key(v.y);
+          key[i + 2] = order_key(v.z);
+          key[i + 3] = order_key(v.w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) key[i + e] = (j + i + e < c.L) ? order_key(c.sc[j + i + e]) : 0u;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRunMax; ++i)
+      if (i < n) key[i] = (j + i < c.L) ? order_key(c.sc[j + i]) : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kRunMax; ++i) {
+    const int p = j + i;
+    if (i >= n || p < c.s_end || p >= c.w_start) key[i] = 0u;
+  }
+}
+
+// Finds, among the counted keys, the digit of the `want`-th largest and the
+// rank left inside that digit.  hist holds nb bins; all threads call.
+__device__ void find_digit(const uint32_t* hist, uint32_t nb, int shift, uint32_t& prefix,
+                           uint32_t& want, uint32_t* s_wave, uint32_t* s_out) {
+  const int tid = threadIdx.x;
+  uint32_t cnt[4];
+  const int top = (int)nb - 1 - 4 * tid;  // thread t owns bins top .. top-3 (descending)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cnt[q] = (top - q >= 0) ? hist[top - q] : 0u;
+  uint32_t tot;
+  uint32_t above = block_exclusive_scan(cnt[0] + cnt[1] + cnt[2] + cnt[3], s_wave, tot);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (top - q >= 0 && above < want && want <= above + cnt[q]) {
+      s_out[0] = prefix | ((uint32_t)(top - q) << shift);
+      s_out[1] = want - above;
+    }
+    above += cnt[q];
+  }
+  __syncthreads();
+  prefix = s_out[0];
+  want = s_out[1];
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
     int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     int32_t k, int32_t n_sink, int32_t window, int32_t* __restrict__ idx, int32_t idx_stride,
     int32_t* __restrict__ n_idx) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t s_wave[kWavesTk];
-  __shared__ uint32_t s_prefix, s_want;
+  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t cand_key[kCandMax];
+  __shared__ int32_t cand_pos[kCandMax];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int L = min(max(seq_lens[b], 0), max_ctx);
   int32_t* out = idx + (size_t)b * idx_stride;
-  const float* sc = scores + (size_t)b * max_ctx;
 
   if (L <= k) {
     for (int j = tid; j < L; j += kThreadsTk) out[j] = j;
     if (tid == 0) n_idx[b] = L;
     return;
   }
-  const int s_end = min(n_sink, L);
-  const int w_start = max(s_end, L - window);
-  const int r = k - (s_end + (L - w_start));  // >= 0: n_sink + window <= k is checked on the host
+  Row c;
+  c.sc = scores + (size_t)b * max_ctx;
+  c.L = L;
+  c.s_end = min(n_sink, L);
+  c.w_start = max(c.s_end, L - window);
+  c.run = (L + kThreadsTk - 1) / kThreadsTk;
+  c.j0 = tid * c.run;
+  c.vec = (c.run % 4 == 0) && (max_ctx % 4 == 0);
+  const int r = k - (c.s_end + (L - c.w_start));  // >= 0: n_sink + window <= k is checked on the host
+  const int tail = L - c.w_start;
 
+  // Forced positions: [0, s_end) first, [w_start, L) last.
+  for (int i = tid; i < c.s_end; i += kThreadsTk) out[i] = i;
+  for (int i = tid; i < tail; i += kThreadsTk) out[c.s_end + r + i] = c.w_start + i;
+  if (tid == 0) n_idx[b] = k;
+  if (r == 0) return;
+
+  const bool resident = c.run <= kRunMax;
+  uint32_t key[kRunMax];
+  int n = 0;
+  if (resident) load_keys(c, 0, key, n);
+
+  // Pass 1 over all keys: top 12 bits.
+  for (int i = tid; i < kBins; i += kThreadsTk) hist[i] = 0u;
+  __syncthreads();
+  for (int base = 0; base < c.run; base += kRunMax) {
+    if (!resident) load_keys(c, base, key, n);
+#pragma unroll
+    for (int i = 0; i < kRunMax; ++i)
+      if (key[i] != 0u && i < n) atomicAdd(&hist[key[i] >> 20], 1u);
+  }
+  __syncthreads();
   uint32_t prefix = 0u, want = (uint32_t)r;
-  if (r > 0) {
-    // digits: bits [31:20], [19:8], [7:0]
-    const int shifts[3] = {20, 8, 0};
-    const int widths[3] = {12, 12, 8};
+  find_digit(hist, kBins, 20, prefix, want, s_wave, s_out);
+  const uint32_t cand_lo = prefix;  // keys >= cand_lo: the threshold bin and above
+
+  // Count candidates; compact them into the LDS list if they fit.
+  uint32_t ccount = 0u;
+  for (int base = 0; base < c.run; base += kRunMax) {
+    if (!resident) load_keys(c, base, key, n);
+#pragma unroll
+    for (int i = 0; i < kRunMax; ++i) ccount += (i < n && key[i] >= cand_lo) ? 1u : 0u;
+  }
+  uint32_t ctotal;
+  const uint32_t cbase = block_exclusive_scan(ccount, s_wave, ctotal);
+
+  const int shifts[2] = {8, 0};
+  const uint32_t masks[2] = {0xFFF00000u, 0xFFFFFF00u};
+  const uint32_t nbs[2] = {4096u, 256u};
+  if (ctotal <= (uint32_t)kCandMax) {
+    // ---------------- fast path: resolve and emit from the candidate list
+    uint32_t o = cbase;
+    for (int base = 0; base < c.run; base += kRunMax) {
+      if (!resident) load_keys(c, base, key, n);
+#pragma unroll
+      for (int i = 0; i < kRunMax; ++i)
+        if (i < n && key[i] >= cand_lo) {
+          cand_key[o] = key[i];
+          cand_pos[o] = c.j0 + base + i;
+          ++o;
+        }
+    }
+    // passes 2 and 3 over the candidates of the threshold bin
 #pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = shifts[pass];
-      const uint32_t nb = 1u << widths[pass];
-      const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shifts[pass - 1]));
+    for (int pass = 0; pass < 2; ++pass) {
       for (int i = tid; i < kBins; i += kThreadsTk) hist[i] = 0u;
       __syncthreads();
-      for (int j = s_end + tid; j < w_start; j += kThreadsTk) {
-        const uint32_t key = order_key(sc[j]);
-        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1u)], 1u);
+      for (int q = tid; q < (int)ctotal; q += kThreadsTk) {
+        const uint32_t kk = cand_key[q];
+        if ((kk & masks[pass]) == prefix) atomicAdd(&hist[(kk >> shifts[pass]) & (nbs[pass] - 1u)], 1u);
       }
       __syncthreads();
-      // Thread t owns the 4 bins nb-1-4t .. nb-4-4t (descending); the
-      // exclusive scan gives how many keys lie above its highest bin.
-      uint32_t c[4] = {0u, 0u, 0u, 0u};
-      const int top = (int)nb - 1 - 4 * tid;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) c[q] = (top - q >= 0) ? hist[top - q] : 0u;
-      uint32_t tot;
-      uint32_t above = block_exclusive_scan(c[0] + c[1] + c[2] + c[3], s_wave, tot);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (top - q >= 0 && above < want && want <= above + c[q]) {
-          s_prefix = prefix | ((uint32_t)(top - q) << shift);
-          s_want = want - above;
-        }
-        above += c[q];
-      }
-      __syncthreads();
-      prefix = s_prefix;
-      want = s_want;
-      __syncthreads();
+      find_digit(hist, nbs[pass], shifts[pass], prefix, want, s_wave, s_out);
     }
+    const uint32_t thr = prefix, need_eq = want;
+    // ordered emit: thread t owns list entries [4t, 4t+4)
+    uint32_t kk[kCandPerThread];
+    uint32_t ceq = 0u;
+#pragma unroll
+    for (int q = 0; q < kCandPerThread; ++q) {
+      const int e = tid * kCandPerThread + q;
+      kk[q] = e < (int)ctotal ? cand_key[e] : 0u;
+      ceq += kk[q] == thr ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t eq = block_exclusive_scan(ceq, s_wave, tot);
+    uint32_t csel = 0u;
+    bool keep[kCandPerThread];
+#pragma unroll
+    for (int q = 0; q < kCandPerThread; ++q) {
+      keep[q] = kk[q] > thr || (kk[q] == thr && eq++ < need_eq);
+      csel += keep[q] ? 1u : 0u;
+    }
+    uint32_t so = block_exclusive_scan(csel, s_wave, tot) + (uint32_t)c.s_end;
+#pragma unroll
+    for (int q = 0; q < kCandPerThread; ++q)
+      if (keep[q] && so < (uint32_t)idx_stride) out[so++] = cand_pos[tid * kCandPerThread + q];
+    return;
   }
-  const uint32_t thr = prefix;     // key of the r-th largest score in M
-  const uint32_t need_eq = want;   // keys equal to thr that are kept (lowest positions first)
 
-  // Ordered compaction over contiguous runs, one run per thread.
-  const int run = (L + kThreadsTk - 1) / kThreadsTk;
-  const int j0 = min(tid * run, L), j1 = min(j0 + run, L);
+  // ---------------- general path: passes 2 and 3 and the emit over all keys
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int i = tid; i < kBins; i += kThreadsTk) hist[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < c.run; base += kRunMax) {
+      if (!resident) load_keys(c, base, key, n);
+#pragma unroll
+      for (int i = 0; i < kRunMax; ++i)
+        if (i < n && key[i] != 0u && (key[i] & masks[pass]) == prefix)
+          atomicAdd(&hist[(key[i] >> shifts[pass]) & (nbs[pass] - 1u)], 1u);
+    }
+    __syncthreads();
+    find_digit(hist, nbs[pass], shifts[pass], prefix, want, s_wave, s_out);
+  }
+  const uint32_t thr = prefix, need_eq = want;
   uint32_t ceq = 0u;
-  if (r > 0) {
-    for (int j = max(j0, s_end); j < min(j1, w_start); ++j) ceq += order_key(sc[j]) == thr;
+  for (int base = 0; base < c.run; base += kRunMax) {
+    if (!resident) load_keys(c, base, key, n);
+#pragma unroll
+    for (int i = 0; i < kRunMax; ++i) ceq += (i < n && key[i] == thr) ? 1u : 0u;
   }
   uint32_t tot;
   const uint32_t eq_base = block_exclusive_scan(ceq, s_wave, tot);
-
-  auto keep = [&](int j, uint32_t& e) -> bool {
-    if (j < s_end || j >= w_start) return true;
-    if (r == 0) return false;
-    const uint32_t key = order_key(sc[j]);
-    if (key > thr) return true;
-    if (key == thr) return e++ < need_eq;
-    return false;
-  };
   uint32_t e = eq_base, csel = 0u;
-  for (int j = j0; j < j1; ++j) csel += keep(j, e);
-  const uint32_t out_base = block_exclusive_scan(csel, s_wave, tot);
+  for (int base = 0; base < c.run; base += kRunMax) {
+    if (!resident) load_keys(c, base, key, n);
+#pragma unroll
+    for (int i = 0; i < kRunMax; ++i)
+      if (i < n) csel += (key[i] > thr || (key[i] == thr && e++ < need_eq)) ? 1u : 0u;
+  }
+  uint32_t o = block_exclusive_scan(csel, s_wave, tot) + (uint32_t)c.s_end;
   e = eq_base;
-  uint32_t o = out_base;
-  for (int j = j0; j < j1; ++j)
-    if (keep(j, e) && o < (uint32_t)idx_stride) out[o++] = j;
-  if (tid == 0) n_idx[b] = (int32_t)tot;
+  for (int base = 0; base < c.run; base += kRunMax) {
+    if (!resident) load_keys(c, base, key, n);
+#pragma unroll
+    for (int i = 0; i < kRunMax; ++i)
+      if (i < n && (key[i] > thr || (key[i] == thr && e++ < need_eq)) && o < (uint32_t)idx_stride)
+        out[o++] = c.j0 + base + i;
+  }
 }
 
 }  // namespace
