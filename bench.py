@@ -66,6 +66,25 @@ def alg_bytes(w, lens):
     }
 
 
+def counter_traffic(workload_name):
+    """HBM bytes per verify launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy kernel), or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"verify_{workload_name}.md")
+    src = os.path.join(ROOT, "sparse_attention_long_amd", "csrc", "attention.hip")
+    try:
+        text = open(path).read()
+        m = re.search(r"traffic_bytes=(\d+) source_sha256_prefix=([0-9a-f]+)", text)
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if not m or not digest.startswith(m.group(2)):
+        return None
+    return int(m.group(1))
+
+
 def cpu_baseline(w, x, seconds):
     """The fp64 oracle, as it stands, on whole sequences of the workload until
     `seconds` have passed; scaled to iterations/s of the full batch."""
@@ -277,7 +296,7 @@ def main():
                    "budget": w.budget, "n_sink": w.n_sink, "window": w.window,
                    "paged": w.paged, "logits": "kvgroup_sum"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
                      "kernel": "attn_partials_kernel (verify)",
                      "alg_bytes_per_launch": ab["verify_kernel"], "avg_launch_us": verify_us},
         "iteration_alg_bytes": ab["iteration"],
