@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: capture one step as a HIP graph and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain fp32 copy of this many MiB three times (a kernel of "
@@ -212,17 +214,30 @@ def main():
         if ev is not None:
             ev[4].record()
         if w.sparse_verify:
-            Bn.sparse_partials(desc, q, k, v, lens, bt, idx, n_idx, ws_s)
+            Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
+                                out=out_s, lse=lse_s, workspace=ws_s)
             if ev is not None:
                 ev[5].record()
-            Bn.combine_partials(desc, stride, n_idx, ws_s, out_s, lse_s)
-            if ev is not None:
-                ev[6].record()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        # one step captured as a HIP graph (no memsets are recorded: every
+        # kernel writes its outputs); replays run the same kernels
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                step()
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps; events around the verify kernel
     K = args.steps
@@ -233,7 +248,7 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     e_start.record()
-    for i in range(K):
+    for i in range(K if graph is None else 0):
         a, b_ = ev_pairs[i]
         a.record()
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
@@ -242,17 +257,21 @@ def main():
         Bn.aggregate_scores(logits, lens, Hq, Hkv, scores=scores)
         Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         if w.sparse_verify:
-            Bn.sparse_partials(desc, q, k, v, lens, bt, idx, n_idx, ws_s)
-            Bn.combine_partials(desc, stride, n_idx, ws_s, out_s, lse_s)
+            Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
+                                out=out_s, lse=lse_s, workspace=ws_s)
+    if graph is not None:
+        for i in range(K):
+            graph.replay()
     e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gpu_ms = e_start.elapsed_time(e_end)
-    verify_us = float(np.mean([a.elapsed_time(b_) for a, b_ in ev_pairs])) * 1e3
+    verify_us = (float(np.mean([a.elapsed_time(b_) for a, b_ in ev_pairs])) * 1e3
+                 if graph is None else float("nan"))
     log(f"[bench] {K} steps: wall {wall * 1e3:.2f} ms, gpu {gpu_ms:.2f} ms, verify kernel {verify_us:.1f} us")
 
     # ---- stage breakdown and logit-emit overhead (outside the timed region)
-    nst = 7
+    nst = 6
     stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(K)]
     for i in range(K):
         step(stage_ev[i])
@@ -264,8 +283,7 @@ def main():
     stages = {"verify_partials": span(0, 1), "verify_combine": span(1, 2), "aggregate": span(2, 3),
               "select": span(3, 4)}
     if w.sparse_verify:
-        stages["sparse_partials"] = span(4, 5)
-        stages["sparse_combine"] = span(5, 6)
+        stages["sparse"] = span(4, 5)
     none_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(K)]
     for a, b_ in none_ev:
@@ -306,12 +324,13 @@ def main():
         "verify_partials_no_logits_us": verify_none_us,
         "logit_emit_overhead": stages["verify_partials"] / verify_none_us - 1.0,
     }
-    if w.sparse_verify and stages.get("sparse_partials"):
+    if w.sparse_verify and stages.get("sparse"):
         sb = ab["sparse_kernel_kv"]
-        result["sparse_roofline"] = {"achieved": sb / (stages["sparse_partials"] * 1e-6) / 1e9,
+        result["sparse_roofline"] = {"achieved": sb / (stages["sparse"] * 1e-6) / 1e9,
                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "alg_bytes_per_launch": sb,
-                                     "avg_launch_us": stages["sparse_partials"]}
+                                     "avg_launch_us": stages["sparse"],
+                                     "note": "whole sparse call (one kernel when it fits one split)"}
         result["sparse_roofline"]["frac"] = result["sparse_roofline"]["achieved"] / HBM_PEAK_GBS
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")

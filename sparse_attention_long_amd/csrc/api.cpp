@@ -89,6 +89,9 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
   a.part_ml = c.part_ml;
   a.layout = VGSA_LOGITS_NONE;
   a.row0 = a.row1 = -1;
+  a.out = nullptr;
+  a.lse = nullptr;
+  a.direct = 0;
   return a;
 }
 
@@ -104,8 +107,10 @@ vgsa_status check_attn_pointers(const vgsa_attn_desc& d, const void* q, const vo
 }  // namespace
 
 SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span) {
+  if (span < 1) span = 1;  // callers validate; keep the plan total anyway
   const int64_t bh = (int64_t)(batch > 0 ? batch : 1) * num_kv_heads;
-  const int64_t max_splits = ceil_div(span, kMinChunk) > 0 ? ceil_div(span, kMinChunk) : 1;
+  const int64_t max_splits =
+      span <= kDirectSpan ? 1 : (ceil_div(span, kMinChunk) > 0 ? ceil_div(span, kMinChunk) : 1);
   int64_t s = ceil_div(kTargetWorkgroups, bh);
   if (s < 1) s = 1;
   if (s > max_splits) s = max_splits;
@@ -163,11 +168,17 @@ size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_strid
   return partial_bytes(*desc, make_plan(desc->batch, desc->num_kv_heads, idx_stride));
 }
 
-vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
-                                 const void* v_cache, const int32_t* block_table,
-                                 const int32_t* seq_lens, int32_t collect_row0,
-                                 int32_t collect_row1, vgsa_logit_layout layout, float* logits,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Verify launch: partials into the workspace, or (out != null, one split)
+// the final output directly.
+vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t collect_row0, int32_t collect_row1, vgsa_logit_layout layout,
+                          float* logits, void* workspace, size_t workspace_bytes, void* out,
+                          float* lse, void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
@@ -189,14 +200,17 @@ vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, cons
   a.logits = layout == VGSA_LOGITS_NONE ? nullptr : logits;
   a.row0 = collect_row0;
   a.row1 = collect_row1;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.direct = out != nullptr ? 1 : 0;
   return hip_status(launch_attention_partials(a, false, static_cast<hipStream_t>(stream)));
 }
 
-vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
-                                 const void* v_cache, const int32_t* block_table,
-                                 const int32_t* seq_lens, const int32_t* idx,
-                                 const int32_t* n_idx, int32_t idx_stride, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* idx, const int32_t* n_idx, int32_t idx_stride,
+                          void* workspace, size_t workspace_bytes, void* out, float* lse,
+                          void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
@@ -210,7 +224,33 @@ vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, cons
   a.idx = idx;
   a.n_idx = n_idx;
   a.idx_stride = idx_stride;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.direct = out != nullptr ? 1 : 0;
   return hip_status(launch_attention_partials(a, true, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t collect_row0,
+                                 int32_t collect_row1, vgsa_logit_layout layout, float* logits,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_row0,
+                       collect_row1, layout, logits, workspace, workspace_bytes, nullptr, nullptr,
+                       stream);
+}
+
+vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* idx,
+                                 const int32_t* n_idx, int32_t idx_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
+                       workspace, workspace_bytes, nullptr, nullptr, stream);
 }
 
 vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
@@ -250,9 +290,15 @@ vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, con
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   if (out == nullptr) return VGSA_ERR_INVALID_ARG;
-  st = vgsa_verify_partials(desc, q, k_cache, v_cache, block_table, seq_lens,
-                                        collect_row0, collect_row1, layout, logits, workspace,
-                                        workspace_bytes, stream);
+  const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, desc->max_ctx);
+  if (p.num_splits == 1) {
+    // one split: the partials kernel finishes the softmax and writes out / lse
+    return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_row0,
+                         collect_row1, layout, logits, workspace, workspace_bytes, out, lse,
+                         stream);
+  }
+  st = verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_row0, collect_row1,
+                     layout, logits, workspace, workspace_bytes, nullptr, nullptr, stream);
   if (st != VGSA_OK) return st;
   return vgsa_combine_partials(desc, desc->max_ctx, seq_lens, workspace, workspace_bytes, out,
                                lse, stream);
@@ -265,9 +311,14 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
                                   void* workspace, size_t workspace_bytes, void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
-  if (out == nullptr) return VGSA_ERR_INVALID_ARG;
-  st = vgsa_sparse_partials(desc, q, k_cache, v_cache, block_table, seq_lens, idx,
-                                        n_idx, idx_stride, workspace, workspace_bytes, stream);
+  if (out == nullptr || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
+  const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, idx_stride);
+  if (p.num_splits == 1) {
+    return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
+                         workspace, workspace_bytes, out, lse, stream);
+  }
+  st = sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
+                     workspace, workspace_bytes, nullptr, nullptr, stream);
   if (st != VGSA_OK) return st;
   return vgsa_combine_partials(desc, idx_stride, n_idx, workspace, workspace_bytes, out, lse,
                                stream);

@@ -70,48 +70,63 @@ constexpr float kRescaleLog2 = 8.0f;
 
 // D: head dim (64/128); QB: 16-row query blocks (G*T <= 16*QB); SPARSE: index
 // list; EMIT: logit layout written by the verify pass (VGSA_LOGITS_*).
-template <int D, int QB, bool SPARSE, int EMIT>
-__global__ __launch_bounds__(kThreads)
+// WAVES: wavefronts per workgroup (4 for split launches; 8 for one-split
+// sparse launches, so a short index list is covered in fewer serial tiles).
+template <int D, int QB, bool SPARSE, int EMIT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(Occupancy<D, QB>::kWavesPerEU, Occupancy<D, QB>::kWavesPerEU)))
 void attn_partials_kernel(AttnArgs a) {
+  constexpr int NT = WAVES * 64;   // threads per workgroup
   constexpr int KS = D / 32;       // MFMA steps over the head dimension
   constexpr int DB = D / 16;       // 16-wide blocks of the head dimension
   constexpr int VS = D + 16;       // V tile row stride (elements): rows land 32 B apart in the banks
   constexpr int OS = D + 4;        // merge-buffer row stride (floats)
-  static_assert(kWaves * kTile * VS * 2 >= kMaxRows * OS * 4, "merge buffer must fit in the V tiles");
-  // V tiles of the four wavefronts, [position][d]; reused at the end as the
-  // fp32 merge buffer [64][D + 4].
-  __shared__ __align__(16) uint16_t sbuf[kWaves * kTile * VS];
+  constexpr int NBUF = WAVES / 4;  // merge buffers: wavefronts merge NBUF at a time
+  static_assert(WAVES % 4 == 0, "wavefronts merge in groups");
+  static_assert(WAVES * kTile * VS * 2 >= NBUF * kMaxRows * OS * 4, "merge buffers must fit in the V tiles");
+  // Per-wavefront K/V tiles, [position][d]; reused at the end as the fp32
+  // merge buffers.
+  __shared__ __align__(16) uint16_t sbuf[WAVES * kTile * VS];
   // Query fragments, already in MFMA operand order: [qb][ks][lane] x 16 B.
   __shared__ __align__(16) u32x4 sq[QB * KS * 64];
-  __shared__ float s_m[kWaves][kMaxRows];
-  __shared__ float s_l[kWaves][kMaxRows];
-  __shared__ int s_idx[kWaves][kTile];
+  __shared__ float s_m[WAVES][kMaxRows];
+  __shared__ float s_l[WAVES][kMaxRows];
+  __shared__ int s_idx[WAVES][kTile];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, kg = lane >> 4;
 
+  const int start = split * a.chunk;
+  // Sparse: the list entries of this wavefront's first kPreTiles tiles are
+  // loaded (clamped in bounds) together with the lengths, so those tiles
+  // need no index round trip of their own.
+  constexpr int kPreTiles = 4;
+  int idx_pre[kPreTiles];
+#pragma unroll
+  for (int i = 0; i < kPreTiles; ++i) {
+    idx_pre[i] = 0;
+    if (SPARSE && lane < kTile)
+      idx_pre[i] = a.idx[(size_t)b * a.idx_stride +
+                         min(start + (i * WAVES + wave) * kTile + lane, a.idx_stride - 1)];
+  }
   const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int count = SPARSE ? min(max(a.n_idx[b], 0), a.idx_stride) : L;
-  const int start = split * a.chunk;
-  if (start >= count) return;  // whole workgroup: nothing in this split
-  const int end = min(start + a.chunk, count);
   const int G = a.group, T = a.q_len, rows = G * T;
-
-  // Stage the query fragments (B operand of S^T = K Q^T): fragment
-  // (qb, ks, lane) holds row m = qb*16 + lane%16, d = ks*32 + (lane/16)*8 .. +8.
-  for (int f = threadIdx.x; f < QB * KS * 64; f += kThreads) {
-    const int fl = f & 63, fks = (f >> 6) % KS, fqb = (f >> 6) / KS;
-    const int m = fqb * 16 + (fl & 15);
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (m < rows) {
-      const int h = g * G + m / T, t = m % T;
-      val = *reinterpret_cast<const u32x4*>(a.q + (((size_t)b * a.hq + h) * T + t) * D +
-                                            fks * 32 + (fl >> 4) * 8);
+  if (start >= count) {  // whole workgroup: nothing in this split
+    if (a.direct) {      // the only split: the rows see nothing -> o = 0, lse = -inf
+      for (int e = threadIdx.x; e < rows * D; e += NT) {
+        const int m = e / D, h = g * G + m / T, t = m % T;
+        a.out[(((size_t)b * a.hq + h) * T + t) * D + e % D] = 0;
+      }
+      if (a.lse != nullptr && (int)threadIdx.x < rows) {
+        const int m = threadIdx.x, h = g * G + m / T, t = m % T;
+        a.lse[((size_t)b * a.hq + h) * T + t] = kNegInf;
+      }
     }
-    sq[f] = val;
+    return;
   }
+  const int end = min(start + a.chunk, count);
 
   // This lane's query column c16 of block qb: causal limit and collected row.
   int lim[QB], rowc[QB], head[QB];
@@ -140,7 +155,7 @@ void attn_partials_kernel(AttnArgs a) {
 
   uint16_t* vt = sbuf + wave * kTile * VS;  // this wavefront's K/V tile
   int* sidx = s_idx[wave];
-  const int step = kWaves * kTile;
+  const int step = WAVES * kTile;
 
   // Global -> register loads use whole rows: instruction i of a tile covers
   // rows i*RPI + lane/CPR, 16-byte chunk lane%CPR (RPI rows of D bf16 = 1 KB).
@@ -158,11 +173,17 @@ void attn_partials_kernel(AttnArgs a) {
   const int32_t* btab = a.paged ? a.block_table + (size_t)b * a.max_blocks : nullptr;
 
   // Issue the K/V loads of tile t0 (staging its positions first when sparse).
-  auto issue = [&](int t0, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+  // Issue the K/V loads of this wavefront's tile number `it` (starting at t0),
+  // staging its positions first when sparse.
+  auto issue = [&](int t0, int it, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
     if (SPARSE) {
       if (lane < kTile) {
         const int li = t0 + lane;
-        const int p = li < end ? a.idx[(size_t)b * a.idx_stride + li] : 0;
+        int p = 0;
+        if (li < end) {
+          p = it == 0 ? idx_pre[0] : it == 1 ? idx_pre[1] : it == 2 ? idx_pre[2]
+            : it == 3 ? idx_pre[3] : a.idx[(size_t)b * a.idx_stride + li];
+        }
         sidx[lane] = min(max(p, 0), max(L - 1, 0));
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -187,7 +208,23 @@ void attn_partials_kernel(AttnArgs a) {
 
   u32x4 kraw[NI], vraw[NI];
   int ts = start + wave * kTile;
-  if (ts < end) issue(ts, kraw, vraw);
+  int tile_no = 0;
+  if (ts < end) issue(ts, 0, kraw, vraw);
+
+  // Stage the query fragments (B operand of S^T = K Q^T) once the first
+  // tile's loads are in flight: fragment (qb, ks, lane) holds row
+  // m = qb*16 + lane%16, d = ks*32 + (lane/16)*8 .. +8.
+  for (int f = threadIdx.x; f < QB * KS * 64; f += NT) {
+    const int fl = f & 63, fks = (f >> 6) % KS, fqb = (f >> 6) / KS;
+    const int m = fqb * 16 + (fl & 15);
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (m < rows) {
+      const int h = g * G + m / T, t = m % T;
+      val = *reinterpret_cast<const u32x4*>(a.q + (((size_t)b * a.hq + h) * T + t) * D +
+                                            fks * 32 + (fl >> 4) * 8);
+    }
+    sq[f] = val;
+  }
   __syncthreads();  // query fragments staged
 
   for (; ts < end; ts += step) {
@@ -248,7 +285,8 @@ void attn_partials_kernel(AttnArgs a) {
 
     // Prefetch the next tile's K/V rows while this one is consumed.
     const int tn = ts + step;
-    if (tn < end) issue(tn, kraw, vraw);
+    ++tile_no;
+    if (tn < end) issue(tn, tile_no, kraw, vraw);
 
     // Collect-2-Query epilogue: pre-softmax logits of rows row0 / row1.
     if (EMIT == VGSA_LOGITS_PER_HEAD) {
@@ -379,51 +417,82 @@ void attn_partials_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Merge the four wavefronts into obuf (relative to the workgroup max).
-  float* obuf = reinterpret_cast<float*>(sbuf);
+  // Merge the wavefronts, relative to each row's workgroup max M: groups of
+  // NBUF wavefronts accumulate into NBUF fp32 buffers (4 barrier rounds);
+  // every row's (M, l) is computed once.
+  float* obuf = reinterpret_cast<float*>(sbuf);      // NBUF x [64][D + 4]
+  float* s_M = s_m[0];                                // reused after the reads below
   float scl[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qb * 16 + c16;
     float M = s_m[0][row];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][row]);
+    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_m[w][row]);
     scl[qb] = m_run[qb] == kNegInf ? 0.f : fast_exp2(m_run[qb] - M);
   }
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  float rowM = kNegInf, rowL = 0.f;  // threads < rows: their row's merged (M, l)
+  if ((int)threadIdx.x < rows) {
+    const int m = threadIdx.x;
+    rowM = s_m[0][m];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) rowM = fmaxf(rowM, s_m[w][m]);
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+      if (s_m[w][m] != kNegInf) rowL += s_l[w][m] * fast_exp2(s_m[w][m] - rowM);
+  }
+  for (int r = 0; r < WAVES / NBUF; ++r) {
+    if (wave / NBUF == r) {
+      float* buf = obuf + (wave % NBUF) * kMaxRows * OS;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          f32x4* dst = reinterpret_cast<f32x4*>(obuf + (qb * 16 + c16) * OS + db * 16 + 4 * kg);
+          f32x4* dst = reinterpret_cast<f32x4*>(buf + (qb * 16 + c16) * OS + db * 16 + 4 * kg);
           const f32x4 add = oacc[db][qb] * scl[qb];
-          *dst = (w == 0) ? add : (*dst + add);
+          *dst = (r == 0) ? add : (*dst + add);
         }
     }
     __syncthreads();
   }
+  // s_m is no longer read: publish each row's (M, l) there.
+  if ((int)threadIdx.x < rows) {
+    s_M[threadIdx.x] = rowM;
+    s_M[kMaxRows + threadIdx.x] = rowL;
+  }
+  __syncthreads();
 
+  if (a.direct) {  // the only split: normalise and write the output
+    for (int e = threadIdx.x; e < rows * D; e += NT) {
+      const int m = e / D, d = e % D;
+      const int h = g * G + m / T, t = m % T;
+      const float l = s_M[kMaxRows + m];
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) acc += obuf[i * kMaxRows * OS + m * OS + d];
+      const float o = l > 0.f ? acc / l : 0.f;
+      a.out[(((size_t)b * a.hq + h) * T + t) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
+      if (a.lse != nullptr && d == 0)
+        a.lse[((size_t)b * a.hq + h) * T + t] = l > 0.f ? (s_M[m] + __log2f(l)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   const int S = a.num_splits;
-  for (int e = threadIdx.x; e < rows * D; e += kThreads) {
+  for (int e = threadIdx.x; e < rows * D; e += NT) {
     const int m = e / D, d = e % D;
     const int h = g * G + m / T, t = m % T;
     const size_t prow = (((size_t)b * a.hq + h) * T + t) * S + split;
-    a.part_o[prow * D + d] = obuf[m * OS + d];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) acc += obuf[i * kMaxRows * OS + m * OS + d];
+    a.part_o[prow * D + d] = acc;
   }
   if ((int)threadIdx.x < rows) {
     const int m = threadIdx.x;
     const int h = g * G + m / T, t = m % T;
     const size_t prow = (((size_t)b * a.hq + h) * T + t) * S + split;
-    float M = s_m[0][m];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][m]);
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (s_m[w][m] != kNegInf) l += s_l[w][m] * fast_exp2(s_m[w][m] - M);
-    a.part_ml[prow * 2 + 0] = M;
-    a.part_ml[prow * 2 + 1] = l;
+    a.part_ml[prow * 2 + 0] = rowM;
+    a.part_ml[prow * 2 + 1] = rowL;
   }
 }
 
@@ -454,28 +523,35 @@ __global__ __launch_bounds__(D) void combine_kernel(CombineArgs a) {
   if (a.lse != nullptr && d == 0) a.lse[row] = l > 0.f ? (M + __log2f(l)) * kLn2 : kNegInf;
 }
 
-template <int D, bool SPARSE, int EMIT>
+template <int D, bool SPARSE, int EMIT, int WAVES>
 hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int rows = a.group * a.q_len;
+  const dim3 block(WAVES * 64);
   if (rows <= 16) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 1, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 1, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
   } else if (rows <= 32) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 2, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 2, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
   } else if (rows <= 48) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 3, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 3, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dim(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) {
-  if (sparse) return launch_d<D, true, VGSA_LOGITS_NONE>(a, grid, s);
+  if (sparse) {
+    // one split over a list longer than one round of 4 wavefronts: 8 wavefronts
+    if (a.num_splits == 1 && a.chunk > kMinChunk)
+      return launch_d<D, true, VGSA_LOGITS_NONE, kWavesWide>(a, grid, s);
+    return launch_d<D, true, VGSA_LOGITS_NONE, kWaves>(a, grid, s);
+  }
   switch (a.layout) {
-    case VGSA_LOGITS_PER_HEAD: return launch_d<D, false, VGSA_LOGITS_PER_HEAD>(a, grid, s);
-    case VGSA_LOGITS_KVGROUP_SUM: return launch_d<D, false, VGSA_LOGITS_KVGROUP_SUM>(a, grid, s);
-    default: return launch_d<D, false, VGSA_LOGITS_NONE>(a, grid, s);
+    case VGSA_LOGITS_PER_HEAD: return launch_d<D, false, VGSA_LOGITS_PER_HEAD, kWaves>(a, grid, s);
+    case VGSA_LOGITS_KVGROUP_SUM:
+      return launch_d<D, false, VGSA_LOGITS_KVGROUP_SUM, kWaves>(a, grid, s);
+    default: return launch_d<D, false, VGSA_LOGITS_NONE, kWaves>(a, grid, s);
   }
 }
 

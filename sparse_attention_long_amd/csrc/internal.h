@@ -14,10 +14,15 @@ namespace vgsa {
 // smallest chunk a workgroup is given (one step of every wave).
 constexpr int kTile = 32;
 constexpr int kWaves = 4;
+constexpr int kWavesWide = 8;  // one-split sparse launches
 constexpr int kThreads = kWaves * 64;
 constexpr int kMinChunk = kTile * kWaves;
 // Workgroups aimed for per attention launch: 4 per CU on 256 CUs.
 constexpr int kTargetWorkgroups = 1024;
+// Spans up to this many positions get one split: a single workgroup per
+// (sequence, kv-head) finishes the softmax itself and writes the output
+// directly (no partials, no combine launch).
+constexpr int kDirectSpan = 1024;
 // Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.
 constexpr int kMaxRows = 64;
 
@@ -47,6 +52,9 @@ struct AttnArgs {
   int32_t row0, row1;
   float* part_o;
   float* part_ml;
+  uint16_t* out;     // direct mode (one split): final bf16 output ...
+  float* lse;        // ... and lse (may be null)
+  int32_t direct;
   int32_t batch, hq, hkv, group, q_len, head_dim;
   int32_t max_ctx, paged, max_blocks, num_blocks;
   int32_t num_splits, chunk;

@@ -209,3 +209,41 @@ def test_determinism_bitwise():
                      idx.cpu().numpy(), so.view(torch.int16).cpu().numpy(), sl.cpu().numpy()])
     for a, b in zip(*runs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["g4t5_d64", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])
+def test_two_phase_api_matches_one_call(name):
+    """partials + combine gives the same bytes as the one-call entry points, for
+    one split (the one-call path then writes the output directly) and several."""
+    w = CASES[name]
+    x = W.make_layer(w)
+    d = to_device(x)
+    desc = Bn.make_desc(d.q, d.k, d.block_table, d.max_ctx)
+    B, Hq, T, D = d.q.shape
+    for layout, code in (("kvgroup_sum", Bn.LOGITS_KVGROUP_SUM), ("per_head", Bn.LOGITS_PER_HEAD)):
+        out1, lse1, lg1 = run_verify(d, w, layout)
+        ws = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        lg2 = torch.empty_like(lg1)
+        Bn.verify_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, w.collect_rows, code, lg2, ws)
+        out2 = torch.empty_like(out1)
+        lse2 = torch.empty_like(lse1)
+        Bn.combine_partials(desc, d.max_ctx, d.seq_lens, ws, out2, lse2)
+        torch.cuda.synchronize()
+        assert_out_close(out2, oracle.verify_attention(x.q, x.k, x.v, x.seq_lens)[0], f"{name} two-phase")
+        # same softmax merge order within a split; the direct path divides once
+        np.testing.assert_allclose(out2.float().cpu().numpy(), out1.float().cpu().numpy(), atol=8e-3)
+        np.testing.assert_allclose(lse2.cpu().numpy(), lse1.cpu().numpy(), atol=1e-5)
+        for b in range(w.batch):
+            L = int(x.seq_lens[b])
+            assert torch.equal(lg1[b, ..., :L], lg2[b, ..., :L])
+    idx, n = W.index_lists(w.seed + 1, x.seq_lens, count=max(1, w.budget // 2), stride=w.budget)
+    idx_d, n_d = dev_i32(idx), dev_i32(n)
+    so1, sl1 = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx_d, n_d, block_table=d.block_table,
+                                   max_ctx=d.max_ctx)
+    ws = torch.empty(Bn.sparse_workspace_bytes(desc, idx.shape[1]), dtype=torch.uint8, device="cuda")
+    Bn.sparse_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, idx_d, n_d, ws)
+    so2, sl2 = torch.empty_like(so1), torch.empty_like(sl1)
+    Bn.combine_partials(desc, idx.shape[1], n_d, ws, so2, sl2)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(so2.float().cpu().numpy(), so1.float().cpu().numpy(), atol=8e-3)
+    np.testing.assert_allclose(sl2.cpu().numpy(), sl1.cpu().numpy(), atol=1e-5)
