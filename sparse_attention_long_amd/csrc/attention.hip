@@ -173,9 +173,9 @@ void attn_partials_kernel(AttnArgs a) {
   const int32_t* btab = a.paged ? a.block_table + (size_t)b * a.max_blocks : nullptr;
 
   // Issue the K/V loads of tile t0 (staging its positions first when sparse).
-  // Issue the K/V loads of this wavefront's tile number `it` (starting at t0),
-  // staging its positions first when sparse.
-  auto issue = [&](int t0, int it, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+  // Stage (sparse) the positions of this wavefront's tile number `it`
+  // (starting at t0) into sidx.
+  auto stage = [&](int t0, int it) {
     if (SPARSE) {
       if (lane < kTile) {
         const int li = t0 + lane;
@@ -189,6 +189,9 @@ void attn_partials_kernel(AttnArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
     }
+  };
+  // Issue the loads of one tensor's rows for the tile starting at t0.
+  auto issue = [&](int t0, const uint16_t* base, u32x4 (&dst)[NI]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = i * RPI + lrow;
@@ -200,16 +203,18 @@ void attn_partials_kernel(AttnArgs a) {
       } else {
         off = (uint32_t)pos * D;
       }
-      off += lchunk * 8;
-      kr[i] = load16_stream(kbase + off);
-      vr[i] = load16_stream(vbase + off);
+      dst[i] = load16_stream(base + off + lchunk * 8);
     }
   };
 
   u32x4 kraw[NI], vraw[NI];
   int ts = start + wave * kTile;
   int tile_no = 0;
-  if (ts < end) issue(ts, 0, kraw, vraw);
+  if (ts < end) {
+    stage(ts, 0);
+    issue(ts, kbase, kraw);
+    issue(ts, vbase, vraw);
+  }
 
   // Stage the query fragments (B operand of S^T = K Q^T) once the first
   // tile's loads are in flight: fragment (qb, ks, lane) holds row
@@ -250,13 +255,20 @@ void attn_partials_kernel(AttnArgs a) {
       }
     }
 
-    // K tile -> LDS [position][d]; read back as A fragments of S^T = K Q^T
-    // (lane (c16, kg) of step ks holds row pb*16 + c16, d = ks*32 + kg*8 ..).
-    // Per 16-row half: read the K fragments, overwrite those rows with V (LDS
-    // executes one wavefront's operations in order), multiply.
+    // K tile -> LDS [position][d]; its registers are free at once, so the
+    // next tile's K loads go out right away.  Per 16-row half: read the K
+    // fragments (A of S^T = K Q^T: lane (c16, kg) of step ks holds row
+    // pb*16 + c16, d = ks*32 + kg*8 ..), overwrite those rows with V (LDS
+    // executes one wavefront's operations in order), multiply.  V's loads
+    // for the next tile go out once V is in LDS.
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       *reinterpret_cast<u32x4*>(vt + (i * RPI + lrow) * VS + lchunk * 8) = kraw[i];
+    const int tn = ts + step;
+    if (tn < end) {
+      stage(tn, tile_no + 1);
+      issue(tn, kbase, kraw);
+    }
     f32x4 sacc[2][QB];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
@@ -272,6 +284,7 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = pb * (NI / 2); i < (pb + 1) * (NI / 2); ++i)
         *reinterpret_cast<u32x4*>(vt + (i * RPI + lrow) * VS + lchunk * 8) = vraw[i];
+      if (pb == 1 && tn < end) issue(tn, vbase, vraw);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -282,11 +295,6 @@ void attn_partials_kernel(AttnArgs a) {
         sacc[pb][qb] = acc;
       }
     }
-
-    // Prefetch the next tile's K/V rows while this one is consumed.
-    const int tn = ts + step;
-    ++tile_no;
-    if (tn < end) issue(tn, tile_no, kraw, vraw);
 
     // Collect-2-Query epilogue: pre-softmax logits of rows row0 / row1.
     if (EMIT == VGSA_LOGITS_PER_HEAD) {
@@ -299,7 +307,9 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = pb * 16 + 4 * kg + r;
-            if (e < n_in) lp[e] = (full || e < vis[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
+            if (e < n_in)
+              __builtin_nontemporal_store((full || e < vis[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf,
+                                          lp + e);
           }
       }
     } else if (EMIT == VGSA_LOGITS_KVGROUP_SUM) {
@@ -336,7 +346,9 @@ void attn_partials_kernel(AttnArgs a) {
       float v1 = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 2);
       v1 += __shfl_xor(v1, 1);
       const int e = (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
-      if ((c16 & 1) == 0 && e < n_in) a.logits[((size_t)b * a.hkv + g) * a.max_ctx + ts + e] = v1;
+      // nontemporal: written once here and read once by the next kernel
+      if ((c16 & 1) == 0 && e < n_in)
+        __builtin_nontemporal_store(v1, a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + ts + e);
     }
 
     // Online softmax (log2 units, lazily rescaled) and the P fragments
@@ -400,6 +412,7 @@ void attn_partials_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    ++tile_no;
   }
 
   // Row sums: combine the four 16-lane groups.
@@ -485,7 +498,7 @@ void attn_partials_kernel(AttnArgs a) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < NBUF; ++i) acc += obuf[i * kMaxRows * OS + m * OS + d];
-    a.part_o[prow * D + d] = acc;
+    __builtin_nontemporal_store(acc, a.part_o + prow * D + d);  // written once, read once
   }
   if ((int)threadIdx.x < rows) {
     const int m = threadIdx.x;

@@ -247,3 +247,22 @@ def test_two_phase_api_matches_one_call(name):
     torch.cuda.synchronize()
     np.testing.assert_allclose(so2.float().cpu().numpy(), so1.float().cpu().numpy(), atol=8e-3)
     np.testing.assert_allclose(sl2.cpu().numpy(), sl1.cpu().numpy(), atol=1e-5)
+
+
+@pytest.mark.parametrize("count,stride", [(1000, 1000), (3000, 3000), (700, 1024)])
+def test_sparse_long_lists_many_tiles_per_wavefront(count, stride):
+    """Lists long enough that every wavefront walks several tiles (one split
+    with 8 wavefronts up to 1024 entries; several splits beyond), including
+    tiles past the preloaded ones."""
+    w = W.small("longlist", batch=2, num_q_heads=16, num_kv_heads=2, head_dim=64, gamma=4,
+                lens=(4000, 3500), budget=64, n_sink=4, window=16, seed=21)
+    say(f"[sparse long lists] count={count} stride={stride}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    idx, n = W.index_lists(31 + count, x.seq_lens, count=count, stride=stride)
+    out, lse = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, dev_i32(idx), dev_i32(n))
+    torch.cuda.synchronize()
+    lists = [idx[b, :n[b]] for b in range(w.batch)]
+    o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, x.seq_lens, lists)
+    assert_out_close(out, o_ref, f"long list {count}")
+    assert_lse_close(lse, lse_ref, f"long list {count} lse")
