@@ -204,20 +204,18 @@ def main():
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
         if ev is not None:
             ev[1].record()
-        Bn.combine_partials(desc, max_ctx, lens, ws_v, out, lse)
+        # split combine + score aggregation in one launch
+        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
         if ev is not None:
             ev[2].record()
-        Bn.aggregate_scores(logits, lens, Hq, Hkv, scores=scores)
-        if ev is not None:
-            ev[3].record()
         Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         if ev is not None:
-            ev[4].record()
+            ev[3].record()
         if w.sparse_verify:
             Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                 out=out_s, lse=lse_s, workspace=ws_s)
             if ev is not None:
-                ev[5].record()
+                ev[4].record()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -253,8 +251,7 @@ def main():
         a.record()
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
         b_.record()
-        Bn.combine_partials(desc, max_ctx, lens, ws_v, out, lse)
-        Bn.aggregate_scores(logits, lens, Hq, Hkv, scores=scores)
+        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
         Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         if w.sparse_verify:
             Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
@@ -271,7 +268,7 @@ def main():
     log(f"[bench] {K} steps: wall {wall * 1e3:.2f} ms, gpu {gpu_ms:.2f} ms, verify kernel {verify_us:.1f} us")
 
     # ---- stage breakdown and logit-emit overhead (outside the timed region)
-    nst = 6
+    nst = 5
     stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(K)]
     for i in range(K):
         step(stage_ev[i])
@@ -280,10 +277,9 @@ def main():
     def span(i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in stage_ev])) * 1e3
 
-    stages = {"verify_partials": span(0, 1), "verify_combine": span(1, 2), "aggregate": span(2, 3),
-              "select": span(3, 4)}
+    stages = {"verify_partials": span(0, 1), "combine_aggregate": span(1, 2), "select": span(2, 3)}
     if w.sparse_verify:
-        stages["sparse"] = span(4, 5)
+        stages["sparse"] = span(3, 4)
     none_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(K)]
     for a, b_ in none_ev:

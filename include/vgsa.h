@@ -45,6 +45,11 @@
  *     and < seq_lens[b]; n_idx[b] <= idx_stride; block ids < num_blocks.  The
  *     kernels clamp them into range so a violation gives wrong numbers, never
  *     an out-of-bounds access.
+ *   - Alignment: q, k_cache, v_cache and out are read or written as 16-byte
+ *     vectors and must be 16-byte aligned; a workspace must be 256-byte
+ *     aligned (hipMalloc and caching-allocator blocks are).  Checked on the
+ *     host: VGSA_ERR_INVALID_ARG, or VGSA_ERR_WORKSPACE for the workspace.
+ *     Other pointers need only their element's natural alignment.
  *   - Row-major layouts.  GQA: q-head h reads kv-head h / (Hq / Hkv).
  *   - No global mutable state; calls are reentrant.  Calls that share a
  *     workspace must be ordered on one stream.
@@ -67,7 +72,7 @@ typedef enum vgsa_status {
   VGSA_OK = 0,
   VGSA_ERR_INVALID_ARG = 1, /* a scalar, shape or pointer is invalid         */
   VGSA_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels implement */
-  VGSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  VGSA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned    */
   VGSA_ERR_HIP = 4          /* a HIP launch failed                           */
 } vgsa_status;
 
@@ -219,6 +224,21 @@ vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, cons
 vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
                                   const int32_t* lengths, const void* workspace,
                                   size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/* Steps 1 (second phase) and 2 in one launch: merge the verify partials into
+ * out / lse exactly as vgsa_combine_partials(span = max_ctx, lengths =
+ * seq_lens) and, when scores is non-NULL, aggregate the collected logits into
+ * scores exactly as vgsa_aggregate_scores (same per-position summation order,
+ * so the values are identical).  Both only read what vgsa_verify_partials
+ * wrote, so one kernel does both.
+ * (Vegas §2 step 1 and "A. aggregated attention-logit selection".)
+ * layout   the layout logits were written in (PER_HEAD or KVGROUP_SUM);
+ *          ignored when scores is NULL
+ * scores   fp32 [B][max_ctx] or NULL */
+vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
+                               const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                               vgsa_logit_layout layout, const float* logits, float* scores,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -50,6 +50,8 @@ SIGNATURES = {
                                      c_vp, c_i32, c_vp, c_sz, c_vp]),
     "vgsa_combine_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_i32, c_vp, c_vp, c_sz, c_vp,
                                       c_vp, c_vp]),
+    "vgsa_verify_finish": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp, c_i32,
+                                   c_vp, c_vp, c_vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -262,3 +264,12 @@ def combine_partials(desc: AttnDesc, span: int, lengths, workspace, out, lse) ->
     _check(load().vgsa_combine_partials(
         ctypes.byref(desc), span, _p(lengths), _p(workspace), workspace.numel(), _p(out), _p(lse),
         _stream(out.device)), "vgsa_combine_partials")
+
+
+def verify_finish(desc: AttnDesc, seq_lens, workspace, out, lse, layout: int = LOGITS_NONE,
+                  logits=None, scores=None) -> None:
+    """vgsa_verify_finish: combine the verify partials and (with `scores`)
+    aggregate the collected logits, in one launch."""
+    _check(load().vgsa_verify_finish(
+        ctypes.byref(desc), _p(seq_lens), _p(workspace), workspace.numel(), _p(out), _p(lse),
+        layout, _p(logits), _p(scores), _stream(out.device)), "vgsa_verify_finish")

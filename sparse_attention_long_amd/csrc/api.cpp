@@ -12,6 +12,7 @@ namespace {
 
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr int64_t kMaxOffset = 0xFFFFFFFFLL;
+constexpr uintptr_t kWorkspaceAlign = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -95,11 +96,23 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
   return a;
 }
 
+bool aligned(const void* p, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
+
+// The partials are read and written as 16-byte vectors.
+vgsa_status check_workspace(const void* ws, size_t have, size_t need) {
+  if (ws == nullptr || have < need || !aligned(ws, kWorkspaceAlign)) return VGSA_ERR_WORKSPACE;
+  return VGSA_OK;
+}
+
 vgsa_status check_attn_pointers(const vgsa_attn_desc& d, const void* q, const void* k,
                                 const void* v, const int32_t* block_table,
                                 const int32_t* seq_lens) {
   if (q == nullptr || k == nullptr || v == nullptr || seq_lens == nullptr)
     return VGSA_ERR_INVALID_ARG;
+  // q, K and V rows are loaded as 16-byte vectors
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return VGSA_ERR_INVALID_ARG;
   if ((d.block_size == 16) != (block_table != nullptr)) return VGSA_ERR_INVALID_ARG;
   return VGSA_OK;
 }
@@ -139,7 +152,7 @@ const char* vgsa_status_string(vgsa_status status) {
     case VGSA_OK: return "ok";
     case VGSA_ERR_INVALID_ARG: return "invalid argument";
     case VGSA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case VGSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case VGSA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case VGSA_ERR_HIP: return "HIP launch failed";
   }
   return "unknown status";
@@ -193,7 +206,8 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
       return VGSA_ERR_INVALID_ARG;
   }
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
-  if (workspace == nullptr || workspace_bytes < partial_bytes(d, p)) return VGSA_ERR_WORKSPACE;
+  st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
+  if (st != VGSA_OK) return st;
   if (d.batch == 0) return VGSA_OK;
   AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens, workspace);
   a.layout = layout;
@@ -218,7 +232,8 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   if (st != VGSA_OK) return st;
   if (idx == nullptr || n_idx == nullptr || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, idx_stride);
-  if (workspace == nullptr || workspace_bytes < partial_bytes(d, p)) return VGSA_ERR_WORKSPACE;
+  st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
+  if (st != VGSA_OK) return st;
   if (d.batch == 0) return VGSA_OK;
   AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens, workspace);
   a.idx = idx;
@@ -259,9 +274,11 @@ vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
-  if (span < 1 || lengths == nullptr || out == nullptr) return VGSA_ERR_INVALID_ARG;
+  if (span < 1 || lengths == nullptr || out == nullptr || !aligned(out, 16))
+    return VGSA_ERR_INVALID_ARG;
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, span);
-  if (workspace == nullptr || workspace_bytes < partial_bytes(d, p)) return VGSA_ERR_WORKSPACE;
+  st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
+  if (st != VGSA_OK) return st;
   const int64_t rows = (int64_t)d.batch * d.num_q_heads * d.q_len;
   if (rows > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
   if (rows == 0) return VGSA_OK;
@@ -289,7 +306,7 @@ vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, con
                                   void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
-  if (out == nullptr) return VGSA_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16)) return VGSA_ERR_INVALID_ARG;
   const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, desc->max_ctx);
   if (p.num_splits == 1) {
     // one split: the partials kernel finishes the softmax and writes out / lse
@@ -311,7 +328,7 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
                                   void* workspace, size_t workspace_bytes, void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
-  if (out == nullptr || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned(out, 16) || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
   const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, idx_stride);
   if (p.num_splits == 1) {
     return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
@@ -322,6 +339,43 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
   if (st != VGSA_OK) return st;
   return vgsa_combine_partials(desc, idx_stride, n_idx, workspace, workspace_bytes, out, lse,
                                stream);
+}
+
+vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
+                               const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                               vgsa_logit_layout layout, const float* logits, float* scores,
+                               void* stream) {
+  vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  const vgsa_attn_desc& d = *desc;
+  if (seq_lens == nullptr || out == nullptr || !aligned(out, 16)) return VGSA_ERR_INVALID_ARG;
+  if (scores != nullptr) {
+    if (layout != VGSA_LOGITS_PER_HEAD && layout != VGSA_LOGITS_KVGROUP_SUM)
+      return VGSA_ERR_INVALID_ARG;
+    if (logits == nullptr) return VGSA_ERR_INVALID_ARG;
+  }
+  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
+  st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
+  if (st != VGSA_OK) return st;
+  const int64_t rows = (int64_t)d.batch * d.num_q_heads * d.q_len;
+  if (rows > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
+  if (rows == 0) return VGSA_OK;
+  const Carve c = carve(d, p, const_cast<void*>(workspace));
+  CombineArgs ca{};
+  ca.part_o = c.part_o;
+  ca.part_ml = c.part_ml;
+  ca.lengths = seq_lens;
+  ca.rows = (int32_t)rows;
+  ca.rows_per_seq = d.num_q_heads * d.q_len;
+  ca.head_dim = d.head_dim;
+  ca.num_splits = p.num_splits;
+  ca.chunk = p.chunk;
+  ca.span = d.max_ctx;
+  ca.out = static_cast<uint16_t*>(out);
+  ca.lse = lse;
+  AggregateArgs ag{d.batch, d.num_q_heads, d.num_kv_heads, d.max_ctx, (int32_t)layout, logits,
+                   seq_lens, scores};
+  return hip_status(launch_combine_aggregate(ca, ag, static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -26,6 +26,7 @@
 // The four wavefronts are merged through LDS at the end and the workgroup
 // writes its un-normalised partial (o, m, l) for the combine kernel.
 #include "internal.h"
+#include "merge_ops.h"
 
 namespace vgsa {
 namespace {
@@ -511,29 +512,8 @@ void attn_partials_kernel(AttnArgs a) {
 
 // One block of D threads per (sequence, head, row): exact merge of the splits.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(CombineArgs a) {
-  const int row = blockIdx.x;
-  const int b = row / a.rows_per_seq;
-  const int d = threadIdx.x;
-  const int len = min(max(a.lengths[b], 0), a.span);
-  const int nvalid = min((len + a.chunk - 1) / a.chunk, a.num_splits);
-  const float* ml = a.part_ml + (size_t)row * a.num_splits * 2;
-  const float* po = a.part_o + (size_t)row * a.num_splits * D;
-  float M = kNegInf;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, ml[2 * s]);
-  float l = 0.f, acc = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < nvalid; ++s) {
-      const float ms = ml[2 * s];
-      if (ms == kNegInf) continue;
-      const float w = fast_exp2(ms - M);
-      l += w * ml[2 * s + 1];
-      acc += w * po[(size_t)s * D + d];
-    }
-  }
-  const float o = l > 0.f ? acc / l : 0.f;
-  a.out[(size_t)row * D + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
-  if (a.lse != nullptr && d == 0) a.lse[row] = l > 0.f ? (M + __log2f(l)) * kLn2 : kNegInf;
+__global__ __launch_bounds__(kMergeBlock) void combine_kernel(CombineArgs a) {
+  combine_block<D>(a, blockIdx.x);
 }
 
 template <int D, bool SPARSE, int EMIT, int WAVES>
@@ -577,9 +557,11 @@ hipError_t launch_attention_partials(const AttnArgs& a, bool sparse, hipStream_t
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.head_dim == 64) {
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(a.rows), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(combine_blocks<64>(a.rows)), dim3(kMergeBlock), 0,
+                       s, a);
   } else {
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(a.rows), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(combine_blocks<128>(a.rows)), dim3(kMergeBlock),
+                       0, s, a);
   }
   return hipGetLastError();
 }

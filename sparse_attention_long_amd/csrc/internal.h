@@ -78,6 +78,17 @@ struct CombineArgs {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
+struct AggregateArgs {
+  int32_t batch, hq, hkv, max_ctx, layout;
+  const float* logits;
+  const int32_t* seq_lens;
+  float* scores;
+};
+
+// Combine and (when ag.scores != null) aggregate in one launch.
+hipError_t launch_combine_aggregate(const CombineArgs& c, const AggregateArgs& ag,
+                                    hipStream_t stream);
+
 hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t layout,
                             const float* logits, const int32_t* seq_lens, float* scores,
                             hipStream_t stream);

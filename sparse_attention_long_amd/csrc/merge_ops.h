@@ -1,0 +1,104 @@
+// Device-side pieces shared by the combine, aggregate and fused kernels.
+#pragma once
+
+#include "internal.h"
+
+namespace vgsa {
+
+// Threads of a combine / aggregate workgroup.
+constexpr int kMergeBlock = 256;
+
+// Splits (or logit rows) whose loads are issued together before any is used:
+// the merge is a chain of dependent HBM round trips otherwise.
+constexpr int kMergeBatch = 8;
+
+// Exact merge of the split partials of four output elements (row of
+// [B][Hq][T], columns 4t..4t+3): m = max_s m_s, l = sum_s l_s 2^(m_s - m),
+// o = sum_s o_s 2^(m_s - m) / l, lse = ln 2 * (m + log2 l).  The m_s are in
+// log2 units.  Splits at or past the sequence's length hold nothing; a split
+// the row sees nothing of has m_s = -inf and is skipped.  Splits are merged
+// kMergeBatch at a time, each batch rescaled to its running maximum, in split
+// order (with at most kMergeBatch splits this is the plain two-pass sum).
+template <int D>
+__device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int t) {
+  constexpr float kNegInf = -__builtin_huge_valf();
+  constexpr int Q = D / 4;
+  const int b = row / a.rows_per_seq;
+  const int len = min(max(a.lengths[b], 0), a.span);
+  const int nvalid = min((len + a.chunk - 1) / a.chunk, a.num_splits);
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)row * a.num_splits;
+  const float4* po = reinterpret_cast<const float4*>(a.part_o) + (size_t)row * a.num_splits * Q + t;
+  float M = kNegInf, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < nvalid; s0 += kMergeBatch) {
+    float2 m[kMergeBatch];
+    float4 o[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (s0 + i < nvalid) {
+        m[i] = ml[s0 + i];
+        o[i] = po[(size_t)(s0 + i) * Q];
+      } else {
+        m[i] = make_float2(kNegInf, 0.f);
+        o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) mc = fmaxf(mc, m[i].x);
+    if (mc == kNegInf) continue;
+    const float r = __builtin_amdgcn_exp2f(M - mc);  // 0 while nothing was merged
+    l *= r;
+    acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (m[i].x == kNegInf) continue;  // also skips unused slots of the batch
+      const float w = __builtin_amdgcn_exp2f(m[i].x - mc);
+      l += w * m[i].y;
+      acc.x += w * o[i].x; acc.y += w * o[i].y; acc.z += w * o[i].z; acc.w += w * o[i].w;
+    }
+    M = mc;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc.x * inv)) |
+                      (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.y * inv)) << 16;
+  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)(acc.z * inv)) |
+                      (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.w * inv)) << 16;
+  reinterpret_cast<uint2*>(a.out)[(size_t)row * Q + t] = make_uint2(lo, hi);
+  if (a.lse != nullptr && t == 0)
+    a.lse[row] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994530942f : kNegInf;
+}
+
+// One workgroup of kMergeBlock threads combines kMergeBlock / (D / 4) rows.
+template <int D>
+__device__ __forceinline__ void combine_block(const CombineArgs& a, int block) {
+  constexpr int Q = D / 4;
+  const int row = block * (kMergeBlock / Q) + threadIdx.x / Q;
+  if (row < a.rows) combine_quad<D>(a, row, threadIdx.x % Q);
+}
+
+template <int D>
+constexpr int combine_blocks(int rows) {
+  return (rows + kMergeBlock / (D / 4) - 1) / (kMergeBlock / (D / 4));
+}
+
+// Score of position j of sequence b: the collected logits summed in a fixed
+// order (kv-groups ascending, or rows then heads ascending).
+__device__ __forceinline__ void aggregate_position(const AggregateArgs& a, int b, int j) {
+  const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
+  if (j >= L) return;
+  const int n = a.layout == VGSA_LOGITS_KVGROUP_SUM ? a.hkv : 2 * a.hq;
+  const float* p = a.logits + (size_t)b * n * a.max_ctx + j;
+  float s = 0.f;
+  for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
+    float v[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) v[i] = r0 + i < n ? p[(size_t)(r0 + i) * a.max_ctx] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (r0 + i < n) s += v[i];
+  }
+  a.scores[(size_t)b * a.max_ctx + j] = s;
+}
+
+}  // namespace vgsa

@@ -10,28 +10,29 @@
 // then head; or kv-group ascending), so results are deterministic.  The
 // kernel is a coalesced streaming read, bound by HBM bandwidth.
 #include "internal.h"
+#include "merge_ops.h"
 
 namespace vgsa {
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = kMergeBlock;
 
-__global__ __launch_bounds__(kBlock) void aggregate_kernel(int32_t hq, int32_t hkv, int32_t max_ctx,
-                                                           int32_t layout, const float* logits,
-                                                           const int32_t* seq_lens, float* scores) {
-  const int b = blockIdx.y;
-  const int j = blockIdx.x * kBlock + threadIdx.x;
-  const int L = min(max(seq_lens[b], 0), max_ctx);
-  if (j >= L) return;
-  float s = 0.f;
-  if (layout == VGSA_LOGITS_KVGROUP_SUM) {
-    const float* p = logits + (size_t)b * hkv * max_ctx + j;
-    for (int g = 0; g < hkv; ++g) s += p[(size_t)g * max_ctx];
-  } else {
-    const float* p = logits + (size_t)b * 2 * hq * max_ctx + j;
-    for (int r = 0; r < 2 * hq; ++r) s += p[(size_t)r * max_ctx];
+__global__ __launch_bounds__(kBlock) void aggregate_kernel(AggregateArgs a) {
+  aggregate_position(a, blockIdx.y, blockIdx.x * kBlock + threadIdx.x);
+}
+
+// Combine (the first n_combine workgroups) and aggregate (the rest, kBlock
+// positions each, sequences in order) in one launch.
+template <int D>
+__global__ __launch_bounds__(kBlock) void combine_aggregate_kernel(CombineArgs c, AggregateArgs ag,
+                                                                   int32_t n_combine,
+                                                                   int32_t pos_blocks) {
+  if ((int)blockIdx.x < n_combine) {
+    combine_block<D>(c, blockIdx.x);
+    return;
   }
-  scores[(size_t)b * max_ctx + j] = s;
+  const int q = blockIdx.x - n_combine;
+  aggregate_position(ag, q / pos_blocks, (q % pos_blocks) * kBlock + threadIdx.x);
 }
 
 }  // namespace
@@ -39,9 +40,25 @@ __global__ __launch_bounds__(kBlock) void aggregate_kernel(int32_t hq, int32_t h
 hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t layout,
                             const float* logits, const int32_t* seq_lens, float* scores,
                             hipStream_t stream) {
+  AggregateArgs a{batch, hq, hkv, max_ctx, layout, logits, seq_lens, scores};
   const dim3 grid((max_ctx + kBlock - 1) / kBlock, batch);
-  hipLaunchKernelGGL(aggregate_kernel, grid, dim3(kBlock), 0, stream, hq, hkv, max_ctx, layout,
-                     logits, seq_lens, scores);
+  hipLaunchKernelGGL(aggregate_kernel, grid, dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_aggregate(const CombineArgs& c, const AggregateArgs& ag,
+                                    hipStream_t stream) {
+  const int n_combine = c.head_dim == 64 ? combine_blocks<64>(c.rows) : combine_blocks<128>(c.rows);
+  const int pos_blocks = ag.scores ? (ag.max_ctx + kBlock - 1) / kBlock : 0;
+  const int64_t total = (int64_t)n_combine + (int64_t)pos_blocks * (ag.scores ? ag.batch : 0);
+  if (total <= 0) return hipSuccess;
+  if (c.head_dim == 64) {
+    hipLaunchKernelGGL(combine_aggregate_kernel<64>, dim3((unsigned)total), dim3(kBlock), 0, stream,
+                       c, ag, n_combine, pos_blocks);
+  } else {
+    hipLaunchKernelGGL(combine_aggregate_kernel<128>, dim3((unsigned)total), dim3(kBlock), 0,
+                       stream, c, ag, n_combine, pos_blocks);
+  }
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -119,6 +119,14 @@ def test_verify_argument_checks(lib):
     # workspace missing or one byte short
     assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, None, ws, None) == WORKSPACE
     assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
+    # misaligned q / cache / out; misaligned workspace
+    ODD = ctypes.c_void_p(0x1008)
+    assert V(dp, ODD, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, ODD, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, ODD, None, FAKE, 0, 3, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, ODD, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 0, 3, 2, FAKE, FAKE, None, ctypes.c_void_p(0x1010),
+             ws, None) == WORKSPACE
     # paged cache without a block table
     dpg = desc(block_size=16, max_blocks_per_seq=63, num_blocks=100, max_ctx=1000)
     wsp = lib.vgsa_verify_workspace_bytes(ctypes.byref(dpg))
@@ -138,6 +146,14 @@ def test_sparse_and_combine_argument_checks(lib):
     assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
     C = lib.vgsa_combine_partials
     assert C(dp, 0, FAKE, FAKE, ws, FAKE, None, None) == INVALID
+    F = lib.vgsa_verify_finish
+    wv = lib.vgsa_verify_workspace_bytes(dp)
+    assert F(dp, None, FAKE, wv, FAKE, None, 2, FAKE, FAKE, None) == INVALID
+    assert F(dp, FAKE, FAKE, wv, None, None, 2, FAKE, FAKE, None) == INVALID
+    assert F(dp, FAKE, FAKE, wv, FAKE, None, 0, FAKE, FAKE, None) == INVALID   # scores need a layout
+    assert F(dp, FAKE, FAKE, wv, FAKE, None, 2, None, FAKE, None) == INVALID   # ... and logits
+    assert F(dp, FAKE, FAKE, wv - 1, FAKE, None, 2, FAKE, FAKE, None) == WORKSPACE
+    assert F(ctypes.byref(desc(head_dim=96)), FAKE, FAKE, wv, FAKE, None, 2, FAKE, FAKE, None) == UNSUPPORTED
     assert C(dp, 64, None, FAKE, ws, FAKE, None, None) == INVALID
     assert C(dp, 64, FAKE, FAKE, ws, None, None, None) == INVALID
     assert C(dp, 64, FAKE, FAKE, ws - 1, FAKE, None, None) == WORKSPACE

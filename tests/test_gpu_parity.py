@@ -266,3 +266,36 @@ def test_sparse_long_lists_many_tiles_per_wavefront(count, stride):
     o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, x.seq_lens, lists)
     assert_out_close(out, o_ref, f"long list {count}")
     assert_lse_close(lse, lse_ref, f"long list {count} lse")
+
+
+@pytest.mark.parametrize("name", ["g8t5_d128", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])
+def test_verify_finish_equals_combine_and_aggregate(name):
+    """The fused combine + aggregate launch gives the same bytes as the two
+    separate calls (same per-element code and summation order)."""
+    w = CASES[name]
+    x = W.make_layer(w)
+    d = to_device(x)
+    desc = Bn.make_desc(d.q, d.k, d.block_table, d.max_ctx)
+    for layout, code in (("kvgroup_sum", Bn.LOGITS_KVGROUP_SUM), ("per_head", Bn.LOGITS_PER_HEAD)):
+        ws = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        shape = (w.batch, w.num_kv_heads, d.max_ctx) if code == Bn.LOGITS_KVGROUP_SUM else \
+            (w.batch, 2, w.num_q_heads, d.max_ctx)
+        lg = torch.empty(shape, dtype=torch.float32, device="cuda")
+        Bn.verify_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, w.collect_rows, code, lg, ws)
+        o1, l1 = torch.empty_like(d.q), torch.empty(d.q.shape[:3], dtype=torch.float32, device="cuda")
+        Bn.combine_partials(desc, d.max_ctx, d.seq_lens, ws, o1, l1)
+        s1 = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads, layout=layout)
+        o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+        s2 = torch.full_like(s1, 7.0)
+        Bn.verify_finish(desc, d.seq_lens, ws, o2, l2, code, lg, s2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1, l2)
+        for b in range(w.batch):
+            L = int(x.seq_lens[b])
+            assert torch.equal(s1[b, :L], s2[b, :L])
+            assert torch.all(s2[b, L:] == 7.0)  # positions past the length are untouched
+        o3 = torch.empty_like(o1)
+        Bn.verify_finish(desc, d.seq_lens, ws, o3, None)  # combine only
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
