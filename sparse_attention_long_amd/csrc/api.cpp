@@ -128,6 +128,7 @@ SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span) {
   if (s < 1) s = 1;
   if (s > max_splits) s = max_splits;
   int64_t chunk = ceil_div(ceil_div(span, s), kMinChunk) * kMinChunk;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
   s = ceil_div(span, chunk);
   SplitPlan p;
   p.num_splits = (int32_t)s;

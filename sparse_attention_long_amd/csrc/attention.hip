@@ -19,7 +19,11 @@
 //      ahead in registers),
 //   2. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (positions are the
 //      M side, query rows the N side),
-//   3. writes the collected logits (per head, or summed over the kv-group),
+//   3. writes the collected logits: per head straight to HBM, or summed over
+//      the kv-group into an LDS copy of the chunk that goes out in one burst
+//      after the loop (the sum comes from two extra query columns holding
+//      the summed collected queries when the group leaves them free, else
+//      from a cross-lane reduction),
 //   4. runs an online softmax in log2 units per query row,
 //   5. accumulates O^T += V^T P^T with the same MFMA; P comes straight from
 //      the S^T accumulators, V^T is read from a per-wavefront LDS tile.
@@ -63,6 +67,20 @@ struct Occupancy {
   static constexpr int kWavesPerEU = (D == 128 && QB == 4) ? 1 : 2;
 };
 
+// Kv-group-summed logits taken straight from the MFMA: the logit sum over the
+// collected rows of the group is K . (sum of their scaled queries), so the
+// summed query, split into a bf16 high part and the bf16 rounding of the
+// remainder (about 16 significant bits together), rides in the last two
+// query columns of the last 16-row block when the group leaves them free.
+// Internal emit mode; the layout written is VGSA_LOGITS_KVGROUP_SUM.
+constexpr int kEmitSumColumn = 3;
+
+__device__ __forceinline__ float swap_adjacent_lanes(float x) {  // lane i <-> lane i ^ 1
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                           0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF,
+                                                           true));
+}
+
 // Lazy rescaling: a row's running max is only raised (and O, l rescaled)
 // when a tile exceeds it by more than 2^kRescaleLog2; otherwise the stale max
 // is kept, so p <= 2^kRescaleLog2.  The combine uses the same (m, l, O)
@@ -93,6 +111,11 @@ void attn_partials_kernel(AttnArgs a) {
   __shared__ float s_m[WAVES][kMaxRows];
   __shared__ float s_l[WAVES][kMaxRows];
   __shared__ int s_idx[WAVES][kTile];
+  // Kv-group logits of the chunk, written out after the loop: one burst of
+  // contiguous 16-byte stores instead of 128 bytes per tile, which would
+  // interleave small writes with the K/V read stream.
+  constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || EMIT == kEmitSumColumn;
+  __shared__ __align__(16) float slog[kGroupLogits ? kMaxChunk : 4];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -228,6 +251,26 @@ void attn_partials_kernel(AttnArgs a) {
       const int h = g * G + m / T, t = m % T;
       val = *reinterpret_cast<const u32x4*>(a.q + (((size_t)b * a.hq + h) * T + t) * D +
                                             fks * 32 + (fl >> 4) * 8);
+    } else if (EMIT == kEmitSumColumn && m >= QB * 16 - 2) {
+      // summed query of the collected rows (heads ascending, row0 then row1):
+      // column QB*16-2 its bf16 rounding, column QB*16-1 the rest
+      float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int t = c == 0 ? a.row0 : a.row1;
+          const bf16x8 qv = load16(a.q + (((size_t)b * a.hq + g * G + hh) * T + t) * D + fks * 32 +
+                                   (fl >> 4) * 8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qs[j] += (float)qv[j];
+        }
+      bf16x8 part;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const __bf16 hi = (__bf16)qs[j];
+        part[j] = m == QB * 16 - 2 ? hi : (__bf16)(qs[j] - (float)hi);
+      }
+      val = __builtin_bit_cast(u32x4, part);
     }
     sq[f] = val;
   }
@@ -347,9 +390,29 @@ void attn_partials_kernel(AttnArgs a) {
       float v1 = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 2);
       v1 += __shfl_xor(v1, 1);
       const int e = (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
-      // nontemporal: written once here and read once by the next kernel
-      if ((c16 & 1) == 0 && e < n_in)
-        __builtin_nontemporal_store(v1, a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + ts + e);
+      if ((c16 & 1) == 0) slog[ts - start + e] = v1;
+    }
+
+    if (EMIT == kEmitSumColumn) {
+      // Lanes c16 = 14 / 15 of the last block hold K . (high / low part);
+      // after the exchange both hold the sum.  The earlier collected row sees
+      // a prefix of what the later one sees, so past its causal limit the
+      // sum is -inf.
+      const int vis0 = full ? kTile : max(0, min(L - T + a.row0, ts + n_in - 1) - ts + 1);
+      f32x4 lv[2];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = sacc[pb][QB - 1][r];
+          x += swap_adjacent_lanes(x);
+          lv[pb][r] = (pb * 16 + 4 * kg + r) < vis0 ? x * a.scale : kNegInf;
+        }
+      if (c16 == 14) {
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb)
+          *reinterpret_cast<f32x4*>(slog + (ts - start) + pb * 16 + 4 * kg) = lv[pb];
+      }
     }
 
     // Online softmax (log2 units, lazily rescaled) and the P fragments
@@ -430,6 +493,19 @@ void attn_partials_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+
+  if (kGroupLogits) {  // the chunk's logits [start, end), nontemporal (read once, later)
+    float* lp = a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + start;
+    const int n = end - start;
+    if ((reinterpret_cast<uintptr_t>(lp) & 15) == 0) {
+      for (int i = threadIdx.x * 4; i + 4 <= n; i += NT * 4)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(slog + i),
+                                    reinterpret_cast<f32x4*>(lp + i));
+      for (int i = (n & ~3) + threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
+    } else {
+      for (int i = threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
+    }
+  }
 
   // Merge the wavefronts, relative to each row's workgroup max M: groups of
   // NBUF wavefronts accumulate into NBUF fp32 buffers (4 barrier rounds);
@@ -536,14 +612,21 @@ template <int D>
 hipError_t launch_dim(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) {
   if (sparse) {
     // one split over a list longer than one round of 4 wavefronts: 8 wavefronts
-    if (a.num_splits == 1 && a.chunk > kMinChunk)
+    // (not for four query blocks of d = 128, whose registers allow one
+    // wavefront per SIMD only)
+    if (a.num_splits == 1 && a.chunk > kMinChunk && (D == 64 || a.group * a.q_len <= 48))
       return launch_d<D, true, VGSA_LOGITS_NONE, kWavesWide>(a, grid, s);
     return launch_d<D, true, VGSA_LOGITS_NONE, kWaves>(a, grid, s);
   }
   switch (a.layout) {
     case VGSA_LOGITS_PER_HEAD: return launch_d<D, false, VGSA_LOGITS_PER_HEAD, kWaves>(a, grid, s);
-    case VGSA_LOGITS_KVGROUP_SUM:
+    case VGSA_LOGITS_KVGROUP_SUM: {
+      // the summed query fits in the last block's two spare columns
+      const int rows = a.group * a.q_len;
+      if (rows + 2 <= (rows + 15) / 16 * 16)
+        return launch_d<D, false, kEmitSumColumn, kWaves>(a, grid, s);
       return launch_d<D, false, VGSA_LOGITS_KVGROUP_SUM, kWaves>(a, grid, s);
+    }
     default: return launch_d<D, false, VGSA_LOGITS_NONE, kWaves>(a, grid, s);
   }
 }
@@ -551,6 +634,7 @@ hipError_t launch_dim(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) 
 }  // namespace
 
 hipError_t launch_attention_partials(const AttnArgs& a, bool sparse, hipStream_t s) {
+  if (a.chunk > kMaxChunk) return hipErrorInvalidValue;  // the split plan never makes one
   const dim3 grid(a.num_splits, a.hkv, a.batch);
   return a.head_dim == 64 ? launch_dim<64>(a, sparse, grid, s) : launch_dim<128>(a, sparse, grid, s);
 }

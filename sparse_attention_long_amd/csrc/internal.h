@@ -23,6 +23,9 @@ constexpr int kTargetWorkgroups = 1024;
 // (sequence, kv-head) finishes the softmax itself and writes the output
 // directly (no partials, no combine launch).
 constexpr int kDirectSpan = 1024;
+// Largest chunk of one split: a workgroup keeps its chunk's kv-group logits
+// in LDS (fp32) and writes them out in one burst at the end.
+constexpr int kMaxChunk = 4096;
 // Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.
 constexpr int kMaxRows = 64;
 
