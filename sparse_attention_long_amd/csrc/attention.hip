@@ -99,10 +99,6 @@ void attn_partials_kernel(AttnArgs a) {
   constexpr int KS = D / 32;       // MFMA steps over the head dimension
   constexpr int DB = D / 16;       // 16-wide blocks of the head dimension
   constexpr int VS = D + 16;       // V tile row stride (elements): rows land 32 B apart in the banks
-  constexpr int OS = D + 4;        // merge-buffer row stride (floats)
-  constexpr int NBUF = WAVES / 4;  // merge buffers: wavefronts merge NBUF at a time
-  static_assert(WAVES % 4 == 0, "wavefronts merge in groups");
-  static_assert(WAVES * kTile * VS * 2 >= NBUF * kMaxRows * OS * 4, "merge buffers must fit in the V tiles");
   // Per-wavefront K/V tiles, [position][d]; reused at the end as the fp32
   // merge buffers.
   __shared__ __align__(16) uint16_t sbuf[WAVES * kTile * VS];
@@ -110,6 +106,7 @@ void attn_partials_kernel(AttnArgs a) {
   __shared__ __align__(16) u32x4 sq[QB * KS * 64];
   __shared__ float s_m[WAVES][kMaxRows];
   __shared__ float s_l[WAVES][kMaxRows];
+  __shared__ float s_inv[kMaxRows];  // 1 / (merged row sum), for the one-split output
   __shared__ int s_idx[WAVES][kTile];
   // Kv-group logits of the chunk, written out after the loop: one burst of
   // contiguous 16-byte stores instead of 128 bytes per tile, which would
@@ -137,16 +134,13 @@ void attn_partials_kernel(AttnArgs a) {
   const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int count = SPARSE ? min(max(a.n_idx[b], 0), a.idx_stride) : L;
   const int G = a.group, T = a.q_len, rows = G * T;
+  // Rows [B][Hq][T] of this kv-group are contiguous: row m = hh*T + t of the
+  // group (q-head g*G + hh, query t) is row row_base + m.
+  const size_t row_base = ((size_t)b * a.hq + (size_t)g * G) * T;
   if (start >= count) {  // whole workgroup: nothing in this split
     if (a.direct) {      // the only split: the rows see nothing -> o = 0, lse = -inf
-      for (int e = threadIdx.x; e < rows * D; e += NT) {
-        const int m = e / D, h = g * G + m / T, t = m % T;
-        a.out[(((size_t)b * a.hq + h) * T + t) * D + e % D] = 0;
-      }
-      if (a.lse != nullptr && (int)threadIdx.x < rows) {
-        const int m = threadIdx.x, h = g * G + m / T, t = m % T;
-        a.lse[((size_t)b * a.hq + h) * T + t] = kNegInf;
-      }
+      for (int e = threadIdx.x; e < rows * D; e += NT) a.out[row_base * D + e] = 0;
+      if (a.lse != nullptr && (int)threadIdx.x < rows) a.lse[row_base + threadIdx.x] = kNegInf;
     }
     return;
   }
@@ -248,9 +242,7 @@ void attn_partials_kernel(AttnArgs a) {
     const int m = fqb * 16 + (fl & 15);
     u32x4 val = u32x4{0u, 0u, 0u, 0u};
     if (m < rows) {
-      const int h = g * G + m / T, t = m % T;
-      val = *reinterpret_cast<const u32x4*>(a.q + (((size_t)b * a.hq + h) * T + t) * D +
-                                            fks * 32 + (fl >> 4) * 8);
+      val = *reinterpret_cast<const u32x4*>(a.q + (row_base + m) * D + fks * 32 + (fl >> 4) * 8);
     } else if (EMIT == kEmitSumColumn && m >= QB * 16 - 2) {
       // summed query of the collected rows (heads ascending, row0 then row1):
       // column QB*16-2 its bf16 rounding, column QB*16-1 the rest
@@ -259,8 +251,7 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int t = c == 0 ? a.row0 : a.row1;
-          const bf16x8 qv = load16(a.q + (((size_t)b * a.hq + g * G + hh) * T + t) * D + fks * 32 +
-                                   (fl >> 4) * 8);
+          const bf16x8 qv = load16(a.q + (row_base + hh * T + t) * D + fks * 32 + (fl >> 4) * 8);
 #pragma unroll
           for (int j = 0; j < 8; ++j) qs[j] += (float)qv[j];
         }
@@ -507,11 +498,16 @@ void attn_partials_kernel(AttnArgs a) {
     }
   }
 
-  // Merge the wavefronts, relative to each row's workgroup max M: groups of
-  // NBUF wavefronts accumulate into NBUF fp32 buffers (4 barrier rounds);
-  // every row's (M, l) is computed once.
-  float* obuf = reinterpret_cast<float*>(sbuf);      // NBUF x [64][D + 4]
-  float* s_M = s_m[0];                                // reused after the reads below
+  // Merge the wavefronts, relative to each row's workgroup max M, in four
+  // rounds of D/4 head-dim columns: every wavefront parks its scaled
+  // accumulators for those columns in LDS (the K/V tiles are free now), then
+  // all threads sum the wavefronts element by element and write the result.
+  constexpr int DC = D / 4;        // columns per round
+  constexpr int DBR = DB / 4;      // 16-wide column blocks per round
+  constexpr int RP = QB * 16;      // rows held by the accumulators
+  constexpr int CS = DC + 4;       // row stride of a parked block (floats)
+  static_assert(WAVES * RP * CS * 4 <= (int)sizeof(sbuf), "merge rounds must fit in the K/V tiles");
+  float* obuf = reinterpret_cast<float*>(sbuf);  // [WAVES][RP][CS]
   float scl[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -530,59 +526,40 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w)
       if (s_m[w][m] != kNegInf) rowL += s_l[w][m] * fast_exp2(s_m[w][m] - rowM);
+    s_inv[m] = rowL > 0.f ? 1.f / rowL : 0.f;
   }
-  for (int r = 0; r < WAVES / NBUF; ++r) {
-    if (wave / NBUF == r) {
-      float* buf = obuf + (wave % NBUF) * kMaxRows * OS;
+  const int S = a.num_splits;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+  for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          f32x4* dst = reinterpret_cast<f32x4*>(buf + (qb * 16 + c16) * OS + db * 16 + 4 * kg);
-          const f32x4 add = oacc[db][qb] * scl[qb];
-          *dst = (r == 0) ? add : (*dst + add);
-        }
+    for (int j = 0; j < DBR; ++j)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        *reinterpret_cast<f32x4*>(obuf + (wave * RP + qb * 16 + c16) * CS + j * 16 + 4 * kg) =
+            oacc[r * DBR + j][qb] * scl[qb];
+    __syncthreads();
+    for (int e = threadIdx.x; e < rows * DC; e += NT) {
+      const int m = e / DC, dc = e % DC;
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) acc += obuf[(w * RP + m) * CS + dc];
+      const int d = r * DC + dc;
+      if (a.direct)
+        a.out[(row_base + m) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc * s_inv[m]));
+      else  // written once, read once
+        __builtin_nontemporal_store(acc, a.part_o + ((row_base + m) * S + split) * D + d);
     }
     __syncthreads();
   }
-  // s_m is no longer read: publish each row's (M, l) there.
   if ((int)threadIdx.x < rows) {
-    s_M[threadIdx.x] = rowM;
-    s_M[kMaxRows + threadIdx.x] = rowL;
-  }
-  __syncthreads();
-
-  if (a.direct) {  // the only split: normalise and write the output
-    for (int e = threadIdx.x; e < rows * D; e += NT) {
-      const int m = e / D, d = e % D;
-      const int h = g * G + m / T, t = m % T;
-      const float l = s_M[kMaxRows + m];
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < NBUF; ++i) acc += obuf[i * kMaxRows * OS + m * OS + d];
-      const float o = l > 0.f ? acc / l : 0.f;
-      a.out[(((size_t)b * a.hq + h) * T + t) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
-      if (a.lse != nullptr && d == 0)
-        a.lse[((size_t)b * a.hq + h) * T + t] = l > 0.f ? (s_M[m] + __log2f(l)) * kLn2 : kNegInf;
+    if (a.direct) {
+      if (a.lse != nullptr)
+        a.lse[row_base + threadIdx.x] = rowL > 0.f ? (rowM + __log2f(rowL)) * kLn2 : kNegInf;
+    } else {
+      const size_t prow = (row_base + threadIdx.x) * S + split;
+      a.part_ml[prow * 2 + 0] = rowM;
+      a.part_ml[prow * 2 + 1] = rowL;
     }
-    return;
-  }
-  const int S = a.num_splits;
-  for (int e = threadIdx.x; e < rows * D; e += NT) {
-    const int m = e / D, d = e % D;
-    const int h = g * G + m / T, t = m % T;
-    const size_t prow = (((size_t)b * a.hq + h) * T + t) * S + split;
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < NBUF; ++i) acc += obuf[i * kMaxRows * OS + m * OS + d];
-    __builtin_nontemporal_store(acc, a.part_o + prow * D + d);  // written once, read once
-  }
-  if ((int)threadIdx.x < rows) {
-    const int m = threadIdx.x;
-    const int h = g * G + m / T, t = m % T;
-    const size_t prow = (((size_t)b * a.hq + h) * T + t) * S + split;
-    a.part_ml[prow * 2 + 0] = rowM;
-    a.part_ml[prow * 2 + 1] = rowL;
   }
 }
 

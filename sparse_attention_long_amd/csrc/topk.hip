@@ -7,7 +7,10 @@
 // attention-sink prefix positions and a window of recent positions are kept
 // first and the remaining budget is filled by score.
 //
-// One workgroup of 1024 threads per sequence.
+// One workgroup of 1024 threads per sequence.  Rows of up to 32768 positions
+// (a multiple of 4, 16-byte aligned) take select_topk_kernel (keys in
+// registers, the threshold bin ranked directly); other rows take
+// select_topk_large_kernel, described here:
 //   * F = [0, s_end) U [w_start, L) is forced; r = k - |F| positions are
 //     picked from the middle range M = [s_end, w_start).
 //   * Scores become order-preserving 32-bit keys (larger score, larger key;
@@ -109,8 +112,9 @@ __device__ __forceinline__ void load_keys(const Row& c, int base, uint32_t (&key
   }
 }
 
-// Finds, among the counted keys, the digit of the `want`-th largest and the
-// rank left inside that digit.  hist holds nb bins; all threads call.
+// Finds, among the counted keys, the digit of the `want`-th largest, the rank
+// left inside that digit, and (in s_out[2]) how many keys the digit's bin
+// holds.  hist holds nb bins; all threads call.
 __device__ void find_digit(const uint32_t* hist, uint32_t nb, int shift, uint32_t& prefix,
                            uint32_t& want, uint32_t* s_wave, uint32_t* s_out) {
   const int tid = threadIdx.x;
@@ -125,6 +129,7 @@ __device__ void find_digit(const uint32_t* hist, uint32_t nb, int shift, uint32_
     if (top - q >= 0 && above < want && want <= above + cnt[q]) {
       s_out[0] = prefix | ((uint32_t)(top - q) << shift);
       s_out[1] = want - above;
+      s_out[2] = cnt[q];
     }
     above += cnt[q];
   }
@@ -134,13 +139,13 @@ __device__ void find_digit(const uint32_t* hist, uint32_t nb, int shift, uint32_
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
+__global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
     int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     int32_t k, int32_t n_sink, int32_t window, int32_t* __restrict__ idx, int32_t idx_stride,
     int32_t* __restrict__ n_idx) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t s_wave[kWavesTk];
-  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_out[4];
   __shared__ uint32_t cand_key[kCandMax];
   __shared__ int32_t cand_pos[kCandMax];
 
@@ -296,14 +301,189 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sequences of up to kSmallMax positions.
+//   * Keys stay in registers: thread t holds positions 4096c + 4t + e
+//     (c < 8, e < 4), so every load instruction reads 1 KB of contiguous
+//     scores.
+//   * Radix passes (12, 12, then 8 bits; usually the first suffices) find the
+//     bin of the r-th largest key, stopping as soon as that bin holds at most
+//     kBinCap keys.
+//   * Keys above the bin are marked in an LDS bitmap of the positions; the
+//     bin's members go to an LDS list, are ranked directly (larger key, then
+//     lower position) and the best `want` are marked too.  If the bin is
+//     bigger than kBinCap after the last pass, its keys are all equal and the
+//     lowest positions win: they are marked from a second bitmap.
+//   * The output is written from the bitmap: thread t owns bitmap word t
+//     (positions 32t .. 32t + 31), one block scan orders the words.
+constexpr int kSmallChunks = 8;                          // 4096-position chunks
+constexpr int kSmallMax = kSmallChunks * 4 * kThreadsTk;  // positions per sequence
+constexpr int kBinCap = 2044;                            // bin members ranked directly
+constexpr int kMapWords = kSmallMax / 32;                // bitmap words (= threads)
+static_assert(kMapWords == kThreadsTk, "one bitmap word per thread");
+
+__global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
+    int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
+    int32_t k, int32_t n_sink, int32_t window, int32_t* __restrict__ idx, int32_t idx_stride,
+    int32_t* __restrict__ n_idx) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t s_wave[kWavesTk];
+  __shared__ uint32_t s_out[4];
+  __shared__ uint32_t taken[kMapWords];    // positions selected (above the bin, or ranked in)
+  __shared__ uint32_t in_bin[kMapWords];   // bin members, when they are all equal
+  // bin members as (key << 32 | ~position): larger means ranked first
+  __shared__ __align__(16) uint64_t bin_rank_key[kBinCap + 4];
+  __shared__ uint32_t s_count;
+
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int L = min(max(seq_lens[b], 0), max_ctx);
+  int32_t* out = idx + (size_t)b * idx_stride;
+  if (L <= k) {
+    for (int j = tid; j < L; j += kThreadsTk) out[j] = j;
+    if (tid == 0) n_idx[b] = L;
+    return;
+  }
+  const int s_end = min(n_sink, L), w_start = max(s_end, L - window);
+  const int r = k - (s_end + (L - w_start));  // >= 0: n_sink + window <= k is checked on the host
+  const int tail = L - w_start;
+  if (r == 0) {
+    for (int i = tid; i < s_end; i += kThreadsTk) out[i] = i;
+    for (int i = tid; i < tail; i += kThreadsTk) out[s_end + i] = w_start + i;
+    if (tid == 0) n_idx[b] = k;
+    return;
+  }
+
+  // Keys; 0 outside M = [s_end, w_start).  16-byte loads (the launcher
+  // guarantees max_ctx % 4 == 0 and an aligned score array); addresses are
+  // clamped into the row rather than branched on, so all loads are in flight
+  // together (a clamped load only serves positions at or past the row end,
+  // which are masked).
+  const float* sc = scores + (size_t)b * max_ctx;
+  uint32_t key[kSmallChunks][4];
+  float v[kSmallChunks][4];
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int p0 = min(c * 4 * kThreadsTk + 4 * tid, max_ctx - 4);
+    const float4 x = *reinterpret_cast<const float4*>(sc + p0);
+    v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
+  }
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = c * 4 * kThreadsTk + 4 * tid + e;
+      key[c][e] = (p >= s_end && p < w_start) ? order_key(v[c][e]) : 0u;
+    }
+  taken[tid] = 0u;
+  in_bin[tid] = 0u;
+  if (tid == 0) s_count = 0u;
+
+  // Radix passes: after each, keys whose masked value exceeds `prefix` are
+  // taken and `want` more come from the bin (masked value == prefix).
+  uint32_t prefix = 0u, mask = 0u, want = (uint32_t)r, nbin = 0u;
+  int level = 0;
+#pragma unroll 1
+  for (; level < 3; ++level) {
+    const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
+    const uint32_t nb = level == 2 ? 256u : (uint32_t)kBins;
+    for (int i = tid; i < (int)nb; i += kThreadsTk) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
+          atomicAdd(&hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
+    __syncthreads();
+    find_digit(hist, nb, shift, prefix, want, s_wave, s_out);
+    nbin = s_out[2];
+    mask |= (nb - 1u) << shift;
+    if (nbin <= (uint32_t)kBinCap) break;
+  }
+  const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
+
+  // Mark keys above the bin; collect (or mark) the bin's members.
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    uint32_t above = 0u, inb = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t m = key[c][e] & mask;
+      above |= (key[c][e] != 0u && m > prefix) ? (1u << e) : 0u;
+      inb |= (key[c][e] != 0u && m == prefix) ? (1u << e) : 0u;
+    }
+    const int p0 = c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word, bits p0 % 32 ..
+    if (above != 0u) atomicOr(&taken[p0 >> 5], above << (p0 & 31));
+    if (inb != 0u) {
+      if (exact) {
+        atomicOr(&in_bin[p0 >> 5], inb << (p0 & 31));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((inb >> e) & 1u) {
+            const uint32_t slot = atomicAdd(&s_count, 1u);  // < nbin <= kBinCap
+            bin_rank_key[slot] = ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(p0 + e);
+          }
+      }
+    }
+  }
+  if (!exact && tid < 4) bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
+  __syncthreads();
+  if (!exact) {
+    // rank = members with a larger key, or an equal key at a lower position
+    const int n4 = (int)(nbin + 3u) / 4;
+    for (int q = tid; q < (int)nbin; q += kThreadsTk) {
+      const uint64_t cq = bin_rank_key[q];
+      uint32_t rank = 0u;
+      for (int f = 0; f < n4; ++f) {
+        const uint64_t* c4 = bin_rank_key + 4 * f;
+        rank += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
+                (c4[3] > cq ? 1u : 0u);
+      }
+      if (rank < want) {
+        const int pq = (int)~(uint32_t)cq;
+        atomicOr(&taken[pq >> 5], 1u << (pq & 31));
+      }
+    }
+    __syncthreads();
+  }
+
+  // Ordered emit: [0, s_end) ++ taken middle positions ++ [w_start, L).
+  uint32_t word = taken[tid];
+  uint32_t tot;
+  if (exact) {  // the first `want` bin members in position order
+    const uint32_t ib = in_bin[tid];
+    const uint32_t before = block_exclusive_scan((uint32_t)__builtin_popcount(ib), s_wave, tot);
+    uint32_t bits = ib;
+    for (uint32_t q = before; bits != 0u && q < want; ++q) {
+      word |= bits & (~bits + 1u);  // lowest remaining member
+      bits &= bits - 1u;
+    }
+  }
+  uint32_t o = block_exclusive_scan((uint32_t)__builtin_popcount(word), s_wave, tot) + (uint32_t)s_end;
+  while (word != 0u) {
+    const int i = __builtin_ctz(word);
+    word &= word - 1u;
+    if (o < (uint32_t)idx_stride) out[o++] = 32 * tid + i;
+  }
+  for (int i = tid; i < s_end; i += kThreadsTk) out[i] = i;
+  for (int i = tid; i < tail; i += kThreadsTk) out[s_end + r + i] = w_start + i;
+  if (tid == 0) n_idx[b] = k;
+}
+
 }  // namespace
 
 hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
                               const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
                               int32_t* idx, int32_t idx_stride, int32_t* n_idx,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(select_topk_kernel, dim3(batch), dim3(kThreadsTk), 0, stream, max_ctx, scores,
-                     seq_lens, k, n_sink, window, idx, idx_stride, n_idx);
+  if (max_ctx <= kSmallMax && max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) {
+    hipLaunchKernelGGL(select_topk_kernel, dim3(batch), dim3(kThreadsTk), 0, stream, max_ctx, scores,
+                       seq_lens, k, n_sink, window, idx, idx_stride, n_idx);
+  } else {
+    hipLaunchKernelGGL(select_topk_large_kernel, dim3(batch), dim3(kThreadsTk), 0, stream, max_ctx,
+                       scores, seq_lens, k, n_sink, window, idx, idx_stride, n_idx);
+  }
   return hipGetLastError();
 }
 

@@ -176,6 +176,21 @@ def test_select_random_scores(L):
         _select_case(sc, lens, k, ns, win)
 
 
+@pytest.mark.parametrize("L", [5, 64, 1000, 4096, 20001, 32768])
+def test_select_random_scores_register_path(L):
+    """Rows whose length is a multiple of 4 and at most 32768 take the
+    register-resident selection kernel; other rows the general one."""
+    rng = np.random.default_rng(100 + L)
+    ctx = (L + 3) // 4 * 4
+    lens = [L, max(1, L // 3), max(1, L - 1), max(1, L // 2 + 1)]
+    sc = rng.standard_normal((len(lens), ctx)).astype(np.float32) * 10
+    sc[3, ::7] = sc[3, 0]  # a repeated value across the row
+    for k, ns, win in [(1, 0, 0), (16, 4, 8), (512, 4, 64), (2048, 4, 128), (L, 0, 0)]:
+        if k < 1 or ns + win > k:
+            continue
+        _select_case(sc, lens, k, ns, win)
+
+
 def test_select_ties_zeros_and_infinities():
     rng = np.random.default_rng(5)
     ctx = 5000
