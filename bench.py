@@ -198,24 +198,14 @@ def main():
     rows = w.collect_rows
     KV = Bn.LOGITS_KVGROUP_SUM
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step():
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
-        if ev is not None:
-            ev[1].record()
         # split combine + score aggregation in one launch
         Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
-        if ev is not None:
-            ev[2].record()
         Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
-        if ev is not None:
-            ev[3].record()
         if w.sparse_verify:
             Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                 out=out_s, lse=lse_s, workspace=ws_s)
-            if ev is not None:
-                ev[4].record()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -237,20 +227,26 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps; events around the verify kernel
+    # ---- timed region: exactly `steps` steps.  HIP events bracket the verify
+    # kernel on every EVENT_EVERY-th step only: an event record drains the
+    # queue (about 6 us of idle GPU each), so bracketing every launch would
+    # inflate the step time the events are meant to explain.
     K = args.steps
+    EVENT_EVERY = 4
     ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(K)]
+                for _ in range(0, K, EVENT_EVERY)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     e_start.record()
     for i in range(K if graph is None else 0):
-        a, b_ = ev_pairs[i]
-        a.record()
+        timed = i % EVENT_EVERY == 0
+        if timed:
+            ev_pairs[i // EVENT_EVERY][0].record()
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
-        b_.record()
+        if timed:
+            ev_pairs[i // EVENT_EVERY][1].record()
         Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
         Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         if w.sparse_verify:
@@ -267,27 +263,34 @@ def main():
                  if graph is None else float("nan"))
     log(f"[bench] {K} steps: wall {wall * 1e3:.2f} ms, gpu {gpu_ms:.2f} ms, verify kernel {verify_us:.1f} us")
 
-    # ---- stage breakdown and logit-emit overhead (outside the timed region)
-    nst = 5
-    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(K)]
-    for i in range(K):
-        step(stage_ev[i])
-    torch.cuda.synchronize()
+    # ---- stage breakdown and logit-emit overhead (outside the timed region):
+    # each stage launched K times back to back between one pair of events, so
+    # the figure is its pipelined per-launch time (no queue drain per launch)
+    def per_launch_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
 
-    def span(i, j):
-        return float(np.mean([e[i].elapsed_time(e[j]) for e in stage_ev])) * 1e3
-
-    stages = {"verify_partials": span(0, 1), "combine_aggregate": span(1, 2), "select": span(2, 3)}
+    stages = {
+        "verify_partials": per_launch_us(
+            lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)),
+        "combine_aggregate": per_launch_us(
+            lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)),
+        "select": per_launch_us(
+            lambda: Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)),
+    }
     if w.sparse_verify:
-        stages["sparse"] = span(3, 4)
-    none_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(K)]
-    for a, b_ in none_ev:
-        a.record()
-        Bn.verify_partials(desc, q, k, v, lens, bt, rows, Bn.LOGITS_NONE, None, ws_v)
-        b_.record()
-    torch.cuda.synchronize()
-    verify_none_us = float(np.mean([a.elapsed_time(b_) for a, b_ in none_ev])) * 1e3
+        stages["sparse"] = per_launch_us(
+            lambda: Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
+                                        out=out_s, lse=lse_s, workspace=ws_s))
+    verify_none_us = per_launch_us(
+        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, Bn.LOGITS_NONE, None, ws_v))
 
     ab = alg_bytes(w, x.seq_lens)
     iters = K / wall

@@ -88,7 +88,10 @@ typedef enum vgsa_logit_layout {
 /* Shape of one attention call.  The KV cache is either contiguous,
  * K/V [B][Hkv][max_ctx][head_dim] bf16, or a paged pool of 16-position blocks,
  * K/V [num_blocks][Hkv][16][head_dim] bf16 addressed through
- * block_table[B][max_blocks_per_seq] (int32 block ids). */
+ * block_table[B][max_blocks_per_seq] (int32 block ids).  Cache rows are
+ * addressed with 32-bit byte offsets: max_ctx * head_dim (contiguous) and
+ * num_blocks * Hkv * 16 * head_dim (paged) must stay below 2^31, else
+ * VGSA_ERR_UNSUPPORTED. */
 typedef struct vgsa_attn_desc {
   int32_t batch;              /* B >= 0                                          */
   int32_t num_q_heads;        /* Hq >= 1, a multiple of num_kv_heads             */

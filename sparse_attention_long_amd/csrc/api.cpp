@@ -11,7 +11,7 @@ namespace vgsa {
 namespace {
 
 constexpr int64_t kMaxGridYZ = 65535;
-constexpr int64_t kMaxOffset = 0xFFFFFFFFLL;
+constexpr int64_t kMaxOffset = 0x7FFFFFFFLL;  // elements: byte offsets stay within 32 bits
 constexpr uintptr_t kWorkspaceAlign = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -221,7 +221,9 @@ void attn_partials_kernel(AttnArgs a) {
       } else {
         off = (uint32_t)pos * D;
       }
-      dst[i] = load16_stream(base + off + lchunk * 8);
+      // byte offset in 32 bits from the uniform base: a scalar-base load
+      const uint32_t boff = (off + (uint32_t)lchunk * 8u) * 2u;
+      dst[i] = load16_stream(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + boff));
     }
   };
 
@@ -426,10 +428,12 @@ void attn_partials_kernel(AttnArgs a) {
       const bool grow = mx > m_run[qb] + kRescaleLog2;
       if (__any(grow)) {
         const float m_new = grow ? mx : m_run[qb];
-        const float alpha = grow ? fast_exp2(m_run[qb] - m_new) : 1.f;
-        l_run[qb] *= alpha;
+        if (__any(grow && m_run[qb] != kNegInf)) {  // a row still at -inf holds O = 0, l = 0
+          const float alpha = grow ? fast_exp2(m_run[qb] - m_new) : 1.f;
+          l_run[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+          for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+        }
         m_run[qb] = m_new;
       }
       const float m_use = m_run[qb] == kNegInf ? 0.f : m_run[qb];
