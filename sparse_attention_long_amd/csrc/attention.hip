@@ -108,11 +108,11 @@ void attn_partials_kernel(AttnArgs a) {
   __shared__ float s_l[WAVES][kMaxRows];
   __shared__ float s_inv[kMaxRows];  // 1 / (merged row sum), for the one-split output
   __shared__ int s_idx[WAVES][kTile];
-  // Kv-group logits of the chunk, written out after the loop: one burst of
-  // contiguous 16-byte stores instead of 128 bytes per tile, which would
-  // interleave small writes with the K/V read stream.
+  // Kv-group logits of the chunk, written out in bursts of kLogitBuf
+  // positions: contiguous 16-byte stores instead of 128 bytes per tile, which
+  // would interleave small writes with the K/V read stream.
   constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || EMIT == kEmitSumColumn;
-  __shared__ __align__(16) float slog[kGroupLogits ? kMaxChunk : 4];
+  __shared__ __align__(16) float slog[kGroupLogits ? kLogitBuf : 4];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -269,6 +269,18 @@ void attn_partials_kernel(AttnArgs a) {
   }
   __syncthreads();  // query fragments staged
 
+  int lbase = start;  // first position held in slog
+  auto flush_logits = [&](int n) {  // slog[0, n) -> logits[lbase, lbase + n), nontemporal
+    float* lp = a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + lbase;
+    if ((reinterpret_cast<uintptr_t>(lp) & 15) == 0) {
+      for (int i = threadIdx.x * 4; i + 4 <= n; i += NT * 4)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(slog + i),
+                                    reinterpret_cast<f32x4*>(lp + i));
+      for (int i = (n & ~3) + threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
+    } else {
+      for (int i = threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
+    }
+  };
   for (; ts < end; ts += step) {
     // Entry e of the tile (e = pb*16 + 4*kg + r for this lane's S^T values)
     // is visible to query row qb iff e < vis[qb]: positions ascend within a
@@ -383,7 +395,7 @@ void attn_partials_kernel(AttnArgs a) {
       float v1 = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 2);
       v1 += __shfl_xor(v1, 1);
       const int e = (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
-      if ((c16 & 1) == 0) slog[ts - start + e] = v1;
+      if ((c16 & 1) == 0) slog[ts - lbase + e] = v1;
     }
 
     if (EMIT == kEmitSumColumn) {
@@ -404,7 +416,7 @@ void attn_partials_kernel(AttnArgs a) {
       if (c16 == 14) {
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb)
-          *reinterpret_cast<f32x4*>(slog + (ts - start) + pb * 16 + 4 * kg) = lv[pb];
+          *reinterpret_cast<f32x4*>(slog + (ts - lbase) + pb * 16 + 4 * kg) = lv[pb];
       }
     }
 
@@ -472,6 +484,14 @@ void attn_partials_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     ++tile_no;
+    if (kGroupLogits && tile_no == kLogitBuf / step && end - start > kLogitBuf) {
+      // every wavefront has at least kLogitBuf / step tiles in this chunk, so
+      // all of them reach this point once: the buffer is full
+      __syncthreads();
+      flush_logits(kLogitBuf);
+      __syncthreads();
+      lbase += kLogitBuf;
+    }
   }
 
   // Row sums: combine the four 16-lane groups.
@@ -489,18 +509,7 @@ void attn_partials_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  if (kGroupLogits) {  // the chunk's logits [start, end), nontemporal (read once, later)
-    float* lp = a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + start;
-    const int n = end - start;
-    if ((reinterpret_cast<uintptr_t>(lp) & 15) == 0) {
-      for (int i = threadIdx.x * 4; i + 4 <= n; i += NT * 4)
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(slog + i),
-                                    reinterpret_cast<f32x4*>(lp + i));
-      for (int i = (n & ~3) + threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
-    } else {
-      for (int i = threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
-    }
-  }
+  if (kGroupLogits) flush_logits(end - lbase);  // the rest of the chunk's logits (read once, later)
 
   // Merge the wavefronts, relative to each row's workgroup max M, in four
   // rounds of D/4 head-dim columns: every wavefront parks its scaled
@@ -615,7 +624,8 @@ hipError_t launch_dim(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) 
 }  // namespace
 
 hipError_t launch_attention_partials(const AttnArgs& a, bool sparse, hipStream_t s) {
-  if (a.chunk > kMaxChunk) return hipErrorInvalidValue;  // the split plan never makes one
+  // the split plan never makes these: LDS logit buffer and mid-chunk flush
+  if (a.chunk > kMaxChunk || a.chunk % kMinChunk != 0) return hipErrorInvalidValue;
   const dim3 grid(a.num_splits, a.hkv, a.batch);
   return a.head_dim == 64 ? launch_dim<64>(a, sparse, grid, s) : launch_dim<128>(a, sparse, grid, s);
 }

@@ -17,15 +17,18 @@ constexpr int kWaves = 4;
 constexpr int kWavesWide = 8;  // one-split sparse launches
 constexpr int kThreads = kWaves * 64;
 constexpr int kMinChunk = kTile * kWaves;
-// Workgroups aimed for per attention launch: 4 per CU on 256 CUs.
-constexpr int kTargetWorkgroups = 1024;
+// Workgroups aimed for per attention launch: one round of 2 per CU on 256
+// CUs, so each workgroup slot pays its start-up and merge once.
+constexpr int kTargetWorkgroups = 512;
 // Spans up to this many positions get one split: a single workgroup per
 // (sequence, kv-head) finishes the softmax itself and writes the output
 // directly (no partials, no combine launch).
 constexpr int kDirectSpan = 1024;
-// Largest chunk of one split: a workgroup keeps its chunk's kv-group logits
-// in LDS (fp32) and writes them out in one burst at the end.
-constexpr int kMaxChunk = 4096;
+// Largest chunk of one split.  A workgroup keeps kv-group logits for
+// kLogitBuf positions in LDS (fp32) and writes them out in bursts of that
+// size (mid-chunk once, for chunks longer than kLogitBuf).
+constexpr int kMaxChunk = 8192;
+constexpr int kLogitBuf = 4096;
 // Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.
 constexpr int kMaxRows = 64;
 

@@ -182,6 +182,10 @@ def test_split_plan_covers_span(lib):
                           (16, 8, 512), (1, 8, 2049)]:
         d = desc(batch=B_, num_kv_heads=Hkv, num_q_heads=Hkv, q_len=1, max_ctx=span)
         s, c = B.split_plan(d, span)
-        assert s >= 1 and c % 128 == 0 and c <= 4096 and s * c >= span and (s - 1) * c < span
+        assert s >= 1 and c % 128 == 0 and c <= 8192 and s * c >= span and (s - 1) * c < span
+    # one round of 512 workgroups (2 per CU) at the 32K x b16 shape
     d = desc(batch=16, num_q_heads=64, num_kv_heads=8, q_len=5, max_ctx=32768)
-    assert B.split_plan(d, 32768) == (8, 4096)
+    assert B.split_plan(d, 32768) == (4, 8192)
+    # chunks are capped at 8192 positions
+    d = desc(batch=8, num_q_heads=32, num_kv_heads=8, q_len=7, max_ctx=131078)
+    assert B.split_plan(d, 131078) == (17, 8192)

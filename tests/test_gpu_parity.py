@@ -33,6 +33,11 @@ CASES = {
                               ctx=None, ctx_range=(40, 300), paged=True, budget=48, n_sink=4,
                               window=12, seed=15),
     "ctx2k_b1_h32kv8_d128": W.WORKLOADS["ctx2k_b1_h32kv8_d128"],
+    # 8 x 8 workgroup rows -> 4224-position chunks: a mid-chunk logit flush,
+    # ragged last chunks, chunks shorter than the LDS logit buffer
+    "chunk4224_g1t3_d64": W.small("c4224", batch=8, num_q_heads=8, num_kv_heads=8, head_dim=64,
+                                  gamma=2, lens=(33000, 20000, 4500, 8300, 12289, 30000, 4097, 16500),
+                                  budget=300, n_sink=4, window=32, seed=16),
 }
 
 
