@@ -227,41 +227,26 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps.  HIP events bracket the verify
-    # kernel on every EVENT_EVERY-th step only: an event record drains the
-    # queue (about 6 us of idle GPU each), so bracketing every launch would
-    # inflate the step time the events are meant to explain.
+    # ---- timed region: exactly `steps` steps, launched back to back.  No event
+    # is recorded inside it: an event record drains the queue (about 6 us of
+    # idle GPU), which would slow the very steps being timed.
     K = args.steps
-    EVENT_EVERY = 4
-    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(0, K, EVENT_EVERY)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     e_start.record()
-    for i in range(K if graph is None else 0):
-        timed = i % EVENT_EVERY == 0
-        if timed:
-            ev_pairs[i // EVENT_EVERY][0].record()
-        Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
-        if timed:
-            ev_pairs[i // EVENT_EVERY][1].record()
-        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
-        Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
-        if w.sparse_verify:
-            Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
-                                out=out_s, lse=lse_s, workspace=ws_s)
-    if graph is not None:
-        for i in range(K):
+    if graph is None:
+        for _ in range(K):
+            step()
+    else:
+        for _ in range(K):
             graph.replay()
     e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gpu_ms = e_start.elapsed_time(e_end)
-    verify_us = (float(np.mean([a.elapsed_time(b_) for a, b_ in ev_pairs])) * 1e3
-                 if graph is None else float("nan"))
-    log(f"[bench] {K} steps: wall {wall * 1e3:.2f} ms, gpu {gpu_ms:.2f} ms, verify kernel {verify_us:.1f} us")
+    log(f"[bench] {K} steps: wall {wall * 1e3:.2f} ms, gpu {gpu_ms:.2f} ms")
 
     # ---- stage breakdown and logit-emit overhead (outside the timed region):
     # each stage launched K times back to back between one pair of events, so
@@ -277,9 +262,13 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / K
 
+    # the verify kernel's launch duration for the roofline: K launches of the
+    # timed configuration back to back on the launch stream
+    verify_us = per_launch_us(
+        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v))
+    log(f"[bench] verify kernel {verify_us:.1f} us per launch")
     stages = {
-        "verify_partials": per_launch_us(
-            lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)),
+        "verify_partials": verify_us,
         "combine_aggregate": per_launch_us(
             lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)),
         "select": per_launch_us(
