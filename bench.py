@@ -151,8 +151,6 @@ def main():
 
     name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
-    if w.draft_steps and not hasattr(Bn, "append_positions"):
-        raise SystemExit(f"{name}: draft steps are not wired into the benchmark yet")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     Bn.load()
@@ -197,6 +195,22 @@ def main():
     lse_s = torch.empty_like(lse)
     rows = w.collect_rows
     KV = Bn.LOGITS_KVGROUP_SUM
+    # draft steps: step s attends with one fresh query per head over the
+    # selected positions plus the s positions drafted since (lengths L + s)
+    n_draft = w.draft_steps
+    q_draft = [d_bf16(x.q_draft[s]) for s in range(n_draft)]
+    lens_draft = [(lens + s).contiguous() for s in range(1, n_draft + 1)]
+    if n_draft:
+        desc_d = Bn.make_desc(q_draft[0], k, bt, max_ctx)
+        ws_d = torch.empty(Bn.sparse_workspace_bytes(desc_d, stride), dtype=torch.uint8, device=dev)
+        out_d = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=dev)
+        lse_d = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
+
+    def draft_steps():
+        for s in range(n_draft):
+            Bn.append_positions(lens, s, 1, idx, n_idx)
+            Bn.sparse_attention(q_draft[s], k, v, lens_draft[s], idx, n_idx, block_table=bt,
+                                max_ctx=max_ctx, out=out_d, lse=lse_d, workspace=ws_d)
 
     def step():
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
@@ -206,6 +220,7 @@ def main():
         if w.sparse_verify:
             Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                 out=out_s, lse=lse_s, workspace=ws_s)
+        draft_steps()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -278,6 +293,12 @@ def main():
         stages["sparse"] = per_launch_us(
             lambda: Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                         out=out_s, lse=lse_s, workspace=ws_s))
+    if n_draft:
+        # the draft loop appends to the lists: select restores them each time
+        def select_and_draft():
+            Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+            draft_steps()
+        stages["draft_steps"] = per_launch_us(select_and_draft) - stages["select"]
     verify_none_us = per_launch_us(
         lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, Bn.LOGITS_NONE, None, ws_v))
 
@@ -300,6 +321,7 @@ def main():
         "config": {"workload": name, "batch": B, "ctx": w.ctx if w.ctx else list(w.ctx_range),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "gamma": w.gamma,
                    "budget": w.budget, "n_sink": w.n_sink, "window": w.window,
+                   "draft_steps": n_draft, "sparse_verify": w.sparse_verify,
                    "paged": w.paged, "logits": "kvgroup_sum"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),

@@ -202,6 +202,20 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
                                   const int32_t* n_idx, int32_t idx_stride, void* out, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Draft steps: append consecutive positions to index lists.
+ *    (Vegas section 2 step 3: each drafting step attends over the selected
+ *    entries and the tokens drafted since the selection.)
+ * For each b, positions base[b] + first, ..., base[b] + first + count - 1 are
+ * written at idx[b][n_idx[b]], ... and n_idx[b] grows by count; entries that
+ * would land at or past idx_stride are dropped (n_idx[b] stops at
+ * idx_stride).  The row stays ascending when the new positions lie past every
+ * listed one, as drafted tokens past the selection's lengths do.
+ * base      int32 [B], e.g. the lengths the lists were selected at
+ * idx       int32 [B][idx_stride]; n_idx int32 [B]: both updated in place
+ * count 0 or batch 0: nothing is launched. */
+vgsa_status vgsa_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,
+                                  int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Two-phase form of steps 1 and 4, for callers that time or schedule the
  * phases separately.  vgsa_verify_attention == vgsa_verify_partials followed

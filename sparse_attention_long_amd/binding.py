@@ -52,6 +52,7 @@ SIGNATURES = {
                                       c_vp, c_vp]),
     "vgsa_verify_finish": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp, c_i32,
                                    c_vp, c_vp, c_vp]),
+    "vgsa_append_positions": (c_i32, [c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -241,6 +242,16 @@ def sparse_attention(q, k_cache, v_cache, seq_lens, idx, n_idx, *, block_table=N
         _p(n_idx), idx.shape[1], _p(out), _p(lse), _p(ws), ws.numel(), _stream(dev)),
         "vgsa_sparse_attention")
     return out, lse
+
+
+def append_positions(base, first: int, count: int, idx, n_idx) -> None:
+    """vgsa_append_positions: idx[b][n_idx[b] + i] = base[b] + first + i for
+    i < count, n_idx[b] += count (in place)."""
+    _need(base, "base", torch.int32, 1)
+    _need(idx, "idx", torch.int32, 2)
+    _need(n_idx, "n_idx", torch.int32, 1)
+    _check(load().vgsa_append_positions(idx.shape[0], _p(base), first, count, _p(idx), idx.shape[1],
+                                        _p(n_idx), _stream(idx.device)), "vgsa_append_positions")
 
 
 # --------------------------------------------------------------------------- two-phase form

@@ -406,4 +406,14 @@ vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores
                                        idx_stride, n_idx, static_cast<hipStream_t>(stream)));
 }
 
+vgsa_status vgsa_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,
+                                  int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream) {
+  if (batch < 0 || first < 0 || count < 0 || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
+  if (batch == 0 || count == 0) return VGSA_OK;
+  if (base == nullptr || idx == nullptr || n_idx == nullptr) return VGSA_ERR_INVALID_ARG;
+  if (batch > 0x7fffffff / idx_stride) return VGSA_ERR_UNSUPPORTED;
+  return hip_status(launch_append_positions(batch, base, first, count, idx, idx_stride, n_idx,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

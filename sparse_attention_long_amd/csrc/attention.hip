@@ -107,7 +107,9 @@ void attn_partials_kernel(AttnArgs a) {
   __shared__ float s_m[WAVES][kMaxRows];
   __shared__ float s_l[WAVES][kMaxRows];
   __shared__ float s_inv[kMaxRows];  // 1 / (merged row sum), for the one-split output
-  __shared__ int s_idx[WAVES][kTile];
+  __shared__ int s_idx[WAVES][kTile];           // sparse: positions of the staged tile
+  __shared__ uint32_t s_row[WAVES][kTile];      // sparse: cache element offsets of those rows
+  __shared__ int s_blk[SPARSE ? 1 : kMaxChunk / 16];  // paged verify: the chunk's block ids
   // Kv-group logits of the chunk, written out in bursts of kLogitBuf
   // positions: contiguous 16-byte stores instead of 128 bytes per tile, which
   // would interleave small writes with the K/V read stream.
@@ -132,6 +134,15 @@ void attn_partials_kernel(AttnArgs a) {
                          min(start + (i * WAVES + wave) * kTile + lane, a.idx_stride - 1)];
   }
   const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
+  const int32_t* btab = a.paged ? a.block_table + (size_t)b * a.max_blocks : nullptr;
+  // Paged sparse: block ids of the preloaded entries, fetched together.
+  int blk_pre[kPreTiles];
+#pragma unroll
+  for (int i = 0; i < kPreTiles; ++i) {
+    blk_pre[i] = 0;
+    if (SPARSE && lane < kTile && a.paged)
+      blk_pre[i] = btab[min(max(idx_pre[i], 0), max(L - 1, 0)) >> 4];
+  }
   const int count = SPARSE ? min(max(a.n_idx[b], 0), a.idx_stride) : L;
   const int G = a.group, T = a.q_len, rows = G * T;
   // Rows [B][Hq][T] of this kv-group are contiguous: row m = hh*T + t of the
@@ -173,6 +184,7 @@ void attn_partials_kernel(AttnArgs a) {
 
   uint16_t* vt = sbuf + wave * kTile * VS;  // this wavefront's K/V tile
   int* sidx = s_idx[wave];
+  uint32_t* srow = s_row[wave];
   const int step = WAVES * kTile;
 
   // Global -> register loads use whole rows: instruction i of a tile covers
@@ -188,7 +200,6 @@ void attn_partials_kernel(AttnArgs a) {
   const size_t bg_off = a.paged ? 0 : ((size_t)b * a.hkv + g) * a.max_ctx * D;
   const uint16_t* kbase = a.k + bg_off;
   const uint16_t* vbase = a.v + bg_off;
-  const int32_t* btab = a.paged ? a.block_table + (size_t)b * a.max_blocks : nullptr;
 
   // Issue the K/V loads of tile t0 (staging its positions first when sparse).
   // Stage (sparse) the positions of this wavefront's tile number `it`
@@ -202,7 +213,17 @@ void attn_partials_kernel(AttnArgs a) {
           p = it == 0 ? idx_pre[0] : it == 1 ? idx_pre[1] : it == 2 ? idx_pre[2]
             : it == 3 ? idx_pre[3] : a.idx[(size_t)b * a.idx_stride + li];
         }
-        sidx[lane] = min(max(p, 0), max(L - 1, 0));
+        p = min(max(p, 0), max(L - 1, 0));
+        sidx[lane] = p;
+        uint32_t off = (uint32_t)p * D;
+        if (a.paged) {
+          int blk = it == 0 ? blk_pre[0] : it == 1 ? blk_pre[1] : it == 2 ? blk_pre[2]
+                  : it == 3 ? blk_pre[3] : btab[p >> 4];
+          if (li >= end) blk = 0;  // entries past the list: any in-range row will do
+          blk = min(max(blk, 0), a.num_blocks - 1);
+          off = (((uint32_t)blk * a.hkv + g) * 16u + (uint32_t)(p & 15)) * D;
+        }
+        srow[lane] = off;
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -213,19 +234,32 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = i * RPI + lrow;
-      const int pos = SPARSE ? sidx[r] : min(t0 + r, end - 1);
       uint32_t off;
-      if (a.paged) {
-        const int blk = min(max(btab[pos >> 4], 0), a.num_blocks - 1);
-        off = (((uint32_t)blk * a.hkv + g) * 16u + (uint32_t)(pos & 15)) * D;
+      if (SPARSE) {
+        off = srow[r];
       } else {
-        off = (uint32_t)pos * D;
+        const int pos = min(t0 + r, end - 1);
+        if (a.paged) {
+          off = (((uint32_t)s_blk[(pos >> 4) - (start >> 4)] * a.hkv + g) * 16u +
+                 (uint32_t)(pos & 15)) * D;
+        } else {
+          off = (uint32_t)pos * D;
+        }
       }
       // byte offset in 32 bits from the uniform base: a scalar-base load
       const uint32_t boff = (off + (uint32_t)lchunk * 8u) * 2u;
       dst[i] = load16_stream(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + boff));
     }
   };
+
+  // Paged verify: the chunk's block ids (clamped) go to LDS once, so no load
+  // address waits on a block-table read inside the loop.
+  if (!SPARSE && a.paged) {
+    const int nblk = (end - 1 - start) / 16 + 1;
+    for (int i = threadIdx.x; i < nblk; i += NT)
+      s_blk[i] = min(max(btab[(start >> 4) + i], 0), a.num_blocks - 1);
+    __syncthreads();
+  }
 
   u32x4 kraw[NI], vraw[NI];
   int ts = start + wave * kTile;

@@ -99,6 +99,9 @@ hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_
                             const float* logits, const int32_t* seq_lens, float* scores,
                             hipStream_t stream);
 
+hipError_t launch_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,
+                                   int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                                   hipStream_t stream);
 hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
                               const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
                               int32_t* idx, int32_t idx_stride, int32_t* n_idx,

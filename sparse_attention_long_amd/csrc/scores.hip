@@ -35,7 +35,30 @@ __global__ __launch_bounds__(kBlock) void combine_aggregate_kernel(CombineArgs c
   aggregate_position(ag, q / pos_blocks, (q % pos_blocks) * kBlock + threadIdx.x);
 }
 
+// One workgroup per sequence: list entries n .. n + count - 1 (those below
+// idx_stride) receive base + first + i; then the count grows.
+__global__ __launch_bounds__(kBlock) void append_positions_kernel(const int32_t* base, int32_t first,
+                                                                  int32_t count, int32_t* idx,
+                                                                  int32_t idx_stride,
+                                                                  int32_t* n_idx) {
+  const int b = blockIdx.x;
+  const int n = min(max(n_idx[b], 0), idx_stride);
+  const int p0 = base[b] + first;
+  for (int i = threadIdx.x; i < count && n + i < idx_stride; i += kBlock)
+    idx[(size_t)b * idx_stride + n + i] = p0 + i;
+  __syncthreads();  // every thread has read n_idx[b]
+  if (threadIdx.x == 0) n_idx[b] = (int32_t)min((int64_t)n + count, (int64_t)idx_stride);
+}
+
 }  // namespace
+
+hipError_t launch_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,
+                                   int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(append_positions_kernel, dim3(batch), dim3(kBlock), 0, stream, base, first,
+                     count, idx, idx_stride, n_idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t layout,
                             const float* logits, const int32_t* seq_lens, float* scores,

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -175,6 +175,18 @@ def test_aggregate_and_select_argument_checks(lib):
     assert T(2, 100, None, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == INVALID
     assert T(2, 0, FAKE, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == INVALID
     assert T(0, 100, FAKE, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == OK
+
+
+def test_append_argument_checks(lib):
+    P = lib.vgsa_append_positions
+    assert P(-1, FAKE, 0, 1, FAKE, 8, FAKE, None) == INVALID
+    assert P(2, FAKE, -1, 1, FAKE, 8, FAKE, None) == INVALID
+    assert P(2, FAKE, 0, -1, FAKE, 8, FAKE, None) == INVALID
+    assert P(2, FAKE, 0, 1, FAKE, 0, FAKE, None) == INVALID
+    assert P(2, None, 0, 1, FAKE, 8, FAKE, None) == INVALID
+    assert P(2, FAKE, 0, 1, FAKE, 8, None, None) == INVALID
+    assert P(2, None, 0, 0, None, 8, None, None) == OK   # nothing to append: nothing launched
+    assert P(0, None, 0, 3, None, 8, None, None) == OK
 
 
 def test_split_plan_covers_span(lib):

@@ -319,3 +319,19 @@ def test_verify_finish_equals_combine_and_aggregate(name):
         Bn.verify_finish(desc, d.seq_lens, ws, o3, None)  # combine only
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_append_positions_for_draft_steps():
+    """Draft-step lists: the selected positions followed by the drafted ones,
+    appended in place; entries past the stride are dropped."""
+    lens = np.array([100, 7, 50], np.int32)
+    idx_h, n_h = W.index_lists(3, lens, count=5, stride=9)
+    idx, n = dev_i32(idx_h), dev_i32(n_h)
+    Bn.append_positions(dev_i32(lens), 0, 2, idx, n)      # draft step 1 and 2 at once
+    Bn.append_positions(dev_i32(lens), 2, 3, idx, n)      # 3 more: the third list overflows
+    torch.cuda.synchronize()
+    got, cnt = idx.cpu().numpy(), n.cpu().numpy()
+    for b, L in enumerate(lens):
+        want = np.concatenate([idx_h[b, :n_h[b]], np.arange(L, L + 5)])[:9]
+        assert cnt[b] == len(want)
+        assert np.array_equal(got[b, :cnt[b]], want)
