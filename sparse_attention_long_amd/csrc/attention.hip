@@ -518,11 +518,12 @@ void attn_partials_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     ++tile_no;
-    if (kGroupLogits && tile_no == kLogitBuf / step && end - start > kLogitBuf) {
-      // every wavefront has at least kLogitBuf / step tiles in this chunk, so
-      // all of them reach this point once: the buffer is full
+    if (kGroupLogits && tile_no % (kLogitBuf / step) == 0 &&
+        start + (tile_no - 1) * step + (WAVES - 1) * kTile < end) {
+      // the last wavefront has a tile_no-th tile, so every wavefront reaches
+      // this point (the condition is the same for all): the buffer is full
       __syncthreads();
-      flush_logits(kLogitBuf);
+      flush_logits(min(kLogitBuf, end - lbase));
       __syncthreads();
       lbase += kLogitBuf;
     }
@@ -543,7 +544,7 @@ void attn_partials_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  if (kGroupLogits) flush_logits(end - lbase);  // the rest of the chunk's logits (read once, later)
+  if (kGroupLogits && end > lbase) flush_logits(end - lbase);  // the rest (read once, later)
 
   // Merge the wavefronts, relative to each row's workgroup max M, in four
   // rounds of D/4 head-dim columns: every wavefront parks its scaled

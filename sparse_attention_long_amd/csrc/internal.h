@@ -26,7 +26,9 @@ constexpr int kTargetWorkgroups = 512;
 constexpr int kDirectSpan = 1024;
 // Largest chunk of one split.  A workgroup keeps kv-group logits for
 // kLogitBuf positions in LDS (fp32) and writes them out in bursts of that
-// size (mid-chunk once, for chunks longer than kLogitBuf).
+// size (every kLogitBuf positions of a longer chunk).  Longer chunks measured
+// slower at 128K x b8 (one round of 512 workgroups then spans 4 GB of K/V at
+// once; two rounds of 8192-position chunks span 2 GB each).
 constexpr int kMaxChunk = 8192;
 constexpr int kLogitBuf = 4096;
 // Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.

@@ -7,9 +7,9 @@
 // attention-sink prefix positions and a window of recent positions are kept
 // first and the remaining budget is filled by score.
 //
-// One workgroup of 1024 threads per sequence.  Rows of up to 32768 positions
-// (a multiple of 4, 16-byte aligned) take select_topk_kernel (keys in
-// registers, the threshold bin ranked directly); other rows take
+// One workgroup of 1024 threads per sequence.  Rows of up to 262144 positions
+// take select_topk_kernel (radix pass over coalesced keys, the threshold bin
+// ranked directly, output from a position bitmap); longer rows take
 // select_topk_large_kernel, described here:
 //   * F = [0, s_end) U [w_start, L) is forced; r = k - |F| positions are
 //     picked from the middle range M = [s_end, w_start).
@@ -302,10 +302,12 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Sequences of up to kSmallMax positions.
-//   * Keys stay in registers: thread t holds positions 4096c + 4t + e
+// Rows of up to R * 32768 positions (R <= 8 rounds).
+//   * Round r of the keys: thread t holds positions r*32768 + 4096c + 4t + e
 //     (c < 8, e < 4), so every load instruction reads 1 KB of contiguous
-//     scores.
+//     scores (16-byte loads when rows are 16-byte aligned, 4-byte loads
+//     otherwise).  With one round the keys stay in registers for the whole
+//     kernel; otherwise each pass reloads them (from L2 after the first).
 //   * Radix passes (12, 12, then 8 bits; usually the first suffices) find the
 //     bin of the r-th largest key, stopping as soon as that bin holds at most
 //     kBinCap keys.
@@ -314,23 +316,26 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
 //     lower position) and the best `want` are marked too.  If the bin is
 //     bigger than kBinCap after the last pass, its keys are all equal and the
 //     lowest positions win: they are marked from a second bitmap.
-//   * The output is written from the bitmap: thread t owns bitmap word t
-//     (positions 32t .. 32t + 31), one block scan orders the words.
-constexpr int kSmallChunks = 8;                          // 4096-position chunks
-constexpr int kSmallMax = kSmallChunks * 4 * kThreadsTk;  // positions per sequence
+//   * The output is written from the bitmap: thread t owns bitmap words
+//     R*t .. R*t + R - 1 (positions 32Rt .. 32R(t+1) - 1), one block scan
+//     orders the threads.
+constexpr int kSmallChunks = 8;                          // 4096-position chunks per round
+constexpr int kRoundLen = kSmallChunks * 4 * kThreadsTk;  // positions per round (32768)
+constexpr int kMaxRounds = 8;
 constexpr int kBinCap = 2044;                            // bin members ranked directly
-constexpr int kMapWords = kSmallMax / 32;                // bitmap words (= threads)
-static_assert(kMapWords == kThreadsTk, "one bitmap word per thread");
 
+// VEC: 16-byte score loads (rows 16-byte aligned).
+template <bool VEC>
 __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
     int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     int32_t k, int32_t n_sink, int32_t window, int32_t* __restrict__ idx, int32_t idx_stride,
     int32_t* __restrict__ n_idx) {
+  constexpr int kWords = kMaxRounds * kThreadsTk;  // bitmap words (the first R * 1024 are used)
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t s_wave[kWavesTk];
   __shared__ uint32_t s_out[4];
-  __shared__ uint32_t taken[kMapWords];    // positions selected (above the bin, or ranked in)
-  __shared__ uint32_t in_bin[kMapWords];   // bin members, when they are all equal
+  __shared__ uint32_t taken[kWords];    // positions selected (above the bin, or ranked in)
+  __shared__ uint32_t in_bin[kWords];   // bin members, when they are all equal
   // bin members as (key << 32 | ~position): larger means ranked first
   __shared__ __align__(16) uint64_t bin_rank_key[kBinCap + 4];
   __shared__ uint32_t s_count;
@@ -352,30 +357,44 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
     if (tid == 0) n_idx[b] = k;
     return;
   }
+  // Rounds this row needs (the launcher guarantees max_ctx <= kMaxRounds rounds);
+  // with one round the keys stay in registers.
+  const int R = (L + kRoundLen - 1) / kRoundLen;
+  const bool reload = R > 1;
 
-  // Keys; 0 outside M = [s_end, w_start).  16-byte loads (the launcher
-  // guarantees max_ctx % 4 == 0 and an aligned score array); addresses are
-  // clamped into the row rather than branched on, so all loads are in flight
-  // together (a clamped load only serves positions at or past the row end,
-  // which are masked).
+  // Keys of round `rd`; 0 outside M = [s_end, w_start).  16-byte loads (the
+  // launcher guarantees max_ctx % 4 == 0 and an aligned score array);
+  // addresses are clamped into the row rather than branched on, so all loads
+  // are in flight together (a clamped load only serves positions at or past
+  // the row end, which are masked).
   const float* sc = scores + (size_t)b * max_ctx;
   uint32_t key[kSmallChunks][4];
-  float v[kSmallChunks][4];
+  auto load_round = [&](int rd) {
+    float v[kSmallChunks][4];
 #pragma unroll
-  for (int c = 0; c < kSmallChunks; ++c) {
-    const int p0 = min(c * 4 * kThreadsTk + 4 * tid, max_ctx - 4);
-    const float4 x = *reinterpret_cast<const float4*>(sc + p0);
-    v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
-  }
+    for (int c = 0; c < kSmallChunks; ++c) {
+      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
+      if (VEC) {
+        const float4 x = *reinterpret_cast<const float4*>(sc + min(p0, max_ctx - 4));
+        v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
+      } else {
 #pragma unroll
-  for (int c = 0; c < kSmallChunks; ++c)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int p = c * 4 * kThreadsTk + 4 * tid + e;
-      key[c][e] = (p >= s_end && p < w_start) ? order_key(v[c][e]) : 0u;
+        for (int e = 0; e < 4; ++e) v[c][e] = sc[min(p0 + e, max_ctx - 1)];
+      }
     }
-  taken[tid] = 0u;
-  in_bin[tid] = 0u;
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid + e;
+        key[c][e] = (p >= s_end && p < w_start) ? order_key(v[c][e]) : 0u;
+      }
+  };
+  if (!reload) load_round(0);
+  for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) {
+    taken[i] = 0u;
+    in_bin[i] = 0u;
+  }
   if (tid == 0) s_count = 0u;
 
   // Radix passes: after each, keys whose masked value exceeds `prefix` are
@@ -388,12 +407,16 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
     const uint32_t nb = level == 2 ? 256u : (uint32_t)kBins;
     for (int i = tid; i < (int)nb; i += kThreadsTk) hist[i] = 0u;
     __syncthreads();
+#pragma unroll 1
+    for (int rd = 0; rd < R; ++rd) {
+      if (reload) load_round(rd);
 #pragma unroll
-    for (int c = 0; c < kSmallChunks; ++c)
+      for (int c = 0; c < kSmallChunks; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
-          atomicAdd(&hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
+        for (int e = 0; e < 4; ++e)
+          if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
+            atomicAdd(&hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
+    }
     __syncthreads();
     find_digit(hist, nb, shift, prefix, want, s_wave, s_out);
     nbin = s_out[2];
@@ -403,27 +426,31 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
   const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
 
   // Mark keys above the bin; collect (or mark) the bin's members.
+#pragma unroll 1
+  for (int rd = 0; rd < R; ++rd) {
+    if (reload) load_round(rd);
 #pragma unroll
-  for (int c = 0; c < kSmallChunks; ++c) {
-    uint32_t above = 0u, inb = 0u;
+    for (int c = 0; c < kSmallChunks; ++c) {
+      uint32_t above = 0u, inb = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t m = key[c][e] & mask;
-      above |= (key[c][e] != 0u && m > prefix) ? (1u << e) : 0u;
-      inb |= (key[c][e] != 0u && m == prefix) ? (1u << e) : 0u;
-    }
-    const int p0 = c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word, bits p0 % 32 ..
-    if (above != 0u) atomicOr(&taken[p0 >> 5], above << (p0 & 31));
-    if (inb != 0u) {
-      if (exact) {
-        atomicOr(&in_bin[p0 >> 5], inb << (p0 & 31));
-      } else {
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t m = key[c][e] & mask;
+        above |= (key[c][e] != 0u && m > prefix) ? (1u << e) : 0u;
+        inb |= (key[c][e] != 0u && m == prefix) ? (1u << e) : 0u;
+      }
+      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
+      if (above != 0u) atomicOr(&taken[p0 >> 5], above << (p0 & 31));
+      if (inb != 0u) {
+        if (exact) {
+          atomicOr(&in_bin[p0 >> 5], inb << (p0 & 31));
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((inb >> e) & 1u) {
-            const uint32_t slot = atomicAdd(&s_count, 1u);  // < nbin <= kBinCap
-            bin_rank_key[slot] = ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(p0 + e);
-          }
+          for (int e = 0; e < 4; ++e)
+            if ((inb >> e) & 1u) {
+              const uint32_t slot = atomicAdd(&s_count, 1u);  // < nbin <= kBinCap
+              bin_rank_key[slot] = ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(p0 + e);
+            }
+        }
       }
     }
   }
@@ -449,23 +476,28 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
   }
 
   // Ordered emit: [0, s_end) ++ taken middle positions ++ [w_start, L).
-  uint32_t word = taken[tid];
+  // Thread t owns words R*t .. R*t + R - 1.
+  uint32_t* my = taken + R * tid;
   uint32_t tot;
-  if (exact) {  // the first `want` bin members in position order
-    const uint32_t ib = in_bin[tid];
-    const uint32_t before = block_exclusive_scan((uint32_t)__builtin_popcount(ib), s_wave, tot);
-    uint32_t bits = ib;
-    for (uint32_t q = before; bits != 0u && q < want; ++q) {
-      word |= bits & (~bits + 1u);  // lowest remaining member
-      bits &= bits - 1u;
+  if (exact) {  // the first `want` bin members in position order join the taken set
+    uint32_t n_in = 0u;
+    for (int j = 0; j < R; ++j) n_in += (uint32_t)__builtin_popcount(in_bin[R * tid + j]);
+    uint32_t q = block_exclusive_scan(n_in, s_wave, tot);
+    for (int j = 0; j < R; ++j) {
+      uint32_t w = my[j];
+      for (uint32_t bits = in_bin[R * tid + j]; bits != 0u && q < want; ++q) {
+        w |= bits & (~bits + 1u);  // lowest remaining member
+        bits &= bits - 1u;
+      }
+      my[j] = w;
     }
   }
-  uint32_t o = block_exclusive_scan((uint32_t)__builtin_popcount(word), s_wave, tot) + (uint32_t)s_end;
-  while (word != 0u) {
-    const int i = __builtin_ctz(word);
-    word &= word - 1u;
-    if (o < (uint32_t)idx_stride) out[o++] = 32 * tid + i;
-  }
+  uint32_t n_sel = 0u;
+  for (int j = 0; j < R; ++j) n_sel += (uint32_t)__builtin_popcount(my[j]);
+  uint32_t o = block_exclusive_scan(n_sel, s_wave, tot) + (uint32_t)s_end;
+  for (int j = 0; j < R; ++j)
+    for (uint32_t bits = my[j]; bits != 0u; bits &= bits - 1u)
+      if (o < (uint32_t)idx_stride) out[o++] = 32 * (R * tid + j) + __builtin_ctz(bits);
   for (int i = tid; i < s_end; i += kThreadsTk) out[i] = i;
   for (int i = tid; i < tail; i += kThreadsTk) out[s_end + r + i] = w_start + i;
   if (tid == 0) n_idx[b] = k;
@@ -477,12 +509,17 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
                               const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
                               int32_t* idx, int32_t idx_stride, int32_t* n_idx,
                               hipStream_t stream) {
-  if (max_ctx <= kSmallMax && max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) {
-    hipLaunchKernelGGL(select_topk_kernel, dim3(batch), dim3(kThreadsTk), 0, stream, max_ctx, scores,
-                       seq_lens, k, n_sink, window, idx, idx_stride, n_idx);
+  const bool vec = max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  const int rounds = (max_ctx + kRoundLen - 1) / kRoundLen;
+  const dim3 grid(batch), block(kThreadsTk);
+  const auto args = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, max_ctx, scores, seq_lens, k, n_sink, window,
+                       idx, idx_stride, n_idx);
+  };
+  if (rounds <= kMaxRounds) {
+    if (vec) args(select_topk_kernel<true>); else args(select_topk_kernel<false>);
   } else {
-    hipLaunchKernelGGL(select_topk_large_kernel, dim3(batch), dim3(kThreadsTk), 0, stream, max_ctx,
-                       scores, seq_lens, k, n_sink, window, idx, idx_stride, n_idx);
+    args(select_topk_large_kernel);
   }
   return hipGetLastError();
 }

@@ -201,3 +201,5 @@ def test_split_plan_covers_span(lib):
     # chunks are capped at 8192 positions
     d = desc(batch=8, num_q_heads=32, num_kv_heads=8, q_len=7, max_ctx=131078)
     assert B.split_plan(d, 131078) == (17, 8192)
+    d = desc(batch=1, num_q_heads=8, num_kv_heads=1, q_len=2, head_dim=64, max_ctx=1 << 24)
+    assert B.split_plan(d, 1 << 24) == (2048, 8192)

@@ -181,16 +181,18 @@ def test_select_random_scores(L):
         _select_case(sc, lens, k, ns, win)
 
 
-@pytest.mark.parametrize("L", [5, 64, 1000, 4096, 20001, 32768])
-def test_select_random_scores_register_path(L):
-    """Rows whose length is a multiple of 4 and at most 32768 take the
-    register-resident selection kernel; other rows the general one."""
+@pytest.mark.parametrize("L", [5, 64, 1000, 4096, 20001, 32768, 32769, 65536, 100001, 131072, 270000])
+def test_select_random_scores_aligned_rows(L):
+    """Rows whose length is a multiple of 4 (16-byte aligned): one round of
+    32768 positions with keys in registers, up to 8 reloaded rounds, and the
+    general kernel beyond 262144 positions.  (Rows in
+    test_select_random_scores are not a multiple of 4: 4-byte loads.)"""
     rng = np.random.default_rng(100 + L)
     ctx = (L + 3) // 4 * 4
     lens = [L, max(1, L // 3), max(1, L - 1), max(1, L // 2 + 1)]
     sc = rng.standard_normal((len(lens), ctx)).astype(np.float32) * 10
     sc[3, ::7] = sc[3, 0]  # a repeated value across the row
-    for k, ns, win in [(1, 0, 0), (16, 4, 8), (512, 4, 64), (2048, 4, 128), (L, 0, 0)]:
+    for k, ns, win in [(1, 0, 0), (16, 4, 8), (512, 4, 64), (2048, 4, 128), (6554, 4, 256), (L, 0, 0)]:
         if k < 1 or ns + win > k:
             continue
         _select_case(sc, lens, k, ns, win)
@@ -206,6 +208,11 @@ def test_select_ties_zeros_and_infinities():
     lens = [5000, 4000, 4999, 3000]
     for k, ns, win in [(7, 0, 0), (100, 4, 16), (1000, 10, 990), (1000, 0, 1000), (2500, 3, 5)]:
         _select_case(sc, lens, k, ns, win, stride=k + 7)
+    # a long all-equal row (every radix pass keeps the whole bin) and a two-valued one
+    sc3 = np.ones((2, 70000), np.float32)
+    sc3[1, ::2] = 2.0
+    for k, ns, win in [(3000, 4, 64), (40000, 0, 100)]:
+        _select_case(sc3, [70000, 69999], k, ns, win)
     # -inf must rank below every finite score
     sc2 = np.full((1, 64), -np.inf, np.float32)
     sc2[0, 10] = -1e30
