@@ -47,16 +47,18 @@ float effective_scale(const vgsa_attn_desc& d) {
 }
 
 struct Carve {
+  int32_t* header;
   float* part_o;
   float* part_ml;
 };
 
 Carve carve(const vgsa_attn_desc& d, const SplitPlan& p, void* ws) {
-  const size_t o_bytes = (size_t)d.batch * d.num_q_heads * d.q_len * p.num_splits * d.head_dim * 4;
+  const size_t o_bytes = (size_t)d.batch * d.num_q_heads * d.q_len * p.part_splits * d.head_dim * 4;
   const size_t o_aligned = (o_bytes + 255) / 256 * 256;
   Carve c;
-  c.part_o = static_cast<float*>(ws);
-  c.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + o_aligned);
+  c.header = static_cast<int32_t*>(ws);
+  c.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + kHeaderBytes);
+  c.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + kHeaderBytes + o_aligned);
   return c;
 }
 
@@ -88,6 +90,9 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
   const Carve c = carve(d, p, workspace);
   a.part_o = c.part_o;
   a.part_ml = c.part_ml;
+  a.header = c.header;
+  a.part_splits = p.part_splits;
+  a.balance = 0;
   a.layout = VGSA_LOGITS_NONE;
   a.row0 = a.row1 = -1;
   a.out = nullptr;
@@ -133,13 +138,15 @@ SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span) {
   SplitPlan p;
   p.num_splits = (int32_t)s;
   p.chunk = (int32_t)chunk;
+  p.part_splits = (s > 1 && batch > 1 && batch <= kMaxBalanceBatch) ? (int32_t)(kBalanceSplits * s)
+                                                                    : (int32_t)s;
   return p;
 }
 
 size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p) {
-  const size_t rows = (size_t)d.batch * d.num_q_heads * d.q_len * p.num_splits;
+  const size_t rows = (size_t)d.batch * d.num_q_heads * d.q_len * p.part_splits;
   const size_t o_bytes = rows * d.head_dim * 4;
-  return (o_bytes + 255) / 256 * 256 + rows * 2 * 4;
+  return kHeaderBytes + (o_bytes + 255) / 256 * 256 + rows * 2 * 4;
 }
 
 }  // namespace vgsa
@@ -218,6 +225,7 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.direct = out != nullptr ? 1 : 0;
+  a.balance = (!a.direct && p.part_splits > p.num_splits) ? 1 : 0;
   return hip_status(launch_attention_partials(a, false, static_cast<hipStream_t>(stream)));
 }
 
@@ -294,6 +302,8 @@ vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
   a.num_splits = p.num_splits;
   a.chunk = p.chunk;
   a.span = span;
+  a.part_splits = p.part_splits;
+  a.header = c.header;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   return hip_status(launch_combine(a, static_cast<hipStream_t>(stream)));
@@ -372,6 +382,8 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
   ca.num_splits = p.num_splits;
   ca.chunk = p.chunk;
   ca.span = d.max_ctx;
+  ca.part_splits = p.part_splits;
+  ca.header = c.header;
   ca.out = static_cast<uint16_t*>(out);
   ca.lse = lse;
   AggregateArgs ag{d.batch, d.num_q_heads, d.num_kv_heads, d.max_ctx, (int32_t)layout, logits,

@@ -116,11 +116,44 @@ void attn_partials_kernel(AttnArgs a) {
   constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || EMIT == kEmitSumColumn;
   __shared__ __align__(16) float slog[kGroupLogits ? kLogitBuf : 4];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y;
+  int split = blockIdx.x, b = blockIdx.z, chunk = a.chunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, kg = lane >> 4;
 
-  const int start = split * a.chunk;
+  // Ragged batches (verify): every workgroup derives the same item length
+  // from the lengths, short enough that the non-empty items of a kv-head fill
+  // its S * B workgroups, and takes the u-th of them (u = split + S * b):
+  // the longest workgroup then has about the mean work, not the longest row's.
+  if (!SPARSE && a.balance) {
+    const int S = a.num_splits, B = a.batch;
+    int64_t total = 0;
+    for (int i = 0; i < B; ++i) total += min(max(a.seq_lens[i], 0), a.max_ctx);
+    const int64_t fit = (total + (int64_t)S * B - B - 1) / ((int64_t)S * B - B);  // S > 1 here
+    const int floor_len = (a.chunk / kBalanceSplits + kMinChunk - 1) / kMinChunk * kMinChunk;
+    const int cp = (int)min((int64_t)a.chunk,
+                            max((int64_t)floor_len, (fit + kMinChunk - 1) / kMinChunk * kMinChunk));
+    const int u = split + S * b;
+    int acc = 0, bi = -1, si = 0;
+    for (int i = 0; i < B && bi < 0; ++i) {
+      const int n = (min(max(a.seq_lens[i], 0), a.max_ctx) + cp - 1) / cp;
+      if (u < acc + n) {
+        bi = i;
+        si = u - acc;
+      }
+      acc += n;
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) a.header[0] = cp;
+    if (bi < 0) return;  // more workgroups than items
+    b = bi;
+    split = si;
+    chunk = cp;
+  } else if (!a.direct && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 &&
+             threadIdx.x == 0) {
+    a.header[0] = chunk;
+  }
+
+  const int start = split * chunk;
   // Sparse: the list entries of this wavefront's first kPreTiles tiles are
   // loaded (clamped in bounds) together with the lengths, so those tiles
   // need no index round trip of their own.
@@ -155,7 +188,7 @@ void attn_partials_kernel(AttnArgs a) {
     }
     return;
   }
-  const int end = min(start + a.chunk, count);
+  const int end = min(start + chunk, count);
 
   // This lane's query column c16 of block qb: causal limit and collected row.
   int lim[QB], rowc[QB], head[QB];
@@ -576,7 +609,7 @@ void attn_partials_kernel(AttnArgs a) {
       if (s_m[w][m] != kNegInf) rowL += s_l[w][m] * fast_exp2(s_m[w][m] - rowM);
     s_inv[m] = rowL > 0.f ? 1.f / rowL : 0.f;
   }
-  const int S = a.num_splits;
+  const int S = a.part_splits;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
 #pragma unroll

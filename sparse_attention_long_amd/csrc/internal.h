@@ -37,13 +37,25 @@ constexpr int kMaxRows = 64;
 struct SplitPlan {
   int32_t num_splits;
   int32_t chunk;
+  int32_t part_splits;  // row stride of the partial arrays: num_splits, or
+                        // kBalanceSplits * num_splits when items may shrink
 };
+
+// Ragged batches: a verify launch over several sequences (at most
+// kMaxBalanceBatch) shrinks its items so that the non-empty ones fill the
+// grid (see attn_partials_kernel); an item is never shorter than
+// chunk / kBalanceSplits, so the partials hold kBalanceSplits times the splits.
+constexpr int kBalanceSplits = 4;
+constexpr int kMaxBalanceBatch = 256;
 
 SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span);
 
 // Partial results of one attention launch, carved out of the workspace:
-//   part_o  fp32 [B][Hq][T][S][d]   un-normalised sum of p * v of the split
-//   part_ml fp32 [B][Hq][T][S][2]   (running max m in log2 units, sum l)
+//   header  int32 [64]               [0]: the item length the launch used
+//   part_o  fp32 [B][Hq][T][P][d]    un-normalised sum of p * v of the item
+//   part_ml fp32 [B][Hq][T][P][2]    (running max m in log2 units, sum l)
+// with P = part_splits.
+constexpr size_t kHeaderBytes = 256;
 size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p);
 
 struct AttnArgs {
@@ -60,6 +72,9 @@ struct AttnArgs {
   int32_t row0, row1;
   float* part_o;
   float* part_ml;
+  int32_t* header;   // the launch records its item length in header[0]
+  int32_t part_splits;
+  int32_t balance;   // shrink items to the lengths (verify, several sequences)
   uint16_t* out;     // direct mode (one split): final bf16 output ...
   float* lse;        // ... and lse (may be null)
   int32_t direct;
@@ -80,6 +95,8 @@ struct CombineArgs {
   int32_t rows_per_seq;  // Hq * T
   int32_t head_dim;
   int32_t num_splits, chunk, span;
+  int32_t part_splits;    // row stride of the partials
+  const int32_t* header;  // header[0]: the item length the partials were made with
   uint16_t* out;
   float* lse;
 };

@@ -25,9 +25,12 @@ __device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int 
   constexpr int Q = D / 4;
   const int b = row / a.rows_per_seq;
   const int len = min(max(a.lengths[b], 0), a.span);
-  const int nvalid = min((len + a.chunk - 1) / a.chunk, a.num_splits);
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)row * a.num_splits;
-  const float4* po = reinterpret_cast<const float4*>(a.part_o) + (size_t)row * a.num_splits * Q + t;
+  // the item length the partials were made with (clamped: the header only
+  // ever narrows the plan's chunk)
+  const int chunk = min(max(a.header[0], kMinChunk), a.chunk);
+  const int nvalid = min((len + chunk - 1) / chunk, a.part_splits);
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)row * a.part_splits;
+  const float4* po = reinterpret_cast<const float4*>(a.part_o) + (size_t)row * a.part_splits * Q + t;
   float M = kNegInf, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < nvalid; s0 += kMergeBatch) {
