@@ -129,20 +129,25 @@ def verify_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens: Sequ
 
 # --------------------------------------------------------------------------- logits
 def collected_logits(q: np.ndarray, k: np.ndarray, seq_lens: Sequence[int],
-                     rows: Tuple[int, int], scale: Optional[float] = None) -> np.ndarray:
-    """Pre-softmax logits of the two collected rows (Vegas, "B. Collect-2-Query";
-    section 3: written before softmax normalisation).
+                     rows: Sequence[int], scale: Optional[float] = None) -> np.ndarray:
+    """Pre-softmax logits of the collected rows (Vegas, section 3: written
+    before softmax normalisation).  "A." sums its score over every verify row
+    t = 1..gamma+1; "B. Collect-2-Query" keeps only the first draft row and
+    the bonus row.  `rows` names the collected rows (0-based, ascending), so
+    both readings are this one function.
 
-    Returns l [B, 2, Hq, ctx]: l[b, c, h, j] = scale * q[b, h, rows[c]] . k[b, g, j]
-    for j <= L_b - T + rows[c], -inf for the causally hidden positions up to
-    L_b, NaN beyond L_b (undefined).
+    Returns l [B, R, Hq, ctx], R = len(rows):
+    l[b, c, h, j] = scale * q[b, h, rows[c]] . k[b, g, j] for
+    j <= L_b - T + rows[c], -inf for the causally hidden positions up to L_b,
+    NaN beyond L_b (undefined).
     """
     q = _f64(q)
     B, Hq, T, d = q.shape
     Hkv, ctx = k.shape[1], k.shape[2]
     G = Hq // Hkv
     sc = default_scale(d) if scale is None else scale
-    out = np.full((B, 2, Hq, ctx), np.nan)
+    rows = [int(t) for t in rows]
+    out = np.full((B, len(rows), Hq, ctx), np.nan)
     for b in range(B):
         L = int(seq_lens[b])
         for g in range(Hkv):
@@ -157,8 +162,8 @@ def collected_logits(q: np.ndarray, k: np.ndarray, seq_lens: Sequence[int],
 
 
 def kvgroup_sum(logits: np.ndarray, num_kv_heads: int) -> np.ndarray:
-    """Collected logits summed over the two rows and over the q-heads of each
-    kv-head: [B, 2, Hq, ctx] -> [B, Hkv, ctx]."""
+    """Collected logits summed over the collected rows and over the q-heads of
+    each kv-head: [B, R, Hq, ctx] -> [B, Hkv, ctx]."""
     B, _, Hq, ctx = logits.shape
     G = Hq // num_kv_heads
     out = np.zeros((B, num_kv_heads, ctx))
@@ -170,7 +175,7 @@ def kvgroup_sum(logits: np.ndarray, num_kv_heads: int) -> np.ndarray:
 def aggregate_scores(logits: np.ndarray) -> np.ndarray:
     """One importance score per KV position (Vegas, "A.", the summand of the
     argmax: sum over the collected draft/bonus rows and all query heads).
-    Accepts per-head logits [B, 2, Hq, ctx] or kv-group sums [B, Hkv, ctx]."""
+    Accepts per-head logits [B, R, Hq, ctx] or kv-group sums [B, Hkv, ctx]."""
     if logits.ndim == 4:
         return logits.sum(axis=(1, 2))
     return logits.sum(axis=1)

@@ -97,11 +97,11 @@ def test_single_visible_position():
 
 
 # ------------------------------------------------------------------ collected logits
-def test_logits_closed_form_basis_keys():
+@pytest.mark.parametrize("rows", [(0, 4), (0, 1, 2, 3, 4), (2,), (1, 3)])
+def test_logits_closed_form_basis_keys(rows):
     # k[g, j] = (g + 1) * e_{(j + g) mod d}  =>  l[c, h, j] = scale * (g+1) * q[h, r_c][(j+g) mod d]
     B, Hq, Hkv, T, d, ctx = 2, 6, 3, 5, 8, 30
     lens = [30, 17]
-    rows = (0, 4)
     q = rnd((B, Hq, T, d), 14)
     k = np.zeros((B, Hkv, ctx, d))
     for g in range(Hkv):
@@ -146,6 +146,29 @@ def test_scores_per_head_equal_regrouped_sum():
     # linearity: the score of position j is the sum of its 2*Hq logits
     b, j = 1, 7
     assert abs(s1[b, j] - sum(l[b, c, h, j] for c in range(2) for h in range(Hq))) < 1e-12
+
+
+def test_scores_all_rows_closed_form():
+    # Collecting every verify row (the full sum of Vegas "A."): for a position
+    # every row sees, the score is scale * k_g[j] . (sum over rows and the
+    # group's heads of q), one dot product per kv-head; the last T - 1
+    # positions are hidden from row 0 and score -inf.
+    B, Hq, Hkv, T, d = 2, 8, 2, 5, 16
+    lens = [40, 23]
+    q, k = rnd((B, Hq, T, d), 19), rnd((B, Hkv, 40, d), 20)
+    sc = 0.3
+    l = oracle.collected_logits(q, k, lens, range(T), scale=sc)
+    assert l.shape == (B, T, Hq, 40)
+    s = oracle.aggregate_scores(oracle.kvgroup_sum(l, Hkv))
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        qsum = [q[b, g * G:(g + 1) * G].sum(axis=(0, 1)) for g in range(Hkv)]
+        want = sc * sum(k[b, g, :L - T + 1] @ qsum[g] for g in range(Hkv))
+        np.testing.assert_allclose(s[b, :L - T + 1], want, rtol=1e-12, atol=1e-12)
+        assert np.all(np.isneginf(s[b, L - T + 1:L]))
+    # the Collect-2 rows are a subset: their per-head logits are the same values
+    l2 = oracle.collected_logits(q, k, lens, (0, T - 1), scale=sc)
+    assert np.array_equal(l2, l[:, [0, T - 1]], equal_nan=True)
 
 
 # ------------------------------------------------------------------ selection
