@@ -15,6 +15,10 @@ events on the stream it runs on; `cpu_baseline` is the fp64 oracle on a
 bounded sample of the same workload on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
+                    [--logits kvgroup_sum|per_head] [--collect two|all]
+
+The defaults are the kv-group-summed layout and the two Collect-2-Query rows;
+the JSON also reports the verify kernel with every row collected.
 """
 from __future__ import annotations
 
@@ -37,16 +41,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(w, lens):
+def alg_bytes(w, lens, layout="kvgroup_sum", n_rows=2):
     """Algorithmic HBM bytes of one iteration, by stage (what the method must
     move: every K/V row read once, the collected logits written once, scores
-    and indices once; split partials are implementation overhead and excluded)."""
+    and indices once; split partials are implementation overhead and excluded).
+    Logits are one fp32 per (kv-head, position), or per (collected row,
+    q-head, position) in the per-head layout."""
     B, Hq, Hkv, d, T, k = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.q_len, w.budget
     Ls = [int(L) for L in lens]
     kv = sum(Hkv * L * d * 2 * 2 for L in Ls)
     q_in = B * Hq * T * d * 2
     o_out = B * Hq * T * d * 2
-    emit = sum(Hkv * L * 4 for L in Ls)
+    per_pos = Hkv if layout == "kvgroup_sum" else n_rows * Hq
+    emit = sum(per_pos * L * 4 for L in Ls)
     agg = emit + sum(L * 4 for L in Ls)
     sel = sum(L * 4 for L in Ls) + B * k * 4
     n_sel = [min(k, L) for L in Ls]
@@ -85,7 +92,7 @@ def counter_traffic(workload_name):
     return int(m.group(1))
 
 
-def cpu_baseline(w, x, seconds):
+def cpu_baseline(w, x, seconds, rows):
     """The fp64 oracle, as it stands, on whole sequences of the workload until
     `seconds` have passed; scaled to iterations/s of the full batch."""
     import oracle
@@ -100,7 +107,7 @@ def cpu_baseline(w, x, seconds):
         sl = slice(b, b + 1)
         lens = x.seq_lens[sl]
         oracle.verify_attention(x.q[sl], x.k[sl], x.v[sl], lens)
-        lg = oracle.collected_logits(x.q[sl], x.k[sl], lens, w.collect_rows)
+        lg = oracle.collected_logits(x.q[sl], x.k[sl], lens, rows)
         sc = oracle.aggregate_scores(oracle.kvgroup_sum(lg, w.num_kv_heads))
         idx = oracle.select_topk(sc[0], int(lens[0]), w.budget, w.n_sink, w.window)
         if w.sparse_verify:
@@ -129,6 +136,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--logits", choices=("kvgroup_sum", "per_head"), default="kvgroup_sum",
+                    help="layout of the collected logits")
+    ap.add_argument("--collect", choices=("two", "all"), default="two",
+                    help="collected verify rows: first draft + bonus (Collect-2-Query), or every row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=0,
                     help="1: capture one step as a HIP graph and time its replays")
@@ -183,7 +194,10 @@ def main():
     max_ctx = w.max_ctx()
     desc = Bn.make_desc(q, k, bt, max_ctx)
     ws_v = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    logits = torch.empty((B, Hkv, max_ctx), dtype=torch.float32, device=dev)
+    rows = w.collect_rows if args.collect == "two" else tuple(range(T))
+    KV = Bn.LOGITS_KVGROUP_SUM if args.logits == "kvgroup_sum" else Bn.LOGITS_PER_HEAD
+    lshape = (B, Hkv, max_ctx) if KV == Bn.LOGITS_KVGROUP_SUM else (B, len(rows), Hq, max_ctx)
+    logits = torch.empty(lshape, dtype=torch.float32, device=dev)
     out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
     scores = torch.empty((B, max_ctx), dtype=torch.float32, device=dev)
@@ -193,8 +207,6 @@ def main():
     ws_s = torch.empty(Bn.sparse_workspace_bytes(desc, stride), dtype=torch.uint8, device=dev)
     out_s = torch.empty_like(out)
     lse_s = torch.empty_like(lse)
-    rows = w.collect_rows
-    KV = Bn.LOGITS_KVGROUP_SUM
     # draft steps: step s attends with one fresh query per head over the
     # selected positions plus the s positions drafted since (lengths L + s)
     n_draft = w.draft_steps
@@ -215,7 +227,7 @@ def main():
     def step():
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
         # split combine + score aggregation in one launch
-        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
+        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores, num_rows=len(rows))
         Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         if w.sparse_verify:
             Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
@@ -285,7 +297,7 @@ def main():
     stages = {
         "verify_partials": verify_us,
         "combine_aggregate": per_launch_us(
-            lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)),
+            lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores, num_rows=len(rows))),
         "select": per_launch_us(
             lambda: Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)),
     }
@@ -301,8 +313,16 @@ def main():
         stages["draft_steps"] = per_launch_us(select_and_draft) - stages["select"]
     verify_none_us = per_launch_us(
         lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, Bn.LOGITS_NONE, None, ws_v))
+    # every verify row collected (the score summed over all T rows), same layout
+    all_rows = tuple(range(T))
+    logits_all = logits
+    if KV == Bn.LOGITS_PER_HEAD and len(rows) != T:
+        logits_all = torch.empty((B, T, Hq, max_ctx), dtype=torch.float32, device=dev)
+    verify_all_us = per_launch_us(
+        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, all_rows, KV, logits_all, ws_v))
+    del logits_all
 
-    ab = alg_bytes(w, x.seq_lens)
+    ab = alg_bytes(w, x.seq_lens, args.logits, len(rows))
     iters = K / wall
     achieved = ab["verify_kernel"] / (verify_us * 1e-6) / 1e9
     result = {
@@ -322,7 +342,7 @@ def main():
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "gamma": w.gamma,
                    "budget": w.budget, "n_sink": w.n_sink, "window": w.window,
                    "draft_steps": n_draft, "sparse_verify": w.sparse_verify,
-                   "paged": w.paged, "logits": "kvgroup_sum"},
+                   "paged": w.paged, "logits": args.logits, "collect_rows": list(rows)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
                      "kernel": "attn_partials_kernel (verify)",
@@ -333,6 +353,8 @@ def main():
         "stages_us": stages,
         "verify_partials_no_logits_us": verify_none_us,
         "logit_emit_overhead": stages["verify_partials"] / verify_none_us - 1.0,
+        "verify_partials_all_rows_us": verify_all_us,
+        "logit_emit_overhead_all_rows": verify_all_us / verify_none_us - 1.0,
     }
     if w.sparse_verify and stages.get("sparse"):
         sb = ab["sparse_kernel_kv"]
@@ -344,7 +366,7 @@ def main():
         result["sparse_roofline"]["frac"] = result["sparse_roofline"]["achieved"] / HBM_PEAK_GBS
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, rows)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

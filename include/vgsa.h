@@ -6,8 +6,9 @@
  *
  *   1. vgsa_verify_attention  full attention of the T = gamma + 1 verify rows
  *      (gamma draft tokens + the bonus token) over the whole KV cache, writing
- *      the pre-softmax logits of two rows only: the first draft token and the
- *      bonus token.
+ *      the pre-softmax logits of the collected rows only: normally two, the
+ *      first draft token and the bonus token (any subset of the T rows can be
+ *      collected, all of them included).
  *        Vegas (gist.science 2602.07223), section 2 "core mechanism", step 1
  *        (the verify pass computes the logits of every KV entry);
  *        "B. Collect-2-Query" (collect the first draft and the bonus token);
@@ -76,13 +77,15 @@ typedef enum vgsa_status {
   VGSA_ERR_HIP = 4          /* a HIP launch failed                           */
 } vgsa_status;
 
-/* Layout of the collected pre-softmax logits written by the verify pass. */
+/* Layout of the collected pre-softmax logits written by the verify pass.
+ * R = number of collected rows (2 for Collect-2-Query). */
 typedef enum vgsa_logit_layout {
   VGSA_LOGITS_NONE = 0,        /* no logits are written                           */
-  VGSA_LOGITS_PER_HEAD = 1,    /* fp32 [B][2][Hq][max_ctx]; [b][c][h][j] is row c */
-  VGSA_LOGITS_KVGROUP_SUM = 2  /* fp32 [B][Hkv][max_ctx]: sum over the 2 rows and
-                                  the q-heads of kv-head g (same total as PER_HEAD
-                                  summed, 2*G times fewer bytes)                  */
+  VGSA_LOGITS_PER_HEAD = 1,    /* fp32 [B][R][Hq][max_ctx]; [b][c][h][j] is the
+                                  c-th collected row (ascending row index)       */
+  VGSA_LOGITS_KVGROUP_SUM = 2  /* fp32 [B][Hkv][max_ctx]: sum over the collected
+                                  rows and the q-heads of kv-head g (same total as
+                                  PER_HEAD summed, R*G times fewer bytes)         */
 } vgsa_logit_layout;
 
 /* Shape of one attention call.  The KV cache is either contiguous,
@@ -139,10 +142,12 @@ size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_strid
  * v_cache      bf16, contiguous or paged (see vgsa_attn_desc)
  * block_table  int32 [B][max_blocks_per_seq]; NULL iff block_size == 0
  * seq_lens     int32 [B]; L_b includes the T verify tokens
- * collect_row0,
- * collect_row1 the two rows whose logits are written, 0 <= r0 < r1 < T
- *              (the first draft token's row 0 and the bonus row gamma); ignored
- *              when layout == VGSA_LOGITS_NONE
+ * collect_mask the rows whose logits are written: bit t for query row t, at
+ *              least one bit, none at or above T.  Collect-2-Query: the first
+ *              draft token's row 0 and the bonus row gamma, (1 | 1 << gamma).
+ *              All rows, (1 << T) - 1, is the full sum of Vegas "A." (every
+ *              draft token, accepted or not).  Ignored when layout ==
+ *              VGSA_LOGITS_NONE.
  * logits       fp32 in `layout`; NULL iff layout == NONE.  Written for
  *              positions j < L_b only: scale * q.k for visible positions,
  *              -inf where the row may not see j.  Entries j >= L_b untouched.
@@ -153,22 +158,24 @@ size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_strid
  */
 vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
-                                  const int32_t* seq_lens, int32_t collect_row0,
-                                  int32_t collect_row1, vgsa_logit_layout layout, float* logits,
-                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                  void* stream);
+                                  const int32_t* seq_lens, uint32_t collect_mask,
+                                  vgsa_logit_layout layout, float* logits, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* 2. Aggregate collected logits into one score per position.
  *    (Vegas, "A. aggregated attention-logit selection": the sum over draft
  *    rows t and heads h of l_ti^(h).)
  * logits   fp32 in `layout` (PER_HEAD or KVGROUP_SUM) as written by step 1
+ * num_rows PER_HEAD: the collected rows R per sequence (popcount of the
+ *          collect mask), 1..16; ignored for KVGROUP_SUM
  * scores   fp32 [B][max_ctx]; scores[b][j] for j < L_b is the sum, in a fixed
  *          order, over the collected rows and all q-heads (or over kv-groups).
  *          Entries j >= L_b untouched.
  */
 vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                  int32_t max_ctx, vgsa_logit_layout layout, const float* logits,
-                                  const int32_t* seq_lens, float* scores, void* stream);
+                                  int32_t max_ctx, vgsa_logit_layout layout, int32_t num_rows,
+                                  const float* logits, const int32_t* seq_lens, float* scores,
+                                  void* stream);
 
 /* 3. Select the positions kept for the next step.
  *    (Vegas "A." argmax over |T| = k; Dustin "1." protected sinks and window.)
@@ -225,9 +232,9 @@ vgsa_status vgsa_append_positions(int32_t batch, const int32_t* base, int32_t fi
  * The partials live in the workspace between the two calls. */
 vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table,
-                                 const int32_t* seq_lens, int32_t collect_row0,
-                                 int32_t collect_row1, vgsa_logit_layout layout, float* logits,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 const int32_t* seq_lens, uint32_t collect_mask,
+                                 vgsa_logit_layout layout, float* logits, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table,
@@ -251,11 +258,12 @@ vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
  * (Vegas §2 step 1 and "A. aggregated attention-logit selection".)
  * layout   the layout logits were written in (PER_HEAD or KVGROUP_SUM);
  *          ignored when scores is NULL
+ * num_rows PER_HEAD: collected rows per sequence, 1..q_len
  * scores   fp32 [B][max_ctx] or NULL */
 vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
                                const void* workspace, size_t workspace_bytes, void* out, float* lse,
-                               vgsa_logit_layout layout, const float* logits, float* scores,
-                               void* stream);
+                               vgsa_logit_layout layout, int32_t num_rows, const float* logits,
+                               float* scores, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,7 @@ LOGITS_NONE, LOGITS_PER_HEAD, LOGITS_KVGROUP_SUM = 0, 1, 2
 _LAYOUTS = {"none": LOGITS_NONE, "per_head": LOGITS_PER_HEAD, "kvgroup_sum": LOGITS_KVGROUP_SUM}
 
 c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+c_u32 = ctypes.c_uint32
 P_i32 = ctypes.POINTER(ctypes.c_int32)
 
 
@@ -37,21 +38,22 @@ SIGNATURES = {
     "vgsa_split_plan": (c_i32, [ctypes.POINTER(AttnDesc), c_i32, P_i32, P_i32]),
     "vgsa_verify_workspace_bytes": (c_sz, [ctypes.POINTER(AttnDesc)]),
     "vgsa_sparse_workspace_bytes": (c_sz, [ctypes.POINTER(AttnDesc), c_i32]),
-    "vgsa_verify_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
-                                      c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
-    "vgsa_aggregate_scores": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "vgsa_verify_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
+                                      c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "vgsa_aggregate_scores": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                      c_vp]),
     "vgsa_select_topk": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_i32,
                                  c_vp, c_vp]),
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
-    "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
-                                     c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]),
+    "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
+                                     c_i32, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_sparse_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                      c_vp, c_i32, c_vp, c_sz, c_vp]),
     "vgsa_combine_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_i32, c_vp, c_vp, c_sz, c_vp,
                                       c_vp, c_vp]),
     "vgsa_verify_finish": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp, c_i32,
-                                   c_vp, c_vp, c_vp]),
+                                   c_i32, c_vp, c_vp, c_vp]),
     "vgsa_append_positions": (c_i32, [c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]),
 }
 
@@ -166,6 +168,18 @@ def _check_attn(q, k_cache, v_cache, seq_lens, block_table):
 
 
 # --------------------------------------------------------------------------- entry points
+def row_mask(rows: Sequence[int], q_len: int) -> int:
+    """Collect mask from row indices: bit t set collects row t.  Rows must be
+    distinct, ascending and below q_len (the logits are stored in row order)."""
+    rows = [int(r) for r in rows]
+    if not rows or any(r < 0 or r >= q_len for r in rows) or sorted(set(rows)) != rows:
+        raise ValueError(f"collect rows {rows} must be distinct, ascending and in [0, {q_len})")
+    m = 0
+    for r in rows:
+        m |= 1 << r
+    return m
+
+
 def verify_attention(q, k_cache, v_cache, seq_lens, *, block_table=None, max_ctx=None,
                      collect_rows: Optional[Sequence[int]] = None, layout: str = "kvgroup_sum",
                      logits=None, out=None, lse=None, workspace=None, scale: float = 0.0):
@@ -175,9 +189,10 @@ def verify_attention(q, k_cache, v_cache, seq_lens, *, block_table=None, max_ctx
     lay = _LAYOUTS[layout]
     B, Hq, T, d = q.shape
     dev = q.device
-    r0, r1 = (0, T - 1) if collect_rows is None else collect_rows
+    mask = row_mask((0, T - 1) if collect_rows is None else collect_rows, T)
     if lay != LOGITS_NONE and logits is None:
-        shape = (B, 2, Hq, desc.max_ctx) if lay == LOGITS_PER_HEAD else (B, desc.num_kv_heads, desc.max_ctx)
+        R = bin(mask).count("1")
+        shape = (B, R, Hq, desc.max_ctx) if lay == LOGITS_PER_HEAD else (B, desc.num_kv_heads, desc.max_ctx)
         logits = torch.empty(shape, dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
@@ -185,7 +200,7 @@ def verify_attention(q, k_cache, v_cache, seq_lens, *, block_table=None, max_ctx
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
     ws = _workspace(verify_workspace_bytes(desc), dev, workspace)
     _check(load().vgsa_verify_attention(
-        ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens), r0, r1,
+        ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens), mask,
         lay, _p(logits) if lay != LOGITS_NONE else None, _p(out), _p(lse), _p(ws), ws.numel(),
         _stream(dev)), "vgsa_verify_attention")
     return out, lse, logits
@@ -193,14 +208,16 @@ def verify_attention(q, k_cache, v_cache, seq_lens, *, block_table=None, max_ctx
 
 def aggregate_scores(logits, seq_lens, num_q_heads: int, num_kv_heads: int, *,
                      layout: str = "kvgroup_sum", scores=None):
-    """vgsa_aggregate_scores.  Returns scores fp32 [B, max_ctx]."""
+    """vgsa_aggregate_scores.  Returns scores fp32 [B, max_ctx]; for the
+    per-head layout the collected row count is logits.shape[1]."""
     _need(logits, "logits", torch.float32)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     lay = _LAYOUTS[layout]
     B, max_ctx = logits.shape[0], logits.shape[-1]
+    n_rows = logits.shape[1] if lay == LOGITS_PER_HEAD and logits.dim() == 4 else 0
     if scores is None:
         scores = torch.empty((B, max_ctx), dtype=torch.float32, device=logits.device)
-    _check(load().vgsa_aggregate_scores(B, num_q_heads, num_kv_heads, max_ctx, lay, _p(logits),
+    _check(load().vgsa_aggregate_scores(B, num_q_heads, num_kv_heads, max_ctx, lay, n_rows, _p(logits),
                                         _p(seq_lens), _p(scores), _stream(logits.device)),
            "vgsa_aggregate_scores")
     return scores
@@ -257,9 +274,10 @@ def append_positions(base, first: int, count: int, idx, n_idx) -> None:
 # --------------------------------------------------------------------------- two-phase form
 def verify_partials(desc: AttnDesc, q, k_cache, v_cache, seq_lens, block_table, rows, layout: int,
                     logits, workspace) -> None:
+    """vgsa_verify_partials; `rows` are the collected row indices (ascending)."""
     _check(load().vgsa_verify_partials(
         ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens),
-        rows[0], rows[1], layout, _p(logits) if layout != LOGITS_NONE else None, _p(workspace),
+        row_mask(rows, desc.q_len), layout, _p(logits) if layout != LOGITS_NONE else None, _p(workspace),
         workspace.numel(), _stream(q.device)), "vgsa_verify_partials")
 
 
@@ -278,9 +296,10 @@ def combine_partials(desc: AttnDesc, span: int, lengths, workspace, out, lse) ->
 
 
 def verify_finish(desc: AttnDesc, seq_lens, workspace, out, lse, layout: int = LOGITS_NONE,
-                  logits=None, scores=None) -> None:
+                  logits=None, scores=None, num_rows: int = 2) -> None:
     """vgsa_verify_finish: combine the verify partials and (with `scores`)
-    aggregate the collected logits, in one launch."""
+    aggregate the collected logits, in one launch.  `num_rows` is the number
+    of collected rows (per-head layout only)."""
     _check(load().vgsa_verify_finish(
         ctypes.byref(desc), _p(seq_lens), _p(workspace), workspace.numel(), _p(out), _p(lse),
-        layout, _p(logits), _p(scores), _stream(out.device)), "vgsa_verify_finish")
+        layout, num_rows, _p(logits), _p(scores), _stream(out.device)), "vgsa_verify_finish")

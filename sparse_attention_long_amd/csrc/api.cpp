@@ -94,7 +94,8 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
   a.part_splits = p.part_splits;
   a.balance = 0;
   a.layout = VGSA_LOGITS_NONE;
-  a.row0 = a.row1 = -1;
+  a.row_mask = 0u;
+  a.n_rows = 0;
   a.out = nullptr;
   a.lse = nullptr;
   a.direct = 0;
@@ -197,7 +198,7 @@ namespace {
 // the final output directly.
 vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                          int32_t collect_row0, int32_t collect_row1, vgsa_logit_layout layout,
+                          uint32_t collect_mask, vgsa_logit_layout layout,
                           float* logits, void* workspace, size_t workspace_bytes, void* out,
                           float* lse, void* stream) {
   vgsa_status st = check_desc(desc);
@@ -210,8 +211,7 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
     return VGSA_ERR_INVALID_ARG;
   if (layout != VGSA_LOGITS_NONE) {
     if (logits == nullptr) return VGSA_ERR_INVALID_ARG;
-    if (collect_row0 < 0 || collect_row1 >= d.q_len || collect_row0 >= collect_row1)
-      return VGSA_ERR_INVALID_ARG;
+    if (collect_mask == 0u || (collect_mask >> d.q_len) != 0u) return VGSA_ERR_INVALID_ARG;
   }
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
   st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
@@ -220,8 +220,8 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
   AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens, workspace);
   a.layout = layout;
   a.logits = layout == VGSA_LOGITS_NONE ? nullptr : logits;
-  a.row0 = collect_row0;
-  a.row1 = collect_row1;
+  a.row_mask = layout == VGSA_LOGITS_NONE ? 0u : collect_mask;
+  a.n_rows = __builtin_popcount(a.row_mask);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.direct = out != nullptr ? 1 : 0;
@@ -260,11 +260,11 @@ extern "C" {
 
 vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table,
-                                 const int32_t* seq_lens, int32_t collect_row0,
-                                 int32_t collect_row1, vgsa_logit_layout layout, float* logits,
+                                 const int32_t* seq_lens, uint32_t collect_mask,
+                                 vgsa_logit_layout layout, float* logits,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_row0,
-                       collect_row1, layout, logits, workspace, workspace_bytes, nullptr, nullptr,
+  return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, layout,
+                       logits, workspace, workspace_bytes, nullptr, nullptr,
                        stream);
 }
 
@@ -311,8 +311,8 @@ vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
 
 vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
-                                  const int32_t* seq_lens, int32_t collect_row0,
-                                  int32_t collect_row1, vgsa_logit_layout layout, float* logits,
+                                  const int32_t* seq_lens, uint32_t collect_mask,
+                                  vgsa_logit_layout layout, float* logits,
                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   vgsa_status st = check_desc(desc);
@@ -321,11 +321,11 @@ vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, con
   const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, desc->max_ctx);
   if (p.num_splits == 1) {
     // one split: the partials kernel finishes the softmax and writes out / lse
-    return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_row0,
-                         collect_row1, layout, logits, workspace, workspace_bytes, out, lse,
+    return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, layout,
+                         logits, workspace, workspace_bytes, out, lse,
                          stream);
   }
-  st = verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_row0, collect_row1,
+  st = verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask,
                      layout, logits, workspace, workspace_bytes, nullptr, nullptr, stream);
   if (st != VGSA_OK) return st;
   return vgsa_combine_partials(desc, desc->max_ctx, seq_lens, workspace, workspace_bytes, out,
@@ -354,8 +354,8 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
 
 vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
                                const void* workspace, size_t workspace_bytes, void* out, float* lse,
-                               vgsa_logit_layout layout, const float* logits, float* scores,
-                               void* stream) {
+                               vgsa_logit_layout layout, int32_t num_rows, const float* logits,
+                               float* scores, void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
@@ -364,6 +364,8 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
     if (layout != VGSA_LOGITS_PER_HEAD && layout != VGSA_LOGITS_KVGROUP_SUM)
       return VGSA_ERR_INVALID_ARG;
     if (logits == nullptr) return VGSA_ERR_INVALID_ARG;
+    if (layout == VGSA_LOGITS_PER_HEAD && (num_rows < 1 || num_rows > d.q_len))
+      return VGSA_ERR_INVALID_ARG;
   }
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
   st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
@@ -386,23 +388,25 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
   ca.header = c.header;
   ca.out = static_cast<uint16_t*>(out);
   ca.lse = lse;
-  AggregateArgs ag{d.batch, d.num_q_heads, d.num_kv_heads, d.max_ctx, (int32_t)layout, logits,
-                   seq_lens, scores};
+  AggregateArgs ag{d.batch,  d.num_q_heads, d.num_kv_heads, d.max_ctx, (int32_t)layout,
+                   num_rows, logits,        seq_lens,       scores};
   return hip_status(launch_combine_aggregate(ca, ag, static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                  int32_t max_ctx, vgsa_logit_layout layout, const float* logits,
-                                  const int32_t* seq_lens, float* scores, void* stream) {
+                                  int32_t max_ctx, vgsa_logit_layout layout, int32_t num_rows,
+                                  const float* logits, const int32_t* seq_lens, float* scores,
+                                  void* stream) {
   if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_ctx < 1) return VGSA_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return VGSA_ERR_INVALID_ARG;
   if (layout != VGSA_LOGITS_PER_HEAD && layout != VGSA_LOGITS_KVGROUP_SUM)
     return VGSA_ERR_INVALID_ARG;
+  if (layout == VGSA_LOGITS_PER_HEAD && (num_rows < 1 || num_rows > 16)) return VGSA_ERR_INVALID_ARG;
   if (logits == nullptr || seq_lens == nullptr || scores == nullptr) return VGSA_ERR_INVALID_ARG;
   if (batch > kMaxGridYZ) return VGSA_ERR_UNSUPPORTED;
   if (batch == 0) return VGSA_OK;
-  return hip_status(launch_aggregate(batch, num_q_heads, num_kv_heads, max_ctx, layout, logits,
-                                     seq_lens, scores, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_aggregate(batch, num_q_heads, num_kv_heads, max_ctx, layout, num_rows,
+                                     logits, seq_lens, scores, static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores,

@@ -115,6 +115,14 @@ void attn_partials_kernel(AttnArgs a) {
   // would interleave small writes with the K/V read stream.
   constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || EMIT == kEmitSumColumn;
   __shared__ __align__(16) float slog[kGroupLogits ? kLogitBuf : 4];
+  // Per-head logits: each wavefront turns its 16 x 32 tile of one row block
+  // around in LDS so that a store instruction writes two rows' 32 positions
+  // as contiguous 128-byte runs (any row alignment); s_lrow[m] is the element
+  // offset of query row m's logit row, -1 when the row is not collected.
+  constexpr int kHS = kTile + 4;  // row stride of the turned tile (floats)
+  constexpr bool kHeadLogits = EMIT == VGSA_LOGITS_PER_HEAD;
+  __shared__ __align__(16) float shl[kHeadLogits ? WAVES * 16 * kHS : 4];
+  __shared__ int64_t s_lrow[kHeadLogits ? QB * 16 : 1];
 
   const int g = blockIdx.y;
   int split = blockIdx.x, b = blockIdx.z, chunk = a.chunk;
@@ -199,7 +207,12 @@ void attn_partials_kernel(AttnArgs a) {
     const int hh = ok ? m / T : 0, t = ok ? m % T : 0;
     head[qb] = g * G + hh;
     lim[qb] = ok ? L - T + t : 0x7fffffff;  // row t sees positions <= L - T + t
-    rowc[qb] = (EMIT != VGSA_LOGITS_NONE && ok) ? (t == a.row0 ? 0 : (t == a.row1 ? 1 : -1)) : -1;
+    // collected row: its rank among the collected rows (PER_HEAD row index)
+    rowc[qb] = (EMIT != VGSA_LOGITS_NONE && ok && ((a.row_mask >> t) & 1u))
+                   ? __builtin_popcount(a.row_mask & ((1u << t) - 1u)) : -1;
+    if (kHeadLogits && threadIdx.x < 16)
+      s_lrow[m] = rowc[qb] < 0 ? -1
+                               : (((int64_t)b * a.n_rows + rowc[qb]) * a.hq + head[qb]) * a.max_ctx;
   }
   const int lim_min = L - T;  // every row sees positions <= L - T
 
@@ -313,17 +326,30 @@ void attn_partials_kernel(AttnArgs a) {
     if (m < rows) {
       val = *reinterpret_cast<const u32x4*>(a.q + (row_base + m) * D + fks * 32 + (fl >> 4) * 8);
     } else if (EMIT == kEmitSumColumn && m >= QB * 16 - 2) {
-      // summed query of the collected rows (heads ascending, row0 then row1):
-      // column QB*16-2 its bf16 rounding, column QB*16-1 the rest
+      // summed query of the collected rows (heads ascending, then rows
+      // ascending): column QB*16-2 its bf16 rounding, column QB*16-1 the rest
+      // Loads go out kSumBatch at a time: one after another they would be
+      // G * R dependent round trips before the first tile is computed.
+      constexpr int kSumBatch = 4;
       float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int hh = 0; hh < G; ++hh)
+      const int R = __builtin_popcount(a.row_mask), n_sum = G * R;
+      for (int k0 = 0; k0 < n_sum; k0 += kSumBatch) {
+        bf16x8 qv[kSumBatch];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int t = c == 0 ? a.row0 : a.row1;
-          const bf16x8 qv = load16(a.q + (row_base + hh * T + t) * D + fks * 32 + (fl >> 4) * 8);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) qs[j] += (float)qv[j];
+        for (int i = 0; i < kSumBatch; ++i) {
+          const int k = min(k0 + i, n_sum - 1);  // uniform: head k / R, its (k % R)-th row
+          const int hh = k / R;
+          uint32_t mm = a.row_mask;
+          for (int c = k - hh * R; c > 0; --c) mm &= mm - 1u;
+          qv[i] = load16(a.q + (row_base + hh * T + __builtin_ctz(mm)) * D + fks * 32 + (fl >> 4) * 8);
         }
+#pragma unroll
+        for (int i = 0; i < kSumBatch; ++i)
+          if (k0 + i < n_sum) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qs[j] += (float)qv[i][j];
+          }
+      }
       bf16x8 part;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -339,13 +365,15 @@ void attn_partials_kernel(AttnArgs a) {
   int lbase = start;  // first position held in slog
   auto flush_logits = [&](int n) {  // slog[0, n) -> logits[lbase, lbase + n), nontemporal
     float* lp = a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + lbase;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // recomputed here, not held across the loop
     if ((reinterpret_cast<uintptr_t>(lp) & 15) == 0) {
-      for (int i = threadIdx.x * 4; i + 4 <= n; i += NT * 4)
+      for (int i = tid * 4; i + 4 <= n; i += NT * 4)
         __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(slog + i),
                                     reinterpret_cast<f32x4*>(lp + i));
-      for (int i = (n & ~3) + threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
+      for (int i = (n & ~3) + tid; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
     } else {
-      for (int i = threadIdx.x; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
+      for (int i = tid; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
     }
   };
   for (; ts < end; ts += step) {
@@ -412,21 +440,34 @@ void attn_partials_kernel(AttnArgs a) {
       }
     }
 
-    // Collect-2-Query epilogue: pre-softmax logits of rows row0 / row1.
-    if (EMIT == VGSA_LOGITS_PER_HEAD) {
+    // Collect-2-Query epilogue (any set of collected rows): pre-softmax logits.
+    if (kHeadLogits) {
+      float* hs = shl + wave * 16 * kHS;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if (rowc[qb] < 0) continue;
-        float* lp = a.logits + (((size_t)b * 2 + rowc[qb]) * a.hq + head[qb]) * a.max_ctx + ts;
+        // lane (c16, kg) holds row c16 at positions pb*16 + 4*kg .. +3
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb)
+        for (int pb = 0; pb < 2; ++pb) {
+          f32x4 val;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = pb * 16 + 4 * kg + r;
-            if (e < n_in)
-              __builtin_nontemporal_store((full || e < vis[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf,
-                                          lp + e);
+            val[r] = (full || e < vis[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
           }
+          *reinterpret_cast<f32x4*>(hs + c16 * kHS + pb * 16 + 4 * kg) = val;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int e = lane & 31;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int rr = 2 * i + (lane >> 5);
+          const int64_t off = s_lrow[qb * 16 + rr];
+          const float v = hs[rr * kHS + e];
+          if (off >= 0 && e < n_in) __builtin_nontemporal_store(v, a.logits + off + ts + e);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
       }
     } else if (EMIT == VGSA_LOGITS_KVGROUP_SUM) {
       // v8[pb*4 + r]: this lane's collected rows summed, at position pb*16 + 4*kg + r.
@@ -470,7 +511,8 @@ void attn_partials_kernel(AttnArgs a) {
       // after the exchange both hold the sum.  The earlier collected row sees
       // a prefix of what the later one sees, so past its causal limit the
       // sum is -inf.
-      const int vis0 = full ? kTile : max(0, min(L - T + a.row0, ts + n_in - 1) - ts + 1);
+      const int row_first = __builtin_ctz(a.row_mask);  // the earliest collected row
+      const int vis0 = full ? kTile : max(0, min(L - T + row_first, ts + n_in - 1) - ts + 1);
       f32x4 lv[2];
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb)

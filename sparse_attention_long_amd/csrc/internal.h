@@ -69,7 +69,8 @@ struct AttnArgs {
   int32_t idx_stride;
   float* logits;         // verify only, may be null
   int32_t layout;
-  int32_t row0, row1;
+  uint32_t row_mask;  // collected rows: bit t set for query row t
+  int32_t n_rows;     // popcount(row_mask): PER_HEAD rows per sequence
   float* part_o;
   float* part_ml;
   int32_t* header;   // the launch records its item length in header[0]
@@ -105,6 +106,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 struct AggregateArgs {
   int32_t batch, hq, hkv, max_ctx, layout;
+  int32_t n_rows;  // PER_HEAD: collected rows per sequence
   const float* logits;
   const int32_t* seq_lens;
   float* scores;
@@ -115,6 +117,7 @@ hipError_t launch_combine_aggregate(const CombineArgs& c, const AggregateArgs& a
                                     hipStream_t stream);
 
 hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t layout,
+                            int32_t n_rows,
                             const float* logits, const int32_t* seq_lens, float* scores,
                             hipStream_t stream);
 

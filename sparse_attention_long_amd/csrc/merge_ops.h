@@ -90,7 +90,7 @@ constexpr int combine_blocks(int rows) {
 __device__ __forceinline__ void aggregate_position(const AggregateArgs& a, int b, int j) {
   const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
   if (j >= L) return;
-  const int n = a.layout == VGSA_LOGITS_KVGROUP_SUM ? a.hkv : 2 * a.hq;
+  const int n = a.layout == VGSA_LOGITS_KVGROUP_SUM ? a.hkv : a.n_rows * a.hq;
   const float* p = a.logits + (size_t)b * n * a.max_ctx + j;
   float s = 0.f;
   for (int r0 = 0; r0 < n; r0 += kMergeBatch) {

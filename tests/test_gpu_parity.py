@@ -328,6 +328,58 @@ def test_verify_finish_equals_combine_and_aggregate(name):
         assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
+def _row_set(kind, T):
+    return {"all": tuple(range(T)), "first": (0,), "bonus": (T - 1,),
+            "even": tuple(range(0, T, 2)), "mid": tuple(range(1, T - 1)) or (0,)}[kind]
+
+
+@pytest.mark.parametrize("kind", ["all", "first", "bonus", "even", "mid"])
+@pytest.mark.parametrize("name", ["g4t5_d64", "g8t8_d64", "paged_g8t6_d64", "chunk4224_g1t3_d64"])
+def test_collect_any_row_set(name, kind):
+    """Logits of any subset of the verify rows (all of them is the full score
+    sum over every verify row): logits and scores against the oracle in both
+    layouts, through the one-call and the partials + finish entry points; the
+    attention output does not depend on which rows are collected."""
+    w = CASES[name]
+    T = w.gamma + 1
+    rows = _row_set(kind, T)
+    say(f"[collect rows] {name} rows={rows}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    o_ref, lse_ref = oracle.verify_attention(x.q, x.k, x.v, x.seq_lens)
+    l_ref = oracle.collected_logits(x.q, x.k, x.seq_lens, rows)
+    absl = np.where(np.isneginf(l_ref), 0.0, np.abs(l_ref))
+    s_ref, s_floor = oracle.aggregate_scores(l_ref), oracle.aggregate_scores(absl)
+    desc = Bn.make_desc(d.q, d.k, d.block_table, d.max_ctx)
+    for layout, code in (("per_head", Bn.LOGITS_PER_HEAD), ("kvgroup_sum", Bn.LOGITS_KVGROUP_SUM)):
+        out, lse, lg = Bn.verify_attention(d.q, d.k, d.v, d.seq_lens, block_table=d.block_table,
+                                           max_ctx=d.max_ctx, collect_rows=rows, layout=layout)
+        torch.cuda.synchronize()
+        assert_out_close(out, o_ref, f"{name}/{layout}/{kind} out")
+        assert_lse_close(lse, lse_ref, f"{name}/{layout}/{kind} lse")
+        if layout == "per_head":
+            assert lg.shape[1] == len(rows)
+            assert_logits_close(lg.cpu().numpy(), l_ref, f"{name}/{kind} per-head logits")
+        else:
+            assert_logits_close(lg.cpu().numpy(), oracle.kvgroup_sum(l_ref, w.num_kv_heads),
+                                f"{name}/{kind} group logits",
+                                floor=oracle.kvgroup_sum(absl, w.num_kv_heads))
+        sc = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads, layout=layout)
+        # two-phase: partials, then combine + aggregate in one launch
+        ws = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        lg2 = torch.empty_like(lg)
+        Bn.verify_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, rows, code, lg2, ws)
+        o2, l2 = torch.empty_like(out), torch.empty_like(lse)
+        s2 = torch.empty_like(sc)
+        Bn.verify_finish(desc, d.seq_lens, ws, o2, l2, code, lg2, s2, num_rows=len(rows))
+        torch.cuda.synchronize()
+        assert_logits_close(sc.cpu().numpy(), s_ref, f"{name}/{layout}/{kind} scores", floor=s_floor)
+        for b in range(w.batch):
+            L = int(x.seq_lens[b])
+            assert torch.equal(lg[b, ..., :L], lg2[b, ..., :L])
+            assert torch.equal(sc[b, :L], s2[b, :L])
+
+
 def test_append_positions_for_draft_steps():
     """Draft-step lists: the selected positions followed by the drafted ones,
     appended in place; entries past the stride are dropped."""
