@@ -7,6 +7,8 @@ from .attention import (  # noqa: F401
     kvgroup_sum,
     select_topk,
     select_topk_batch,
+    select_topk_hybrid,
+    select_topk_hybrid_batch,
     sparse_attention,
     verify_attention,
     widen_bf16,

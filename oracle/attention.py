@@ -24,6 +24,10 @@ Sources (pages are cited by title and section):
   * Dustin, "1. hybrid attention aggregation": a few attention-sink prefix
     tokens and a local window of recent tokens are protected first, and the
     remaining budget is filled by score.  -> select_topk
+  * Dustin, "1. hybrid attention aggregation": the two signals (target
+    historical attention from the previous forward pass, draft lookahead
+    attention from drafting) fill that budget hierarchically, the top-m by the
+    draft signal first, the rest by the target signal.  -> select_topk_hybrid
 
 Readings where the pages are silent (each one is listed with its reason in
 the design notes):
@@ -31,10 +35,14 @@ the design notes):
     L counts the cached positions including the T verify tokens themselves; it
     sees positions j <= L-T+t (causal, bottom-right aligned).  Masked logits
     are -inf.
-  * The collected rows are row 0 (first draft token) and row gamma (bonus).
+  * The collected rows are row 0 (first draft token) and row gamma (bonus)
+    unless a caller names others (every row: the full sum of "A.").
   * A logit is scale * q.k with scale = 1/sqrt(d), the quantity softmax reads.
   * The budget k includes sinks and window; if k >= L every position is kept.
   * Ties in score are broken by the lower position; -0.0 equals +0.0.
+  * Hybrid selection: m counts the draft-chosen positions among those not
+    protected, clamped to the remaining budget; the draft scores are an input
+    array of the same shape as the target scores.
   * Selected indices are returned in ascending order.
   * Sparse attention applies the same causal rule to the absolute positions in
     the index list; a row with no visible index yields o = 0, lse = -inf.
@@ -210,6 +218,50 @@ def select_topk(scores: np.ndarray, length: int, k: int, n_sink: int, window: in
     keep = forced.copy()
     keep[chosen] = True
     return np.flatnonzero(keep).astype(np.int64)
+
+
+def _top_by(values: np.ndarray, candidates: np.ndarray, count: int) -> np.ndarray:
+    """`count` candidates of largest value, lower position first among equals."""
+    order = np.lexsort((candidates, -np.asarray(values, dtype=np.float64)[candidates]))
+    return candidates[order[:count]]
+
+
+def select_topk_hybrid(target: np.ndarray, draft: np.ndarray, length: int, k: int, m: int,
+                       n_sink: int, window: int) -> np.ndarray:
+    """Hierarchical selection from two signals (Dustin, "1. hybrid attention
+    aggregation"): the sink prefix and the recent window are protected first;
+    of the remaining budget r = k - |F|, min(m, r) positions go to the largest
+    draft-lookahead scores, then the other r - min(m, r) to the largest
+    target-historical scores among the positions still free.  Ties: lower
+    position first.  If k >= L all positions are kept.  Returns ascending
+    int64 positions.
+    """
+    L = int(length)
+    if L <= 0:
+        return np.zeros(0, dtype=np.int64)
+    if k >= L:
+        return np.arange(L, dtype=np.int64)
+    forced = np.zeros(L, dtype=bool)
+    forced[:min(n_sink, L)] = True
+    forced[max(0, L - window):] = True
+    nf = int(forced.sum())
+    if nf > k:
+        raise ValueError("sinks and window exceed the budget")
+    r = k - nf
+    m_eff = min(max(int(m), 0), r)
+    free = np.flatnonzero(~forced)
+    by_draft = _top_by(draft[:L], free, m_eff)
+    keep = forced.copy()
+    keep[by_draft] = True
+    by_target = _top_by(target[:L], np.flatnonzero(~keep), r - m_eff)
+    keep[by_target] = True
+    return np.flatnonzero(keep).astype(np.int64)
+
+
+def select_topk_hybrid_batch(target: np.ndarray, draft: np.ndarray, seq_lens: Sequence[int], k: int,
+                             m: int, n_sink: int, window: int) -> List[np.ndarray]:
+    return [select_topk_hybrid(target[b], draft[b], int(seq_lens[b]), k, m, n_sink, window)
+            for b in range(target.shape[0])]
 
 
 def select_topk_batch(scores: np.ndarray, seq_lens: Sequence[int], k: int, n_sink: int,

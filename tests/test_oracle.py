@@ -225,6 +225,66 @@ def test_select_edge_cases():
         oracle.select_topk(s, 8, 3, 2, 2)
 
 
+def _lexmin_best(values, cands, size):
+    """Brute force: the size-`size` subsets of `cands` with the largest value
+    sum; of those, the one whose sorted positions come first."""
+    best, best_set = -np.inf, None
+    for sub in itertools.combinations(sorted(cands), size):
+        tot = sum(values[j] for j in sub)
+        if tot > best or (tot == best and (best_set is None or sub < best_set)):
+            best, best_set = tot, sub
+    return set(best_set if best_set is not None else ())
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("L,k,m,n_sink,window", [(10, 6, 2, 1, 2), (12, 7, 3, 2, 1), (11, 5, 5, 0, 0),
+                                                 (12, 6, 0, 1, 1), (9, 5, 9, 1, 1), (13, 8, 4, 0, 3)])
+def test_hybrid_select_bruteforce(seed, L, k, m, n_sink, window):
+    """Dustin "1.": sinks + window, then the best min(m, r) free positions by
+    the draft signal, then the best of the rest by the target signal: each
+    stage checked by brute force over all subsets (tie-heavy integer scores;
+    among equal sums the lowest positions)."""
+    rng = np.random.default_rng(100 + seed)
+    tgt = rng.integers(-2, 3, size=L).astype(np.float64)
+    drf = rng.integers(-2, 3, size=L).astype(np.float64)
+    got = set(int(x) for x in oracle.select_topk_hybrid(tgt, drf, L, k, m, n_sink, window))
+    forced = set(range(min(n_sink, L))) | set(range(max(0, L - window), L))
+    r = k - len(forced)
+    m_eff = min(m, r)
+    free = [j for j in range(L) if j not in forced]
+    from_draft = _lexmin_best(drf, free, m_eff)
+    rest = [j for j in free if j not in from_draft]
+    from_target = _lexmin_best(tgt, rest, r - m_eff)
+    assert got == forced | from_draft | from_target
+    assert len(got) == k
+
+
+def test_hybrid_select_reductions():
+    rng = np.random.default_rng(7)
+    L, k, n_sink, window = 300, 40, 4, 16
+    tgt = rng.standard_normal(L)
+    drf = rng.standard_normal(L)
+    plain_t = oracle.select_topk(tgt, L, k, n_sink, window)
+    plain_d = oracle.select_topk(drf, L, k, n_sink, window)
+    # m = 0: the target signal alone; m >= r: the draft signal alone
+    assert np.array_equal(oracle.select_topk_hybrid(tgt, drf, L, k, 0, n_sink, window), plain_t)
+    for m in (k - n_sink - window, k, 10 ** 6):
+        assert np.array_equal(oracle.select_topk_hybrid(tgt, drf, L, k, m, n_sink, window), plain_d)
+    # one signal for both stages: the hierarchy is the plain top-k, for every m
+    for m in (0, 1, 7, 20, 25):
+        assert np.array_equal(oracle.select_topk_hybrid(tgt, tgt, L, k, m, n_sink, window), plain_t)
+    # the draft stage's picks are the top-m of the draft signal among the free positions
+    got = oracle.select_topk_hybrid(tgt, drf, L, k, 9, n_sink, window)
+    free = np.arange(n_sink, L - window)
+    top_d = free[np.argsort(-drf[free], kind="stable")[:9]]
+    assert set(top_d.tolist()) <= set(got.tolist())
+    # k >= L, L = 0, and a budget the protected ranges exceed
+    assert list(oracle.select_topk_hybrid(tgt, drf, 30, 30, 5, 1, 1)) == list(range(30))
+    assert list(oracle.select_topk_hybrid(tgt, drf, 0, 4, 1, 1, 1)) == []
+    with pytest.raises(ValueError):
+        oracle.select_topk_hybrid(tgt, drf, L, 10, 2, 6, 6)
+
+
 def test_select_planted_positions_win_on_small_workload():
     """Planted keys (aligned with the group's queries) must be selected: their
     summed logit is far above the spread of the unplanted ones."""
