@@ -16,9 +16,11 @@ bounded sample of the same workload on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
                     [--logits kvgroup_sum|per_head] [--collect two|all]
+                    [--select plain|hybrid]
 
 The defaults are the kv-group-summed layout and the two Collect-2-Query rows;
-the JSON also reports the verify kernel with every row collected.
+the JSON also reports the verify kernel with every row collected and the
+hybrid (draft signal first) selection on the same scores.
 """
 from __future__ import annotations
 
@@ -140,6 +142,9 @@ def main():
                     help="layout of the collected logits")
     ap.add_argument("--collect", choices=("two", "all"), default="two",
                     help="collected verify rows: first draft + bonus (Collect-2-Query), or every row")
+    ap.add_argument("--select", choices=("plain", "hybrid"), default="plain",
+                    help="top-k by the verify scores, or hybrid: top-m by a draft-lookahead score "
+                         "first (synthetic draft scores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=0,
                     help="1: capture one step as a HIP graph and time its replays")
@@ -224,11 +229,20 @@ def main():
             Bn.sparse_attention(q_draft[s], k, v, lens_draft[s], idx, n_idx, block_table=bt,
                                 max_ctx=max_ctx, out=out_d, lse=lse_d, workspace=ws_d)
 
+    draft_sc = torch.from_numpy(W.draft_scores(w)).to(dev)
+
+    def select():
+        if args.select == "hybrid":
+            Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink, w.window,
+                                  idx=idx, n_idx=n_idx)
+        else:
+            Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+
     def step():
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
         # split combine + score aggregation in one launch
         Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores, num_rows=len(rows))
-        Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+        select()
         if w.sparse_verify:
             Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                 out=out_s, lse=lse_s, workspace=ws_s)
@@ -298,8 +312,7 @@ def main():
         "verify_partials": verify_us,
         "combine_aggregate": per_launch_us(
             lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores, num_rows=len(rows))),
-        "select": per_launch_us(
-            lambda: Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)),
+        "select": per_launch_us(select),
     }
     if w.sparse_verify:
         stages["sparse"] = per_launch_us(
@@ -308,7 +321,7 @@ def main():
     if n_draft:
         # the draft loop appends to the lists: select restores them each time
         def select_and_draft():
-            Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+            select()
             draft_steps()
         stages["draft_steps"] = per_launch_us(select_and_draft) - stages["select"]
     verify_none_us = per_launch_us(
@@ -321,6 +334,10 @@ def main():
     verify_all_us = per_launch_us(
         lambda: Bn.verify_partials(desc, q, k, v, lens, bt, all_rows, KV, logits_all, ws_v))
     del logits_all
+    # hybrid selection (draft signal first) on the same scores, for comparison
+    select_hybrid_us = per_launch_us(
+        lambda: Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink,
+                                      w.window, idx=idx, n_idx=n_idx))
 
     ab = alg_bytes(w, x.seq_lens, args.logits, len(rows))
     iters = K / wall
@@ -342,7 +359,8 @@ def main():
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "gamma": w.gamma,
                    "budget": w.budget, "n_sink": w.n_sink, "window": w.window,
                    "draft_steps": n_draft, "sparse_verify": w.sparse_verify,
-                   "paged": w.paged, "logits": args.logits, "collect_rows": list(rows)},
+                   "paged": w.paged, "logits": args.logits, "collect_rows": list(rows),
+                   "select": args.select, "draft_m": w.draft_m if args.select == "hybrid" else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
                      "kernel": "attn_partials_kernel (verify)",
@@ -355,6 +373,7 @@ def main():
         "logit_emit_overhead": stages["verify_partials"] / verify_none_us - 1.0,
         "verify_partials_all_rows_us": verify_all_us,
         "logit_emit_overhead_all_rows": verify_all_us / verify_none_us - 1.0,
+        "select_hybrid_us": select_hybrid_us,
     }
     if w.sparse_verify and stages.get("sparse"):
         sb = ab["sparse_kernel_kv"]

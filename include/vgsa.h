@@ -24,7 +24,8 @@
  *        Vegas "A." (argmax of the summed logits; it is separable, so it is a
  *        top-k of per-position sums); Dustin (gist.science 2606.24957),
  *        "1. hybrid attention aggregation" (sinks and local window protected,
- *        remaining budget by score).
+ *        remaining budget by score).  vgsa_select_topk_hybrid fills that
+ *        budget from two signals, the top m by a draft-lookahead score first.
  *   4. vgsa_sparse_attention  attention over only the selected positions, an
  *      index list used as a page-size-1 page table.
  *        Vegas section 2 step 3 (drafting with the selected entries) and
@@ -193,6 +194,28 @@ vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t nu
 vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
                              const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
                              int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream);
+
+/* 3'. Hybrid selection from two signals.
+ *    (Dustin, "1. hybrid attention aggregation": target-historical attention
+ *    from the previous forward pass and draft-lookahead attention from the
+ *    draft; after the protected sinks and window the budget is filled
+ *    hierarchically, the top m by the draft signal first, the remainder by
+ *    the target signal.)
+ * target_scores  fp32 [B][max_ctx], e.g. as written by step 2
+ * draft_scores   fp32 [B][max_ctx], the draft-lookahead score per position
+ *                (the library does not compute it: it comes from the draft)
+ * m              draft-chosen positions, >= 0; clamped to r = k - |F|
+ * k, n_sink, window, idx, idx_stride, n_idx  as vgsa_select_topk.  Row b
+ *           receives, ascending, F plus the min(m, r) positions of F's
+ *           complement with the highest draft scores plus the r - min(m, r)
+ *           positions of highest target score among the rest (ties: lower
+ *           position first); every position when k >= L.
+ * Rows are limited to max_ctx <= 262144 (VGSA_ERR_UNSUPPORTED beyond).
+ */
+vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float* target_scores,
+                                    const float* draft_scores, const int32_t* seq_lens, int32_t k,
+                                    int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
+                                    int32_t idx_stride, int32_t* n_idx, void* stream);
 
 /* 4. Sparse attention over an index list (page size 1).
  *    (Vegas section 2 step 3 and section 3; Dustin "3.")

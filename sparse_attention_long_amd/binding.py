@@ -44,6 +44,8 @@ SIGNATURES = {
                                       c_vp]),
     "vgsa_select_topk": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_i32,
                                  c_vp, c_vp]),
+    "vgsa_select_topk_hybrid": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                        c_vp, c_i32, c_vp, c_vp]),
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
@@ -237,6 +239,26 @@ def select_topk(scores, seq_lens, k: int, n_sink: int, window: int, *, idx_strid
     _check(load().vgsa_select_topk(B, max_ctx, _p(scores), _p(seq_lens), k, n_sink, window,
                                    _p(idx), idx.shape[1], _p(n_idx), _stream(scores.device)),
            "vgsa_select_topk")
+    return idx, n_idx
+
+
+def select_topk_hybrid(target_scores, draft_scores, seq_lens, k: int, m: int, n_sink: int,
+                       window: int, *, idx_stride=None, idx=None, n_idx=None):
+    """vgsa_select_topk_hybrid.  Returns (idx int32 [B, idx_stride], n_idx int32 [B])."""
+    _need(target_scores, "target_scores", torch.float32, 2)
+    _need(draft_scores, "draft_scores", torch.float32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if draft_scores.shape != target_scores.shape:
+        raise ValueError("draft_scores must have the shape of target_scores")
+    B, max_ctx = target_scores.shape
+    stride = k if idx_stride is None else idx_stride
+    if idx is None:
+        idx = torch.empty((B, stride), dtype=torch.int32, device=target_scores.device)
+    if n_idx is None:
+        n_idx = torch.empty((B,), dtype=torch.int32, device=target_scores.device)
+    _check(load().vgsa_select_topk_hybrid(
+        B, max_ctx, _p(target_scores), _p(draft_scores), _p(seq_lens), k, m, n_sink, window,
+        _p(idx), idx.shape[1], _p(n_idx), _stream(target_scores.device)), "vgsa_select_topk_hybrid")
     return idx, n_idx
 
 

@@ -418,8 +418,27 @@ vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores
   if (scores == nullptr || seq_lens == nullptr || idx == nullptr || n_idx == nullptr)
     return VGSA_ERR_INVALID_ARG;
   if (batch == 0) return VGSA_OK;
-  return hip_status(launch_select_topk(batch, max_ctx, scores, seq_lens, k, n_sink, window, idx,
-                                       idx_stride, n_idx, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_select_topk(batch, max_ctx, scores, nullptr, seq_lens, k, 0, n_sink,
+                                       window, idx, idx_stride, n_idx,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float* target_scores,
+                                    const float* draft_scores, const int32_t* seq_lens, int32_t k,
+                                    int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
+                                    int32_t idx_stride, int32_t* n_idx, void* stream) {
+  if (batch < 0 || max_ctx < 1 || k < 1 || m < 0 || n_sink < 0 || window < 0)
+    return VGSA_ERR_INVALID_ARG;
+  if ((int64_t)n_sink + window > k) return VGSA_ERR_INVALID_ARG;
+  if (idx_stride < k) return VGSA_ERR_INVALID_ARG;
+  if (target_scores == nullptr || draft_scores == nullptr || seq_lens == nullptr ||
+      idx == nullptr || n_idx == nullptr)
+    return VGSA_ERR_INVALID_ARG;
+  if (max_ctx > kMaxHybridRow) return VGSA_ERR_UNSUPPORTED;
+  if (batch == 0) return VGSA_OK;
+  return hip_status(launch_select_topk(batch, max_ctx, target_scores, draft_scores, seq_lens, k,
+                                       m, n_sink, window, idx, idx_stride, n_idx,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,

@@ -124,9 +124,13 @@ hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_
 hipError_t launch_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,
                                    int32_t* idx, int32_t idx_stride, int32_t* n_idx,
                                    hipStream_t stream);
+// draft_scores non-null: hybrid selection (m positions by draft_scores
+// first); rows longer than the one-workgroup kernel's limit are then refused.
 hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
-                              const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
-                              int32_t* idx, int32_t idx_stride, int32_t* n_idx,
-                              hipStream_t stream);
+                              const float* draft_scores, const int32_t* seq_lens, int32_t k,
+                              int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
+                              int32_t idx_stride, int32_t* n_idx, hipStream_t stream);
+// Longest row (positions) the hybrid selection takes.
+constexpr int kMaxHybridRow = 8 * 32768;
 
 }  // namespace vgsa

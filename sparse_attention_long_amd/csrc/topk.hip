@@ -324,22 +324,168 @@ constexpr int kRoundLen = kSmallChunks * 4 * kThreadsTk;  // positions per round
 constexpr int kMaxRounds = 8;
 constexpr int kBinCap = 2044;                            // bin members ranked directly
 
-// VEC: 16-byte score loads (rows 16-byte aligned).
-template <bool VEC>
-__global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
-    int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
-    int32_t k, int32_t n_sink, int32_t window, int32_t* __restrict__ idx, int32_t idx_stride,
-    int32_t* __restrict__ n_idx) {
-  constexpr int kWords = kMaxRounds * kThreadsTk;  // bitmap words (the first R * 1024 are used)
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t s_wave[kWavesTk];
-  __shared__ uint32_t s_out[4];
-  __shared__ uint32_t taken[kWords];    // positions selected (above the bin, or ranked in)
-  __shared__ uint32_t in_bin[kWords];   // bin members, when they are all equal
+// LDS of the one-workgroup selection.
+struct SelectLds {
+  uint32_t hist[kBins];
+  uint32_t s_wave[kWavesTk];
+  uint32_t s_out[4];
+  uint32_t taken[kMaxRounds * kThreadsTk];   // positions selected (above the bin, or ranked in)
+  uint32_t in_bin[kMaxRounds * kThreadsTk];  // bin members, when they are all equal
   // bin members as (key << 32 | ~position): larger means ranked first
-  __shared__ __align__(16) uint64_t bin_rank_key[kBinCap + 4];
-  __shared__ uint32_t s_count;
+  __align__(16) uint64_t bin_rank_key[kBinCap + 4];
+  uint32_t count;
+};
 
+// One selection stage: marks in sh.taken the `want_stage` middle positions
+// [s_end, w_start) of highest score in row `sc` (lower position first among
+// equal keys).  EXCL: positions already marked are no candidates; a thread
+// only marks positions whose keys it has already read, so the marks it reads
+// are the earlier stage's.  Starts and ends with a workgroup barrier.
+template <bool VEC, bool EXCL>
+__device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restrict__ sc,
+                                             int max_ctx, int R, int s_end, int w_start,
+                                             uint32_t want_stage) {
+  const int tid = threadIdx.x;
+  const bool reload = R > 1;
+  // Keys of round `rd`; 0 outside M = [s_end, w_start) (and for excluded
+  // positions).  Addresses are clamped into the row rather than branched on,
+  // so all loads are in flight together (a clamped load only serves
+  // positions at or past the row end, which are masked).
+  uint32_t key[kSmallChunks][4];
+  auto load_round = [&](int rd) {
+    float v[kSmallChunks][4];
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c) {
+      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
+      if (VEC) {
+        const float4 x = *reinterpret_cast<const float4*>(sc + min(p0, max_ctx - 4));
+        v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[c][e] = sc[min(p0 + e, max_ctx - 1)];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c) {
+      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
+      const uint32_t gone = EXCL ? (sh.taken[p0 >> 5] >> (p0 & 31)) : 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = p0 + e;
+        key[c][e] = (p >= s_end && p < w_start && ((gone >> e) & 1u) == 0u) ? order_key(v[c][e]) : 0u;
+      }
+    }
+  };
+  if (tid == 0) sh.count = 0u;
+  __syncthreads();  // earlier marks complete
+  if (!reload) load_round(0);
+
+  // Radix passes: after each, keys whose masked value exceeds `prefix` are
+  // taken and `want` more come from the bin (masked value == prefix).
+  uint32_t prefix = 0u, mask = 0u, want = want_stage, nbin = 0u;
+  int level = 0;
+#pragma unroll 1
+  for (; level < 3; ++level) {
+    const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
+    const uint32_t nb = level == 2 ? 256u : (uint32_t)kBins;
+    for (int i = tid; i < (int)nb; i += kThreadsTk) sh.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll 1
+    for (int rd = 0; rd < R; ++rd) {
+      if (reload) load_round(rd);
+#pragma unroll
+      for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
+            atomicAdd(&sh.hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
+    }
+    __syncthreads();
+    find_digit(sh.hist, nb, shift, prefix, want, sh.s_wave, sh.s_out);
+    nbin = sh.s_out[2];
+    mask |= (nb - 1u) << shift;
+    if (nbin <= (uint32_t)kBinCap) break;
+  }
+  const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
+
+  // Mark keys above the bin; collect (or mark) the bin's members.
+#pragma unroll 1
+  for (int rd = 0; rd < R; ++rd) {
+    if (reload) load_round(rd);
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c) {
+      uint32_t above = 0u, inb = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t mk = key[c][e] & mask;
+        above |= (key[c][e] != 0u && mk > prefix) ? (1u << e) : 0u;
+        inb |= (key[c][e] != 0u && mk == prefix) ? (1u << e) : 0u;
+      }
+      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
+      if (above != 0u) atomicOr(&sh.taken[p0 >> 5], above << (p0 & 31));
+      if (inb != 0u) {
+        if (exact) {
+          atomicOr(&sh.in_bin[p0 >> 5], inb << (p0 & 31));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((inb >> e) & 1u) {
+              const uint32_t slot = atomicAdd(&sh.count, 1u);  // < nbin <= kBinCap
+              sh.bin_rank_key[slot] = ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(p0 + e);
+            }
+        }
+      }
+    }
+  }
+  if (!exact && tid < 4) sh.bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
+  __syncthreads();
+  if (!exact) {
+    // rank = members with a larger key, or an equal key at a lower position
+    const int n4 = (int)(nbin + 3u) / 4;
+    for (int q = tid; q < (int)nbin; q += kThreadsTk) {
+      const uint64_t cq = sh.bin_rank_key[q];
+      uint32_t rank = 0u;
+      for (int f = 0; f < n4; ++f) {
+        const uint64_t* c4 = sh.bin_rank_key + 4 * f;
+        rank += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
+                (c4[3] > cq ? 1u : 0u);
+      }
+      if (rank < want) {
+        const int pq = (int)~(uint32_t)cq;
+        atomicOr(&sh.taken[pq >> 5], 1u << (pq & 31));
+      }
+    }
+  } else {
+    // the first `want` bin members in position order join the taken set;
+    // thread t owns words R*t .. R*t + R - 1
+    uint32_t n_in = 0u, tot;
+    for (int j = 0; j < R; ++j) n_in += (uint32_t)__builtin_popcount(sh.in_bin[R * tid + j]);
+    uint32_t q = block_exclusive_scan(n_in, sh.s_wave, tot);
+    for (int j = 0; j < R; ++j) {
+      uint32_t w = sh.taken[R * tid + j];
+      for (uint32_t bits = sh.in_bin[R * tid + j]; bits != 0u && q < want; ++q) {
+        w |= bits & (~bits + 1u);  // lowest remaining member
+        bits &= bits - 1u;
+      }
+      sh.taken[R * tid + j] = w;
+      sh.in_bin[R * tid + j] = 0u;
+    }
+  }
+  __syncthreads();
+}
+
+// VEC: 16-byte score loads (rows 16-byte aligned).
+// HYBRID: two stages (Dustin, "1. hybrid attention aggregation"): the first
+// picks min(m, r) free positions by `first` (the draft-lookahead scores), the
+// second the other r - min(m, r) by `scores` (the target-historical scores)
+// among the positions the first stage left free.  Without HYBRID only the
+// second stage runs, picking all r by `scores`.
+template <bool VEC, bool HYBRID>
+__global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
+    int32_t max_ctx, const float* __restrict__ scores, const float* __restrict__ first,
+    const int32_t* __restrict__ seq_lens, int32_t k, int32_t m, int32_t n_sink, int32_t window,
+    int32_t* __restrict__ idx, int32_t idx_stride, int32_t* __restrict__ n_idx) {
+  __shared__ SelectLds sh;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int L = min(max(seq_lens[b], 0), max_ctx);
   int32_t* out = idx + (size_t)b * idx_stride;
@@ -357,144 +503,27 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
     if (tid == 0) n_idx[b] = k;
     return;
   }
-  // Rounds this row needs (the launcher guarantees max_ctx <= kMaxRounds rounds);
-  // with one round the keys stay in registers.
+  // Rounds this row needs (the launcher guarantees max_ctx <= kMaxRounds
+  // rounds); with one round the keys stay in registers within a stage.
   const int R = (L + kRoundLen - 1) / kRoundLen;
-  const bool reload = R > 1;
-
-  // Keys of round `rd`; 0 outside M = [s_end, w_start).  16-byte loads (the
-  // launcher guarantees max_ctx % 4 == 0 and an aligned score array);
-  // addresses are clamped into the row rather than branched on, so all loads
-  // are in flight together (a clamped load only serves positions at or past
-  // the row end, which are masked).
-  const float* sc = scores + (size_t)b * max_ctx;
-  uint32_t key[kSmallChunks][4];
-  auto load_round = [&](int rd) {
-    float v[kSmallChunks][4];
-#pragma unroll
-    for (int c = 0; c < kSmallChunks; ++c) {
-      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
-      if (VEC) {
-        const float4 x = *reinterpret_cast<const float4*>(sc + min(p0, max_ctx - 4));
-        v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[c][e] = sc[min(p0 + e, max_ctx - 1)];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kSmallChunks; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid + e;
-        key[c][e] = (p >= s_end && p < w_start) ? order_key(v[c][e]) : 0u;
-      }
-  };
-  if (!reload) load_round(0);
   for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) {
-    taken[i] = 0u;
-    in_bin[i] = 0u;
+    sh.taken[i] = 0u;
+    sh.in_bin[i] = 0u;
   }
-  if (tid == 0) s_count = 0u;
-
-  // Radix passes: after each, keys whose masked value exceeds `prefix` are
-  // taken and `want` more come from the bin (masked value == prefix).
-  uint32_t prefix = 0u, mask = 0u, want = (uint32_t)r, nbin = 0u;
-  int level = 0;
-#pragma unroll 1
-  for (; level < 3; ++level) {
-    const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
-    const uint32_t nb = level == 2 ? 256u : (uint32_t)kBins;
-    for (int i = tid; i < (int)nb; i += kThreadsTk) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll 1
-    for (int rd = 0; rd < R; ++rd) {
-      if (reload) load_round(rd);
-#pragma unroll
-      for (int c = 0; c < kSmallChunks; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
-            atomicAdd(&hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
-    }
-    __syncthreads();
-    find_digit(hist, nb, shift, prefix, want, s_wave, s_out);
-    nbin = s_out[2];
-    mask |= (nb - 1u) << shift;
-    if (nbin <= (uint32_t)kBinCap) break;
-  }
-  const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
-
-  // Mark keys above the bin; collect (or mark) the bin's members.
-#pragma unroll 1
-  for (int rd = 0; rd < R; ++rd) {
-    if (reload) load_round(rd);
-#pragma unroll
-    for (int c = 0; c < kSmallChunks; ++c) {
-      uint32_t above = 0u, inb = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t m = key[c][e] & mask;
-        above |= (key[c][e] != 0u && m > prefix) ? (1u << e) : 0u;
-        inb |= (key[c][e] != 0u && m == prefix) ? (1u << e) : 0u;
-      }
-      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
-      if (above != 0u) atomicOr(&taken[p0 >> 5], above << (p0 & 31));
-      if (inb != 0u) {
-        if (exact) {
-          atomicOr(&in_bin[p0 >> 5], inb << (p0 & 31));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if ((inb >> e) & 1u) {
-              const uint32_t slot = atomicAdd(&s_count, 1u);  // < nbin <= kBinCap
-              bin_rank_key[slot] = ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(p0 + e);
-            }
-        }
-      }
-    }
-  }
-  if (!exact && tid < 4) bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
-  __syncthreads();
-  if (!exact) {
-    // rank = members with a larger key, or an equal key at a lower position
-    const int n4 = (int)(nbin + 3u) / 4;
-    for (int q = tid; q < (int)nbin; q += kThreadsTk) {
-      const uint64_t cq = bin_rank_key[q];
-      uint32_t rank = 0u;
-      for (int f = 0; f < n4; ++f) {
-        const uint64_t* c4 = bin_rank_key + 4 * f;
-        rank += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
-                (c4[3] > cq ? 1u : 0u);
-      }
-      if (rank < want) {
-        const int pq = (int)~(uint32_t)cq;
-        atomicOr(&taken[pq >> 5], 1u << (pq & 31));
-      }
-    }
-    __syncthreads();
-  }
+  const int m_first = HYBRID ? min(max(m, 0), r) : 0;
+  if (HYBRID && m_first > 0)
+    select_stage<VEC, false>(sh, first + (size_t)b * max_ctx, max_ctx, R, s_end, w_start,
+                             (uint32_t)m_first);
+  if (r > m_first)
+    select_stage<VEC, HYBRID>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s_end, w_start,
+                              (uint32_t)(r - m_first));
 
   // Ordered emit: [0, s_end) ++ taken middle positions ++ [w_start, L).
   // Thread t owns words R*t .. R*t + R - 1.
-  uint32_t* my = taken + R * tid;
-  uint32_t tot;
-  if (exact) {  // the first `want` bin members in position order join the taken set
-    uint32_t n_in = 0u;
-    for (int j = 0; j < R; ++j) n_in += (uint32_t)__builtin_popcount(in_bin[R * tid + j]);
-    uint32_t q = block_exclusive_scan(n_in, s_wave, tot);
-    for (int j = 0; j < R; ++j) {
-      uint32_t w = my[j];
-      for (uint32_t bits = in_bin[R * tid + j]; bits != 0u && q < want; ++q) {
-        w |= bits & (~bits + 1u);  // lowest remaining member
-        bits &= bits - 1u;
-      }
-      my[j] = w;
-    }
-  }
-  uint32_t n_sel = 0u;
+  const uint32_t* my = sh.taken + R * tid;
+  uint32_t n_sel = 0u, tot;
   for (int j = 0; j < R; ++j) n_sel += (uint32_t)__builtin_popcount(my[j]);
-  uint32_t o = block_exclusive_scan(n_sel, s_wave, tot) + (uint32_t)s_end;
+  uint32_t o = block_exclusive_scan(n_sel, sh.s_wave, tot) + (uint32_t)s_end;
   for (int j = 0; j < R; ++j)
     for (uint32_t bits = my[j]; bits != 0u; bits &= bits - 1u)
       if (o < (uint32_t)idx_stride) out[o++] = 32 * (R * tid + j) + __builtin_ctz(bits);
@@ -506,20 +535,28 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
 }  // namespace
 
 hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
-                              const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
-                              int32_t* idx, int32_t idx_stride, int32_t* n_idx,
-                              hipStream_t stream) {
-  const bool vec = max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+                              const float* draft_scores, const int32_t* seq_lens, int32_t k,
+                              int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
+                              int32_t idx_stride, int32_t* n_idx, hipStream_t stream) {
+  const auto al16 = [](const float* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool hybrid = draft_scores != nullptr;
+  const bool vec = max_ctx % 4 == 0 && al16(scores) && (!hybrid || al16(draft_scores));
   const int rounds = (max_ctx + kRoundLen - 1) / kRoundLen;
   const dim3 grid(batch), block(kThreadsTk);
   const auto args = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, max_ctx, scores, seq_lens, k, n_sink, window,
-                       idx, idx_stride, n_idx);
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, max_ctx, scores, draft_scores, seq_lens, k,
+                       m, n_sink, window, idx, idx_stride, n_idx);
   };
   if (rounds <= kMaxRounds) {
-    if (vec) args(select_topk_kernel<true>); else args(select_topk_kernel<false>);
+    if (hybrid) {
+      if (vec) args(select_topk_kernel<true, true>); else args(select_topk_kernel<false, true>);
+    } else {
+      if (vec) args(select_topk_kernel<true, false>); else args(select_topk_kernel<false, false>);
+    }
   } else {
-    args(select_topk_large_kernel);
+    if (hybrid) return hipErrorInvalidValue;  // rows past kMaxRounds rounds: plain selection only
+    hipLaunchKernelGGL(select_topk_large_kernel, grid, block, 0, stream, max_ctx, scores, seq_lens,
+                       k, n_sink, window, idx, idx_stride, n_idx);
   }
   return hipGetLastError();
 }

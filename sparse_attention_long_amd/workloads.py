@@ -29,6 +29,12 @@ Input recipe (the same for every workload):
   * Ragged lengths are integers drawn uniformly from an inclusive range.
   * Paged caches use 16-position blocks; physical block ids are one seeded
     random permutation, shared by all layers.
+  * Draft-lookahead scores (the second signal of hybrid selection; the draft
+    model that would produce them is not part of this path) are i.i.d.
+    N(0, 1) float32 per position below the length, with the planted
+    positions raised by 8 (the draft also attends the salient entries), and 0
+    past the length.  The draft share m is half of the budget left after the
+    sinks and the window.
 
 bf16 tensors are returned as uint16 numpy arrays holding the raw bits.
 """
@@ -42,7 +48,7 @@ from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
-TAG_Q, TAG_K, TAG_V, TAG_QDRAFT, TAG_PLANT, TAG_LEN, TAG_BLOCKS = 1, 2, 3, 4, 5, 6, 7
+TAG_Q, TAG_K, TAG_V, TAG_QDRAFT, TAG_PLANT, TAG_LEN, TAG_BLOCKS, TAG_DRAFTSC = 1, 2, 3, 4, 5, 6, 7, 8
 PAGE_BLOCK = 16
 
 
@@ -83,6 +89,11 @@ class Workload:
     def collect_rows(self) -> Tuple[int, int]:
         # first draft token's row and the bonus token's row (Vegas, "Collect-2-Query")
         return (0, self.gamma)
+
+    @property
+    def draft_m(self) -> int:
+        # hybrid selection: positions picked by the draft signal (half the free budget)
+        return max(0, self.budget - self.n_sink - self.window) // 2
 
     def max_len(self) -> int:
         if self.lens is not None:
@@ -292,6 +303,19 @@ def to_paged(logical: np.ndarray, table: np.ndarray, need: List[int]) -> np.ndar
         for i in range(need[b]):
             pool[int(table[b, i])] = logical[b, :, i * PAGE_BLOCK:(i + 1) * PAGE_BLOCK, :]
     return pool
+
+
+def draft_scores(w: Workload, layer: int = 0) -> np.ndarray:
+    """Synthetic draft-lookahead scores: float32 [B, max_ctx] (recipe in the
+    module docstring)."""
+    lens = seq_lens(w)
+    out = np.zeros((w.batch, w.max_ctx()), dtype=np.float32)
+    for b, L in enumerate(lens):
+        L = int(L)
+        out[b, :L] = _rng(w, layer, b, 0, TAG_DRAFTSC).standard_normal(L, dtype=np.float32)
+        pos = planted_positions(w, layer, b, L)
+        out[b, pos] += np.float32(8.0)
+    return out
 
 
 def small(name: str = "small", **kw) -> Workload:

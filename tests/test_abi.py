@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -181,6 +181,15 @@ def test_aggregate_and_select_argument_checks(lib):
     assert T(2, 100, None, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == INVALID
     assert T(2, 0, FAKE, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == INVALID
     assert T(0, 100, FAKE, FAKE, 8, 4, 4, FAKE, 8, FAKE, None) == OK
+    H = lib.vgsa_select_topk_hybrid
+    assert H(0, 100, FAKE, FAKE, FAKE, 8, 2, 2, 2, FAKE, 8, FAKE, None) == OK   # empty batch
+    assert H(2, 100, FAKE, None, FAKE, 8, 2, 2, 2, FAKE, 8, FAKE, None) == INVALID  # no draft scores
+    assert H(2, 100, None, FAKE, FAKE, 8, 2, 2, 2, FAKE, 8, FAKE, None) == INVALID
+    assert H(2, 100, FAKE, FAKE, FAKE, 8, -1, 2, 2, FAKE, 8, FAKE, None) == INVALID   # m < 0
+    assert H(2, 100, FAKE, FAKE, FAKE, 8, 2, 4, 5, FAKE, 8, FAKE, None) == INVALID    # sinks + window > k
+    assert H(2, 100, FAKE, FAKE, FAKE, 8, 2, 2, 2, FAKE, 7, FAKE, None) == INVALID    # idx_stride < k
+    assert H(2, 100, FAKE, FAKE, FAKE, 0, 0, 0, 0, FAKE, 8, FAKE, None) == INVALID    # k < 1
+    assert H(2, 262145, FAKE, FAKE, FAKE, 8, 2, 2, 2, FAKE, 8, FAKE, None) == UNSUPPORTED
 
 
 def test_append_argument_checks(lib):

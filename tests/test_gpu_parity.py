@@ -219,6 +219,93 @@ def test_select_ties_zeros_and_infinities():
     _select_case(sc2, [64], 1, 0, 0)
 
 
+# ------------------------------------------------------------------ hybrid selection
+def _hybrid_case(tgt_h, drf_h, lens, k, m, n_sink, window, stride=None):
+    tgt = torch.from_numpy(np.ascontiguousarray(tgt_h, dtype=np.float32)).cuda()
+    drf = torch.from_numpy(np.ascontiguousarray(drf_h, dtype=np.float32)).cuda()
+    idx, n = Bn.select_topk_hybrid(tgt, drf, dev_i32(lens), k, m, n_sink, window,
+                                   idx_stride=stride or k)
+    torch.cuda.synchronize()
+    idx_h, n_h = idx.cpu().numpy(), n.cpu().numpy()
+    for b, L in enumerate(lens):
+        want = oracle.select_topk_hybrid(tgt_h[b], drf_h[b], int(L), k, m, n_sink, window)
+        assert n_h[b] == len(want), (b, L, k, m, n_h[b], len(want))
+        assert np.array_equal(idx_h[b, :n_h[b]], want), (b, L, k, m, n_sink, window)
+
+
+@pytest.mark.parametrize("L", [1, 7, 1000, 4097, 32768, 40001, 131072, 262143])
+def test_hybrid_select_random(L):
+    """Both stages against the oracle: one round of keys in registers and
+    reloaded rounds, aligned and unaligned rows, m from 0 past the free budget."""
+    say(f"[hybrid select] L={L}")
+    rng = np.random.default_rng(300 + L)
+    for ctx in ((L + 3) // 4 * 4, L + 1):
+        lens = [L, max(1, L // 3), max(1, L - 1)]
+        tgt = rng.standard_normal((3, ctx)).astype(np.float32) * 10
+        drf = rng.standard_normal((3, ctx)).astype(np.float32)
+        for k, ns, win in [(1, 0, 0), (16, 4, 8), (512, 4, 64), (6554, 4, 256)]:
+            if ns + win > k:
+                continue
+            r = k - ns - win
+            for m in sorted({0, 1, r // 2, r, r + 5}):
+                _hybrid_case(tgt, drf, lens, k, m, ns, win)
+
+
+def test_hybrid_select_ties_and_overlap():
+    """Tie-heavy and all-equal draft and target rows (every radix pass keeps
+    the whole bin: the lowest positions win in each stage), the target's best
+    positions taken by the draft stage first, and one signal for both stages."""
+    rng = np.random.default_rng(17)
+    ctx = 70000
+    tgt = rng.integers(-3, 4, size=(4, ctx)).astype(np.float32)
+    drf = rng.integers(-2, 3, size=(4, ctx)).astype(np.float32)
+    drf[1] = 1.0                       # all equal: the draft stage takes the lowest free positions
+    tgt[2] = 5.0
+    drf[2] = tgt[2]                    # all equal in both
+    drf[3] = tgt[3]                    # one signal for both stages
+    lens = [70000, 69999, 50000, 65000]
+    for k, m, ns, win in [(3000, 1500, 4, 64), (3000, 2932, 4, 64), (40000, 20000, 0, 100),
+                          (100, 37, 10, 5)]:
+        _hybrid_case(tgt, drf, lens, k, m, ns, win, stride=k + 3)
+    # the draft signal favours exactly the target's top positions: the target
+    # stage must skip them and take the next ones
+    t2 = rng.standard_normal((1, 5000)).astype(np.float32)
+    d2 = t2.copy()
+    _hybrid_case(t2, d2, [5000], 300, 100, 4, 16)
+    d3 = -t2
+    _hybrid_case(t2, d3, [5000], 300, 100, 4, 16)
+
+
+@pytest.mark.parametrize("name", ["g4t4_d128_ragged", "paged_g8t6_d64", "ctx2k_b1_h32kv8_d128"])
+def test_hybrid_select_on_verify_scores(name):
+    """The target signal as the verify pass writes it (the GPU's scores), the
+    draft signal from the seeded generator; then sparse attention over the
+    hybrid selection."""
+    w = CASES[name]
+    say(f"[hybrid pipeline] {name}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    _, _, lg = run_verify(d, w, "kvgroup_sum")
+    sc = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads)
+    drf_h = W.draft_scores(w)
+    drf = torch.from_numpy(drf_h).cuda()
+    idx, n = Bn.select_topk_hybrid(sc, drf, d.seq_lens, w.budget, w.draft_m, w.n_sink, w.window)
+    torch.cuda.synchronize()
+    sc_h = sc.cpu().numpy()
+    want = oracle.select_topk_hybrid_batch(sc_h, drf_h, x.seq_lens, w.budget, w.draft_m, w.n_sink,
+                                           w.window)
+    idx_h, n_h = idx.cpu().numpy(), n.cpu().numpy()
+    for b in range(w.batch):
+        assert n_h[b] == len(want[b])
+        assert np.array_equal(idx_h[b, :n_h[b]], want[b]), f"{name} b={b}"
+    out, lse = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n, block_table=d.block_table,
+                                   max_ctx=d.max_ctx)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, x.seq_lens, want)
+    assert_out_close(out, o_ref, f"{name} hybrid sparse out")
+    assert_lse_close(lse, lse_ref, f"{name} hybrid sparse lse")
+
+
 def test_determinism_bitwise():
     w = CASES["g8t5_d128"]
     x = W.make_layer(w)

@@ -65,3 +65,20 @@ def test_paged_pool_holds_logical_rows():
             blk, off = tab[b, j // 16], j % 16
             assert np.array_equal(x.k_pool[blk, :, off], x.k[b, :, j])
             assert np.array_equal(x.v_pool[blk, :, off], x.v[b, :, j])
+
+
+def test_draft_scores_recipe():
+    """Seeded N(0, 1) per position below the length, planted positions raised
+    by 8, zero past the length; regenerates bit-identically."""
+    w = W.small("ds", batch=3, lens=(300, 41, 1000), budget=64, n_sink=4, window=16,
+                planted=5, seed=9)
+    a, b = W.draft_scores(w), W.draft_scores(w)
+    assert a.dtype == np.float32 and a.shape == (3, w.max_ctx())
+    assert np.array_equal(a, b)
+    for i, L in enumerate(W.seq_lens(w)):
+        assert np.all(a[i, L:] == 0)
+        pos = W.planted_positions(w, 0, i, int(L))
+        others = np.setdiff1d(np.arange(L), pos)
+        assert np.all(a[i, pos] > a[i, others].max() - 8 + 2) or pos.size == 0
+        assert abs(a[i, others].mean()) < 0.3 and 0.7 < a[i, others].std() < 1.3
+    assert w.draft_m == (64 - 4 - 16) // 2
