@@ -137,17 +137,22 @@ def verify_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens: Sequ
 
 # --------------------------------------------------------------------------- logits
 def collected_logits(q: np.ndarray, k: np.ndarray, seq_lens: Sequence[int],
-                     rows: Sequence[int], scale: Optional[float] = None) -> np.ndarray:
+                     rows: Sequence[int], scale: Optional[float] = None,
+                     heads: Optional[Sequence[int]] = None) -> np.ndarray:
     """Pre-softmax logits of the collected rows (Vegas, section 3: written
     before softmax normalisation).  "A." sums its score over every verify row
     t = 1..gamma+1; "B. Collect-2-Query" keeps only the first draft row and
     the bonus row.  `rows` names the collected rows (0-based, ascending), so
     both readings are this one function.
 
-    Returns l [B, R, Hq, ctx], R = len(rows):
-    l[b, c, h, j] = scale * q[b, h, rows[c]] . k[b, g, j] for
-    j <= L_b - T + rows[c], -inf for the causally hidden positions up to L_b,
-    NaN beyond L_b (undefined).
+    `heads` restricts collection to a subset of the query heads (Dustin,
+    "2. ... semantic retrieval heads", online part: scores are computed on the
+    chosen heads only); default all heads, in order.
+
+    Returns l [B, R, H, ctx], R = len(rows), H = len(heads):
+    l[b, c, i, j] = scale * q[b, heads[i], rows[c]] . k[b, g, j] (g the kv-head
+    of heads[i]) for j <= L_b - T + rows[c], -inf for the causally hidden
+    positions up to L_b, NaN beyond L_b (undefined).
     """
     q = _f64(q)
     B, Hq, T, d = q.shape
@@ -155,28 +160,34 @@ def collected_logits(q: np.ndarray, k: np.ndarray, seq_lens: Sequence[int],
     G = Hq // Hkv
     sc = default_scale(d) if scale is None else scale
     rows = [int(t) for t in rows]
-    out = np.full((B, len(rows), Hq, ctx), np.nan)
+    heads = list(range(Hq)) if heads is None else [int(h) for h in heads]
+    out = np.full((B, len(rows), len(heads), ctx), np.nan)
     for b in range(B):
         L = int(seq_lens[b])
-        for g in range(Hkv):
-            kg = _f64(k[b, g, :L])
+        for i, h in enumerate(heads):
+            kg = _f64(k[b, h // G, :L])
             for c, t in enumerate(rows):
-                last = L - T + t
-                for h in range(g * G, (g + 1) * G):
-                    row = sc * (kg @ q[b, h, t])
-                    row[last + 1:] = -np.inf
-                    out[b, c, h, :L] = row
+                row = sc * (kg @ q[b, h, t])
+                row[L - T + t + 1:] = -np.inf
+                out[b, c, i, :L] = row
     return out
 
 
-def kvgroup_sum(logits: np.ndarray, num_kv_heads: int) -> np.ndarray:
-    """Collected logits summed over the collected rows and over the q-heads of
-    each kv-head: [B, R, Hq, ctx] -> [B, Hkv, ctx]."""
-    B, _, Hq, ctx = logits.shape
-    G = Hq // num_kv_heads
+def kvgroup_sum(logits: np.ndarray, num_kv_heads: int, heads: Optional[Sequence[int]] = None,
+                num_q_heads: Optional[int] = None) -> np.ndarray:
+    """Collected logits summed over the collected rows and over the collected
+    q-heads of each kv-head: [B, R, H, ctx] -> [B, Hkv, ctx].  With a head
+    subset, `heads` and `num_q_heads` give each logit row's head and the group
+    size; a kv-head none of whose heads is collected sums to 0."""
+    B, _, H, ctx = logits.shape
+    if heads is None:
+        heads, num_q_heads = list(range(H)), H
+    G = num_q_heads // num_kv_heads
     out = np.zeros((B, num_kv_heads, ctx))
     for g in range(num_kv_heads):
-        out[:, g] = logits[:, :, g * G:(g + 1) * G, :].sum(axis=(1, 2))
+        sel = [i for i, h in enumerate(heads) if h // G == g]
+        if sel:
+            out[:, g] = logits[:, :, sel, :].sum(axis=(1, 2))
     return out
 
 

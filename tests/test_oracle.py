@@ -171,6 +171,54 @@ def test_scores_all_rows_closed_form():
     assert np.array_equal(l2, l[:, [0, T - 1]], equal_nan=True)
 
 
+@pytest.mark.parametrize("heads", [(1, 4), (0,), (5,), (0, 1, 2, 3, 4, 5)])
+def test_logits_head_subset_closed_form(heads):
+    # basis keys again: l[c, i, j] = scale * (g+1) * q[heads[i], r_c][(j+g) mod d], g = heads[i] // G
+    B, Hq, Hkv, T, d, ctx = 2, 6, 3, 4, 8, 30
+    lens = [30, 19]
+    rows = (0, 3)
+    q = rnd((B, Hq, T, d), 21)
+    k = np.zeros((B, Hkv, ctx, d))
+    for g in range(Hkv):
+        for j in range(ctx):
+            k[:, g, j, (j + g) % d] = g + 1
+    sc = 0.5
+    l = oracle.collected_logits(q, k, lens, rows, scale=sc, heads=heads)
+    assert l.shape == (B, len(rows), len(heads), ctx)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        for c, r in enumerate(rows):
+            for i, h in enumerate(heads):
+                g = h // G
+                for j in range(L):
+                    want = sc * (g + 1) * q[b, h, r, (j + g) % d] if j <= L - T + r else -np.inf
+                    assert l[b, c, i, j] == want
+
+
+def test_head_subset_group_sums_closed_form():
+    """Scores restricted to a head subset (Dustin's online SRH scoring): per
+    kv-head, scale * k_g[j] . (sum of the collected rows of its selected
+    heads' queries); a kv-head with no selected head contributes 0."""
+    B, Hq, Hkv, T, d, L = 1, 8, 4, 3, 16, 50
+    q, k = rnd((B, Hq, T, d), 22), rnd((B, Hkv, L, d), 23)
+    heads = [1, 2, 7]          # groups 0, 1, 3 (G = 2); group 2 has none
+    rows = (0, 2)
+    sc = 0.25
+    l = oracle.collected_logits(q, k, [L], rows, scale=sc, heads=heads)
+    gs = oracle.kvgroup_sum(l, Hkv, heads=heads, num_q_heads=Hq)
+    G = Hq // Hkv
+    vis = L - T + 1  # positions every collected row sees (row 0's limit)
+    for g in range(Hkv):
+        qs = sum(q[0, h, t] for h in heads if h // G == g for t in rows)
+        want = sc * (k[0, g, :vis] @ qs) if np.ndim(qs) else np.zeros(vis)
+        np.testing.assert_allclose(gs[0, g, :vis], want, rtol=1e-12, atol=1e-12)
+    assert np.all(gs[0, 2] == 0)
+    assert np.all(np.isneginf(gs[0, [0, 1, 3], vis:L]))
+    # the subset is the restriction of the all-heads logits
+    full = oracle.collected_logits(q, k, [L], rows, scale=sc)
+    assert np.array_equal(l, full[:, :, heads], equal_nan=True)
+
+
 # ------------------------------------------------------------------ selection
 def brute_force_best(scores, L, k, n_sink, window):
     forced = set(range(min(n_sink, L))) | set(range(max(0, L - window), L))
