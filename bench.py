@@ -43,18 +43,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(w, lens, layout="kvgroup_sum", n_rows=2):
+def alg_bytes(w, lens, layout="kvgroup_sum", n_rows=2, n_heads=None):
     """Algorithmic HBM bytes of one iteration, by stage (what the method must
     move: every K/V row read once, the collected logits written once, scores
     and indices once; split partials are implementation overhead and excluded).
     Logits are one fp32 per (kv-head, position), or per (collected row,
-    q-head, position) in the per-head layout."""
+    collected q-head, position) in the per-head layout."""
     B, Hq, Hkv, d, T, k = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.q_len, w.budget
     Ls = [int(L) for L in lens]
     kv = sum(Hkv * L * d * 2 * 2 for L in Ls)
     q_in = B * Hq * T * d * 2
     o_out = B * Hq * T * d * 2
-    per_pos = Hkv if layout == "kvgroup_sum" else n_rows * Hq
+    per_pos = Hkv if layout == "kvgroup_sum" else n_rows * (Hq if n_heads is None else n_heads)
     emit = sum(per_pos * L * 4 for L in Ls)
     agg = emit + sum(L * 4 for L in Ls)
     sel = sum(L * 4 for L in Ls) + B * k * 4
@@ -94,7 +94,7 @@ def counter_traffic(workload_name):
     return int(m.group(1))
 
 
-def cpu_baseline(w, x, seconds, rows):
+def cpu_baseline(w, x, seconds, rows, heads=None):
     """The fp64 oracle, as it stands, on whole sequences of the workload until
     `seconds` have passed; scaled to iterations/s of the full batch."""
     import oracle
@@ -109,8 +109,9 @@ def cpu_baseline(w, x, seconds, rows):
         sl = slice(b, b + 1)
         lens = x.seq_lens[sl]
         oracle.verify_attention(x.q[sl], x.k[sl], x.v[sl], lens)
-        lg = oracle.collected_logits(x.q[sl], x.k[sl], lens, rows)
-        sc = oracle.aggregate_scores(oracle.kvgroup_sum(lg, w.num_kv_heads))
+        lg = oracle.collected_logits(x.q[sl], x.k[sl], lens, rows, heads=heads)
+        sc = oracle.aggregate_scores(oracle.kvgroup_sum(lg, w.num_kv_heads, heads=heads,
+                                                        num_q_heads=w.num_q_heads))
         idx = oracle.select_topk(sc[0], int(lens[0]), w.budget, w.n_sink, w.window)
         if w.sparse_verify:
             oracle.sparse_attention(x.q[sl], x.k[sl], x.v[sl], lens, [idx])
@@ -142,6 +143,8 @@ def main():
                     help="layout of the collected logits")
     ap.add_argument("--collect", choices=("two", "all"), default="two",
                     help="collected verify rows: first draft + bonus (Collect-2-Query), or every row")
+    ap.add_argument("--score-heads", type=int, default=0,
+                    help="score on this many q-heads only, spread evenly (0: every head)")
     ap.add_argument("--select", choices=("plain", "hybrid"), default="plain",
                     help="top-k by the verify scores, or hybrid: top-m by a draft-lookahead score "
                          "first (synthetic draft scores)")
@@ -200,8 +203,13 @@ def main():
     desc = Bn.make_desc(q, k, bt, max_ctx)
     ws_v = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     rows = w.collect_rows if args.collect == "two" else tuple(range(T))
+    # a head subset (online scoring on chosen heads): n heads spread evenly
+    heads = None
+    if 0 < args.score_heads < Hq:
+        heads = tuple(i * Hq // args.score_heads for i in range(args.score_heads))
+    n_heads = Hq if heads is None else len(heads)
     KV = Bn.LOGITS_KVGROUP_SUM if args.logits == "kvgroup_sum" else Bn.LOGITS_PER_HEAD
-    lshape = (B, Hkv, max_ctx) if KV == Bn.LOGITS_KVGROUP_SUM else (B, len(rows), Hq, max_ctx)
+    lshape = (B, Hkv, max_ctx) if KV == Bn.LOGITS_KVGROUP_SUM else (B, len(rows), n_heads, max_ctx)
     logits = torch.empty(lshape, dtype=torch.float32, device=dev)
     out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
@@ -239,9 +247,9 @@ def main():
             Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
 
     def step():
-        Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v)
+        Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v, heads=heads)
         # split combine + score aggregation in one launch
-        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores, num_rows=len(rows))
+        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
         select()
         if w.sparse_verify:
             Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
@@ -306,12 +314,12 @@ def main():
     # the verify kernel's launch duration for the roofline: K launches of the
     # timed configuration back to back on the launch stream
     verify_us = per_launch_us(
-        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v))
+        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v, heads=heads))
     log(f"[bench] verify kernel {verify_us:.1f} us per launch")
     stages = {
         "verify_partials": verify_us,
         "combine_aggregate": per_launch_us(
-            lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores, num_rows=len(rows))),
+            lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)),
         "select": per_launch_us(select),
     }
     if w.sparse_verify:
@@ -330,16 +338,17 @@ def main():
     all_rows = tuple(range(T))
     logits_all = logits
     if KV == Bn.LOGITS_PER_HEAD and len(rows) != T:
-        logits_all = torch.empty((B, T, Hq, max_ctx), dtype=torch.float32, device=dev)
+        logits_all = torch.empty((B, T, n_heads, max_ctx), dtype=torch.float32, device=dev)
     verify_all_us = per_launch_us(
-        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, all_rows, KV, logits_all, ws_v))
+        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, all_rows, KV, logits_all, ws_v,
+                                   heads=heads))
     del logits_all
     # hybrid selection (draft signal first) on the same scores, for comparison
     select_hybrid_us = per_launch_us(
         lambda: Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink,
                                       w.window, idx=idx, n_idx=n_idx))
 
-    ab = alg_bytes(w, x.seq_lens, args.logits, len(rows))
+    ab = alg_bytes(w, x.seq_lens, args.logits, len(rows), n_heads)
     iters = K / wall
     achieved = ab["verify_kernel"] / (verify_us * 1e-6) / 1e9
     result = {
@@ -360,6 +369,7 @@ def main():
                    "budget": w.budget, "n_sink": w.n_sink, "window": w.window,
                    "draft_steps": n_draft, "sparse_verify": w.sparse_verify,
                    "paged": w.paged, "logits": args.logits, "collect_rows": list(rows),
+                   "score_heads": None if heads is None else list(heads),
                    "select": args.select, "draft_m": w.draft_m if args.select == "hybrid" else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
@@ -385,7 +395,7 @@ def main():
         result["sparse_roofline"]["frac"] = result["sparse_roofline"]["achieved"] / HBM_PEAK_GBS
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, rows)
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, rows, heads)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

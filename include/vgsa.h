@@ -79,15 +79,21 @@ typedef enum vgsa_status {
 } vgsa_status;
 
 /* Layout of the collected pre-softmax logits written by the verify pass.
- * R = number of collected rows (2 for Collect-2-Query). */
+ * R = number of collected rows (2 for Collect-2-Query), H = number of
+ * collected q-heads (Hq unless a head subset is given). */
 typedef enum vgsa_logit_layout {
   VGSA_LOGITS_NONE = 0,        /* no logits are written                           */
-  VGSA_LOGITS_PER_HEAD = 1,    /* fp32 [B][R][Hq][max_ctx]; [b][c][h][j] is the
-                                  c-th collected row (ascending row index)       */
+  VGSA_LOGITS_PER_HEAD = 1,    /* fp32 [B][R][H][max_ctx]; [b][c][i][j] is the
+                                  c-th collected row (ascending row index) of the
+                                  i-th collected head (ascending head index)      */
   VGSA_LOGITS_KVGROUP_SUM = 2  /* fp32 [B][Hkv][max_ctx]: sum over the collected
-                                  rows and the q-heads of kv-head g (same total as
-                                  PER_HEAD summed, R*G times fewer bytes)         */
+                                  rows and the collected q-heads of kv-head g
+                                  (same total as PER_HEAD summed, R*G times fewer
+                                  bytes); 0 for a kv-head with no collected head */
 } vgsa_logit_layout;
+
+/* Head mask that collects every q-head (any number of heads). */
+#define VGSA_ALL_HEADS (~(uint64_t)0)
 
 /* Shape of one attention call.  The KV cache is either contiguous,
  * K/V [B][Hkv][max_ctx][head_dim] bf16, or a paged pool of 16-position blocks,
@@ -149,6 +155,12 @@ size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_strid
  *              All rows, (1 << T) - 1, is the full sum of Vegas "A." (every
  *              draft token, accepted or not).  Ignored when layout ==
  *              VGSA_LOGITS_NONE.
+ * head_mask    the q-heads whose logits are collected: VGSA_ALL_HEADS, or bit
+ *              h for q-head h (at least one bit, none at or above Hq; needs
+ *              Hq <= 64, else VGSA_ERR_UNSUPPORTED).  A subset scores on the
+ *              chosen heads only (Dustin, "2. efficient estimation via
+ *              semantic retrieval heads", online part); attention itself
+ *              still runs on every head.  Ignored when layout == NONE.
  * logits       fp32 in `layout`; NULL iff layout == NONE.  Written for
  *              positions j < L_b only: scale * q.k for visible positions,
  *              -inf where the row may not see j.  Entries j >= L_b untouched.
@@ -160,23 +172,26 @@ size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_strid
 vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, uint32_t collect_mask,
-                                  vgsa_logit_layout layout, float* logits, void* out, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream);
+                                  uint64_t head_mask, vgsa_logit_layout layout, float* logits,
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* 2. Aggregate collected logits into one score per position.
  *    (Vegas, "A. aggregated attention-logit selection": the sum over draft
  *    rows t and heads h of l_ti^(h).)
  * logits   fp32 in `layout` (PER_HEAD or KVGROUP_SUM) as written by step 1
- * num_rows PER_HEAD: the collected rows R per sequence (popcount of the
- *          collect mask), 1..16; ignored for KVGROUP_SUM
- * scores   fp32 [B][max_ctx]; scores[b][j] for j < L_b is the sum, in a fixed
- *          order, over the collected rows and all q-heads (or over kv-groups).
- *          Entries j >= L_b untouched.
+ * num_rows PER_HEAD: logit rows per sequence, R * H (collected rows times
+ *          collected heads), 1..16*Hq; ignored for KVGROUP_SUM
+ * accumulate  0: scores[b][j] = the sum; nonzero: scores[b][j] += the sum
+ *          (scores summed over several layers' calls, e.g. the layers whose
+ *          heads are scored)
+ * scores   fp32 [B][max_ctx]; for j < L_b the sum, in a fixed order, over
+ *          the logit rows (or over kv-groups).  Entries j >= L_b untouched.
  */
 vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t max_ctx, vgsa_logit_layout layout, int32_t num_rows,
-                                  const float* logits, const int32_t* seq_lens, float* scores,
-                                  void* stream);
+                                  int32_t accumulate, const float* logits,
+                                  const int32_t* seq_lens, float* scores, void* stream);
 
 /* 3. Select the positions kept for the next step.
  *    (Vegas "A." argmax over |T| = k; Dustin "1." protected sinks and window.)
@@ -256,8 +271,8 @@ vgsa_status vgsa_append_positions(int32_t batch, const int32_t* base, int32_t fi
 vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table,
                                  const int32_t* seq_lens, uint32_t collect_mask,
-                                 vgsa_logit_layout layout, float* logits, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 uint64_t head_mask, vgsa_logit_layout layout, float* logits,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table,
@@ -281,12 +296,13 @@ vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
  * (Vegas §2 step 1 and "A. aggregated attention-logit selection".)
  * layout   the layout logits were written in (PER_HEAD or KVGROUP_SUM);
  *          ignored when scores is NULL
- * num_rows PER_HEAD: collected rows per sequence, 1..q_len
+ * num_rows PER_HEAD: logit rows per sequence (R * H), 1..q_len*Hq
+ * accumulate  as in vgsa_aggregate_scores
  * scores   fp32 [B][max_ctx] or NULL */
 vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
                                const void* workspace, size_t workspace_bytes, void* out, float* lse,
-                               vgsa_logit_layout layout, int32_t num_rows, const float* logits,
-                               float* scores, void* stream);
+                               vgsa_logit_layout layout, int32_t num_rows, int32_t accumulate,
+                               const float* logits, float* scores, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ LOGITS_NONE, LOGITS_PER_HEAD, LOGITS_KVGROUP_SUM = 0, 1, 2
 _LAYOUTS = {"none": LOGITS_NONE, "per_head": LOGITS_PER_HEAD, "kvgroup_sum": LOGITS_KVGROUP_SUM}
 
 c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
-c_u32 = ctypes.c_uint32
+c_u32, c_u64 = ctypes.c_uint32, ctypes.c_uint64
+ALL_HEADS = (1 << 64) - 1
 P_i32 = ctypes.POINTER(ctypes.c_int32)
 
 
@@ -39,9 +40,9 @@ SIGNATURES = {
     "vgsa_verify_workspace_bytes": (c_sz, [ctypes.POINTER(AttnDesc)]),
     "vgsa_sparse_workspace_bytes": (c_sz, [ctypes.POINTER(AttnDesc), c_i32]),
     "vgsa_verify_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
-                                      c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
-    "vgsa_aggregate_scores": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
-                                      c_vp]),
+                                      c_u64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "vgsa_aggregate_scores": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                      c_vp, c_vp]),
     "vgsa_select_topk": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_i32,
                                  c_vp, c_vp]),
     "vgsa_select_topk_hybrid": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
@@ -49,13 +50,13 @@ SIGNATURES = {
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
-                                     c_i32, c_vp, c_vp, c_sz, c_vp]),
+                                     c_u64, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_sparse_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                      c_vp, c_i32, c_vp, c_sz, c_vp]),
     "vgsa_combine_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_i32, c_vp, c_vp, c_sz, c_vp,
                                       c_vp, c_vp]),
     "vgsa_verify_finish": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp, c_i32,
-                                   c_i32, c_vp, c_vp, c_vp]),
+                                   c_i32, c_i32, c_vp, c_vp, c_vp]),
     "vgsa_append_positions": (c_i32, [c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]),
 }
 
@@ -182,19 +183,38 @@ def row_mask(rows: Sequence[int], q_len: int) -> int:
     return m
 
 
+def head_mask(heads: Optional[Sequence[int]], num_q_heads: int) -> int:
+    """Head mask from head indices (None: every head).  Heads must be
+    distinct, ascending and below num_q_heads."""
+    if heads is None:
+        return ALL_HEADS
+    heads = [int(h) for h in heads]
+    if not heads or any(h < 0 or h >= num_q_heads or h >= 64 for h in heads) or \
+            sorted(set(heads)) != heads:
+        raise ValueError(f"heads {heads} must be distinct, ascending and in [0, {min(num_q_heads, 64)})")
+    m = 0
+    for h in heads:
+        m |= 1 << h
+    return m
+
+
 def verify_attention(q, k_cache, v_cache, seq_lens, *, block_table=None, max_ctx=None,
-                     collect_rows: Optional[Sequence[int]] = None, layout: str = "kvgroup_sum",
-                     logits=None, out=None, lse=None, workspace=None, scale: float = 0.0):
-    """vgsa_verify_attention.  Returns (out bf16 [B,Hq,T,d], lse fp32 [B,Hq,T], logits)."""
+                     collect_rows: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
+                     layout: str = "kvgroup_sum", logits=None, out=None, lse=None, workspace=None,
+                     scale: float = 0.0):
+    """vgsa_verify_attention.  Returns (out bf16 [B,Hq,T,d], lse fp32 [B,Hq,T], logits);
+    per-head logits are [B, R, H, max_ctx] for R collected rows and H collected heads."""
     _check_attn(q, k_cache, v_cache, seq_lens, block_table)
     desc = make_desc(q, k_cache, block_table, max_ctx, scale)
     lay = _LAYOUTS[layout]
     B, Hq, T, d = q.shape
     dev = q.device
     mask = row_mask((0, T - 1) if collect_rows is None else collect_rows, T)
+    hmask = head_mask(heads, Hq)
     if lay != LOGITS_NONE and logits is None:
         R = bin(mask).count("1")
-        shape = (B, R, Hq, desc.max_ctx) if lay == LOGITS_PER_HEAD else (B, desc.num_kv_heads, desc.max_ctx)
+        H = Hq if heads is None else len(heads)
+        shape = (B, R, H, desc.max_ctx) if lay == LOGITS_PER_HEAD else (B, desc.num_kv_heads, desc.max_ctx)
         logits = torch.empty(shape, dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
@@ -203,23 +223,26 @@ def verify_attention(q, k_cache, v_cache, seq_lens, *, block_table=None, max_ctx
     ws = _workspace(verify_workspace_bytes(desc), dev, workspace)
     _check(load().vgsa_verify_attention(
         ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens), mask,
-        lay, _p(logits) if lay != LOGITS_NONE else None, _p(out), _p(lse), _p(ws), ws.numel(),
+        hmask, lay, _p(logits) if lay != LOGITS_NONE else None, _p(out), _p(lse), _p(ws), ws.numel(),
         _stream(dev)), "vgsa_verify_attention")
     return out, lse, logits
 
 
 def aggregate_scores(logits, seq_lens, num_q_heads: int, num_kv_heads: int, *,
-                     layout: str = "kvgroup_sum", scores=None):
-    """vgsa_aggregate_scores.  Returns scores fp32 [B, max_ctx]; for the
-    per-head layout the collected row count is logits.shape[1]."""
+                     layout: str = "kvgroup_sum", scores=None, accumulate: bool = False):
+    """vgsa_aggregate_scores.  Returns scores fp32 [B, max_ctx] (added to
+    `scores` when accumulating); per-head logits are [B, R, H, max_ctx]."""
     _need(logits, "logits", torch.float32)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     lay = _LAYOUTS[layout]
     B, max_ctx = logits.shape[0], logits.shape[-1]
-    n_rows = logits.shape[1] if lay == LOGITS_PER_HEAD and logits.dim() == 4 else 0
+    n_rows = logits.shape[1] * logits.shape[2] if lay == LOGITS_PER_HEAD and logits.dim() == 4 else 0
     if scores is None:
         scores = torch.empty((B, max_ctx), dtype=torch.float32, device=logits.device)
-    _check(load().vgsa_aggregate_scores(B, num_q_heads, num_kv_heads, max_ctx, lay, n_rows, _p(logits),
+    if accumulate and scores is None:
+        raise ValueError("accumulate needs the scores to add to")
+    _check(load().vgsa_aggregate_scores(B, num_q_heads, num_kv_heads, max_ctx, lay, n_rows,
+                                        int(bool(accumulate)), _p(logits),
                                         _p(seq_lens), _p(scores), _stream(logits.device)),
            "vgsa_aggregate_scores")
     return scores
@@ -295,11 +318,12 @@ def append_positions(base, first: int, count: int, idx, n_idx) -> None:
 
 # --------------------------------------------------------------------------- two-phase form
 def verify_partials(desc: AttnDesc, q, k_cache, v_cache, seq_lens, block_table, rows, layout: int,
-                    logits, workspace) -> None:
-    """vgsa_verify_partials; `rows` are the collected row indices (ascending)."""
+                    logits, workspace, heads: Optional[Sequence[int]] = None) -> None:
+    """vgsa_verify_partials; `rows` / `heads` are the collected row and head
+    indices (ascending; heads None: every head)."""
     _check(load().vgsa_verify_partials(
         ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens),
-        row_mask(rows, desc.q_len), layout, _p(logits) if layout != LOGITS_NONE else None, _p(workspace),
+        row_mask(rows, desc.q_len), head_mask(heads, desc.num_q_heads), layout, _p(logits) if layout != LOGITS_NONE else None, _p(workspace),
         workspace.numel(), _stream(q.device)), "vgsa_verify_partials")
 
 
@@ -318,10 +342,13 @@ def combine_partials(desc: AttnDesc, span: int, lengths, workspace, out, lse) ->
 
 
 def verify_finish(desc: AttnDesc, seq_lens, workspace, out, lse, layout: int = LOGITS_NONE,
-                  logits=None, scores=None, num_rows: int = 2) -> None:
+                  logits=None, scores=None, accumulate: bool = False) -> None:
     """vgsa_verify_finish: combine the verify partials and (with `scores`)
-    aggregate the collected logits, in one launch.  `num_rows` is the number
-    of collected rows (per-head layout only)."""
+    aggregate the collected logits, in one launch (added to `scores` when
+    accumulating).  Per-head logits are [B, R, H, max_ctx]."""
+    num_rows = 0
+    if layout == LOGITS_PER_HEAD and logits is not None and logits.dim() == 4:
+        num_rows = logits.shape[1] * logits.shape[2]
     _check(load().vgsa_verify_finish(
         ctypes.byref(desc), _p(seq_lens), _p(workspace), workspace.numel(), _p(out), _p(lse),
-        layout, num_rows, _p(logits), _p(scores), _stream(out.device)), "vgsa_verify_finish")
+        layout, num_rows, int(bool(accumulate)), _p(logits), _p(scores), _stream(out.device)), "vgsa_verify_finish")

@@ -96,6 +96,8 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
   a.layout = VGSA_LOGITS_NONE;
   a.row_mask = 0u;
   a.n_rows = 0;
+  a.head_mask = kAllHeads;
+  a.n_heads = d.num_q_heads;
   a.out = nullptr;
   a.lse = nullptr;
   a.direct = 0;
@@ -198,7 +200,7 @@ namespace {
 // the final output directly.
 vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                          uint32_t collect_mask, vgsa_logit_layout layout,
+                          uint32_t collect_mask, uint64_t head_mask, vgsa_logit_layout layout,
                           float* logits, void* workspace, size_t workspace_bytes, void* out,
                           float* lse, void* stream) {
   vgsa_status st = check_desc(desc);
@@ -212,6 +214,12 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
   if (layout != VGSA_LOGITS_NONE) {
     if (logits == nullptr) return VGSA_ERR_INVALID_ARG;
     if (collect_mask == 0u || (collect_mask >> d.q_len) != 0u) return VGSA_ERR_INVALID_ARG;
+    if (head_mask != kAllHeads) {
+      // a head subset names heads by bit: at most 64 heads, at least one named
+      if (d.num_q_heads > 64) return VGSA_ERR_UNSUPPORTED;
+      if (head_mask == 0ull) return VGSA_ERR_INVALID_ARG;
+      if (d.num_q_heads < 64 && (head_mask >> d.num_q_heads) != 0ull) return VGSA_ERR_INVALID_ARG;
+    }
   }
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
   st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
@@ -222,6 +230,8 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
   a.logits = layout == VGSA_LOGITS_NONE ? nullptr : logits;
   a.row_mask = layout == VGSA_LOGITS_NONE ? 0u : collect_mask;
   a.n_rows = __builtin_popcount(a.row_mask);
+  a.head_mask = layout == VGSA_LOGITS_NONE ? kAllHeads : head_mask;
+  a.n_heads = a.head_mask == kAllHeads ? d.num_q_heads : __builtin_popcountll(a.head_mask);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.direct = out != nullptr ? 1 : 0;
@@ -261,9 +271,10 @@ extern "C" {
 vgsa_status vgsa_verify_partials(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table,
                                  const int32_t* seq_lens, uint32_t collect_mask,
-                                 vgsa_logit_layout layout, float* logits,
+                                 uint64_t head_mask, vgsa_logit_layout layout, float* logits,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, layout,
+  return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, head_mask,
+                       layout,
                        logits, workspace, workspace_bytes, nullptr, nullptr,
                        stream);
 }
@@ -312,7 +323,7 @@ vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
 vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, uint32_t collect_mask,
-                                  vgsa_logit_layout layout, float* logits,
+                                  uint64_t head_mask, vgsa_logit_layout layout, float* logits,
                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   vgsa_status st = check_desc(desc);
@@ -321,11 +332,10 @@ vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, con
   const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, desc->max_ctx);
   if (p.num_splits == 1) {
     // one split: the partials kernel finishes the softmax and writes out / lse
-    return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, layout,
-                         logits, workspace, workspace_bytes, out, lse,
-                         stream);
+    return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, head_mask,
+                         layout, logits, workspace, workspace_bytes, out, lse, stream);
   }
-  st = verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask,
+  st = verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, head_mask,
                      layout, logits, workspace, workspace_bytes, nullptr, nullptr, stream);
   if (st != VGSA_OK) return st;
   return vgsa_combine_partials(desc, desc->max_ctx, seq_lens, workspace, workspace_bytes, out,
@@ -354,8 +364,8 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
 
 vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
                                const void* workspace, size_t workspace_bytes, void* out, float* lse,
-                               vgsa_logit_layout layout, int32_t num_rows, const float* logits,
-                               float* scores, void* stream) {
+                               vgsa_logit_layout layout, int32_t num_rows, int32_t accumulate,
+                               const float* logits, float* scores, void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
@@ -364,7 +374,8 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
     if (layout != VGSA_LOGITS_PER_HEAD && layout != VGSA_LOGITS_KVGROUP_SUM)
       return VGSA_ERR_INVALID_ARG;
     if (logits == nullptr) return VGSA_ERR_INVALID_ARG;
-    if (layout == VGSA_LOGITS_PER_HEAD && (num_rows < 1 || num_rows > d.q_len))
+    if (layout == VGSA_LOGITS_PER_HEAD &&
+        (num_rows < 1 || num_rows > (int64_t)d.q_len * d.num_q_heads))
       return VGSA_ERR_INVALID_ARG;
   }
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
@@ -388,25 +399,27 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
   ca.header = c.header;
   ca.out = static_cast<uint16_t*>(out);
   ca.lse = lse;
-  AggregateArgs ag{d.batch,  d.num_q_heads, d.num_kv_heads, d.max_ctx, (int32_t)layout,
-                   num_rows, logits,        seq_lens,       scores};
+  AggregateArgs ag{d.batch,  d.num_q_heads,         d.num_kv_heads, d.max_ctx, (int32_t)layout,
+                   num_rows, accumulate ? 1 : 0, logits,          seq_lens,  scores};
   return hip_status(launch_combine_aggregate(ca, ag, static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t max_ctx, vgsa_logit_layout layout, int32_t num_rows,
-                                  const float* logits, const int32_t* seq_lens, float* scores,
-                                  void* stream) {
+                                  int32_t accumulate, const float* logits,
+                                  const int32_t* seq_lens, float* scores, void* stream) {
   if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_ctx < 1) return VGSA_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return VGSA_ERR_INVALID_ARG;
   if (layout != VGSA_LOGITS_PER_HEAD && layout != VGSA_LOGITS_KVGROUP_SUM)
     return VGSA_ERR_INVALID_ARG;
-  if (layout == VGSA_LOGITS_PER_HEAD && (num_rows < 1 || num_rows > 16)) return VGSA_ERR_INVALID_ARG;
+  if (layout == VGSA_LOGITS_PER_HEAD && (num_rows < 1 || num_rows > (int64_t)16 * num_q_heads))
+    return VGSA_ERR_INVALID_ARG;
   if (logits == nullptr || seq_lens == nullptr || scores == nullptr) return VGSA_ERR_INVALID_ARG;
   if (batch > kMaxGridYZ) return VGSA_ERR_UNSUPPORTED;
   if (batch == 0) return VGSA_OK;
   return hip_status(launch_aggregate(batch, num_q_heads, num_kv_heads, max_ctx, layout, num_rows,
-                                     logits, seq_lens, scores, static_cast<hipStream_t>(stream)));
+                                     accumulate ? 1 : 0, logits, seq_lens, scores,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores,

@@ -198,23 +198,38 @@ void attn_partials_kernel(AttnArgs a) {
   }
   const int end = min(start + chunk, count);
 
+  // Collected heads of this kv-group: bit hh for q-head g*G + hh (a head
+  // subset needs Hq <= 64, checked on the host).
+  const uint64_t all_g = G >= 64 ? ~0ull : (1ull << G) - 1ull;
+  const uint64_t gmask = a.head_mask == kAllHeads ? all_g : (a.head_mask >> (g * G)) & all_g;
+
   // This lane's query column c16 of block qb: causal limit and collected row.
-  int lim[QB], rowc[QB], head[QB];
+  int lim[QB], rowc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int m = qb * 16 + c16;
     const bool ok = m < rows;
     const int hh = ok ? m / T : 0, t = ok ? m % T : 0;
-    head[qb] = g * G + hh;
     lim[qb] = ok ? L - T + t : 0x7fffffff;  // row t sees positions <= L - T + t
-    // collected row: its rank among the collected rows (PER_HEAD row index)
-    rowc[qb] = (EMIT != VGSA_LOGITS_NONE && ok && ((a.row_mask >> t) & 1u))
+    // collected row of a collected head: its rank among the collected rows
+    rowc[qb] = (EMIT != VGSA_LOGITS_NONE && ok && ((a.row_mask >> t) & 1u) && ((gmask >> hh) & 1ull))
                    ? __builtin_popcount(a.row_mask & ((1u << t) - 1u)) : -1;
-    if (kHeadLogits && threadIdx.x < 16)
-      s_lrow[m] = rowc[qb] < 0 ? -1
-                               : (((int64_t)b * a.n_rows + rowc[qb]) * a.hq + head[qb]) * a.max_ctx;
+    if (kHeadLogits && threadIdx.x < 16) {
+      // per-head row: [b][collected row][collected head][position]
+      const int head = g * G + hh;
+      const int hrank = a.head_mask == kAllHeads
+                            ? head : __builtin_popcountll(a.head_mask & ((1ull << head) - 1ull));
+      s_lrow[m] = rowc[qb] < 0
+                      ? -1 : (((int64_t)b * a.n_rows + rowc[qb]) * a.n_heads + hrank) * a.max_ctx;
+    }
   }
   const int lim_min = L - T;  // every row sees positions <= L - T
+  // per-head logits: the collected rows of block qb, bit c16 (wave-uniform),
+  // so blocks and row pairs with nothing to write are skipped
+  uint32_t cmask[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    cmask[qb] = kHeadLogits ? (uint32_t)(__ballot(rowc[qb] >= 0) & 0xFFFFull) : 0u;
 
   f32x4 oacc[DB][QB];
 #pragma unroll
@@ -326,22 +341,25 @@ void attn_partials_kernel(AttnArgs a) {
     if (m < rows) {
       val = *reinterpret_cast<const u32x4*>(a.q + (row_base + m) * D + fks * 32 + (fl >> 4) * 8);
     } else if (EMIT == kEmitSumColumn && m >= QB * 16 - 2) {
-      // summed query of the collected rows (heads ascending, then rows
-      // ascending): column QB*16-2 its bf16 rounding, column QB*16-1 the rest
-      // Loads go out kSumBatch at a time: one after another they would be
-      // G * R dependent round trips before the first tile is computed.
+      // summed query of the collected rows of the collected heads (heads
+      // ascending, then rows ascending): column QB*16-2 its bf16 rounding,
+      // column QB*16-1 the rest.  Loads go out kSumBatch at a time: one after
+      // another they would be dependent round trips before the first tile.
       constexpr int kSumBatch = 4;
       float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const int R = __builtin_popcount(a.row_mask), n_sum = G * R;
+      const int R = __builtin_popcount(a.row_mask), n_sum = __builtin_popcountll(gmask) * R;
       for (int k0 = 0; k0 < n_sum; k0 += kSumBatch) {
         bf16x8 qv[kSumBatch];
 #pragma unroll
         for (int i = 0; i < kSumBatch; ++i) {
-          const int k = min(k0 + i, n_sum - 1);  // uniform: head k / R, its (k % R)-th row
-          const int hh = k / R;
+          // uniform: the (k / R)-th collected head, its (k % R)-th collected row
+          const int k = min(k0 + i, n_sum - 1);
+          uint64_t hm = gmask;
+          for (int c = k / R; c > 0; --c) hm &= hm - 1ull;
           uint32_t mm = a.row_mask;
-          for (int c = k - hh * R; c > 0; --c) mm &= mm - 1u;
-          qv[i] = load16(a.q + (row_base + hh * T + __builtin_ctz(mm)) * D + fks * 32 + (fl >> 4) * 8);
+          for (int c = k % R; c > 0; --c) mm &= mm - 1u;
+          const int hh = __builtin_ctzll(hm), t = __builtin_ctz(mm);
+          qv[i] = load16(a.q + (row_base + hh * T + t) * D + fks * 32 + (fl >> 4) * 8);
         }
 #pragma unroll
         for (int i = 0; i < kSumBatch; ++i)
@@ -445,6 +463,7 @@ void attn_partials_kernel(AttnArgs a) {
       float* hs = shl + wave * 16 * kHS;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
+        if (cmask[qb] == 0u) continue;
         // lane (c16, kg) holds row c16 at positions pb*16 + 4*kg .. +3
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb) {
@@ -461,6 +480,7 @@ void attn_partials_kernel(AttnArgs a) {
         const int e = lane & 31;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+          if (((cmask[qb] >> (2 * i)) & 3u) == 0u) continue;
           const int rr = 2 * i + (lane >> 5);
           const int64_t off = s_lrow[qb * 16 + rr];
           const float v = hs[rr * kHS + e];
@@ -511,8 +531,10 @@ void attn_partials_kernel(AttnArgs a) {
       // after the exchange both hold the sum.  The earlier collected row sees
       // a prefix of what the later one sees, so past its causal limit the
       // sum is -inf.
+      // (a kv-group with no collected head sums to 0 at every position)
       const int row_first = __builtin_ctz(a.row_mask);  // the earliest collected row
-      const int vis0 = full ? kTile : max(0, min(L - T + row_first, ts + n_in - 1) - ts + 1);
+      const int vis0 = (full || gmask == 0ull)
+                           ? kTile : max(0, min(L - T + row_first, ts + n_in - 1) - ts + 1);
       f32x4 lv[2];
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb)
@@ -703,7 +725,10 @@ hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
   } else if (rows <= 48) {
     hipLaunchKernelGGL((attn_partials_kernel<D, 3, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+    // four row blocks of d = 128 leave registers for one wavefront per SIMD:
+    // never launched with 8 wavefronts (not even instantiated)
+    if constexpr (D == 128 && WAVES == kWavesWide) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -58,6 +58,9 @@ SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span);
 constexpr size_t kHeaderBytes = 256;
 size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p);
 
+// Head mask value that collects every q-head (any head count).
+constexpr uint64_t kAllHeads = ~0ull;
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -70,7 +73,9 @@ struct AttnArgs {
   float* logits;         // verify only, may be null
   int32_t layout;
   uint32_t row_mask;  // collected rows: bit t set for query row t
-  int32_t n_rows;     // popcount(row_mask): PER_HEAD rows per sequence
+  int32_t n_rows;     // popcount(row_mask): collected rows per sequence
+  uint64_t head_mask; // collected q-heads: bit h for head h, or kAllHeads
+  int32_t n_heads;    // collected q-heads (PER_HEAD head rows per collected row)
   float* part_o;
   float* part_ml;
   int32_t* header;   // the launch records its item length in header[0]
@@ -106,7 +111,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 struct AggregateArgs {
   int32_t batch, hq, hkv, max_ctx, layout;
-  int32_t n_rows;  // PER_HEAD: collected rows per sequence
+  int32_t n_rows;      // PER_HEAD: logit rows per sequence (rows x heads collected)
+  int32_t accumulate;  // add the sum to scores instead of overwriting them
   const float* logits;
   const int32_t* seq_lens;
   float* scores;
@@ -117,7 +123,7 @@ hipError_t launch_combine_aggregate(const CombineArgs& c, const AggregateArgs& a
                                     hipStream_t stream);
 
 hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t layout,
-                            int32_t n_rows,
+                            int32_t n_rows, int32_t accumulate,
                             const float* logits, const int32_t* seq_lens, float* scores,
                             hipStream_t stream);
 

@@ -86,11 +86,12 @@ constexpr int combine_blocks(int rows) {
 }
 
 // Score of position j of sequence b: the collected logits summed in a fixed
-// order (kv-groups ascending, or rows then heads ascending).
+// order (kv-groups ascending, or rows then heads ascending), then added to
+// the score already there when accumulating (e.g. over layers).
 __device__ __forceinline__ void aggregate_position(const AggregateArgs& a, int b, int j) {
   const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
   if (j >= L) return;
-  const int n = a.layout == VGSA_LOGITS_KVGROUP_SUM ? a.hkv : a.n_rows * a.hq;
+  const int n = a.layout == VGSA_LOGITS_KVGROUP_SUM ? a.hkv : a.n_rows;
   const float* p = a.logits + (size_t)b * n * a.max_ctx + j;
   float s = 0.f;
   for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
@@ -101,7 +102,8 @@ __device__ __forceinline__ void aggregate_position(const AggregateArgs& a, int b
     for (int i = 0; i < kMergeBatch; ++i)
       if (r0 + i < n) s += v[i];
   }
-  a.scores[(size_t)b * a.max_ctx + j] = s;
+  float* dst = a.scores + (size_t)b * a.max_ctx + j;
+  *dst = a.accumulate ? *dst + s : s;
 }
 
 }  // namespace vgsa

@@ -61,9 +61,10 @@ hipError_t launch_append_positions(int32_t batch, const int32_t* base, int32_t f
 }
 
 hipError_t launch_aggregate(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t layout,
-                            int32_t n_rows, const float* logits, const int32_t* seq_lens,
+                            int32_t n_rows, int32_t accumulate, const float* logits,
+                            const int32_t* seq_lens,
                             float* scores, hipStream_t stream) {
-  AggregateArgs a{batch, hq, hkv, max_ctx, layout, n_rows, logits, seq_lens, scores};
+  AggregateArgs a{batch, hq, hkv, max_ctx, layout, n_rows, accumulate, logits, seq_lens, scores};
   const dim3 grid((max_ctx + kBlock - 1) / kBlock, batch);
   hipLaunchKernelGGL(aggregate_kernel, grid, dim3(kBlock), 0, stream, a);
   return hipGetLastError();

@@ -63,6 +63,9 @@ def test_status_strings_and_version(lib):
     assert lib.vgsa_version().decode().startswith("vgsa")
 
 
+ALL = B.ALL_HEADS
+
+
 def desc(**kw):
     base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, q_len=4, max_ctx=1000,
                 block_size=0, max_blocks_per_seq=0, num_blocks=0, softmax_scale=0.0)
@@ -90,7 +93,7 @@ def desc(**kw):
 ])
 def test_bad_desc_rejected_everywhere(lib, kw, code):
     d = ctypes.byref(desc(**kw))
-    assert lib.vgsa_verify_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, 9, 2, FAKE, FAKE, None,
+    assert lib.vgsa_verify_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, 9, ALL, 2, FAKE, FAKE, None,
                                      FAKE, 1 << 40, None) == code
     assert lib.vgsa_sparse_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None,
                                      FAKE, 1 << 40, None) == code
@@ -106,33 +109,40 @@ def test_verify_argument_checks(lib):
     assert ws > 0
     V = lib.vgsa_verify_attention
     # null q / cache / seq_lens / out
-    assert V(dp, None, FAKE, FAKE, None, FAKE, 9, 0, None, FAKE, None, FAKE, ws, None) == INVALID
-    assert V(dp, FAKE, FAKE, FAKE, None, None, 9, 0, None, FAKE, None, FAKE, ws, None) == INVALID
-    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, 0, None, None, None, FAKE, ws, None) == INVALID
+    assert V(dp, None, FAKE, FAKE, None, FAKE, 9, ALL, 0, None, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, None, 9, ALL, 0, None, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 0, None, None, None, FAKE, ws, None) == INVALID
     # block table given for a contiguous cache
-    assert V(dp, FAKE, FAKE, FAKE, FAKE, FAKE, 9, 0, None, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, FAKE, FAKE, 9, ALL, 0, None, FAKE, None, FAKE, ws, None) == INVALID
     # logits requested but missing; collect mask empty or naming a row >= q_len; bad layout
-    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, 1, None, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 1, None, FAKE, None, FAKE, ws, None) == INVALID
     for mask in [0, 1 << 4, 0x11, 0xFFFFFFFF]:
         for lay in (1, 2):
-            assert V(dp, FAKE, FAKE, FAKE, None, FAKE, mask, lay, FAKE, FAKE, None, FAKE, ws,
+            assert V(dp, FAKE, FAKE, FAKE, None, FAKE, mask, ALL, lay, FAKE, FAKE, None, FAKE, ws,
                      None) == INVALID
-    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, 7, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 7, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    # head mask: empty, or naming a head >= Hq; subsets need Hq <= 64
+    for hm in (0, 1 << 8, 0x1FF):
+        assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, hm, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    d128 = desc(num_q_heads=128, num_kv_heads=32, q_len=4)
+    w128 = lib.vgsa_verify_workspace_bytes(ctypes.byref(d128))
+    assert V(ctypes.byref(d128), FAKE, FAKE, FAKE, None, FAKE, 9, 3, 2, FAKE, FAKE, None, FAKE, w128,
+             None) == UNSUPPORTED
     # workspace missing or one byte short
-    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, 2, FAKE, FAKE, None, None, ws, None) == WORKSPACE
-    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, 2, FAKE, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 2, FAKE, FAKE, None, None, ws, None) == WORKSPACE
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 2, FAKE, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
     # misaligned q / cache / out; misaligned workspace
     ODD = ctypes.c_void_p(0x1008)
-    assert V(dp, ODD, FAKE, FAKE, None, FAKE, 9, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
-    assert V(dp, FAKE, ODD, FAKE, None, FAKE, 9, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
-    assert V(dp, FAKE, FAKE, ODD, None, FAKE, 9, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
-    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, 2, FAKE, ODD, None, FAKE, ws, None) == INVALID
-    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, 2, FAKE, FAKE, None, ctypes.c_void_p(0x1010),
+    assert V(dp, ODD, FAKE, FAKE, None, FAKE, 9, ALL, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, ODD, FAKE, None, FAKE, 9, ALL, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, ODD, None, FAKE, 9, ALL, 2, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 2, FAKE, ODD, None, FAKE, ws, None) == INVALID
+    assert V(dp, FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 2, FAKE, FAKE, None, ctypes.c_void_p(0x1010),
              ws, None) == WORKSPACE
     # paged cache without a block table
     dpg = desc(block_size=16, max_blocks_per_seq=63, num_blocks=100, max_ctx=1000)
     wsp = lib.vgsa_verify_workspace_bytes(ctypes.byref(dpg))
-    assert V(ctypes.byref(dpg), FAKE, FAKE, FAKE, None, FAKE, 9, 2, FAKE, FAKE, None, FAKE, wsp,
+    assert V(ctypes.byref(dpg), FAKE, FAKE, FAKE, None, FAKE, 9, ALL, 2, FAKE, FAKE, None, FAKE, wsp,
              None) == INVALID
 
 
@@ -150,14 +160,14 @@ def test_sparse_and_combine_argument_checks(lib):
     assert C(dp, 0, FAKE, FAKE, ws, FAKE, None, None) == INVALID
     F = lib.vgsa_verify_finish
     wv = lib.vgsa_verify_workspace_bytes(dp)
-    assert F(dp, None, FAKE, wv, FAKE, None, 2, 2, FAKE, FAKE, None) == INVALID
-    assert F(dp, FAKE, FAKE, wv, None, None, 2, 2, FAKE, FAKE, None) == INVALID
-    assert F(dp, FAKE, FAKE, wv, FAKE, None, 0, 2, FAKE, FAKE, None) == INVALID   # scores need a layout
-    assert F(dp, FAKE, FAKE, wv, FAKE, None, 2, 2, None, FAKE, None) == INVALID   # ... and logits
-    assert F(dp, FAKE, FAKE, wv - 1, FAKE, None, 2, 2, FAKE, FAKE, None) == WORKSPACE
-    for nr in (0, 5):   # per-head row count outside 1..q_len
-        assert F(dp, FAKE, FAKE, wv, FAKE, None, 1, nr, FAKE, FAKE, None) == INVALID
-    assert F(ctypes.byref(desc(head_dim=96)), FAKE, FAKE, wv, FAKE, None, 2, 2, FAKE, FAKE, None) == UNSUPPORTED
+    assert F(dp, None, FAKE, wv, FAKE, None, 2, 2, 0, FAKE, FAKE, None) == INVALID
+    assert F(dp, FAKE, FAKE, wv, None, None, 2, 2, 0, FAKE, FAKE, None) == INVALID
+    assert F(dp, FAKE, FAKE, wv, FAKE, None, 0, 2, 0, FAKE, FAKE, None) == INVALID   # scores need a layout
+    assert F(dp, FAKE, FAKE, wv, FAKE, None, 2, 2, 0, None, FAKE, None) == INVALID   # ... and logits
+    assert F(dp, FAKE, FAKE, wv - 1, FAKE, None, 2, 2, 0, FAKE, FAKE, None) == WORKSPACE
+    for nr in (0, 33):  # per-head logit rows outside 1..q_len*Hq
+        assert F(dp, FAKE, FAKE, wv, FAKE, None, 1, nr, 0, FAKE, FAKE, None) == INVALID
+    assert F(ctypes.byref(desc(head_dim=96)), FAKE, FAKE, wv, FAKE, None, 2, 2, 0, FAKE, FAKE, None) == UNSUPPORTED
     assert C(dp, 64, None, FAKE, ws, FAKE, None, None) == INVALID
     assert C(dp, 64, FAKE, FAKE, ws, None, None, None) == INVALID
     assert C(dp, 64, FAKE, FAKE, ws - 1, FAKE, None, None) == WORKSPACE
@@ -165,14 +175,14 @@ def test_sparse_and_combine_argument_checks(lib):
 
 def test_aggregate_and_select_argument_checks(lib):
     A = lib.vgsa_aggregate_scores
-    assert A(-1, 8, 2, 100, 2, 2, FAKE, FAKE, FAKE, None) == INVALID
-    assert A(2, 6, 4, 100, 2, 2, FAKE, FAKE, FAKE, None) == INVALID
-    assert A(2, 8, 2, 0, 2, 2, FAKE, FAKE, FAKE, None) == INVALID
-    assert A(2, 8, 2, 100, 0, 2, FAKE, FAKE, FAKE, None) == INVALID   # layout NONE has nothing to sum
-    assert A(2, 8, 2, 100, 2, 2, None, FAKE, FAKE, None) == INVALID
-    for nr in (0, 17):  # per-head row count outside 1..16
-        assert A(2, 8, 2, 100, 1, nr, FAKE, FAKE, FAKE, None) == INVALID
-    assert A(0, 8, 2, 100, 2, 2, FAKE, FAKE, FAKE, None) == OK        # empty batch: nothing launched
+    assert A(-1, 8, 2, 100, 2, 2, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert A(2, 6, 4, 100, 2, 2, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert A(2, 8, 2, 0, 2, 2, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert A(2, 8, 2, 100, 0, 2, 0, FAKE, FAKE, FAKE, None) == INVALID   # layout NONE has nothing to sum
+    assert A(2, 8, 2, 100, 2, 2, 0, None, FAKE, FAKE, None) == INVALID
+    for nr in (0, 129):  # per-head logit rows outside 1..16*Hq
+        assert A(2, 8, 2, 100, 1, nr, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert A(0, 8, 2, 100, 2, 2, 0, FAKE, FAKE, FAKE, None) == OK        # empty batch: nothing launched
     T = lib.vgsa_select_topk
     assert T(2, 100, FAKE, FAKE, 0, 0, 0, FAKE, 8, FAKE, None) == INVALID     # k < 1
     assert T(2, 100, FAKE, FAKE, 8, -1, 0, FAKE, 8, FAKE, None) == INVALID

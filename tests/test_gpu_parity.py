@@ -458,13 +458,105 @@ def test_collect_any_row_set(name, kind):
         Bn.verify_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, rows, code, lg2, ws)
         o2, l2 = torch.empty_like(out), torch.empty_like(lse)
         s2 = torch.empty_like(sc)
-        Bn.verify_finish(desc, d.seq_lens, ws, o2, l2, code, lg2, s2, num_rows=len(rows))
+        Bn.verify_finish(desc, d.seq_lens, ws, o2, l2, code, lg2, s2)
         torch.cuda.synchronize()
         assert_logits_close(sc.cpu().numpy(), s_ref, f"{name}/{layout}/{kind} scores", floor=s_floor)
         for b in range(w.batch):
             L = int(x.seq_lens[b])
             assert torch.equal(lg[b, ..., :L], lg2[b, ..., :L])
             assert torch.equal(sc[b, :L], s2[b, :L])
+
+
+def _head_set(kind, Hq, G):
+    return {"one": (Hq - 1,), "first_group": tuple(range(G)),
+            "scattered": tuple(range(1, Hq, 3)), "one_per_group": tuple(range(0, Hq, G))}[kind]
+
+
+@pytest.mark.parametrize("kind", ["one", "first_group", "scattered", "one_per_group"])
+@pytest.mark.parametrize("name", ["g4t5_d64", "g8t8_d64", "paged_g8t6_d64", "chunk4224_g1t3_d64"])
+def test_head_subset_scoring(name, kind):
+    """Scores on a subset of the query heads (online semantic-retrieval-head
+    scoring): per-head logits of the chosen heads only ([B, R, H, ctx]),
+    kv-group sums over the chosen heads (0 for a kv-head with none), scores,
+    through both entry-point forms; attention output unchanged."""
+    w = CASES[name]
+    T, Hq, Hkv = w.gamma + 1, w.num_q_heads, w.num_kv_heads
+    heads = _head_set(kind, Hq, Hq // Hkv)
+    rows = (0, T - 1)
+    say(f"[head subset] {name} heads={heads}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    o_ref, lse_ref = oracle.verify_attention(x.q, x.k, x.v, x.seq_lens)
+    l_ref = oracle.collected_logits(x.q, x.k, x.seq_lens, rows, heads=heads)
+    absl = np.where(np.isneginf(l_ref), 0.0, np.abs(l_ref))
+    s_ref, s_floor = oracle.aggregate_scores(l_ref), oracle.aggregate_scores(absl)
+    desc = Bn.make_desc(d.q, d.k, d.block_table, d.max_ctx)
+    for layout, code in (("per_head", Bn.LOGITS_PER_HEAD), ("kvgroup_sum", Bn.LOGITS_KVGROUP_SUM)):
+        out, lse, lg = Bn.verify_attention(d.q, d.k, d.v, d.seq_lens, block_table=d.block_table,
+                                           max_ctx=d.max_ctx, collect_rows=rows, heads=heads,
+                                           layout=layout)
+        torch.cuda.synchronize()
+        assert_out_close(out, o_ref, f"{name}/{layout}/{kind} out")
+        assert_lse_close(lse, lse_ref, f"{name}/{layout}/{kind} lse")
+        if layout == "per_head":
+            assert lg.shape[2] == len(heads)
+            assert_logits_close(lg.cpu().numpy(), l_ref, f"{name}/{kind} per-head logits")
+        else:
+            gs = oracle.kvgroup_sum(l_ref, Hkv, heads=heads, num_q_heads=Hq)
+            gf = oracle.kvgroup_sum(absl, Hkv, heads=heads, num_q_heads=Hq)
+            for b, L in enumerate(x.seq_lens):
+                gs[b, :, int(L):] = np.nan  # past the length: not written (an empty group's 0 too)
+            assert_logits_close(lg.cpu().numpy(), gs, f"{name}/{kind} group logits", floor=gf)
+        sc = Bn.aggregate_scores(lg, d.seq_lens, Hq, Hkv, layout=layout)
+        ws = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        lg2 = torch.empty_like(lg)
+        Bn.verify_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, rows, code, lg2, ws,
+                           heads=heads)
+        o2, l2, s2 = torch.empty_like(out), torch.empty_like(lse), torch.empty_like(sc)
+        Bn.verify_finish(desc, d.seq_lens, ws, o2, l2, code, lg2, s2)
+        torch.cuda.synchronize()
+        assert_logits_close(sc.cpu().numpy(), s_ref, f"{name}/{layout}/{kind} scores", floor=s_floor)
+        for b in range(w.batch):
+            L = int(x.seq_lens[b])
+            assert torch.equal(lg[b, ..., :L], lg2[b, ..., :L])
+            assert torch.equal(sc[b, :L], s2[b, :L])
+
+
+def test_scores_accumulate_over_layers():
+    """Scores summed over several layers' calls (the layers whose heads are
+    scored): aggregate and finish add to the scores already there."""
+    w = CASES["g4t5_d64"]
+    heads = (1, 6, 11)
+    rows = (0, w.gamma)
+    say("[accumulate over layers]")
+    layers = [W.make_layer(w, layer=l) for l in (0, 3)]
+    want = sum(oracle.aggregate_scores(oracle.collected_logits(x.q, x.k, x.seq_lens, rows, heads=heads))
+               for x in layers)
+    floor = sum(oracle.aggregate_scores(np.abs(np.nan_to_num(
+        oracle.collected_logits(x.q, x.k, x.seq_lens, rows, heads=heads), neginf=0.0)))
+        for x in layers)
+    for layout, code in (("kvgroup_sum", Bn.LOGITS_KVGROUP_SUM), ("per_head", Bn.LOGITS_PER_HEAD)):
+        s_agg, s_fin = None, None
+        for i, x in enumerate(layers):
+            d = to_device(x)
+            _, _, lg = Bn.verify_attention(d.q, d.k, d.v, d.seq_lens, max_ctx=d.max_ctx,
+                                           collect_rows=rows, heads=heads, layout=layout)
+            s_agg = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads, layout=layout,
+                                        scores=s_agg, accumulate=i > 0)
+            desc = Bn.make_desc(d.q, d.k, None, d.max_ctx)
+            ws = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+            lg2 = torch.empty_like(lg)
+            Bn.verify_partials(desc, d.q, d.k, d.v, d.seq_lens, None, rows, code, lg2, ws, heads=heads)
+            if s_fin is None:
+                s_fin = torch.empty_like(s_agg)
+            Bn.verify_finish(desc, d.seq_lens, ws, torch.empty_like(d.q),
+                             torch.empty(d.q.shape[:3], dtype=torch.float32, device="cuda"), code,
+                             lg2, s_fin, accumulate=i > 0)
+        torch.cuda.synchronize()
+        assert_logits_close(s_agg.cpu().numpy(), want, f"{layout} accumulated scores", floor=floor)
+        for b in range(w.batch):
+            L = int(layers[0].seq_lens[b])
+            assert torch.equal(s_agg[b, :L], s_fin[b, :L])
 
 
 def test_append_positions_for_draft_steps():
