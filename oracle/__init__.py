@@ -2,9 +2,12 @@
 from .attention import (  # noqa: F401
     aggregate_scores,
     attend,
+    block_sums,
     collected_logits,
     default_scale,
     kvgroup_sum,
+    select_blocks,
+    select_blocks_batch,
     select_topk,
     select_topk_batch,
     select_topk_hybrid,

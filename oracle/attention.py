@@ -28,6 +28,8 @@ Sources (pages are cited by title and section):
     historical attention from the previous forward pass, draft lookahead
     attention from drafting) fill that budget hierarchically, the top-m by the
     draft signal first, the rest by the target signal.  -> select_topk_hybrid
+  * The euno.news summary of arXiv 2512.21911, "3. sparse verification
+    engine": attention keeps the top keys in structured blocks.  -> select_blocks
 
 Readings where the pages are silent (each one is listed with its reason in
 the design notes):
@@ -273,6 +275,60 @@ def select_topk_hybrid_batch(target: np.ndarray, draft: np.ndarray, seq_lens: Se
                              m: int, n_sink: int, window: int) -> List[np.ndarray]:
     return [select_topk_hybrid(target[b], draft[b], int(seq_lens[b]), k, m, n_sink, window)
             for b in range(target.shape[0])]
+
+
+def block_sums(scores: np.ndarray, length: int, block: int) -> np.ndarray:
+    """Score of each `block`-position block of [0, L): the sum of its members'
+    scores, accumulated in float32 in position order (the precision and order
+    in which the selection compares them; the last block may be partial)."""
+    L = int(length)
+    nb = -(-L // block)
+    out = np.zeros(nb, dtype=np.float32)
+    x = np.asarray(scores[:L], dtype=np.float32)
+    for i in range(nb):
+        s = np.float32(0.0)
+        for j in range(i * block, min(L, (i + 1) * block)):
+            s = np.float32(s + x[j])
+        out[i] = s
+    return out
+
+
+def select_blocks(scores: np.ndarray, length: int, k_blocks: int, block: int, n_sink: int,
+                  window: int) -> np.ndarray:
+    """Block-granular selection (structured block sparsity, the euno.news
+    summary of arXiv 2512.21911, "3. sparse verification engine"; Quest's
+    page-level selection in Dustin's comparison): whole blocks of `block`
+    positions are kept.  Under Vegas "A."'s summed-logit objective the best
+    k_blocks blocks are those of largest block sum.  The blocks holding the
+    sink prefix [0, n_sink) and the recent window [L - window, L) are kept
+    first; the rest of the k_blocks go to the largest block sums, lower block
+    first among equals.  If k_blocks covers every block all positions are
+    kept.  Returns the kept positions ascending (every member of a kept
+    block below L)."""
+    L = int(length)
+    if L <= 0:
+        return np.zeros(0, dtype=np.int64)
+    nb = -(-L // block)
+    if k_blocks >= nb:
+        return np.arange(L, dtype=np.int64)
+    forced = np.zeros(nb, dtype=bool)
+    forced[:min(-(-n_sink // block), nb)] = True
+    if window > 0:
+        forced[max(0, L - window) // block:] = True
+    nf = int(forced.sum())
+    if nf > k_blocks:
+        raise ValueError("sink and window blocks exceed the block budget")
+    chosen = _top_by(block_sums(scores, L, block), np.flatnonzero(~forced), k_blocks - nf)
+    keep = forced.copy()
+    keep[chosen] = True
+    pos = np.arange(L, dtype=np.int64)
+    return pos[keep[pos // block]]
+
+
+def select_blocks_batch(scores: np.ndarray, seq_lens: Sequence[int], k_blocks: int, block: int,
+                        n_sink: int, window: int) -> List[np.ndarray]:
+    return [select_blocks(scores[b], int(seq_lens[b]), k_blocks, block, n_sink, window)
+            for b in range(scores.shape[0])]
 
 
 def select_topk_batch(scores: np.ndarray, seq_lens: Sequence[int], k: int, n_sink: int,

@@ -333,6 +333,64 @@ def test_hybrid_select_reductions():
         oracle.select_topk_hybrid(tgt, drf, L, 10, 2, 6, 6)
 
 
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("L,kb,block,n_sink,window", [(23, 3, 4, 1, 2), (32, 4, 4, 0, 0), (30, 4, 4, 5, 3),
+                                                      (17, 3, 2, 2, 1), (40, 3, 8, 0, 9), (21, 5, 3, 0, 0)])
+def test_select_blocks_bruteforce(seed, L, kb, block, n_sink, window):
+    """Whole blocks kept: brute force over every set of free blocks (tie-heavy
+    integer scores, exact in float32): the chosen blocks have the largest
+    summed member score, the lowest blocks among equal sums, and the output
+    is every position below L of the forced and chosen blocks."""
+    rng = np.random.default_rng(200 + seed)
+    sc = rng.integers(-3, 4, size=L).astype(np.float64)
+    got = [int(x) for x in oracle.select_blocks(sc, L, kb, block, n_sink, window)]
+    nb = -(-L // block)
+    members = [list(range(i * block, min(L, (i + 1) * block))) for i in range(nb)]
+    forced = set(range(min(-(-n_sink // block), nb)))
+    if window > 0:
+        forced |= set(range(max(0, L - window) // block, nb))
+    free = [i for i in range(nb) if i not in forced]
+    best, best_set = -np.inf, None
+    for sub in itertools.combinations(free, kb - len(forced)):
+        tot = sum(sc[j] for i in sub for j in members[i])
+        if tot > best or (tot == best and sub < best_set):
+            best, best_set = tot, sub
+    want = sorted(j for i in sorted(forced | set(best_set)) for j in members[i])
+    assert got == want
+    # every sink and window position is kept
+    assert set(range(min(n_sink, L))) | set(range(max(0, L - window), L)) <= set(got)
+
+
+def test_select_blocks_reductions_and_edges():
+    rng = np.random.default_rng(9)
+    L = 500
+    sc = rng.standard_normal(L).astype(np.float32)
+    # block 1 is the position-level selection
+    for k, ns, win in [(40, 4, 16), (1, 0, 0), (100, 0, 99)]:
+        assert np.array_equal(oracle.select_blocks(sc, L, k, 1, ns, win),
+                              oracle.select_topk(sc, L, k, ns, win))
+    # block sums: float32, the partial last block holds positions 32..36 only;
+    # exact on integer scores, within float32 rounding otherwise
+    bs = oracle.block_sums(sc, 37, 16)
+    assert bs.dtype == np.float32 and bs.shape == (3,)
+    np.testing.assert_allclose(bs, [sc[0:16].astype(np.float64).sum(), sc[16:32].astype(np.float64).sum(),
+                                    sc[32:37].astype(np.float64).sum()], rtol=1e-5, atol=1e-5)
+    si = rng.integers(-50, 50, size=37).astype(np.float32)
+    assert list(oracle.block_sums(si, 37, 16)) == [si[0:16].sum(), si[16:32].sum(), si[32:].sum()]
+    # k_blocks covering every block keeps everything; L = 0 keeps nothing
+    assert list(oracle.select_blocks(sc, 37, 3, 16, 1, 1)) == list(range(37))
+    assert list(oracle.select_blocks(sc, 0, 3, 16, 1, 1)) == []
+    # a window across a block boundary forces both blocks
+    got = oracle.select_blocks(sc, 64, 3, 16, 0, 20)
+    assert set(range(32, 64)) <= set(got.tolist()) and len(got) == 48
+    with pytest.raises(ValueError):
+        oracle.select_blocks(sc, 64, 2, 16, 1, 20)
+    # a -inf member sinks its whole block
+    s2 = np.ones(64, np.float32)
+    s2[20] = -np.inf
+    assert 20 not in oracle.select_blocks(s2, 64, 3, 16, 0, 0).tolist()
+
+
 def test_select_planted_positions_win_on_small_workload():
     """Planted keys (aligned with the group's queries) must be selected: their
     summed logit is far above the spread of the unplanted ones."""
