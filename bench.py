@@ -43,13 +43,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(w, lens, layout="kvgroup_sum", n_rows=2, n_heads=None):
+def alg_bytes(w, lens, layout="kvgroup_sum", n_rows=2, n_heads=None, k_sel=None):
     """Algorithmic HBM bytes of one iteration, by stage (what the method must
     move: every K/V row read once, the collected logits written once, scores
     and indices once; split partials are implementation overhead and excluded).
     Logits are one fp32 per (kv-head, position), or per (collected row,
     collected q-head, position) in the per-head layout."""
-    B, Hq, Hkv, d, T, k = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.q_len, w.budget
+    B, Hq, Hkv, d, T = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.q_len
+    k = w.budget if k_sel is None else k_sel
     Ls = [int(L) for L in lens]
     kv = sum(Hkv * L * d * 2 * 2 for L in Ls)
     q_in = B * Hq * T * d * 2
@@ -145,9 +146,9 @@ def main():
                     help="collected verify rows: first draft + bonus (Collect-2-Query), or every row")
     ap.add_argument("--score-heads", type=int, default=0,
                     help="score on this many q-heads only, spread evenly (0: every head)")
-    ap.add_argument("--select", choices=("plain", "hybrid"), default="plain",
-                    help="top-k by the verify scores, or hybrid: top-m by a draft-lookahead score "
-                         "first (synthetic draft scores)")
+    ap.add_argument("--select", choices=("plain", "hybrid", "blocks"), default="plain",
+                    help="top-k by the verify scores; hybrid: top-m by a draft-lookahead score "
+                         "first (synthetic draft scores); blocks: whole 16-position blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=0,
                     help="1: capture one step as a HIP graph and time its replays")
@@ -214,7 +215,10 @@ def main():
     out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
     scores = torch.empty((B, max_ctx), dtype=torch.float32, device=dev)
-    stride = w.budget + w.draft_steps
+    # block selection: ceil(k / 16) whole 16-position blocks
+    BLK = 16
+    k_blocks = -(-w.budget // BLK)
+    stride = (k_blocks * BLK if args.select == "blocks" else w.budget) + w.draft_steps
     idx = torch.empty((B, stride), dtype=torch.int32, device=dev)
     n_idx = torch.empty((B,), dtype=torch.int32, device=dev)
     ws_s = torch.empty(Bn.sparse_workspace_bytes(desc, stride), dtype=torch.uint8, device=dev)
@@ -243,6 +247,8 @@ def main():
         if args.select == "hybrid":
             Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink, w.window,
                                   idx=idx, n_idx=n_idx)
+        elif args.select == "blocks":
+            Bn.select_blocks(scores, lens, k_blocks, BLK, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         else:
             Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
 
@@ -347,8 +353,20 @@ def main():
     select_hybrid_us = per_launch_us(
         lambda: Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink,
                                       w.window, idx=idx, n_idx=n_idx))
+    # block selection on the same scores, and the sparse pass over its lists
+    idx_b = torch.empty((B, k_blocks * BLK), dtype=torch.int32, device=dev)
+    n_b = torch.empty((B,), dtype=torch.int32, device=dev)
+    select_blocks_us = per_launch_us(
+        lambda: Bn.select_blocks(scores, lens, k_blocks, BLK, w.n_sink, w.window, idx=idx_b, n_idx=n_b))
+    sparse_blocks_us = None
+    if w.sparse_verify:
+        ws_b = torch.empty(Bn.sparse_workspace_bytes(desc, k_blocks * BLK), dtype=torch.uint8, device=dev)
+        sparse_blocks_us = per_launch_us(
+            lambda: Bn.sparse_attention(q, k, v, lens, idx_b, n_b, block_table=bt, max_ctx=max_ctx,
+                                        out=out_s, lse=lse_s, workspace=ws_b))
 
-    ab = alg_bytes(w, x.seq_lens, args.logits, len(rows), n_heads)
+    ab = alg_bytes(w, x.seq_lens, args.logits, len(rows), n_heads,
+                   k_blocks * BLK if args.select == "blocks" else None)
     iters = K / wall
     achieved = ab["verify_kernel"] / (verify_us * 1e-6) / 1e9
     result = {
@@ -370,7 +388,8 @@ def main():
                    "draft_steps": n_draft, "sparse_verify": w.sparse_verify,
                    "paged": w.paged, "logits": args.logits, "collect_rows": list(rows),
                    "score_heads": None if heads is None else list(heads),
-                   "select": args.select, "draft_m": w.draft_m if args.select == "hybrid" else None},
+                   "select": args.select, "draft_m": w.draft_m if args.select == "hybrid" else None,
+                   "k_blocks": k_blocks if args.select == "blocks" else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
                      "kernel": "attn_partials_kernel (verify)",
@@ -384,6 +403,8 @@ def main():
         "verify_partials_all_rows_us": verify_all_us,
         "logit_emit_overhead_all_rows": verify_all_us / verify_none_us - 1.0,
         "select_hybrid_us": select_hybrid_us,
+        "select_blocks_us": select_blocks_us,
+        "sparse_over_blocks_us": sparse_blocks_us,
     }
     if w.sparse_verify and stages.get("sparse"):
         sb = ab["sparse_kernel_kv"]

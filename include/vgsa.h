@@ -232,6 +232,33 @@ vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float*
                                     int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
                                     int32_t idx_stride, int32_t* n_idx, void* stream);
 
+/* 3''. Block-granular selection (structured block sparsity).
+ *    (The euno.news summary of arXiv 2512.21911, "3. sparse verification
+ *    engine": top keys kept in structured blocks; Quest's page-level
+ *    selection in Dustin's comparison.  Under Vegas "A."'s summed-logit
+ *    objective the best whole blocks are those of largest block sum.)
+ * scores    fp32 [B][max_ctx]
+ * k_blocks  blocks kept, >= 1
+ * block     positions per block, 1..1024 (16 matches a paged cache's pages)
+ * n_sink, window  the blocks holding positions [0, n_sink) and
+ *           [L - window, L) are always kept; ceil(n_sink / block) +
+ *           ceil(window / block) + 1 (the last term only when window > 0)
+ *           must not exceed k_blocks
+ * idx       int32 [B][idx_stride], idx_stride >= k_blocks * block.  Row b
+ *           receives, ascending, every position below L of the kept blocks:
+ *           the forced ones plus the others of largest block sum (the sum of
+ *           the members' scores in float32, position order; lower block first
+ *           among equal sums); every position when the blocks of L number at
+ *           most k_blocks.
+ * n_idx     int32 [B]: positions written
+ * Rows are limited to ceil(max_ctx / block) <= 8704 blocks
+ * (VGSA_ERR_UNSUPPORTED beyond).
+ */
+vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
+                               const int32_t* seq_lens, int32_t k_blocks, int32_t block,
+                               int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
+                               int32_t* n_idx, void* stream);
+
 /* 4. Sparse attention over an index list (page size 1).
  *    (Vegas section 2 step 3 and section 3; Dustin "3.")
  * desc->q_len is T' (1 for a draft step, gamma + 1 for a sparse verify).

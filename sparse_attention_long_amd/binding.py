@@ -47,6 +47,8 @@ SIGNATURES = {
                                  c_vp, c_vp]),
     "vgsa_select_topk_hybrid": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                         c_vp, c_i32, c_vp, c_vp]),
+    "vgsa_select_blocks": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32,
+                                   c_vp, c_vp]),
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
@@ -282,6 +284,24 @@ def select_topk_hybrid(target_scores, draft_scores, seq_lens, k: int, m: int, n_
     _check(load().vgsa_select_topk_hybrid(
         B, max_ctx, _p(target_scores), _p(draft_scores), _p(seq_lens), k, m, n_sink, window,
         _p(idx), idx.shape[1], _p(n_idx), _stream(target_scores.device)), "vgsa_select_topk_hybrid")
+    return idx, n_idx
+
+
+def select_blocks(scores, seq_lens, k_blocks: int, block: int, n_sink: int, window: int, *,
+                  idx_stride=None, idx=None, n_idx=None):
+    """vgsa_select_blocks.  Returns (idx int32 [B, idx_stride] positions of the
+    kept blocks, n_idx int32 [B])."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, max_ctx = scores.shape
+    stride = k_blocks * block if idx_stride is None else idx_stride
+    if idx is None:
+        idx = torch.empty((B, stride), dtype=torch.int32, device=scores.device)
+    if n_idx is None:
+        n_idx = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    _check(load().vgsa_select_blocks(B, max_ctx, _p(scores), _p(seq_lens), k_blocks, block, n_sink,
+                                     window, _p(idx), idx.shape[1], _p(n_idx),
+                                     _stream(scores.device)), "vgsa_select_blocks")
     return idx, n_idx
 
 

@@ -454,6 +454,27 @@ vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float*
                                        static_cast<hipStream_t>(stream)));
 }
 
+vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
+                               const int32_t* seq_lens, int32_t k_blocks, int32_t block,
+                               int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
+                               int32_t* n_idx, void* stream) {
+  if (batch < 0 || max_ctx < 1 || k_blocks < 1 || block < 1 || block > 1024 || n_sink < 0 ||
+      window < 0)
+    return VGSA_ERR_INVALID_ARG;
+  // the sink blocks and (at most ceil(window / block) + 1) window blocks fit the budget
+  const int64_t forced = ((int64_t)n_sink + block - 1) / block +
+                         (window > 0 ? ((int64_t)window + block - 1) / block + 1 : 0);
+  if (forced > k_blocks) return VGSA_ERR_INVALID_ARG;
+  if ((int64_t)idx_stride < (int64_t)k_blocks * block) return VGSA_ERR_INVALID_ARG;
+  if (scores == nullptr || seq_lens == nullptr || idx == nullptr || n_idx == nullptr)
+    return VGSA_ERR_INVALID_ARG;
+  if (((int64_t)max_ctx + block - 1) / block > kMaxSelBlocks) return VGSA_ERR_UNSUPPORTED;
+  if (batch == 0) return VGSA_OK;
+  return hip_status(launch_select_blocks(batch, max_ctx, scores, seq_lens, k_blocks, block, n_sink,
+                                         window, idx, idx_stride, n_idx,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 vgsa_status vgsa_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,
                                   int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream) {
   if (batch < 0 || first < 0 || count < 0 || idx_stride < 1) return VGSA_ERR_INVALID_ARG;

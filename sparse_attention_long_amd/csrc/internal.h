@@ -138,5 +138,11 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
                               int32_t idx_stride, int32_t* n_idx, hipStream_t stream);
 // Longest row (positions) the hybrid selection takes.
 constexpr int kMaxHybridRow = 8 * 32768;
+// Block-granular selection: blocks per row (their sums live in LDS).
+constexpr int kMaxSelBlocks = 8704;
+hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
+                                const int32_t* seq_lens, int32_t k_blocks, int32_t block,
+                                int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
+                                int32_t* n_idx, hipStream_t stream);
 
 }  // namespace vgsa

@@ -532,6 +532,85 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
   if (tid == 0) n_idx[b] = k;
 }
 
+// ---------------------------------------------------------------------------
+// Block-granular selection (structured block sparsity): whole blocks of
+// `block` positions are kept.  The score of a block is the sum of its
+// members' scores (float32, position order); the blocks holding the sinks and
+// the recent window are kept first and the rest of the k_blocks go to the
+// largest block sums, lower block first among equals.  The block sums of the
+// row go to LDS, one selection stage runs over them (keys in registers: a
+// row has at most kMaxSelBlocks blocks), and the kept blocks are written out
+// expanded to their positions, ascending, so the list feeds the sparse
+// attention call as it is.
+template <bool VEC>
+__global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
+    int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
+    int32_t k_blocks, int32_t block, int32_t n_sink, int32_t window, int32_t* __restrict__ idx,
+    int32_t idx_stride, int32_t* __restrict__ n_idx) {
+  __shared__ SelectLds sh;
+  __shared__ __align__(16) float s_bsum[kMaxSelBlocks];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int L = min(max(seq_lens[b], 0), max_ctx);
+  const int nb = (L + block - 1) / block;
+  int32_t* out = idx + (size_t)b * idx_stride;
+  if (nb <= k_blocks) {
+    for (int j = tid; j < L; j += kThreadsTk) out[j] = j;
+    if (tid == 0) n_idx[b] = L;
+    return;
+  }
+  // forced blocks: [0, s_end) hold the sinks, [w_start, nb) the window
+  const int s_end = min((n_sink + block - 1) / block, nb);
+  const int w_start = window > 0 ? max(s_end, max(0, L - window) / block) : nb;
+  const int r = k_blocks - (s_end + (nb - w_start));  // >= 0: checked on the host
+  const int head_pos = min(L, s_end * block), tail0 = w_start * block;
+  const int tail_pos = w_start < nb ? L - tail0 : 0;
+
+  if (r > 0) {
+    // block sums (members below L only), float32 in position order
+    const float* sc = scores + (size_t)b * max_ctx;
+    for (int i = tid; i < nb; i += kThreadsTk) {
+      const int j0 = i * block, j1 = min(L, j0 + block);
+      float sum = 0.f;
+      if (VEC && j1 - j0 == block) {
+        for (int j = j0; j < j1; j += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(sc + j);
+          sum += x.x; sum += x.y; sum += x.z; sum += x.w;
+        }
+      } else {
+        for (int j = j0; j < j1; ++j) sum += sc[j];
+      }
+      s_bsum[i] = sum;
+    }
+    sh.taken[tid] = 0u;  // one round: word t holds blocks 32t .. 32t + 31
+    sh.in_bin[tid] = 0u;
+    select_stage<true, false>(sh, s_bsum, kMaxSelBlocks, 1, s_end, w_start, (uint32_t)r);
+  } else {
+    sh.taken[tid] = 0u;
+    __syncthreads();
+  }
+
+  // Ordered emit: sink positions ++ the chosen middle blocks' positions ++
+  // window positions.  Thread t owns the 32 blocks of bitmap word t.
+  const uint32_t word = sh.taken[tid];
+  uint32_t n_mine = 0u, mid_total;
+  for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
+    const int blk = 32 * tid + __builtin_ctz(bits);
+    n_mine += (uint32_t)(min(L, blk * block + block) - blk * block);
+  }
+  uint32_t o = block_exclusive_scan(n_mine, sh.s_wave, mid_total) + (uint32_t)head_pos;
+  for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
+    const int blk = 32 * tid + __builtin_ctz(bits);
+    for (int j = blk * block; j < min(L, blk * block + block); ++j)
+      if (o < (uint32_t)idx_stride) out[o++] = j;
+  }
+  const int n_total = head_pos + (int)mid_total + tail_pos;
+  for (int i = tid; i < head_pos; i += kThreadsTk)
+    if (i < idx_stride) out[i] = i;
+  for (int i = tid; i < tail_pos; i += kThreadsTk)
+    if (head_pos + (int)mid_total + i < idx_stride) out[head_pos + mid_total + i] = tail0 + i;
+  if (tid == 0) n_idx[b] = min(n_total, idx_stride);
+}
+
 }  // namespace
 
 hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
@@ -558,6 +637,23 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
     hipLaunchKernelGGL(select_topk_large_kernel, grid, block, 0, stream, max_ctx, scores, seq_lens,
                        k, n_sink, window, idx, idx_stride, n_idx);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
+                                const int32_t* seq_lens, int32_t k_blocks, int32_t block,
+                                int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
+                                int32_t* n_idx, hipStream_t stream) {
+  if ((max_ctx + block - 1) / block > kMaxSelBlocks) return hipErrorInvalidValue;
+  const bool vec = max_ctx % 4 == 0 && block % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  const dim3 grid(batch), block_dim(kThreadsTk);
+  if (vec)
+    hipLaunchKernelGGL(select_blocks_kernel<true>, grid, block_dim, 0, stream, max_ctx, scores,
+                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx);
+  else
+    hipLaunchKernelGGL(select_blocks_kernel<false>, grid, block_dim, 0, stream, max_ctx, scores,
+                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -200,6 +200,15 @@ def test_aggregate_and_select_argument_checks(lib):
     assert H(2, 100, FAKE, FAKE, FAKE, 8, 2, 2, 2, FAKE, 7, FAKE, None) == INVALID    # idx_stride < k
     assert H(2, 100, FAKE, FAKE, FAKE, 0, 0, 0, 0, FAKE, 8, FAKE, None) == INVALID    # k < 1
     assert H(2, 262145, FAKE, FAKE, FAKE, 8, 2, 2, 2, FAKE, 8, FAKE, None) == UNSUPPORTED
+    K = lib.vgsa_select_blocks
+    assert K(0, 100, FAKE, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None) == OK        # empty batch
+    assert K(2, 100, FAKE, FAKE, 8, 0, 4, 16, FAKE, 128, FAKE, None) == INVALID     # block < 1
+    assert K(2, 100, FAKE, FAKE, 8, 2048, 4, 16, FAKE, 16384, FAKE, None) == INVALID  # block > 1024
+    assert K(2, 100, FAKE, FAKE, 2, 16, 4, 16, FAKE, 128, FAKE, None) == INVALID    # 1 + 1 + 1 > 2
+    assert K(2, 100, FAKE, FAKE, 3, 16, 4, 16, FAKE, 47, FAKE, None) == INVALID     # idx_stride < 48
+    assert K(2, 100, None, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None) == INVALID
+    assert K(2, 100, FAKE, FAKE, 8, 16, -1, 16, FAKE, 128, FAKE, None) == INVALID
+    assert K(2, 16 * 8704 + 1, FAKE, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None) == UNSUPPORTED
 
 
 def test_append_argument_checks(lib):

@@ -306,6 +306,74 @@ def test_hybrid_select_on_verify_scores(name):
     assert_lse_close(lse, lse_ref, f"{name} hybrid sparse lse")
 
 
+# ------------------------------------------------------------------ block selection
+def _blocks_case(scores_h, lens, kb, block, n_sink, window, stride=None):
+    scores = torch.from_numpy(np.ascontiguousarray(scores_h, dtype=np.float32)).cuda()
+    idx, n = Bn.select_blocks(scores, dev_i32(lens), kb, block, n_sink, window,
+                              idx_stride=stride or kb * block)
+    torch.cuda.synchronize()
+    idx_h, n_h = idx.cpu().numpy(), n.cpu().numpy()
+    out = []
+    for b, L in enumerate(lens):
+        want = oracle.select_blocks(scores_h[b], int(L), kb, block, n_sink, window)
+        assert n_h[b] == len(want), (b, L, kb, block, n_h[b], len(want))
+        assert np.array_equal(idx_h[b, :n_h[b]], want), (b, L, kb, block, n_sink, window)
+        out.append(want)
+    return idx, n, out
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 1000, 4100, 32768, 40001, 131072])
+def test_select_blocks_random(L):
+    """Whole-block selection against the oracle: block sizes 16, 8, 4 and 5
+    (unaligned rows read 4 bytes at a time), partial last blocks, sinks and
+    windows that end mid-block, a budget covering every block."""
+    say(f"[select blocks] L={L}")
+    rng = np.random.default_rng(500 + L)
+    for ctx in ((L + 15) // 16 * 16, L + 3):
+        lens = [L, max(1, L // 3), max(1, L - 5)]
+        sc = rng.standard_normal((3, ctx)).astype(np.float32) * 10
+        for block, kb, ns, win in [(16, 32, 4, 64), (16, 8, 0, 0), (8, 64, 4, 100), (4, 410, 10, 256),
+                                   (5, 20, 3, 7), (16, 8192, 4, 256)]:
+            if -(-ctx // block) > 8704:
+                continue
+            _blocks_case(sc, lens, kb, block, ns, win)
+
+
+def test_select_blocks_ties_and_infinities():
+    rng = np.random.default_rng(23)
+    ctx = 6000
+    sc = rng.integers(-2, 3, size=(4, ctx)).astype(np.float32)   # block-sum ties
+    sc[1] = 0.0
+    sc[1, ::2] = -0.0                                            # all sums +-0: lowest blocks win
+    sc[2, ::37] = -np.inf                                        # -inf sinks whole blocks
+    sc[3] = 1.0
+    lens = [6000, 5999, 5001, 4096]
+    for block, kb, ns, win in [(16, 40, 4, 64), (16, 200, 0, 0), (32, 10, 33, 31), (1, 300, 4, 16)]:
+        _blocks_case(sc, lens, kb, block, ns, win)
+
+
+@pytest.mark.parametrize("name", ["paged_g8t6_d64", "ctx2k_b1_h32kv8_d128", "g4t4_d128_ragged"])
+def test_select_blocks_on_verify_scores_then_sparse(name):
+    """Block selection on the verify pass's own scores, then sparse attention
+    over the kept blocks' positions (contiguous runs; with a paged cache a
+    16-position block is one page)."""
+    w = CASES[name]
+    say(f"[block pipeline] {name}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    _, _, lg = run_verify(d, w, "kvgroup_sum")
+    sc = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads)
+    kb = max(3, w.budget // 16)
+    torch.cuda.synchronize()
+    idx, n, want = _blocks_case(sc.cpu().numpy(), list(x.seq_lens), kb, 16, w.n_sink, w.window)
+    out, lse = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n, block_table=d.block_table,
+                                   max_ctx=d.max_ctx)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, x.seq_lens, want)
+    assert_out_close(out, o_ref, f"{name} block sparse out")
+    assert_lse_close(lse, lse_ref, f"{name} block sparse lse")
+
+
 def test_determinism_bitwise():
     w = CASES["g8t5_d128"]
     x = W.make_layer(w)
