@@ -221,7 +221,7 @@ def main():
     stride = (k_blocks * BLK if args.select == "blocks" else w.budget) + w.draft_steps
     idx = torch.empty((B, stride), dtype=torch.int32, device=dev)
     n_idx = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws_s = torch.empty(Bn.sparse_workspace_bytes(desc, stride), dtype=torch.uint8, device=dev)
+    ws_s = torch.zeros(Bn.sparse_workspace_bytes(desc, stride), dtype=torch.uint8, device=dev)
     out_s = torch.empty_like(out)
     lse_s = torch.empty_like(lse)
     # draft steps: step s attends with one fresh query per head over the
@@ -231,7 +231,7 @@ def main():
     lens_draft = [(lens + s).contiguous() for s in range(1, n_draft + 1)]
     if n_draft:
         desc_d = Bn.make_desc(q_draft[0], k, bt, max_ctx)
-        ws_d = torch.empty(Bn.sparse_workspace_bytes(desc_d, stride), dtype=torch.uint8, device=dev)
+        ws_d = torch.zeros(Bn.sparse_workspace_bytes(desc_d, stride), dtype=torch.uint8, device=dev)
         out_d = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=dev)
         lse_d = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
 
@@ -360,7 +360,7 @@ def main():
         lambda: Bn.select_blocks(scores, lens, k_blocks, BLK, w.n_sink, w.window, idx=idx_b, n_idx=n_b))
     sparse_blocks_us = None
     if w.sparse_verify:
-        ws_b = torch.empty(Bn.sparse_workspace_bytes(desc, k_blocks * BLK), dtype=torch.uint8, device=dev)
+        ws_b = torch.zeros(Bn.sparse_workspace_bytes(desc, k_blocks * BLK), dtype=torch.uint8, device=dev)
         sparse_blocks_us = per_launch_us(
             lambda: Bn.sparse_attention(q, k, v, lens, idx_b, n_b, block_table=bt, max_ctx=max_ctx,
                                         out=out_s, lse=lse_s, workspace=ws_b))

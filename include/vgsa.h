@@ -136,7 +136,12 @@ vgsa_status vgsa_split_plan(const vgsa_attn_desc* desc, int32_t span, int32_t* n
  * this desc (partial outputs of every split).  0 on an invalid desc. */
 size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc);
 
-/* Workspace bytes needed by vgsa_sparse_attention / vgsa_sparse_partials. */
+/* Workspace bytes needed by vgsa_sparse_attention / vgsa_sparse_partials.
+ * vgsa_sparse_attention keeps per-(sequence, kv-head) counters in the last
+ * ceil(B * Hkv * 4 / 256) * 256 of these bytes: they must be zero when the
+ * workspace is first used (allocate it zero-filled), and every call leaves
+ * them zero.  Other calls (vgsa_sparse_partials, the verify calls) must not
+ * be given that part of the buffer. */
 size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_stride);
 
 /* ------------------------------------------------------------------------ */
@@ -266,6 +271,11 @@ vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scor
  *          positions, e.g. freshly drafted tokens, keeping the row ascending)
  * seq_lens L'_b for the causal rule: row t sees listed j <= L'_b - T' + t.
  *          A row that sees no listed position gets out = 0, lse = -inf.
+ * workspace  >= vgsa_sparse_workspace_bytes(desc, idx_stride) bytes, its
+ *          counter part zero on first use (see there).  One launch: the list
+ *          is split over several workgroups per (sequence, kv-head), and the
+ *          last of them to finish merges their partial results.  Calls that
+ *          share a workspace must not overlap.
  * Other arguments as in vgsa_verify_attention.
  */
 vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,

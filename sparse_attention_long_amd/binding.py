@@ -148,7 +148,8 @@ def sparse_workspace_bytes(desc: AttnDesc, idx_stride: int) -> int:
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
     if workspace is None:
-        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        # zero-filled: the one-call sparse path keeps self-resetting counters in it
+        return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
     _need(workspace, "workspace", torch.uint8)
     return workspace
 

@@ -8,6 +8,10 @@
 
 namespace vgsa {
 
+size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p);
+size_t sparse_sync_offset(const vgsa_attn_desc& d, int32_t idx_stride);
+size_t sparse_sync_bytes(const vgsa_attn_desc& d);
+
 namespace {
 
 constexpr int64_t kMaxGridYZ = 65535;
@@ -152,6 +156,16 @@ size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p) {
   return kHeaderBytes + (o_bytes + 255) / 256 * 256 + rows * 2 * 4;
 }
 
+// The sparse workspace: the partials, then the fused merge's arrival
+// counters (one int32 per (sequence, kv-head)).
+size_t sparse_sync_offset(const vgsa_attn_desc& d, int32_t idx_stride) {
+  return (partial_bytes(d, make_plan(d.batch, d.num_kv_heads, idx_stride)) + 255) / 256 * 256;
+}
+
+size_t sparse_sync_bytes(const vgsa_attn_desc& d) {
+  return ((size_t)d.batch * d.num_kv_heads * 4 + 255) / 256 * 256;
+}
+
 }  // namespace vgsa
 
 using namespace vgsa;
@@ -189,7 +203,7 @@ size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc) {
 
 size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_stride) {
   if (check_desc(desc) != VGSA_OK || idx_stride < 1) return 0;
-  return partial_bytes(*desc, make_plan(desc->batch, desc->num_kv_heads, idx_stride));
+  return sparse_sync_offset(*desc, idx_stride) + sparse_sync_bytes(*desc);
 }
 
 }  // extern "C"
@@ -243,15 +257,19 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
                           const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                           const int32_t* idx, const int32_t* n_idx, int32_t idx_stride,
                           void* workspace, size_t workspace_bytes, void* out, float* lse,
-                          void* stream) {
+                          bool fused, void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
   st = check_attn_pointers(d, q, k_cache, v_cache, block_table, seq_lens);
   if (st != VGSA_OK) return st;
   if (idx == nullptr || n_idx == nullptr || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
+  // one split for lists up to kDirectSpan (the output is written directly);
+  // longer lists split, and with `fused` the splits merge in the same launch
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, idx_stride);
-  st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
+  const size_t need = fused ? sparse_sync_offset(d, idx_stride) + sparse_sync_bytes(d)
+                            : partial_bytes(d, p);
+  st = check_workspace(workspace, workspace_bytes, need);
   if (st != VGSA_OK) return st;
   if (d.batch == 0) return VGSA_OK;
   AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens, workspace);
@@ -260,7 +278,13 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   a.idx_stride = idx_stride;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.direct = out != nullptr ? 1 : 0;
+  // one call: a single split writes the output itself, several merge in the launch
+  a.direct = (out != nullptr && p.num_splits == 1) ? 1 : 0;
+  if (fused && p.num_splits > 1) {
+    a.fuse = 1;
+    a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                        sparse_sync_offset(d, idx_stride));
+  }
   return hip_status(launch_attention_partials(a, true, static_cast<hipStream_t>(stream)));
 }
 
@@ -285,7 +309,7 @@ vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, cons
                                  const int32_t* n_idx, int32_t idx_stride, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
-                       workspace, workspace_bytes, nullptr, nullptr, stream);
+                       workspace, workspace_bytes, nullptr, nullptr, false, stream);
 }
 
 vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
@@ -350,16 +374,9 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   if (out == nullptr || !aligned(out, 16) || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
-  const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, idx_stride);
-  if (p.num_splits == 1) {
-    return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
-                         workspace, workspace_bytes, out, lse, stream);
-  }
-  st = sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
-                     workspace, workspace_bytes, nullptr, nullptr, stream);
-  if (st != VGSA_OK) return st;
-  return vgsa_combine_partials(desc, idx_stride, n_idx, workspace, workspace_bytes, out, lse,
-                               stream);
+  // one launch: the splits of a (sequence, kv-head) merge in the same kernel
+  return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
+                       workspace, workspace_bytes, out, lse, true, stream);
 }
 
 vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,

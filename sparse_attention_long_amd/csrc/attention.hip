@@ -190,7 +190,9 @@ void attn_partials_kernel(AttnArgs a) {
   // group (q-head g*G + hh, query t) is row row_base + m.
   const size_t row_base = ((size_t)b * a.hq + (size_t)g * G) * T;
   if (start >= count) {  // whole workgroup: nothing in this split
-    if (a.direct) {      // the only split: the rows see nothing -> o = 0, lse = -inf
+    // the only split, or (fused merge) an empty list that no workgroup
+    // merges: the rows see nothing -> o = 0, lse = -inf
+    if (a.direct || (a.fuse && split == 0)) {
       for (int e = threadIdx.x; e < rows * D; e += NT) a.out[row_base * D + e] = 0;
       if (a.lse != nullptr && (int)threadIdx.x < rows) a.lse[row_base + threadIdx.x] = kNegInf;
     }
@@ -689,10 +691,13 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) acc += obuf[(w * RP + m) * CS + dc];
       const int d = r * DC + dc;
+      float* dst = a.part_o + ((row_base + m) * S + split) * D + d;
       if (a.direct)
         a.out[(row_base + m) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc * s_inv[m]));
-      else  // written once, read once
-        __builtin_nontemporal_store(acc, a.part_o + ((row_base + m) * S + split) * D + d);
+      else if (SPARSE && a.fuse)  // read back in this launch, maybe from another XCD
+        __hip_atomic_store(dst, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else  // written once, read once (next launch)
+        __builtin_nontemporal_store(acc, dst);
     }
     __syncthreads();
   }
@@ -702,8 +707,48 @@ void attn_partials_kernel(AttnArgs a) {
         a.lse[row_base + threadIdx.x] = rowL > 0.f ? (rowM + __log2f(rowL)) * kLn2 : kNegInf;
     } else {
       const size_t prow = (row_base + threadIdx.x) * S + split;
-      a.part_ml[prow * 2 + 0] = rowM;
-      a.part_ml[prow * 2 + 1] = rowL;
+      if (SPARSE && a.fuse) {
+        __hip_atomic_store(a.part_ml + prow * 2 + 0, rowM, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.part_ml + prow * 2 + 1, rowL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        a.part_ml[prow * 2 + 0] = rowM;
+        a.part_ml[prow * 2 + 1] = rowL;
+      }
+    }
+  }
+
+  if (SPARSE && a.fuse) {
+    // Fused merge: every non-empty split of this (sequence, kv-head) counts
+    // itself in once its partials are out; the one that completes the count
+    // merges them all (no workgroup waits on another).  The partials were
+    // stored with device scope (write-through, no cache-wide flush needed);
+    // every thread waits for its stores to complete before the count, and
+    // the merging workgroup reads them with device-scope loads after it.
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int nvalid = (count + chunk - 1) / chunk;
+      int* ctr = a.sync + (size_t)b * a.hkv + g;
+      const int done = atomicAdd(ctr, 1) + 1;
+      s_last = done == nvalid;
+      if (done == nvalid) atomicExch(ctr, 0);  // every split has counted: ready for the next call
+    }
+    __syncthreads();
+    if (s_last) {
+      CombineArgs c{};
+      c.part_o = a.part_o;
+      c.part_ml = a.part_ml;
+      c.lengths = a.n_idx;
+      c.rows_per_seq = a.hq * T;
+      c.span = a.idx_stride;
+      c.chunk = chunk;
+      c.part_splits = S;
+      c.out = a.out;
+      c.lse = a.lse;
+      constexpr int Q = D / 4;
+      for (int e = threadIdx.x; e < rows * Q; e += NT)
+        combine_quad<D, true>(c, (int)row_base + e / Q, e % Q, chunk);
     }
   }
 }

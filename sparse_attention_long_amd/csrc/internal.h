@@ -81,9 +81,15 @@ struct AttnArgs {
   int32_t* header;   // the launch records its item length in header[0]
   int32_t part_splits;
   int32_t balance;   // shrink items to the lengths (verify, several sequences)
-  uint16_t* out;     // direct mode (one split): final bf16 output ...
+  uint16_t* out;     // direct mode (one split) or fused merge: final bf16 output ...
   float* lse;        // ... and lse (may be null)
   int32_t direct;
+  // Fused merge (sparse, several splits): the last workgroup of a (sequence,
+  // kv-head) to finish merges the splits' partials into out / lse.  sync[b *
+  // hkv + g] counts the finished workgroups; zero before the launch, and the
+  // merging workgroup sets it back to zero.
+  int32_t* sync;
+  int32_t fuse;
   int32_t batch, hq, hkv, group, q_len, head_dim;
   int32_t max_ctx, paged, max_blocks, num_blocks;
   int32_t num_splits, chunk;

@@ -19,15 +19,16 @@ constexpr int kMergeBatch = 8;
 // the row sees nothing of has m_s = -inf and is skipped.  Splits are merged
 // kMergeBatch at a time, each batch rescaled to its running maximum, in split
 // order (with at most kMergeBatch splits this is the plain two-pass sum).
-template <int D>
-__device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int t) {
+// `chunk`: the item length the partials were made with.  COHERENT: the
+// partials were written in the same launch by other workgroups (possibly on
+// another XCD, whose L2 this one's does not see): read them with device-scope
+// loads, which bypass stale cache lines.
+template <int D, bool COHERENT = false>
+__device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int t, int chunk) {
   constexpr float kNegInf = -__builtin_huge_valf();
   constexpr int Q = D / 4;
   const int b = row / a.rows_per_seq;
   const int len = min(max(a.lengths[b], 0), a.span);
-  // the item length the partials were made with (clamped: the header only
-  // ever narrows the plan's chunk)
-  const int chunk = min(max(a.header[0], kMinChunk), a.chunk);
   const int nvalid = min((len + chunk - 1) / chunk, a.part_splits);
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)row * a.part_splits;
   const float4* po = reinterpret_cast<const float4*>(a.part_o) + (size_t)row * a.part_splits * Q + t;
@@ -39,8 +40,19 @@ __device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int 
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       if (s0 + i < nvalid) {
-        m[i] = ml[s0 + i];
-        o[i] = po[(size_t)(s0 + i) * Q];
+        if (COHERENT) {
+          const float* mp = reinterpret_cast<const float*>(ml + s0 + i);
+          const float* op = reinterpret_cast<const float*>(po + (size_t)(s0 + i) * Q);
+          m[i].x = __hip_atomic_load(mp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          m[i].y = __hip_atomic_load(mp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          o[i].x = __hip_atomic_load(op, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          o[i].y = __hip_atomic_load(op + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          o[i].z = __hip_atomic_load(op + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          o[i].w = __hip_atomic_load(op + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          m[i] = ml[s0 + i];
+          o[i] = po[(size_t)(s0 + i) * Q];
+        }
       } else {
         m[i] = make_float2(kNegInf, 0.f);
         o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -77,7 +89,10 @@ template <int D>
 __device__ __forceinline__ void combine_block(const CombineArgs& a, int block) {
   constexpr int Q = D / 4;
   const int row = block * (kMergeBlock / Q) + threadIdx.x / Q;
-  if (row < a.rows) combine_quad<D>(a, row, threadIdx.x % Q);
+  // the item length the partials were made with (clamped: the header only
+  // ever narrows the plan's chunk)
+  const int chunk = min(max(a.header[0], kMinChunk), a.chunk);
+  if (row < a.rows) combine_quad<D>(a, row, threadIdx.x % Q, chunk);
 }
 
 template <int D>

@@ -170,7 +170,7 @@ def test_sparse_and_combine_argument_checks(lib):
     assert F(ctypes.byref(desc(head_dim=96)), FAKE, FAKE, wv, FAKE, None, 2, 2, 0, FAKE, FAKE, None) == UNSUPPORTED
     assert C(dp, 64, None, FAKE, ws, FAKE, None, None) == INVALID
     assert C(dp, 64, FAKE, FAKE, ws, None, None, None) == INVALID
-    assert C(dp, 64, FAKE, FAKE, ws - 1, FAKE, None, None) == WORKSPACE
+    assert C(dp, 64, FAKE, FAKE, 256, FAKE, None, None) == WORKSPACE  # header only
 
 
 def test_aggregate_and_select_argument_checks(lib):

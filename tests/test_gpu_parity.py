@@ -431,6 +431,48 @@ def test_two_phase_api_matches_one_call(name):
     np.testing.assert_allclose(sl2.cpu().numpy(), sl1.cpu().numpy(), atol=1e-5)
 
 
+@pytest.mark.parametrize("name", ["g4t5_d64", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])
+def test_sparse_one_launch_merge_repeats_and_resets(name):
+    """The one-call sparse path splits each list over several workgroups and
+    the last one to finish merges them: repeated calls on one workspace give
+    the oracle's result each time (empty, short and full lists mixed), the
+    counters are zero after every call, and the result matches the two-phase
+    partials + combine form."""
+    w = CASES[name]
+    say(f"[sparse one-launch merge] {name}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    desc = Bn.make_desc(d.q, d.k, d.block_table, d.max_ctx)
+    stride = 3000  # longer than one split: the splits merge in the launch
+    nbytes = Bn.sparse_workspace_bytes(desc, stride)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sync_bytes = -(-w.batch * w.num_kv_heads * 4 // 256) * 256
+    for rep, count in enumerate([stride, 5, 0, 1500, stride]):
+        idx, n = W.index_lists(w.seed + 40 + rep, x.seq_lens, count=count, stride=stride)
+        if rep == 3:
+            n[0] = 0  # one empty list among full ones
+        out, lse = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, dev_i32(idx), dev_i32(n),
+                                       block_table=d.block_table, max_ctx=d.max_ctx, workspace=ws)
+        torch.cuda.synchronize()
+        lists = [idx[b, :n[b]] for b in range(w.batch)]
+        o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, x.seq_lens, lists)
+        assert_out_close(out, o_ref, f"{name} rep {rep} out")
+        assert_lse_close(lse, lse_ref, f"{name} rep {rep} lse")
+        assert int(ws[nbytes - sync_bytes:].count_nonzero()) == 0, "counters not reset"
+    # the two-phase form on its own workspace agrees
+    ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    idx_d, n_d = dev_i32(idx), dev_i32(n)
+    Bn.sparse_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, idx_d, n_d, ws2)
+    o2, l2 = torch.empty_like(out), torch.empty_like(lse)
+    Bn.combine_partials(desc, stride, n_d, ws2, o2, l2)
+    torch.cuda.synchronize()
+    # different split plans: the fp32 merge order differs, so a bf16 output
+    # may round one unit apart
+    np.testing.assert_allclose(o2.float().cpu().numpy(), out.float().cpu().numpy(), atol=8e-3,
+                               rtol=1e-2)
+    np.testing.assert_allclose(l2.cpu().numpy(), lse.cpu().numpy(), atol=1e-5)
+
+
 @pytest.mark.parametrize("count,stride", [(1000, 1000), (3000, 3000), (700, 1024)])
 def test_sparse_long_lists_many_tiles_per_wavefront(count, stride):
     """Lists long enough that every wavefront walks several tiles (one split
