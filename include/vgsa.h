@@ -136,7 +136,8 @@ vgsa_status vgsa_split_plan(const vgsa_attn_desc* desc, int32_t span, int32_t* n
  * this desc (partial outputs of every split).  0 on an invalid desc. */
 size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc);
 
-/* Workspace bytes needed by vgsa_sparse_attention / vgsa_sparse_partials.
+/* Workspace bytes needed by vgsa_sparse_attention / vgsa_sparse_partials
+ * (idx_stride: the list capacity, plus the tail of vgsa_sparse_attention).
  * vgsa_sparse_attention keeps per-(sequence, kv-head) counters in the last
  * ceil(B * Hkv * 4 / 256) * 256 of these bytes: they must be zero when the
  * workspace is first used (allocate it zero-filled), and every call leaves
@@ -269,20 +270,25 @@ vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scor
  * desc->q_len is T' (1 for a draft step, gamma + 1 for a sparse verify).
  * idx, n_idx, idx_stride  as written by vgsa_select_topk (a caller may append
  *          positions, e.g. freshly drafted tokens, keeping the row ascending)
+ * tail     >= 0: the last min(tail, L'_b) positions below L'_b are attended
+ *          too, after the listed ones (the tokens drafted since the selection,
+ *          without appending them to the lists); listed positions must lie
+ *          below L'_b - tail.  0: the list alone.
  * seq_lens L'_b for the causal rule: row t sees listed j <= L'_b - T' + t.
  *          A row that sees no listed position gets out = 0, lse = -inf.
- * workspace  >= vgsa_sparse_workspace_bytes(desc, idx_stride) bytes, its
- *          counter part zero on first use (see there).  One launch: the list
- *          is split over several workgroups per (sequence, kv-head), and the
- *          last of them to finish merges their partial results.  Calls that
- *          share a workspace must not overlap.
+ * workspace  >= vgsa_sparse_workspace_bytes(desc, idx_stride + tail) bytes,
+ *          its counter part zero on first use (see there).  One launch: a
+ *          long list is split over several workgroups per (sequence,
+ *          kv-head), and the last of them to finish merges their partial
+ *          results.  Calls that share a workspace must not overlap.
  * Other arguments as in vgsa_verify_attention.
  */
 vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, const int32_t* idx,
-                                  const int32_t* n_idx, int32_t idx_stride, void* out, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream);
+                                  const int32_t* n_idx, int32_t idx_stride, int32_t tail,
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Draft steps: append consecutive positions to index lists.
  *    (Vegas section 2 step 3: each drafting step attends over the selected

@@ -50,7 +50,7 @@ SIGNATURES = {
     "vgsa_select_blocks": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32,
                                    c_vp, c_vp]),
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                      c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+                                      c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
                                      c_u64, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_sparse_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -307,8 +307,9 @@ def select_blocks(scores, seq_lens, k_blocks: int, block: int, n_sink: int, wind
 
 
 def sparse_attention(q, k_cache, v_cache, seq_lens, idx, n_idx, *, block_table=None, max_ctx=None,
-                     out=None, lse=None, workspace=None, scale: float = 0.0):
-    """vgsa_sparse_attention.  Returns (out bf16 [B,Hq,T',d], lse fp32 [B,Hq,T'])."""
+                     tail: int = 0, out=None, lse=None, workspace=None, scale: float = 0.0):
+    """vgsa_sparse_attention.  Returns (out bf16 [B,Hq,T',d], lse fp32 [B,Hq,T']).
+    `tail`: the last `tail` positions below each length are attended after the list."""
     _check_attn(q, k_cache, v_cache, seq_lens, block_table)
     _need(idx, "idx", torch.int32, 2)
     _need(n_idx, "n_idx", torch.int32, 1)
@@ -319,10 +320,10 @@ def sparse_attention(q, k_cache, v_cache, seq_lens, idx, n_idx, *, block_table=N
         out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
-    ws = _workspace(sparse_workspace_bytes(desc, idx.shape[1]), dev, workspace)
+    ws = _workspace(sparse_workspace_bytes(desc, idx.shape[1] + tail), dev, workspace)
     _check(load().vgsa_sparse_attention(
         ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens), _p(idx),
-        _p(n_idx), idx.shape[1], _p(out), _p(lse), _p(ws), ws.numel(), _stream(dev)),
+        _p(n_idx), idx.shape[1], tail, _p(out), _p(lse), _p(ws), ws.numel(), _stream(dev)),
         "vgsa_sparse_attention")
     return out, lse
 

@@ -256,18 +256,21 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
 vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                           const int32_t* idx, const int32_t* n_idx, int32_t idx_stride,
-                          void* workspace, size_t workspace_bytes, void* out, float* lse,
-                          bool fused, void* stream) {
+                          int32_t tail, void* workspace, size_t workspace_bytes, void* out,
+                          float* lse, bool fused, void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
   st = check_attn_pointers(d, q, k_cache, v_cache, block_table, seq_lens);
   if (st != VGSA_OK) return st;
-  if (idx == nullptr || n_idx == nullptr || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
+  if (idx == nullptr || n_idx == nullptr || idx_stride < 1 || tail < 0) return VGSA_ERR_INVALID_ARG;
+  if ((int64_t)idx_stride + tail > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
+  // entries: up to idx_stride listed, then the trailing positions
+  const int32_t span = idx_stride + tail;
   // one split for lists up to kDirectSpan (the output is written directly);
   // longer lists split, and with `fused` the splits merge in the same launch
-  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, idx_stride);
-  const size_t need = fused ? sparse_sync_offset(d, idx_stride) + sparse_sync_bytes(d)
+  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, span);
+  const size_t need = fused ? sparse_sync_offset(d, span) + sparse_sync_bytes(d)
                             : partial_bytes(d, p);
   st = check_workspace(workspace, workspace_bytes, need);
   if (st != VGSA_OK) return st;
@@ -276,6 +279,7 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   a.idx = idx;
   a.n_idx = n_idx;
   a.idx_stride = idx_stride;
+  a.tail = tail;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   // one call: a single split writes the output itself, several merge in the launch
@@ -283,7 +287,7 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   if (fused && p.num_splits > 1) {
     a.fuse = 1;
     a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                        sparse_sync_offset(d, idx_stride));
+                                        sparse_sync_offset(d, span));
   }
   return hip_status(launch_attention_partials(a, true, static_cast<hipStream_t>(stream)));
 }
@@ -309,7 +313,7 @@ vgsa_status vgsa_sparse_partials(const vgsa_attn_desc* desc, const void* q, cons
                                  const int32_t* n_idx, int32_t idx_stride, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
-                       workspace, workspace_bytes, nullptr, nullptr, false, stream);
+                       0, workspace, workspace_bytes, nullptr, nullptr, false, stream);
 }
 
 vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
@@ -369,14 +373,15 @@ vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, con
 vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, const int32_t* idx,
-                                  const int32_t* n_idx, int32_t idx_stride, void* out, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+                                  const int32_t* n_idx, int32_t idx_stride, int32_t tail, void* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   if (out == nullptr || !aligned(out, 16) || idx_stride < 1) return VGSA_ERR_INVALID_ARG;
   // one launch: the splits of a (sequence, kv-head) merge in the same kernel
   return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
-                       workspace, workspace_bytes, out, lse, true, stream);
+                       tail, workspace, workspace_bytes, out, lse, true, stream);
 }
 
 vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,

@@ -184,7 +184,11 @@ void attn_partials_kernel(AttnArgs a) {
     if (SPARSE && lane < kTile && a.paged)
       blk_pre[i] = btab[min(max(idx_pre[i], 0), max(L - 1, 0)) >> 4];
   }
-  const int count = SPARSE ? min(max(a.n_idx[b], 0), a.idx_stride) : L;
+  // sparse: the listed entries, then (virtually) the last `tail` positions
+  // below L, e.g. the tokens drafted since the selection
+  const int nlist = SPARSE ? min(max(a.n_idx[b], 0), a.idx_stride) : 0;
+  const int tail = SPARSE ? min(a.tail, L) : 0;
+  const int count = SPARSE ? nlist + tail : L;
   const int G = a.group, T = a.q_len, rows = G * T;
   // Rows [B][Hq][T] of this kv-group are contiguous: row m = hh*T + t of the
   // group (q-head g*G + hh, query t) is row row_base + m.
@@ -271,17 +275,20 @@ void attn_partials_kernel(AttnArgs a) {
     if (SPARSE) {
       if (lane < kTile) {
         const int li = t0 + lane;
+        const bool listed = li < nlist;
         int p = 0;
-        if (li < end) {
+        if (listed) {
           p = it == 0 ? idx_pre[0] : it == 1 ? idx_pre[1] : it == 2 ? idx_pre[2]
             : it == 3 ? idx_pre[3] : a.idx[(size_t)b * a.idx_stride + li];
+        } else if (li < end) {
+          p = L - tail + (li - nlist);  // a trailing position
         }
         p = min(max(p, 0), max(L - 1, 0));
         sidx[lane] = p;
         uint32_t off = (uint32_t)p * D;
         if (a.paged) {
-          int blk = it == 0 ? blk_pre[0] : it == 1 ? blk_pre[1] : it == 2 ? blk_pre[2]
-                  : it == 3 ? blk_pre[3] : btab[p >> 4];
+          int blk = !listed ? btab[p >> 4] : it == 0 ? blk_pre[0] : it == 1 ? blk_pre[1]
+                  : it == 2 ? blk_pre[2] : it == 3 ? blk_pre[3] : btab[p >> 4];
           if (li >= end) blk = 0;  // entries past the list: any in-range row will do
           blk = min(max(blk, 0), a.num_blocks - 1);
           off = (((uint32_t)blk * a.hkv + g) * 16u + (uint32_t)(p & 15)) * D;
@@ -740,6 +747,7 @@ void attn_partials_kernel(AttnArgs a) {
       c.part_o = a.part_o;
       c.part_ml = a.part_ml;
       c.lengths = a.n_idx;
+      c.tail = tail;
       c.rows_per_seq = a.hq * T;
       c.span = a.idx_stride;
       c.chunk = chunk;

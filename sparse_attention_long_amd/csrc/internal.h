@@ -70,6 +70,7 @@ struct AttnArgs {
   const int32_t* idx;    // sparse only
   const int32_t* n_idx;  // sparse only
   int32_t idx_stride;
+  int32_t tail;          // sparse: the last `tail` positions below the length follow the list
   float* logits;         // verify only, may be null
   int32_t layout;
   uint32_t row_mask;  // collected rows: bit t set for query row t
@@ -111,6 +112,7 @@ struct CombineArgs {
   const int32_t* header;  // header[0]: the item length the partials were made with
   uint16_t* out;
   float* lse;
+  int32_t tail;           // entries after lengths[b] (sparse trailing positions)
 };
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

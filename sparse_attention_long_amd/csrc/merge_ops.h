@@ -28,7 +28,7 @@ __device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int 
   constexpr float kNegInf = -__builtin_huge_valf();
   constexpr int Q = D / 4;
   const int b = row / a.rows_per_seq;
-  const int len = min(max(a.lengths[b], 0), a.span);
+  const int len = min(max(a.lengths[b], 0), a.span) + a.tail;
   const int nvalid = min((len + chunk - 1) / chunk, a.part_splits);
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)row * a.part_splits;
   const float4* po = reinterpret_cast<const float4*>(a.part_o) + (size_t)row * a.part_splits * Q + t;

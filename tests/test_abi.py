@@ -95,7 +95,7 @@ def test_bad_desc_rejected_everywhere(lib, kw, code):
     d = ctypes.byref(desc(**kw))
     assert lib.vgsa_verify_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, 9, ALL, 2, FAKE, FAKE, None,
                                      FAKE, 1 << 40, None) == code
-    assert lib.vgsa_sparse_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None,
+    assert lib.vgsa_sparse_attention(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0, FAKE, None,
                                      FAKE, 1 << 40, None) == code
     assert lib.vgsa_verify_workspace_bytes(d) == 0
     s, c = ctypes.c_int32(), ctypes.c_int32()
@@ -152,10 +152,11 @@ def test_sparse_and_combine_argument_checks(lib):
     ws = lib.vgsa_sparse_workspace_bytes(dp, 64)
     assert ws > 0 and lib.vgsa_sparse_workspace_bytes(dp, 0) == 0
     S = lib.vgsa_sparse_attention
-    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 64, FAKE, None, FAKE, ws, None) == INVALID
-    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 64, FAKE, None, FAKE, ws, None) == INVALID
-    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, ws, None) == INVALID
-    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 64, 0, FAKE, None, FAKE, ws, None) == INVALID
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 64, 0, FAKE, None, FAKE, ws, None) == INVALID
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, 0, FAKE, None, FAKE, ws, None) == INVALID
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, 0, FAKE, None, FAKE, ws - 1, None) == WORKSPACE
+    assert S(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, -1, FAKE, None, FAKE, ws, None) == INVALID  # tail < 0
     C = lib.vgsa_combine_partials
     assert C(dp, 0, FAKE, FAKE, ws, FAKE, None, None) == INVALID
     F = lib.vgsa_verify_finish

@@ -42,7 +42,7 @@ def test_fullsize_sampled(name):
                                            max_ctx=d.max_ctx, collect_rows=w.collect_rows,
                                            layout="kvgroup_sum")
         scores = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads)
-        stride = w.budget + w.draft_steps
+        stride = w.budget
         idx, n_idx = Bn.select_topk(scores, d.seq_lens, w.budget, w.n_sink, w.window,
                                     idx_stride=stride)
         torch.cuda.synchronize()
@@ -88,15 +88,12 @@ def test_fullsize_sampled(name):
 
         for s in range(1, w.draft_steps + 1):
             say(f"[fullsize] {name} layer {layer}: draft step {s}")
-            # step s: s freshly drafted positions L..L+s-1 are appended to the list
+            # step s: the kept list plus the s positions L..L+s-1 drafted since,
+            # passed as the trailing positions of length L + s (as the benchmark does)
             lists = [np.concatenate([want[b], np.arange(lens[b], lens[b] + s)]) for b in range(w.batch)]
-            idx_s = np.zeros((w.batch, stride), np.int32)
-            for b, li in enumerate(lists):
-                idx_s[b, :len(li)] = li
-            n_s = np.array([len(li) for li in lists], np.int32)
             lens_s = [L + s for L in lens]
             qd = dev_bf16(x.q_draft[s - 1])
-            so, sl = Bn.sparse_attention(qd, d.k, d.v, dev_i32(lens_s), dev_i32(idx_s), dev_i32(n_s),
+            so, sl = Bn.sparse_attention(qd, d.k, d.v, dev_i32(lens_s), idx, n_idx, tail=s,
                                          block_table=d.block_table, max_ctx=d.max_ctx)
             torch.cuda.synchronize()
             for b in bs:

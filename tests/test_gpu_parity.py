@@ -473,6 +473,39 @@ def test_sparse_one_launch_merge_repeats_and_resets(name):
     np.testing.assert_allclose(l2.cpu().numpy(), lse.cpu().numpy(), atol=1e-5)
 
 
+@pytest.mark.parametrize("name", ["g4t5_d64", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])
+@pytest.mark.parametrize("count", [20, 900, 2000])
+def test_sparse_trailing_positions(name, count):
+    """Trailing positions (the tokens drafted since the selection) attended
+    after the list without appending them: against the oracle on the
+    explicit lists, and equal to the appended form; one split and several."""
+    w = CASES[name]
+    say(f"[sparse tail] {name} count={count}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    for tail in (1, 3, 7):
+        lens = np.array([max(int(L) - tail, 1) for L in x.seq_lens], np.int32)  # kept below L - tail
+        idx, n = W.index_lists(w.seed + 70 + tail, lens, count=count, stride=count)
+        lens_t = lens + np.int32(tail)
+        qd = d.q[:, :, :1].contiguous()
+        out, lse = Bn.sparse_attention(qd, d.k, d.v, dev_i32(lens_t), dev_i32(idx), dev_i32(n),
+                                       block_table=d.block_table, max_ctx=d.max_ctx, tail=tail)
+        lists = [np.concatenate([idx[b, :n[b]], np.arange(max(0, lens_t[b] - tail), lens_t[b])])
+                 for b in range(w.batch)]
+        ia = np.zeros((w.batch, count + tail), np.int32)
+        for b, li in enumerate(lists):
+            ia[b, :len(li)] = li
+        na = np.array([len(li) for li in lists], np.int32)
+        out2, lse2 = Bn.sparse_attention(qd, d.k, d.v, dev_i32(lens_t), dev_i32(ia), dev_i32(na),
+                                         block_table=d.block_table, max_ctx=d.max_ctx)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.sparse_attention(x.q[:, :, :1], x.k, x.v, lens_t, lists)
+        assert_out_close(out, o_ref, f"{name} tail {tail} out")
+        assert_lse_close(lse, lse_ref, f"{name} tail {tail} lse")
+        np.testing.assert_allclose(out.float().cpu().numpy(), out2.float().cpu().numpy(),
+                                   atol=8e-3, rtol=1e-2)
+
+
 @pytest.mark.parametrize("count,stride", [(1000, 1000), (3000, 3000), (700, 1024)])
 def test_sparse_long_lists_many_tiles_per_wavefront(count, stride):
     """Lists long enough that every wavefront walks several tiles (one split
