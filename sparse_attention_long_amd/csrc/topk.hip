@@ -50,15 +50,25 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return key > 1u ? key : 1u;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves: row
+// shifts by 1, 2, 4, 8 (zero fill) scan each 16-lane row, then the last lane
+// of row 0 / row 2 is added to row 1 / row 3 and the last lane of row 1 to
+// rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return (uint32_t)v;
+}
+
 // Exclusive prefix sum of v over the workgroup; `total` receives the sum.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -310,7 +320,10 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
 //     kernel; otherwise each pass reloads them (from L2 after the first).
 //   * Radix passes (12, 12, then 8 bits; usually the first suffices) find the
 //     bin of the r-th largest key, stopping as soon as that bin holds at most
-//     kBinCap keys.
+//     kBinCapOne keys (one round: another pass over registers costs about
+//     2 us) or kBinCapMany keys (reloaded rounds: a pass reloads the row,
+//     about 17 us at 131072 positions).  Ranking n members directly costs
+//     O(n^2) comparisons: about 75 us for 2000 members.
 //   * Keys above the bin are marked in an LDS bitmap of the positions; the
 //     bin's members go to an LDS list, are ranked directly (larger key, then
 //     lower position) and the best `want` are marked too.  If the bin is
@@ -322,7 +335,9 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
 constexpr int kSmallChunks = 8;                          // 4096-position chunks per round
 constexpr int kRoundLen = kSmallChunks * 4 * kThreadsTk;  // positions per round (32768)
 constexpr int kMaxRounds = 8;
-constexpr int kBinCap = 2044;                            // bin members ranked directly
+constexpr int kBinCapOne = 252;    // bin members ranked directly: one round
+constexpr int kBinCapMany = 764;   // ... reloaded rounds
+constexpr int kBinCap = kBinCapMany;
 
 // LDS of the one-workgroup selection.
 struct SelectLds {
@@ -404,7 +419,7 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
     find_digit(sh.hist, nb, shift, prefix, want, sh.s_wave, sh.s_out);
     nbin = sh.s_out[2];
     mask |= (nb - 1u) << shift;
-    if (nbin <= (uint32_t)kBinCap) break;
+    if (nbin <= (uint32_t)(reload ? kBinCapMany : kBinCapOne)) break;
   }
   const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
 
