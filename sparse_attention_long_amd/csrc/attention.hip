@@ -334,15 +334,12 @@ void attn_partials_kernel(AttnArgs a) {
   u32x4 kraw[NI], vraw[NI];
   int ts = start + wave * kTile;
   int tile_no = 0;
-  if (ts < end) {
-    stage(ts, 0);
-    issue(ts, kbase, kraw);
-    issue(ts, vbase, vraw);
-  }
 
-  // Stage the query fragments (B operand of S^T = K Q^T) once the first
-  // tile's loads are in flight: fragment (qb, ks, lane) holds row
-  // m = qb*16 + lane%16, d = ks*32 + (lane/16)*8 .. +8.
+  // Stage the query fragments (B operand of S^T = K Q^T) before the first
+  // tile's loads go out: a wavefront's loads complete in issue order, so
+  // query loads issued after the first K/V tile would wait for it.
+  // Fragment (qb, ks, lane) holds row m = qb*16 + lane%16,
+  // d = ks*32 + (lane/16)*8 .. +8.
   for (int f = threadIdx.x; f < QB * KS * 64; f += NT) {
     const int fl = f & 63, fks = (f >> 6) % KS, fqb = (f >> 6) / KS;
     const int m = fqb * 16 + (fl & 15);
@@ -386,6 +383,11 @@ void attn_partials_kernel(AttnArgs a) {
       val = __builtin_bit_cast(u32x4, part);
     }
     sq[f] = val;
+  }
+  if (ts < end) {
+    stage(ts, 0);
+    issue(ts, kbase, kraw);
+    issue(ts, vbase, vraw);
   }
   __syncthreads();  // query fragments staged
 
