@@ -219,6 +219,29 @@ def test_select_ties_zeros_and_infinities():
     _select_case(sc2, [64], 1, 0, 0)
 
 
+@pytest.mark.parametrize("L,n_bin,k", [
+    (32768, 200, 200),     # one round, bin of 200: ranked directly
+    (32768, 500, 512),     # one round, bin above the direct-ranking cap: another radix pass
+    (32768, 3000, 512),    # one round, bin of 3000: two more passes
+    (100000, 600, 500),    # reloaded rounds, bin of 600: ranked directly
+    (100000, 1000, 500),   # reloaded rounds, bin above that cap: another radix pass
+])
+def test_select_threshold_bin_sizes(L, n_bin, k):
+    """The bin holding the threshold key has a chosen size: n_bin scores in
+    [2.0, 2.2) share their top 12 key bits, 10 scores lie above them and the
+    rest below, so the bin is ranked directly or refined by further radix
+    passes depending on its size and on the row length."""
+    rng = np.random.default_rng(L + n_bin)
+    n_sink, window = 4, 64
+    sc = rng.uniform(0.0, 0.5, size=(2, L)).astype(np.float32)
+    for b in range(2):
+        pos = rng.choice(np.arange(n_sink, L - window), size=n_bin + 10, replace=False)
+        sc[b, pos[:n_bin]] = (2.0 + 0.2 * rng.random(n_bin)).astype(np.float32)
+        sc[b, pos[n_bin:]] = (5.0 + rng.random(10)).astype(np.float32)
+    assert (k - n_sink - window) - 10 < n_bin  # the threshold key lies in the bin
+    _select_case(sc, [L, L - 1], k, n_sink, window)
+
+
 # ------------------------------------------------------------------ hybrid selection
 def _hybrid_case(tgt_h, drf_h, lens, k, m, n_sink, window, stride=None):
     tgt = torch.from_numpy(np.ascontiguousarray(tgt_h, dtype=np.float32)).cuda()
