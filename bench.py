@@ -37,6 +37,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify+topk+sparse-attn iters/s per layer at 32K, b16; % of HBM peak BW"
 HBM_PEAK_GBS = 8000.0
+# K/V smaller than this rotate through copies (twice the 256 MB Infinity Cache)
+ROTATE_BYTES = 512 << 20
 
 
 def log(*a):
@@ -198,6 +200,24 @@ def main():
         bt = torch.from_numpy(x.block_table).to(dev)
     else:
         k, v, bt = d_bf16(x.k), d_bf16(x.v), None
+    # Cold caches: K/V below 512 MiB would stay in the 256 MB Infinity Cache
+    # from one launch to the next, so such workloads rotate through copies of
+    # K/V (same values, other addresses) whose sizes add up to at least
+    # 512 MiB; every launch that reads K/V takes the next copy.
+    kv_bytes = (k.numel() + v.numel()) * 2
+    n_copies = 1 if kv_bytes >= ROTATE_BYTES else min(64, -(-ROTATE_BYTES // kv_bytes))
+    k_copies, v_copies = [k], [v]
+    for _ in range(n_copies - 1):
+        k_copies.append(k.clone())
+        v_copies.append(v.clone())
+    cur = [0]
+
+    def kv():
+        """The current K/V copy."""
+        return k_copies[cur[0]], v_copies[cur[0]]
+
+    def rotate():
+        cur[0] = (cur[0] + 1) % n_copies
     lens = torch.from_numpy(x.seq_lens).to(dev)
     B, Hq, Hkv, T, d = w.batch, w.num_q_heads, w.num_kv_heads, w.q_len, w.head_dim
     max_ctx = w.max_ctx()
@@ -239,6 +259,7 @@ def main():
     def draft_steps():
         # step s attends the kept positions and the s + 1 drafted since (the
         # trailing positions of its length), in one launch
+        k, v = kv()
         for s in range(n_draft):
             Bn.sparse_attention(q_draft[s], k, v, lens_draft[s], idx, n_idx, block_table=bt,
                                 max_ctx=max_ctx, tail=s + 1, out=out_d, lse=lse_d, workspace=ws_d)
@@ -255,6 +276,8 @@ def main():
             Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
 
     def step():
+        rotate()
+        k, v = kv()
         Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v, heads=heads)
         # split combine + score aggregation in one launch
         Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
@@ -269,19 +292,23 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    graph = None
+    graphs = None
     if args.graph:
-        # one step captured as a HIP graph (no memsets are recorded: every
-        # kernel writes its outputs); replays run the same kernels
-        graph = torch.cuda.CUDAGraph()
+        # one step captured as a HIP graph per K/V copy (no memsets are
+        # recorded: every kernel writes its outputs); replays run the same
+        # kernels
+        graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                step()
+        for _ in range(n_copies):
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g_, stream=cap):
+                    step()
+            graphs.append(g_)
         torch.cuda.current_stream().wait_stream(cap)
-        for _ in range(args.warmup):
-            graph.replay()
+        for i in range(args.warmup):
+            graphs[i % n_copies].replay()
         torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps, launched back to back.  No event
@@ -293,12 +320,12 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     e_start.record()
-    if graph is None:
+    if graphs is None:
         for _ in range(K):
             step()
     else:
-        for _ in range(K):
-            graph.replay()
+        for i in range(K):
+            graphs[i % n_copies].replay()
     e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -314,6 +341,7 @@ def main():
         torch.cuda.synchronize()
         e0.record()
         for _ in range(K):
+            rotate()  # the next K/V copy (the launches below read it through kv())
             fn()
         e1.record()
         torch.cuda.synchronize()
@@ -322,7 +350,7 @@ def main():
     # the verify kernel's launch duration for the roofline: K launches of the
     # timed configuration back to back on the launch stream
     verify_us = per_launch_us(
-        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v, heads=heads))
+        lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, rows, KV, logits, ws_v, heads=heads))
     log(f"[bench] verify kernel {verify_us:.1f} us per launch")
     stages = {
         "verify_partials": verify_us,
@@ -332,19 +360,19 @@ def main():
     }
     if w.sparse_verify:
         stages["sparse"] = per_launch_us(
-            lambda: Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
+            lambda: Bn.sparse_attention(q, *kv(), lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                         out=out_s, lse=lse_s, workspace=ws_s))
     if n_draft:
         stages["draft_steps"] = per_launch_us(draft_steps)
     verify_none_us = per_launch_us(
-        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, rows, Bn.LOGITS_NONE, None, ws_v))
+        lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, rows, Bn.LOGITS_NONE, None, ws_v))
     # every verify row collected (the score summed over all T rows), same layout
     all_rows = tuple(range(T))
     logits_all = logits
     if KV == Bn.LOGITS_PER_HEAD and len(rows) != T:
         logits_all = torch.empty((B, T, n_heads, max_ctx), dtype=torch.float32, device=dev)
     verify_all_us = per_launch_us(
-        lambda: Bn.verify_partials(desc, q, k, v, lens, bt, all_rows, KV, logits_all, ws_v,
+        lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, all_rows, KV, logits_all, ws_v,
                                    heads=heads))
     del logits_all
     # hybrid selection (draft signal first) on the same scores, for comparison
@@ -360,7 +388,7 @@ def main():
     if w.sparse_verify:
         ws_b = torch.zeros(Bn.sparse_workspace_bytes(desc, k_blocks * BLK), dtype=torch.uint8, device=dev)
         sparse_blocks_us = per_launch_us(
-            lambda: Bn.sparse_attention(q, k, v, lens, idx_b, n_b, block_table=bt, max_ctx=max_ctx,
+            lambda: Bn.sparse_attention(q, *kv(), lens, idx_b, n_b, block_table=bt, max_ctx=max_ctx,
                                         out=out_s, lse=lse_s, workspace=ws_b))
 
     ab = alg_bytes(w, x.seq_lens, args.logits, len(rows), n_heads,
@@ -387,7 +415,8 @@ def main():
                    "paged": w.paged, "logits": args.logits, "collect_rows": list(rows),
                    "score_heads": None if heads is None else list(heads),
                    "select": args.select, "draft_m": w.draft_m if args.select == "hybrid" else None,
-                   "k_blocks": k_blocks if args.select == "blocks" else None},
+                   "k_blocks": k_blocks if args.select == "blocks" else None,
+                   "kv_copies": n_copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
                      "kernel": "attn_partials_kernel (verify)",

@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
 //   * Keys above the bin are marked in an LDS bitmap of the positions; the
 //     bin's members go to an LDS list, are ranked directly (larger key, then
 //     lower position) and the best `want` are marked too.  If the bin is
-//     bigger than kBinCap after the last pass, its keys are all equal and the
+//     bigger than the cap after the last pass, its keys are all equal and the
 //     lowest positions win: they are marked from a second bitmap.
 //   * The output is written from the bitmap: thread t owns bitmap words
 //     R*t .. R*t + R - 1 (positions 32Rt .. 32R(t+1) - 1), one block scan
