@@ -265,6 +265,9 @@ def main():
                                 max_ctx=max_ctx, tail=s + 1, out=out_d, lse=lse_d, workspace=ws_d)
 
     draft_sc = torch.from_numpy(W.draft_scores(w)).to(dev)
+    # rows of several 32768-position rounds: selection spread over one workgroup per round
+    n_ws_sel = Bn.select_workspace_bytes(B, max_ctx)
+    ws_sel = torch.empty(n_ws_sel, dtype=torch.uint8, device=dev) if n_ws_sel else None
 
     def select():
         if args.select == "hybrid":
@@ -273,7 +276,8 @@ def main():
         elif args.select == "blocks":
             Bn.select_blocks(scores, lens, k_blocks, BLK, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         else:
-            Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+            Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx,
+                           workspace=ws_sel)
 
     def step():
         rotate()

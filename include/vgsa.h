@@ -216,6 +216,25 @@ vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores
                              const int32_t* seq_lens, int32_t k, int32_t n_sink, int32_t window,
                              int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream);
 
+/* 3 (with a workspace).  The same selection as vgsa_select_topk, same
+ * arguments and results; rows of 2 .. 8 rounds of 32768 positions are
+ * spread over one workgroup per round (three launches on `stream`) instead
+ * of one workgroup per row.
+ * workspace  >= vgsa_select_workspace_bytes(batch, max_ctx) bytes of device
+ *            memory, 256-byte aligned; it holds per-round histograms,
+ *            bitmaps and candidate lists between the launches, needs no
+ *            initial contents, and calls that share it must not overlap.
+ *            When that size is 0 (max_ctx <= 32768 or > 262144) workspace may
+ *            be NULL and the call is vgsa_select_topk.
+ * Errors: as vgsa_select_topk; VGSA_ERR_WORKSPACE for a missing, small or
+ * misaligned workspace.
+ */
+size_t vgsa_select_workspace_bytes(int32_t batch, int32_t max_ctx);
+vgsa_status vgsa_select_topk_ws(int32_t batch, int32_t max_ctx, const float* scores,
+                                const int32_t* seq_lens, int32_t k, int32_t n_sink,
+                                int32_t window, int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* 3'. Hybrid selection from two signals.
  *    (Dustin, "1. hybrid attention aggregation": target-historical attention
  *    from the previous forward pass and draft-lookahead attention from the

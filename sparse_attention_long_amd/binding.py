@@ -45,6 +45,9 @@ SIGNATURES = {
                                       c_vp, c_vp]),
     "vgsa_select_topk": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_i32,
                                  c_vp, c_vp]),
+    "vgsa_select_workspace_bytes": (c_sz, [c_i32, c_i32]),
+    "vgsa_select_topk_ws": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_i32,
+                                    c_vp, c_vp, c_sz, c_vp]),
     "vgsa_select_topk_hybrid": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                         c_vp, c_i32, c_vp, c_vp]),
     "vgsa_select_blocks": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32,
@@ -251,9 +254,14 @@ def aggregate_scores(logits, seq_lens, num_q_heads: int, num_kv_heads: int, *,
     return scores
 
 
+def select_workspace_bytes(batch: int, max_ctx: int) -> int:
+    return int(load().vgsa_select_workspace_bytes(batch, max_ctx))
+
+
 def select_topk(scores, seq_lens, k: int, n_sink: int, window: int, *, idx_stride=None,
-                idx=None, n_idx=None):
-    """vgsa_select_topk.  Returns (idx int32 [B, idx_stride], n_idx int32 [B])."""
+                idx=None, n_idx=None, workspace=None):
+    """vgsa_select_topk_ws (vgsa_select_topk when the row needs no workspace).
+    Returns (idx int32 [B, idx_stride], n_idx int32 [B])."""
     _need(scores, "scores", torch.float32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     B, max_ctx = scores.shape
@@ -262,9 +270,16 @@ def select_topk(scores, seq_lens, k: int, n_sink: int, window: int, *, idx_strid
         idx = torch.empty((B, stride), dtype=torch.int32, device=scores.device)
     if n_idx is None:
         n_idx = torch.empty((B,), dtype=torch.int32, device=scores.device)
-    _check(load().vgsa_select_topk(B, max_ctx, _p(scores), _p(seq_lens), k, n_sink, window,
-                                   _p(idx), idx.shape[1], _p(n_idx), _stream(scores.device)),
-           "vgsa_select_topk")
+    nbytes = select_workspace_bytes(B, max_ctx) if B > 0 else 0
+    if nbytes and workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=scores.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    _check(load().vgsa_select_topk_ws(B, max_ctx, _p(scores), _p(seq_lens), k, n_sink, window,
+                                      _p(idx), idx.shape[1], _p(n_idx), _p(workspace),
+                                      0 if workspace is None else workspace.numel(),
+                                      _stream(scores.device)),
+           "vgsa_select_topk_ws")
     return idx, n_idx
 
 

@@ -458,6 +458,31 @@ vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores
                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t vgsa_select_workspace_bytes(int32_t batch, int32_t max_ctx) {
+  if (batch < 1 || max_ctx < 1 || batch > kMaxGridYZ) return 0;
+  return select_workspace_bytes(batch, max_ctx);
+}
+
+vgsa_status vgsa_select_topk_ws(int32_t batch, int32_t max_ctx, const float* scores,
+                                const int32_t* seq_lens, int32_t k, int32_t n_sink,
+                                int32_t window, int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const size_t need = vgsa_select_workspace_bytes(batch, max_ctx);
+  if (need == 0)
+    return vgsa_select_topk(batch, max_ctx, scores, seq_lens, k, n_sink, window, idx, idx_stride,
+                            n_idx, stream);
+  if (max_ctx < 1 || k < 1 || n_sink < 0 || window < 0) return VGSA_ERR_INVALID_ARG;
+  if ((int64_t)n_sink + window > k) return VGSA_ERR_INVALID_ARG;
+  if (idx_stride < k) return VGSA_ERR_INVALID_ARG;
+  if (scores == nullptr || seq_lens == nullptr || idx == nullptr || n_idx == nullptr)
+    return VGSA_ERR_INVALID_ARG;
+  const vgsa_status st = check_workspace(workspace, workspace_bytes, need);
+  if (st != VGSA_OK) return st;
+  return hip_status(launch_select_topk_split(batch, max_ctx, scores, seq_lens, k, n_sink, window,
+                                             idx, idx_stride, n_idx, workspace,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float* target_scores,
                                     const float* draft_scores, const int32_t* seq_lens, int32_t k,
                                     int32_t m, int32_t n_sink, int32_t window, int32_t* idx,

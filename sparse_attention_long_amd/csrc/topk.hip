@@ -351,6 +351,50 @@ struct SelectLds {
   uint32_t count;
 };
 
+// The threshold bin: sh.bin_rank_key[0, nbin) holds its members (not
+// exact), or sh.in_bin marks them (exact: their keys are all equal).  The
+// best `want` of them join sh.taken: larger key, then lower position.
+// Starts with a workgroup barrier (after the members were written) and ends
+// with one.
+__device__ void resolve_bin(SelectLds& sh, uint32_t nbin, uint32_t want, bool exact, int R) {
+  const int tid = threadIdx.x;
+  if (!exact && tid < 4) sh.bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
+  __syncthreads();
+  if (!exact) {
+    // rank = members with a larger key, or an equal key at a lower position
+    const int n4 = (int)(nbin + 3u) / 4;
+    for (int q = tid; q < (int)nbin; q += kThreadsTk) {
+      const uint64_t cq = sh.bin_rank_key[q];
+      uint32_t rank = 0u;
+      for (int f = 0; f < n4; ++f) {
+        const uint64_t* c4 = sh.bin_rank_key + 4 * f;
+        rank += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
+                (c4[3] > cq ? 1u : 0u);
+      }
+      if (rank < want) {
+        const int pq = (int)~(uint32_t)cq;
+        atomicOr(&sh.taken[pq >> 5], 1u << (pq & 31));
+      }
+    }
+  } else {
+    // the first `want` bin members in position order join the taken set;
+    // thread t owns words R*t .. R*t + R - 1
+    uint32_t n_in = 0u, tot;
+    for (int j = 0; j < R; ++j) n_in += (uint32_t)__builtin_popcount(sh.in_bin[R * tid + j]);
+    uint32_t q = block_exclusive_scan(n_in, sh.s_wave, tot);
+    for (int j = 0; j < R; ++j) {
+      uint32_t w = sh.taken[R * tid + j];
+      for (uint32_t bits = sh.in_bin[R * tid + j]; bits != 0u && q < want; ++q) {
+        w |= bits & (~bits + 1u);  // lowest remaining member
+        bits &= bits - 1u;
+      }
+      sh.taken[R * tid + j] = w;
+      sh.in_bin[R * tid + j] = 0u;
+    }
+  }
+  __syncthreads();
+}
+
 // One selection stage: marks in sh.taken the `want_stage` middle positions
 // [s_end, w_start) of highest score in row `sc` (lower position first among
 // equal keys).  EXCL: positions already marked are no candidates; a thread
@@ -452,41 +496,23 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
       }
     }
   }
-  if (!exact && tid < 4) sh.bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
-  __syncthreads();
-  if (!exact) {
-    // rank = members with a larger key, or an equal key at a lower position
-    const int n4 = (int)(nbin + 3u) / 4;
-    for (int q = tid; q < (int)nbin; q += kThreadsTk) {
-      const uint64_t cq = sh.bin_rank_key[q];
-      uint32_t rank = 0u;
-      for (int f = 0; f < n4; ++f) {
-        const uint64_t* c4 = sh.bin_rank_key + 4 * f;
-        rank += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
-                (c4[3] > cq ? 1u : 0u);
-      }
-      if (rank < want) {
-        const int pq = (int)~(uint32_t)cq;
-        atomicOr(&sh.taken[pq >> 5], 1u << (pq & 31));
-      }
-    }
-  } else {
-    // the first `want` bin members in position order join the taken set;
-    // thread t owns words R*t .. R*t + R - 1
-    uint32_t n_in = 0u, tot;
-    for (int j = 0; j < R; ++j) n_in += (uint32_t)__builtin_popcount(sh.in_bin[R * tid + j]);
-    uint32_t q = block_exclusive_scan(n_in, sh.s_wave, tot);
-    for (int j = 0; j < R; ++j) {
-      uint32_t w = sh.taken[R * tid + j];
-      for (uint32_t bits = sh.in_bin[R * tid + j]; bits != 0u && q < want; ++q) {
-        w |= bits & (~bits + 1u);  // lowest remaining member
-        bits &= bits - 1u;
-      }
-      sh.taken[R * tid + j] = w;
-      sh.in_bin[R * tid + j] = 0u;
-    }
-  }
-  __syncthreads();
+  resolve_bin(sh, nbin, want, exact, R);
+}
+
+// Ordered emit: [0, s_end) ++ the positions marked in sh.taken ++ [w_start, L)
+// (r of them marked).  Thread t owns words R*t .. R*t + R - 1.
+__device__ void emit_taken(SelectLds& sh, int R, int s_end, int w_start, int L, int r,
+                           int32_t* __restrict__ out, int32_t idx_stride) {
+  const int tid = threadIdx.x;
+  const uint32_t* my = sh.taken + R * tid;
+  uint32_t n_sel = 0u, tot;
+  for (int j = 0; j < R; ++j) n_sel += (uint32_t)__builtin_popcount(my[j]);
+  uint32_t o = block_exclusive_scan(n_sel, sh.s_wave, tot) + (uint32_t)s_end;
+  for (int j = 0; j < R; ++j)
+    for (uint32_t bits = my[j]; bits != 0u; bits &= bits - 1u)
+      if (o < (uint32_t)idx_stride) out[o++] = 32 * (R * tid + j) + __builtin_ctz(bits);
+  for (int i = tid; i < s_end; i += kThreadsTk) out[i] = i;
+  for (int i = tid; i < L - w_start; i += kThreadsTk) out[s_end + r + i] = w_start + i;
 }
 
 // VEC: 16-byte score loads (rows 16-byte aligned).
@@ -533,17 +559,7 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
     select_stage<VEC, HYBRID>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s_end, w_start,
                               (uint32_t)(r - m_first));
 
-  // Ordered emit: [0, s_end) ++ taken middle positions ++ [w_start, L).
-  // Thread t owns words R*t .. R*t + R - 1.
-  const uint32_t* my = sh.taken + R * tid;
-  uint32_t n_sel = 0u, tot;
-  for (int j = 0; j < R; ++j) n_sel += (uint32_t)__builtin_popcount(my[j]);
-  uint32_t o = block_exclusive_scan(n_sel, sh.s_wave, tot) + (uint32_t)s_end;
-  for (int j = 0; j < R; ++j)
-    for (uint32_t bits = my[j]; bits != 0u; bits &= bits - 1u)
-      if (o < (uint32_t)idx_stride) out[o++] = 32 * (R * tid + j) + __builtin_ctz(bits);
-  for (int i = tid; i < s_end; i += kThreadsTk) out[i] = i;
-  for (int i = tid; i < tail; i += kThreadsTk) out[s_end + r + i] = w_start + i;
+  emit_taken(sh, R, s_end, w_start, L, r, out, idx_stride);
   if (tid == 0) n_idx[b] = k;
 }
 
@@ -626,6 +642,238 @@ __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
   if (tid == 0) n_idx[b] = min(n_total, idx_stride);
 }
 
+// ---------------------------------------------------------------------------
+// Rows of 2 .. 8 rounds with a workspace: the work of a row is spread over one
+// workgroup per round, in three launches (their boundaries make each
+// launch's writes visible to the next; no workgroup waits on another):
+//   1. select_round_hist_kernel: round rd's 4096-bin histogram of the top 12
+//      key bits -> ws_hist[b][rd].
+//   2. select_round_mark_kernel: every round's workgroup sums the row's
+//      histograms and finds the bin of the r-th largest key (the same result
+//      in every workgroup); it writes its round's bitmap of keys above the
+//      bin -> ws_bits[b], and its round's bin members as (key << 32 |
+//      ~position) -> ws_list[b][rd], their count -> ws_cnt[b][rd].
+//   3. select_final_kernel (one workgroup per row): the bin's members (at
+//      most kFinalCap, else the one-workgroup selection runs instead) are
+//      refined by two more radix passes over the list only and ranked; the
+//      ordered output is written from the bitmap.
+// The one-workgroup kernel spends about 17 us per pass over a 131072-position
+// row on one CU and needs at least two passes over it plus the marking.
+constexpr int kFinalCap = 8192;  // bin members taken through the list
+
+struct SelRow {
+  int L, s_end, w_start, r, R;
+  bool trivial;  // L <= k, or the forced positions fill the budget
+};
+
+__device__ __forceinline__ SelRow sel_row(int b, int32_t max_ctx, const int32_t* seq_lens,
+                                          int32_t k, int32_t n_sink, int32_t window) {
+  SelRow s;
+  s.L = min(max(seq_lens[b], 0), max_ctx);
+  s.s_end = min(n_sink, s.L);
+  s.w_start = max(s.s_end, s.L - window);
+  s.r = k - (s.s_end + (s.L - s.w_start));
+  s.R = (s.L + kRoundLen - 1) / kRoundLen;
+  s.trivial = s.L <= k || s.r <= 0;
+  return s;
+}
+
+// Keys of round rd: thread t holds positions rd*32768 + 4096c + 4t + e;
+// key 0 outside M = [s_end, w_start).
+template <bool VEC>
+__device__ __forceinline__ void round_keys(const float* __restrict__ sc, int32_t max_ctx, int rd,
+                                           const SelRow& s, uint32_t (&key)[kSmallChunks][4]) {
+  const int tid = threadIdx.x;
+  float v[kSmallChunks][4];
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
+    if (VEC) {
+      const float4 x = *reinterpret_cast<const float4*>(sc + min(p0, max_ctx - 4));
+      v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[c][e] = sc[min(p0 + e, max_ctx - 1)];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = p0 + e;
+      key[c][e] = (p >= s.s_end && p < s.w_start) ? order_key(v[c][e]) : 0u;
+    }
+  }
+}
+
+struct SelWorkspace {
+  uint32_t* hist;   // [B][Rm][kBins]
+  uint32_t* bits;   // [B][Rm * kThreadsTk]
+  uint64_t* list;   // [B][Rm][kFinalCap]
+  uint32_t* cnt;    // [B][Rm]
+  uint32_t* meta;   // [B][4]: bin prefix, rank wanted inside the bin, bin size
+  int32_t rounds;   // Rm
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreadsTk) void select_round_hist_kernel(
+    int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
+    int32_t k, int32_t n_sink, int32_t window, SelWorkspace ws) {
+  __shared__ uint32_t hist[kBins];
+  const int rd = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SelRow s = sel_row(b, max_ctx, seq_lens, k, n_sink, window);
+  if (s.trivial || rd >= s.R) return;
+  for (int i = tid; i < kBins; i += kThreadsTk) hist[i] = 0u;
+  __syncthreads();
+  uint32_t key[kSmallChunks][4];
+  round_keys<VEC>(scores + (size_t)b * max_ctx, max_ctx, rd, s, key);
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (key[c][e] != 0u) atomicAdd(&hist[key[c][e] >> 20], 1u);
+  __syncthreads();
+  uint32_t* dst = ws.hist + ((size_t)b * ws.rounds + rd) * kBins;
+  for (int i = tid; i < kBins; i += kThreadsTk) dst[i] = hist[i];
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreadsTk) void select_round_mark_kernel(
+    int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
+    int32_t k, int32_t n_sink, int32_t window, SelWorkspace ws) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t s_wave[kWavesTk];
+  __shared__ uint32_t s_out[4];
+  __shared__ uint32_t bits[kThreadsTk];  // this round's bitmap words
+  __shared__ uint32_t count;
+  const int rd = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SelRow s = sel_row(b, max_ctx, seq_lens, k, n_sink, window);
+  if (s.trivial || rd >= s.R) return;
+  for (int i = tid; i < kBins; i += kThreadsTk) {
+    uint32_t h = 0u;
+    for (int q = 0; q < s.R; ++q) h += ws.hist[((size_t)b * ws.rounds + q) * kBins + i];
+    hist[i] = h;
+  }
+  bits[tid] = 0u;
+  if (tid == 0) count = 0u;
+  __syncthreads();
+  uint32_t prefix = 0u, want = (uint32_t)s.r;
+  find_digit(hist, kBins, 20, prefix, want, s_wave, s_out);  // M holds >= r keys
+  const uint32_t nbin = s_out[2], pbin = prefix >> 20;
+  uint32_t key[kSmallChunks][4];
+  round_keys<VEC>(scores + (size_t)b * max_ctx, max_ctx, rd, s, key);
+  uint64_t* list = ws.list + ((size_t)b * ws.rounds + rd) * kFinalCap;
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int p0 = c * 4 * kThreadsTk + 4 * tid;  // position within the round; 4-aligned
+    uint32_t above = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t kb = key[c][e] >> 20;
+      above |= (key[c][e] != 0u && kb > pbin) ? (1u << e) : 0u;
+      if (key[c][e] != 0u && kb == pbin && nbin <= (uint32_t)kFinalCap) {
+        const uint32_t slot = atomicAdd(&count, 1u);  // < nbin
+        list[slot] = ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(rd * kRoundLen + p0 + e);
+      }
+    }
+    if (above != 0u) atomicOr(&bits[p0 >> 5], above << (p0 & 31));
+  }
+  __syncthreads();
+  ws.bits[(size_t)b * ws.rounds * kThreadsTk + (size_t)rd * kThreadsTk + tid] = bits[tid];
+  if (tid == 0) {
+    ws.cnt[(size_t)b * ws.rounds + rd] = count;
+    if (rd == 0) {
+      ws.meta[(size_t)b * 4 + 0] = prefix;
+      ws.meta[(size_t)b * 4 + 1] = want;
+      ws.meta[(size_t)b * 4 + 2] = nbin;
+    }
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
+    int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
+    int32_t k, int32_t n_sink, int32_t window, int32_t* __restrict__ idx, int32_t idx_stride,
+    int32_t* __restrict__ n_idx, SelWorkspace ws) {
+  __shared__ SelectLds sh;
+  __shared__ uint64_t cand[kFinalCap];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const SelRow s = sel_row(b, max_ctx, seq_lens, k, n_sink, window);
+  int32_t* out = idx + (size_t)b * idx_stride;
+  if (s.L <= k) {
+    for (int j = tid; j < s.L; j += kThreadsTk) out[j] = j;
+    if (tid == 0) n_idx[b] = s.L;
+    return;
+  }
+  if (s.r <= 0) {  // the forced positions fill the budget
+    for (int i = tid; i < s.s_end; i += kThreadsTk) out[i] = i;
+    for (int i = tid; i < s.L - s.w_start; i += kThreadsTk) out[s.s_end + i] = s.w_start + i;
+    if (tid == 0) n_idx[b] = k;
+    return;
+  }
+  const int R = s.R;
+  const uint32_t prefix0 = ws.meta[(size_t)b * 4 + 0];
+  uint32_t want = ws.meta[(size_t)b * 4 + 1];
+  const uint32_t nbin0 = ws.meta[(size_t)b * 4 + 2];
+  for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) sh.in_bin[i] = 0u;
+  if (nbin0 > (uint32_t)kFinalCap) {
+    // the bin is too big for the list (massive ties): one-workgroup selection
+    for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) sh.taken[i] = 0u;
+    select_stage<VEC, false>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
+                             (uint32_t)s.r);
+  } else {
+    for (int i = tid; i < R * kThreadsTk; i += kThreadsTk)
+      sh.taken[i] = ws.bits[(size_t)b * ws.rounds * kThreadsTk + i];
+    // the rounds' lists, concatenated
+    uint32_t base = 0u;
+    for (int q = 0; q < R; ++q) {
+      const uint32_t c = ws.cnt[(size_t)b * ws.rounds + q];
+      const uint64_t* lq = ws.list + ((size_t)b * ws.rounds + q) * kFinalCap;
+      for (uint32_t j = tid; j < c; j += kThreadsTk) cand[base + j] = lq[j];
+      base += c;
+    }
+    if (tid == 0) sh.count = 0u;
+    __syncthreads();
+    // further radix passes over the list while the bin is big
+    uint32_t prefix = prefix0, mask = 0xFFF00000u, nbin = nbin0;
+    int level = 1;
+    for (; level <= 2 && nbin > (uint32_t)kBinCapOne; ++level) {
+      const int shift = level == 1 ? 8 : 0;
+      const uint32_t nb = level == 1 ? (uint32_t)kBins : 256u;
+      for (int i = tid; i < (int)nb; i += kThreadsTk) sh.hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t j = tid; j < nbin0; j += kThreadsTk) {
+        const uint32_t kk = (uint32_t)(cand[j] >> 32);
+        if ((kk & mask) == prefix) atomicAdd(&sh.hist[(kk >> shift) & (nb - 1u)], 1u);
+      }
+      __syncthreads();
+      find_digit(sh.hist, nb, shift, prefix, want, sh.s_wave, sh.s_out);
+      nbin = sh.s_out[2];
+      mask |= (nb - 1u) << shift;
+    }
+    const bool exact = nbin > (uint32_t)kBinCapOne;  // all 32 bits resolved: equal keys
+    for (uint32_t j = tid; j < nbin0; j += kThreadsTk) {
+      const uint64_t cj = cand[j];
+      const uint32_t kk = (uint32_t)(cj >> 32), mk = kk & mask;
+      const int pos = (int)~(uint32_t)cj;
+      if (mk > prefix) {
+        atomicOr(&sh.taken[pos >> 5], 1u << (pos & 31));
+      } else if (mk == prefix) {
+        if (exact) {
+          atomicOr(&sh.in_bin[pos >> 5], 1u << (pos & 31));
+        } else {
+          const uint32_t slot = atomicAdd(&sh.count, 1u);  // < nbin <= kBinCapOne
+          sh.bin_rank_key[slot] = cj;
+        }
+      }
+    }
+    resolve_bin(sh, nbin, want, exact, R);
+  }
+  emit_taken(sh, R, s.s_end, s.w_start, s.L, s.r, out, idx_stride);
+  if (tid == 0) n_idx[b] = k;
+}
+
 }  // namespace
 
 hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
@@ -651,6 +899,53 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
     if (hybrid) return hipErrorInvalidValue;  // rows past kMaxRounds rounds: plain selection only
     hipLaunchKernelGGL(select_topk_large_kernel, grid, block, 0, stream, max_ctx, scores, seq_lens,
                        k, n_sink, window, idx, idx_stride, n_idx);
+  }
+  return hipGetLastError();
+}
+
+size_t select_workspace_bytes(int32_t batch, int32_t max_ctx) {
+  const int64_t rounds = ((int64_t)max_ctx + kRoundLen - 1) / kRoundLen;
+  if (batch < 1 || rounds < 2 || rounds > kMaxRounds) return 0;
+  const size_t per_row = (size_t)rounds * (kBins * 4 + kThreadsTk * 4 + (size_t)kFinalCap * 8 + 4) + 16;
+  return ((size_t)batch * per_row + 4 * 256 + 255) / 256 * 256;
+}
+
+hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float* scores,
+                                    const int32_t* seq_lens, int32_t k, int32_t n_sink,
+                                    int32_t window, int32_t* idx, int32_t idx_stride,
+                                    int32_t* n_idx, void* workspace, hipStream_t stream) {
+  const int rounds = (max_ctx + kRoundLen - 1) / kRoundLen;
+  if (rounds < 2 || rounds > kMaxRounds) return hipErrorInvalidValue;
+  const bool vec = max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  // carve the workspace: 256-byte aligned arrays
+  char* p = static_cast<char*>(workspace);
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += (bytes + 255) / 256 * 256;
+    return q;
+  };
+  SelWorkspace ws;
+  ws.rounds = rounds;
+  ws.list = reinterpret_cast<uint64_t*>(take((size_t)batch * rounds * kFinalCap * 8));
+  ws.hist = reinterpret_cast<uint32_t*>(take((size_t)batch * rounds * kBins * 4));
+  ws.bits = reinterpret_cast<uint32_t*>(take((size_t)batch * rounds * kThreadsTk * 4));
+  ws.cnt = reinterpret_cast<uint32_t*>(take((size_t)batch * rounds * 4));
+  ws.meta = reinterpret_cast<uint32_t*>(take((size_t)batch * 16));
+  const dim3 grid_r(rounds, batch), grid_b(batch), block(kThreadsTk);
+  if (vec) {
+    hipLaunchKernelGGL(select_round_hist_kernel<true>, grid_r, block, 0, stream, max_ctx, scores,
+                       seq_lens, k, n_sink, window, ws);
+    hipLaunchKernelGGL(select_round_mark_kernel<true>, grid_r, block, 0, stream, max_ctx, scores,
+                       seq_lens, k, n_sink, window, ws);
+    hipLaunchKernelGGL(select_final_kernel<true>, grid_b, block, 0, stream, max_ctx, scores,
+                       seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
+  } else {
+    hipLaunchKernelGGL(select_round_hist_kernel<false>, grid_r, block, 0, stream, max_ctx, scores,
+                       seq_lens, k, n_sink, window, ws);
+    hipLaunchKernelGGL(select_round_mark_kernel<false>, grid_r, block, 0, stream, max_ctx, scores,
+                       seq_lens, k, n_sink, window, ws);
+    hipLaunchKernelGGL(select_final_kernel<false>, grid_b, block, 0, stream, max_ctx, scores,
+                       seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
   }
   return hipGetLastError();
 }

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -238,3 +238,23 @@ def test_split_plan_covers_span(lib):
     assert B.split_plan(d, 131078) == (17, 8192)
     d = desc(batch=1, num_q_heads=8, num_kv_heads=1, q_len=2, head_dim=64, max_ctx=1 << 24)
     assert B.split_plan(d, 1 << 24) == (2048, 8192)
+
+
+def test_select_workspace_sizes_and_validation(lib):
+    """The per-round selection needs a workspace only for rows of 2..8 rounds of
+    32768 positions; a missing or small workspace is refused before any launch."""
+    ws = lib.vgsa_select_workspace_bytes
+    assert ws(4, 32768) == 0 and ws(4, 1000) == 0 and ws(4, 262145) == 0 and ws(0, 65536) == 0
+    w2, w8 = ws(4, 32769), ws(4, 262144)
+    assert 0 < w2 < w8 and w2 % 256 == 0 and w8 % 256 == 0
+    assert ws(8, 131072) > ws(4, 131072)
+    fake = ctypes.c_void_p(0x1000)
+    # missing workspace -> VGSA_ERR_WORKSPACE (3); bad arguments -> VGSA_ERR_INVALID_ARG (1)
+    assert lib.vgsa_select_topk_ws(4, 131072, fake, fake, 512, 4, 64, fake, 512, fake,
+                                   None, 0, None) == 3
+    assert lib.vgsa_select_topk_ws(4, 131072, fake, fake, 512, 4, 64, fake, 512, fake,
+                                   fake, w2 - 1, None) == 3
+    assert lib.vgsa_select_topk_ws(4, 131072, fake, fake, 512, 400, 200, fake, 512, fake,
+                                   fake, ws(4, 131072), None) == 1
+    assert lib.vgsa_select_topk_ws(4, 131072, fake, fake, 512, 4, 64, fake, 100, fake,
+                                   fake, ws(4, 131072), None) == 1
