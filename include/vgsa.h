@@ -217,14 +217,14 @@ vgsa_status vgsa_select_topk(int32_t batch, int32_t max_ctx, const float* scores
                              int32_t* idx, int32_t idx_stride, int32_t* n_idx, void* stream);
 
 /* 3 (with a workspace).  The same selection as vgsa_select_topk, same
- * arguments and results; rows of 2 .. 8 rounds of 32768 positions are
- * spread over one workgroup per round (three launches on `stream`) instead
- * of one workgroup per row.
+ * arguments and results; a max_ctx of 49153 .. 262144 positions spreads each
+ * row over one workgroup per round of 32768 (three launches on `stream`)
+ * instead of one workgroup per row.
  * workspace  >= vgsa_select_workspace_bytes(batch, max_ctx) bytes of device
  *            memory, 256-byte aligned; it holds per-round histograms,
  *            bitmaps and candidate lists between the launches, needs no
  *            initial contents, and calls that share it must not overlap.
- *            When that size is 0 (max_ctx <= 32768 or > 262144) workspace may
+ *            When that size is 0 (max_ctx <= 49152 or > 262144) workspace may
  *            be NULL and the call is vgsa_select_topk.
  * Errors: as vgsa_select_topk; VGSA_ERR_WORKSPACE for a missing, small or
  * misaligned workspace.

@@ -905,7 +905,10 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
 
 size_t select_workspace_bytes(int32_t batch, int32_t max_ctx) {
   const int64_t rounds = ((int64_t)max_ctx + kRoundLen - 1) / kRoundLen;
-  if (batch < 1 || rounds < 2 || rounds > kMaxRounds) return 0;
+  // Up to 1.5 rounds the one-workgroup kernel is as fast (its rows may well
+  // fit one round, e.g. a capacity with headroom for drafted tokens), and
+  // one launch beats three.
+  if (batch < 1 || max_ctx <= kRoundLen + kRoundLen / 2 || rounds > kMaxRounds) return 0;
   const size_t per_row = (size_t)rounds * (kBins * 4 + kThreadsTk * 4 + (size_t)kFinalCap * 8 + 4) + 16;
   return ((size_t)batch * per_row + 4 * 256 + 255) / 256 * 256;
 }

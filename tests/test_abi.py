@@ -241,11 +241,12 @@ def test_split_plan_covers_span(lib):
 
 
 def test_select_workspace_sizes_and_validation(lib):
-    """The per-round selection needs a workspace only for rows of 2..8 rounds of
-    32768 positions; a missing or small workspace is refused before any launch."""
+    """The per-round selection needs a workspace only for capacities of 49153 ..
+    262144 positions; a missing or small workspace is refused before any launch."""
     ws = lib.vgsa_select_workspace_bytes
     assert ws(4, 32768) == 0 and ws(4, 1000) == 0 and ws(4, 262145) == 0 and ws(0, 65536) == 0
-    w2, w8 = ws(4, 32769), ws(4, 262144)
+    assert ws(4, 32772) == 0 and ws(4, 49152) == 0  # up to 1.5 rounds: one workgroup per row
+    w2, w8 = ws(4, 49153), ws(4, 262144)
     assert 0 < w2 < w8 and w2 % 256 == 0 and w8 % 256 == 0
     assert ws(8, 131072) > ws(4, 131072)
     fake = ctypes.c_void_p(0x1000)
