@@ -242,6 +242,22 @@ def test_select_threshold_bin_sizes(L, n_bin, k):
     _select_case(sc, [L, L - 1], k, n_sink, window)
 
 
+@pytest.mark.parametrize("ctx", [65536, 65541])
+def test_select_per_round_edge_rows(ctx):
+    """Capacities above 1.5 rounds take the per-round selection (workspace):
+    in one launch, an empty row, rows no longer than the budget, a row whose
+    sinks and window fill the budget, rows of one and of two rounds; with
+    aligned (16-byte loads) and unaligned capacities."""
+    rng = np.random.default_rng(ctx)
+    k, ns, win = 300, 4, 64
+    lens = [0, 100, 300, 65536 if ctx >= 65536 else ctx, 32768, 40000, 50001, 65000]
+    sc = (rng.standard_normal((len(lens), ctx)) * 10).astype(np.float32)
+    sc[6, ::5] = 3.0  # a repeated value
+    assert Bn.select_workspace_bytes(len(lens), ctx) > 0
+    _select_case(sc, lens, k, ns, win, stride=k + 5)
+    _select_case(sc, lens, ns + win, ns, win)  # r = 0: the forced positions only
+
+
 # ------------------------------------------------------------------ hybrid selection
 def _hybrid_case(tgt_h, drf_h, lens, k, m, n_sink, window, stride=None):
     tgt = torch.from_numpy(np.ascontiguousarray(tgt_h, dtype=np.float32)).cuda()
