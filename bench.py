@@ -272,7 +272,7 @@ def main():
     def select():
         if args.select == "hybrid":
             Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink, w.window,
-                                  idx=idx, n_idx=n_idx)
+                                  idx=idx, n_idx=n_idx, workspace=ws_sel)
         elif args.select == "blocks":
             Bn.select_blocks(scores, lens, k_blocks, BLK, w.n_sink, w.window, idx=idx, n_idx=n_idx)
         else:
@@ -382,7 +382,7 @@ def main():
     # hybrid selection (draft signal first) on the same scores, for comparison
     select_hybrid_us = per_launch_us(
         lambda: Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink,
-                                      w.window, idx=idx, n_idx=n_idx))
+                                      w.window, idx=idx, n_idx=n_idx, workspace=ws_sel))
     # block selection on the same scores, and the sparse pass over its lists
     idx_b = torch.empty((B, k_blocks * BLK), dtype=torch.int32, device=dev)
     n_b = torch.empty((B,), dtype=torch.int32, device=dev)

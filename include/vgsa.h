@@ -257,6 +257,19 @@ vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float*
                                     int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
                                     int32_t idx_stride, int32_t* n_idx, void* stream);
 
+/* 3' (with a workspace).  The same selection as vgsa_select_topk_hybrid,
+ * same arguments and results; for a max_ctx of 49153 .. 262144 positions
+ * each stage spreads a row over one workgroup per round of 32768 (six
+ * launches on `stream`).  workspace as for vgsa_select_topk_ws (same size,
+ * vgsa_select_workspace_bytes); when that size is 0 the call is
+ * vgsa_select_topk_hybrid.
+ */
+vgsa_status vgsa_select_topk_hybrid_ws(int32_t batch, int32_t max_ctx, const float* target_scores,
+                                       const float* draft_scores, const int32_t* seq_lens,
+                                       int32_t k, int32_t m, int32_t n_sink, int32_t window,
+                                       int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* 3''. Block-granular selection (structured block sparsity).
  *    (The euno.news summary of arXiv 2512.21911, "3. sparse verification
  *    engine": top keys kept in structured blocks; Quest's page-level

@@ -50,6 +50,8 @@ SIGNATURES = {
                                     c_vp, c_vp, c_sz, c_vp]),
     "vgsa_select_topk_hybrid": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                         c_vp, c_i32, c_vp, c_vp]),
+    "vgsa_select_topk_hybrid_ws": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                           c_i32, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_select_blocks": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32,
                                    c_vp, c_vp]),
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -284,8 +286,9 @@ def select_topk(scores, seq_lens, k: int, n_sink: int, window: int, *, idx_strid
 
 
 def select_topk_hybrid(target_scores, draft_scores, seq_lens, k: int, m: int, n_sink: int,
-                       window: int, *, idx_stride=None, idx=None, n_idx=None):
-    """vgsa_select_topk_hybrid.  Returns (idx int32 [B, idx_stride], n_idx int32 [B])."""
+                       window: int, *, idx_stride=None, idx=None, n_idx=None, workspace=None):
+    """vgsa_select_topk_hybrid_ws (vgsa_select_topk_hybrid when the row needs no
+    workspace).  Returns (idx int32 [B, idx_stride], n_idx int32 [B])."""
     _need(target_scores, "target_scores", torch.float32, 2)
     _need(draft_scores, "draft_scores", torch.float32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
@@ -297,9 +300,16 @@ def select_topk_hybrid(target_scores, draft_scores, seq_lens, k: int, m: int, n_
         idx = torch.empty((B, stride), dtype=torch.int32, device=target_scores.device)
     if n_idx is None:
         n_idx = torch.empty((B,), dtype=torch.int32, device=target_scores.device)
-    _check(load().vgsa_select_topk_hybrid(
+    nbytes = select_workspace_bytes(B, max_ctx) if B > 0 else 0
+    if nbytes and workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=target_scores.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    _check(load().vgsa_select_topk_hybrid_ws(
         B, max_ctx, _p(target_scores), _p(draft_scores), _p(seq_lens), k, m, n_sink, window,
-        _p(idx), idx.shape[1], _p(n_idx), _stream(target_scores.device)), "vgsa_select_topk_hybrid")
+        _p(idx), idx.shape[1], _p(n_idx), _p(workspace),
+        0 if workspace is None else workspace.numel(), _stream(target_scores.device)),
+        "vgsa_select_topk_hybrid_ws")
     return idx, n_idx
 
 

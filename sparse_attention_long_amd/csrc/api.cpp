@@ -478,9 +478,31 @@ vgsa_status vgsa_select_topk_ws(int32_t batch, int32_t max_ctx, const float* sco
     return VGSA_ERR_INVALID_ARG;
   const vgsa_status st = check_workspace(workspace, workspace_bytes, need);
   if (st != VGSA_OK) return st;
-  return hip_status(launch_select_topk_split(batch, max_ctx, scores, seq_lens, k, n_sink, window,
-                                             idx, idx_stride, n_idx, workspace,
+  return hip_status(launch_select_topk_split(batch, max_ctx, scores, nullptr, seq_lens, k, 0,
+                                             n_sink, window, idx, idx_stride, n_idx, workspace,
                                              static_cast<hipStream_t>(stream)));
+}
+
+vgsa_status vgsa_select_topk_hybrid_ws(int32_t batch, int32_t max_ctx, const float* target_scores,
+                                       const float* draft_scores, const int32_t* seq_lens,
+                                       int32_t k, int32_t m, int32_t n_sink, int32_t window,
+                                       int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  const size_t need = vgsa_select_workspace_bytes(batch, max_ctx);
+  if (need == 0)
+    return vgsa_select_topk_hybrid(batch, max_ctx, target_scores, draft_scores, seq_lens, k, m,
+                                   n_sink, window, idx, idx_stride, n_idx, stream);
+  if (max_ctx < 1 || k < 1 || m < 0 || n_sink < 0 || window < 0) return VGSA_ERR_INVALID_ARG;
+  if ((int64_t)n_sink + window > k) return VGSA_ERR_INVALID_ARG;
+  if (idx_stride < k) return VGSA_ERR_INVALID_ARG;
+  if (target_scores == nullptr || draft_scores == nullptr || seq_lens == nullptr ||
+      idx == nullptr || n_idx == nullptr)
+    return VGSA_ERR_INVALID_ARG;
+  const vgsa_status st = check_workspace(workspace, workspace_bytes, need);
+  if (st != VGSA_OK) return st;
+  return hip_status(launch_select_topk_split(batch, max_ctx, target_scores, draft_scores,
+                                             seq_lens, k, m, n_sink, window, idx, idx_stride,
+                                             n_idx, workspace, static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float* target_scores,

@@ -147,10 +147,12 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
 // Rows of 2 .. 8 rounds of 32768 positions with a workspace: one workgroup
 // per round in three launches (select_workspace_bytes is 0 for other rows).
 size_t select_workspace_bytes(int32_t batch, int32_t max_ctx);
+// draft_scores non-null: hybrid selection (m positions by draft_scores first).
 hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float* scores,
-                                    const int32_t* seq_lens, int32_t k, int32_t n_sink,
-                                    int32_t window, int32_t* idx, int32_t idx_stride,
-                                    int32_t* n_idx, void* workspace, hipStream_t stream);
+                                    const float* draft_scores, const int32_t* seq_lens, int32_t k,
+                                    int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
+                                    int32_t idx_stride, int32_t* n_idx, void* workspace,
+                                    hipStream_t stream);
 // Longest row (positions) the hybrid selection takes.
 constexpr int kMaxHybridRow = 8 * 32768;
 // Block-granular selection: blocks per row (their sums live in LDS).

@@ -657,6 +657,9 @@ __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
 //      most kFinalCap, else the one-workgroup selection runs instead) are
 //      refined by two more radix passes over the list only and ranked; the
 //      ordered output is written from the bitmap.
+// Hybrid selection runs the three launches twice: on the draft scores for
+// the first min(m, r) positions (picks kept as a bitmap in the workspace),
+// then on the target scores with those positions excluded.
 // The one-workgroup kernel spends about 17 us per pass over a 131072-position
 // row on one CU and needs at least two passes over it plus the marking.
 constexpr int kFinalCap = 8192;  // bin members taken through the list
@@ -679,10 +682,12 @@ __device__ __forceinline__ SelRow sel_row(int b, int32_t max_ctx, const int32_t*
 }
 
 // Keys of round rd: thread t holds positions rd*32768 + 4096c + 4t + e;
-// key 0 outside M = [s_end, w_start).
+// key 0 outside M = [s_end, w_start) and for positions set in `excl` (the
+// row's bitmap of a first stage's picks, or null).
 template <bool VEC>
 __device__ __forceinline__ void round_keys(const float* __restrict__ sc, int32_t max_ctx, int rd,
-                                           const SelRow& s, uint32_t (&key)[kSmallChunks][4]) {
+                                           const SelRow& s, const uint32_t* __restrict__ excl,
+                                           uint32_t (&key)[kSmallChunks][4]) {
   const int tid = threadIdx.x;
   float v[kSmallChunks][4];
 #pragma unroll
@@ -699,10 +704,11 @@ __device__ __forceinline__ void round_keys(const float* __restrict__ sc, int32_t
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c) {
     const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
+    const uint32_t gone = excl != nullptr ? excl[p0 >> 5] >> (p0 & 31) : 0u;  // p0 4-aligned
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int p = p0 + e;
-      key[c][e] = (p >= s.s_end && p < s.w_start) ? order_key(v[c][e]) : 0u;
+      key[c][e] = (p >= s.s_end && p < s.w_start && ((gone >> e) & 1u) == 0u) ? order_key(v[c][e]) : 0u;
     }
   }
 }
@@ -713,8 +719,24 @@ struct SelWorkspace {
   uint64_t* list;   // [B][Rm][kFinalCap]
   uint32_t* cnt;    // [B][Rm]
   uint32_t* meta;   // [B][4]: bin prefix, rank wanted inside the bin, bin size
+  uint32_t* first;  // [B][Rm * kThreadsTk]: the first stage's picks (hybrid)
   int32_t rounds;   // Rm
+  // 0: one stage (r positions by `scores`); 1: first hybrid stage (min(m, r)
+  // by the draft scores, picks kept in `first`); 2: second hybrid stage (the
+  // rest by the target scores, `first` excluded, output written)
+  int32_t stage;
+  int32_t m;
 };
+
+// Positions the stage picks from the row.
+__device__ __forceinline__ int stage_want(const SelRow& s, const SelWorkspace& ws) {
+  const int m1 = min(max(ws.m, 0), s.r);
+  return ws.stage == 0 ? s.r : ws.stage == 1 ? m1 : s.r - m1;
+}
+
+__device__ __forceinline__ const uint32_t* stage_excl(const SelWorkspace& ws, int b) {
+  return ws.stage == 2 ? ws.first + (size_t)b * ws.rounds * kThreadsTk : nullptr;
+}
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreadsTk) void select_round_hist_kernel(
@@ -723,11 +745,11 @@ __global__ __launch_bounds__(kThreadsTk) void select_round_hist_kernel(
   __shared__ uint32_t hist[kBins];
   const int rd = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const SelRow s = sel_row(b, max_ctx, seq_lens, k, n_sink, window);
-  if (s.trivial || rd >= s.R) return;
+  if (s.trivial || rd >= s.R || stage_want(s, ws) <= 0) return;
   for (int i = tid; i < kBins; i += kThreadsTk) hist[i] = 0u;
   __syncthreads();
   uint32_t key[kSmallChunks][4];
-  round_keys<VEC>(scores + (size_t)b * max_ctx, max_ctx, rd, s, key);
+  round_keys<VEC>(scores + (size_t)b * max_ctx, max_ctx, rd, s, stage_excl(ws, b), key);
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c)
 #pragma unroll
@@ -749,7 +771,8 @@ __global__ __launch_bounds__(kThreadsTk) void select_round_mark_kernel(
   __shared__ uint32_t count;
   const int rd = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const SelRow s = sel_row(b, max_ctx, seq_lens, k, n_sink, window);
-  if (s.trivial || rd >= s.R) return;
+  const int want_stage = stage_want(s, ws);
+  if (s.trivial || rd >= s.R || want_stage <= 0) return;
   for (int i = tid; i < kBins; i += kThreadsTk) {
     uint32_t h = 0u;
     for (int q = 0; q < s.R; ++q) h += ws.hist[((size_t)b * ws.rounds + q) * kBins + i];
@@ -758,11 +781,11 @@ __global__ __launch_bounds__(kThreadsTk) void select_round_mark_kernel(
   bits[tid] = 0u;
   if (tid == 0) count = 0u;
   __syncthreads();
-  uint32_t prefix = 0u, want = (uint32_t)s.r;
-  find_digit(hist, kBins, 20, prefix, want, s_wave, s_out);  // M holds >= r keys
+  uint32_t prefix = 0u, want = (uint32_t)want_stage;
+  find_digit(hist, kBins, 20, prefix, want, s_wave, s_out);  // the stage's keys number >= want
   const uint32_t nbin = s_out[2], pbin = prefix >> 20;
   uint32_t key[kSmallChunks][4];
-  round_keys<VEC>(scores + (size_t)b * max_ctx, max_ctx, rd, s, key);
+  round_keys<VEC>(scores + (size_t)b * max_ctx, max_ctx, rd, s, stage_excl(ws, b), key);
   uint64_t* list = ws.list + ((size_t)b * ws.rounds + rd) * kFinalCap;
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c) {
@@ -802,29 +825,42 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
   const SelRow s = sel_row(b, max_ctx, seq_lens, k, n_sink, window);
   int32_t* out = idx + (size_t)b * idx_stride;
   if (s.L <= k) {
+    if (ws.stage == 1) return;  // the second stage writes the output
     for (int j = tid; j < s.L; j += kThreadsTk) out[j] = j;
     if (tid == 0) n_idx[b] = s.L;
     return;
   }
   if (s.r <= 0) {  // the forced positions fill the budget
+    if (ws.stage == 1) return;
     for (int i = tid; i < s.s_end; i += kThreadsTk) out[i] = i;
     for (int i = tid; i < s.L - s.w_start; i += kThreadsTk) out[s.s_end + i] = s.w_start + i;
     if (tid == 0) n_idx[b] = k;
     return;
   }
   const int R = s.R;
-  const uint32_t prefix0 = ws.meta[(size_t)b * 4 + 0];
-  uint32_t want = ws.meta[(size_t)b * 4 + 1];
-  const uint32_t nbin0 = ws.meta[(size_t)b * 4 + 2];
+  const int want_stage = stage_want(s, ws);
+  uint32_t* first_row = ws.first + (size_t)b * ws.rounds * kThreadsTk;
+  const bool after_first = ws.stage == 2;  // the first stage's picks count as taken
   for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) sh.in_bin[i] = 0u;
-  if (nbin0 > (uint32_t)kFinalCap) {
+  if (want_stage <= 0) {
+    // nothing to pick in this stage
+    for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) sh.taken[i] = after_first ? first_row[i] : 0u;
+    __syncthreads();
+  } else if (ws.meta[(size_t)b * 4 + 2] > (uint32_t)kFinalCap) {
     // the bin is too big for the list (massive ties): one-workgroup selection
-    for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) sh.taken[i] = 0u;
-    select_stage<VEC, false>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
-                             (uint32_t)s.r);
+    for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) sh.taken[i] = after_first ? first_row[i] : 0u;
+    if (after_first)
+      select_stage<VEC, true>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
+                              (uint32_t)want_stage);
+    else
+      select_stage<VEC, false>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
+                               (uint32_t)want_stage);
   } else {
+    const uint32_t prefix0 = ws.meta[(size_t)b * 4 + 0];
+    uint32_t want = ws.meta[(size_t)b * 4 + 1];
+    const uint32_t nbin0 = ws.meta[(size_t)b * 4 + 2];
     for (int i = tid; i < R * kThreadsTk; i += kThreadsTk)
-      sh.taken[i] = ws.bits[(size_t)b * ws.rounds * kThreadsTk + i];
+      sh.taken[i] = ws.bits[(size_t)b * ws.rounds * kThreadsTk + i] | (after_first ? first_row[i] : 0u);
     // the rounds' lists, concatenated
     uint32_t base = 0u;
     for (int q = 0; q < R; ++q) {
@@ -870,6 +906,10 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
     }
     resolve_bin(sh, nbin, want, exact, R);
   }
+  if (ws.stage == 1) {  // keep the picks for the second stage
+    for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) first_row[i] = sh.taken[i];
+    return;
+  }
   emit_taken(sh, R, s.s_end, s.w_start, s.L, s.r, out, idx_stride);
   if (tid == 0) n_idx[b] = k;
 }
@@ -909,17 +949,20 @@ size_t select_workspace_bytes(int32_t batch, int32_t max_ctx) {
   // fit one round, e.g. a capacity with headroom for drafted tokens), and
   // one launch beats three.
   if (batch < 1 || max_ctx <= kRoundLen + kRoundLen / 2 || rounds > kMaxRounds) return 0;
-  const size_t per_row = (size_t)rounds * (kBins * 4 + kThreadsTk * 4 + (size_t)kFinalCap * 8 + 4) + 16;
-  return ((size_t)batch * per_row + 4 * 256 + 255) / 256 * 256;
+  const size_t per_row =
+      (size_t)rounds * (kBins * 4 + 2 * kThreadsTk * 4 + (size_t)kFinalCap * 8 + 4) + 16;
+  return ((size_t)batch * per_row + 5 * 256 + 255) / 256 * 256;
 }
 
 hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float* scores,
-                                    const int32_t* seq_lens, int32_t k, int32_t n_sink,
-                                    int32_t window, int32_t* idx, int32_t idx_stride,
-                                    int32_t* n_idx, void* workspace, hipStream_t stream) {
+                                    const float* draft_scores, const int32_t* seq_lens, int32_t k,
+                                    int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
+                                    int32_t idx_stride, int32_t* n_idx, void* workspace,
+                                    hipStream_t stream) {
   const int rounds = (max_ctx + kRoundLen - 1) / kRoundLen;
   if (rounds < 2 || rounds > kMaxRounds) return hipErrorInvalidValue;
-  const bool vec = max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  const auto al16 = [](const float* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = max_ctx % 4 == 0 && al16(scores) && (draft_scores == nullptr || al16(draft_scores));
   // carve the workspace: 256-byte aligned arrays
   char* p = static_cast<char*>(workspace);
   auto take = [&](size_t bytes) {
@@ -934,21 +977,30 @@ hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float*
   ws.bits = reinterpret_cast<uint32_t*>(take((size_t)batch * rounds * kThreadsTk * 4));
   ws.cnt = reinterpret_cast<uint32_t*>(take((size_t)batch * rounds * 4));
   ws.meta = reinterpret_cast<uint32_t*>(take((size_t)batch * 16));
+  ws.first = reinterpret_cast<uint32_t*>(take((size_t)batch * rounds * kThreadsTk * 4));
+  ws.m = m;
   const dim3 grid_r(rounds, batch), grid_b(batch), block(kThreadsTk);
-  if (vec) {
-    hipLaunchKernelGGL(select_round_hist_kernel<true>, grid_r, block, 0, stream, max_ctx, scores,
-                       seq_lens, k, n_sink, window, ws);
-    hipLaunchKernelGGL(select_round_mark_kernel<true>, grid_r, block, 0, stream, max_ctx, scores,
-                       seq_lens, k, n_sink, window, ws);
-    hipLaunchKernelGGL(select_final_kernel<true>, grid_b, block, 0, stream, max_ctx, scores,
-                       seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
-  } else {
-    hipLaunchKernelGGL(select_round_hist_kernel<false>, grid_r, block, 0, stream, max_ctx, scores,
-                       seq_lens, k, n_sink, window, ws);
-    hipLaunchKernelGGL(select_round_mark_kernel<false>, grid_r, block, 0, stream, max_ctx, scores,
-                       seq_lens, k, n_sink, window, ws);
-    hipLaunchKernelGGL(select_final_kernel<false>, grid_b, block, 0, stream, max_ctx, scores,
-                       seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
+  // hybrid: the first stage on the draft scores, then the second on the
+  // target scores; otherwise one stage
+  const int n_stages = draft_scores != nullptr ? 2 : 1;
+  for (int st = 0; st < n_stages; ++st) {
+    ws.stage = draft_scores == nullptr ? 0 : st + 1;
+    const float* sc = ws.stage == 1 ? draft_scores : scores;
+    if (vec) {
+      hipLaunchKernelGGL(select_round_hist_kernel<true>, grid_r, block, 0, stream, max_ctx, sc,
+                         seq_lens, k, n_sink, window, ws);
+      hipLaunchKernelGGL(select_round_mark_kernel<true>, grid_r, block, 0, stream, max_ctx, sc,
+                         seq_lens, k, n_sink, window, ws);
+      hipLaunchKernelGGL(select_final_kernel<true>, grid_b, block, 0, stream, max_ctx, sc,
+                         seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
+    } else {
+      hipLaunchKernelGGL(select_round_hist_kernel<false>, grid_r, block, 0, stream, max_ctx, sc,
+                         seq_lens, k, n_sink, window, ws);
+      hipLaunchKernelGGL(select_round_mark_kernel<false>, grid_r, block, 0, stream, max_ctx, sc,
+                         seq_lens, k, n_sink, window, ws);
+      hipLaunchKernelGGL(select_final_kernel<false>, grid_b, block, 0, stream, max_ctx, sc,
+                         seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
+    }
   }
   return hipGetLastError();
 }

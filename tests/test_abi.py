@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -259,3 +259,8 @@ def test_select_workspace_sizes_and_validation(lib):
                                    fake, ws(4, 131072), None) == 1
     assert lib.vgsa_select_topk_ws(4, 131072, fake, fake, 512, 4, 64, fake, 100, fake,
                                    fake, ws(4, 131072), None) == 1
+    # the hybrid form takes the same workspace
+    assert lib.vgsa_select_topk_hybrid_ws(4, 131072, fake, fake, fake, 512, 100, 4, 64, fake, 512,
+                                          fake, None, 0, None) == 3
+    assert lib.vgsa_select_topk_hybrid_ws(4, 131072, fake, None, fake, 512, 100, 4, 64, fake, 512,
+                                          fake, fake, ws(4, 131072), None) == 1
