@@ -75,6 +75,7 @@ class Workload:
     layers: int = 1
     seed: int = 1
     lens: Optional[Tuple[int, ...]] = None       # explicit per-sequence lengths (tests)
+    cap_align: int = 16                          # row capacity rounded up to this many positions
 
     # ---- derived sizes ----
     @property
@@ -104,11 +105,12 @@ class Workload:
 
     def max_ctx(self) -> int:
         """Row capacity: the longest context plus headroom for draft-step tokens,
-        rounded up to whole 16-position blocks for paged caches."""
+        rounded up to whole 16-position blocks for paged caches, and to
+        `cap_align` positions otherwise (16: fp32 logit and score rows start
+        64-byte aligned, so they are read and written as 16-byte vectors)."""
         cap = self.max_len() + self.draft_steps
-        if self.paged:
-            cap = -(-cap // PAGE_BLOCK) * PAGE_BLOCK
-        return cap
+        align = PAGE_BLOCK if self.paged else max(1, self.cap_align)
+        return -(-cap // align) * align
 
     def planted_count(self, length: int) -> int:
         if self.planted is not None:

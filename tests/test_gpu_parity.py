@@ -19,10 +19,12 @@ pytestmark = pytest.mark.gpu
 
 CASES = {
     # name: workload (G*T query rows -> MFMA row blocks)
+    # capacities 301 and 257 (cap_align=1): logit and score rows not 16-byte aligned
     "g4t4_d128_ragged": W.small("g4t4", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
-                                gamma=3, lens=(301, 4, 128), budget=40, n_sink=4, window=8),
+                                gamma=3, lens=(301, 4, 128), budget=40, n_sink=4, window=8,
+                                cap_align=1),
     "g4t5_d64": W.small("g4t5", batch=2, num_q_heads=16, num_kv_heads=4, head_dim=64, gamma=4,
-                        lens=(33, 257), budget=24, n_sink=2, window=6, seed=11),
+                        lens=(33, 257), budget=24, n_sink=2, window=6, seed=11, cap_align=1),
     "g8t5_d128": W.small("g8t5", batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128, gamma=4,
                          lens=(700, 129), budget=64, n_sink=4, window=16, seed=12),
     "g8t8_d64": W.small("g8t8", batch=1, num_q_heads=32, num_kv_heads=4, head_dim=64, gamma=7,

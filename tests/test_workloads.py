@@ -48,7 +48,7 @@ def test_workload_table_sizes():
     assert (w.batch, w.group, w.q_len, w.budget, w.collect_rows) == (16, 8, 5, 512, (0, 4))
     assert w.planted_count(32768) == 328
     w4 = c["ctx128k_b8_h32kv8_d128_draft6"]
-    assert w4.planted_count(131072) == 655 and w4.max_ctx() == 131078 and w4.budget == 6554
+    assert w4.planted_count(131072) == 655 and w4.max_ctx() == 131088 and w4.budget == 6554
     w5 = c["ragged8k-64k_b4_h64kv8_d64_paged16_l24"]
     lens = W.seq_lens(w5)
     assert np.all(lens >= 8192) and np.all(lens <= 65536) and w5.max_ctx() % 16 == 0
