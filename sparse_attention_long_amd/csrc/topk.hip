@@ -599,18 +599,50 @@ __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
   if (r > 0) {
     // block sums (members below L only), float32 in position order
     const float* sc = scores + (size_t)b * max_ctx;
-    for (int i = tid; i < nb; i += kThreadsTk) {
-      const int j0 = i * block, j1 = min(L, j0 + block);
-      float sum = 0.f;
-      if (VEC && j1 - j0 == block) {
-        for (int j = j0; j < j1; j += 4) {
-          const float4 x = *reinterpret_cast<const float4*>(sc + j);
-          sum += x.x; sum += x.y; sum += x.z; sum += x.w;
+    if (VEC && block == 16) {
+      // the loads of four blocks go out together (one round trip per four
+      // blocks instead of one per block); blocks wholly below L only
+      const int nfull = L / 16;
+      for (int i0 = tid; i0 < nb; i0 += 4 * kThreadsTk) {
+        float4 x[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * kThreadsTk;
+          if (i < nfull)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[u][q] = *reinterpret_cast<const float4*>(sc + i * 16 + 4 * q);
         }
-      } else {
-        for (int j = j0; j < j1; ++j) sum += sc[j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * kThreadsTk;
+          if (i < nb) {
+            float sum = 0.f;
+            if (i < nfull) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                sum += x[u][q].x; sum += x[u][q].y; sum += x[u][q].z; sum += x[u][q].w;
+              }
+            } else {
+              for (int j = i * 16; j < L; ++j) sum += sc[j];
+            }
+            s_bsum[i] = sum;
+          }
+        }
       }
-      s_bsum[i] = sum;
+    } else {
+      for (int i = tid; i < nb; i += kThreadsTk) {
+        const int j0 = i * block, j1 = min(L, j0 + block);
+        float sum = 0.f;
+        if (VEC && j1 - j0 == block) {
+          for (int j = j0; j < j1; j += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(sc + j);
+            sum += x.x; sum += x.y; sum += x.z; sum += x.w;
+          }
+        } else {
+          for (int j = j0; j < j1; ++j) sum += sc[j];
+        }
+        s_bsum[i] = sum;
+      }
     }
     sh.taken[tid] = 0u;  // one round: word t holds blocks 32t .. 32t + 31
     sh.in_bin[tid] = 0u;
