@@ -9,7 +9,10 @@
 //
 // One workgroup of 1024 threads per sequence.  Rows of up to 262144 positions
 // take select_topk_kernel (radix pass over coalesced keys, the threshold bin
-// ranked directly, output from a position bitmap); longer rows take
+// ranked directly, output from a position bitmap).  With a workspace, a
+// capacity of 49153 .. 262144 positions takes the per-round kernels instead
+// (select_round_hist_kernel, select_round_mark_kernel, select_final_kernel:
+// one workgroup per round of 32768 positions and sequence).  Longer rows take
 // select_topk_large_kernel, described here:
 //   * F = [0, s_end) U [w_start, L) is forced; r = k - |F| positions are
 //     picked from the middle range M = [s_end, w_start).
