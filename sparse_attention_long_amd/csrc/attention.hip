@@ -323,12 +323,15 @@ void attn_partials_kernel(AttnArgs a) {
   };
 
   // Paged verify: the chunk's block ids (clamped) go to LDS once, so no load
-  // address waits on a block-table read inside the loop.
-  if (!SPARSE && a.paged) {
-    const int nblk = (end - 1 - start) / 16 + 1;
-    for (int i = threadIdx.x; i < nblk; i += NT)
-      s_blk[i] = min(max(btab[(start >> 4) + i], 0), a.num_blocks - 1);
-    __syncthreads();
+  // address waits on a block-table read inside the loop.  Their loads go out
+  // with the query fragments' below (one round trip for both).
+  constexpr int kBlkPerThread = (kMaxChunk / 16 + NT - 1) / NT;
+  const int nblk = (!SPARSE && a.paged) ? (end - 1 - start) / 16 + 1 : 0;  // <= kMaxChunk / 16
+  int blk_v[kBlkPerThread];
+#pragma unroll
+  for (int j = 0; j < kBlkPerThread; ++j) {
+    const int i = (int)threadIdx.x + j * NT;
+    blk_v[j] = i < nblk ? btab[(start >> 4) + i] : 0;
   }
 
   u32x4 kraw[NI], vraw[NI];
@@ -383,6 +386,14 @@ void attn_partials_kernel(AttnArgs a) {
       val = __builtin_bit_cast(u32x4, part);
     }
     sq[f] = val;
+  }
+  if (!SPARSE && a.paged) {
+#pragma unroll
+    for (int j = 0; j < kBlkPerThread; ++j) {
+      const int i = (int)threadIdx.x + j * NT;
+      if (i < nblk) s_blk[i] = min(max(blk_v[j], 0), a.num_blocks - 1);
+    }
+    __syncthreads();  // block ids staged (the first tile's addresses need them)
   }
   if (ts < end) {
     stage(ts, 0);
