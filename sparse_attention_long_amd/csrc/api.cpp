@@ -140,7 +140,16 @@ SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span) {
   if (s < 1) s = 1;
   if (s > max_splits) s = max_splits;
   int64_t chunk = ceil_div(ceil_div(span, s), kMinChunk) * kMinChunk;
-  if (chunk > kMaxChunk) chunk = kMaxChunk;
+  if (chunk > kPlanChunk) {
+    chunk = kPlanChunk;
+    // A last split of a sliver would add a workgroup to every (sequence,
+    // kv-head), and one more split changes which workgroups share a CU and
+    // an XCD (17 splits measured 10 % slower than 16 at 128K x b8): the
+    // sliver is spread over the other splits instead (chunk <= kMaxChunk).
+    const int64_t n = ceil_div(span, (int64_t)kPlanChunk);
+    if (n > 1 && span - (n - 1) * kPlanChunk <= kPlanChunk / 8)
+      chunk = ceil_div(ceil_div(span, n - 1), kMinChunk) * kMinChunk;
+  }
   s = ceil_div(span, chunk);
   SplitPlan p;
   p.num_splits = (int32_t)s;

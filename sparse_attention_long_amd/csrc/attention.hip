@@ -131,8 +131,8 @@ void attn_partials_kernel(AttnArgs a) {
 
   // Ragged batches (verify): every workgroup derives the same item length
   // from the lengths, short enough that the non-empty items of a kv-head fill
-  // its S * B workgroups, and takes the u-th of them (u = split + S * b):
-  // the longest workgroup then has about the mean work, not the longest row's.
+  // its S * B workgroups, and takes one of them (below): the longest
+  // workgroup then has about the mean work, not the longest row's.
   if (!SPARSE && a.balance) {
     const int S = a.num_splits, B = a.batch;
     int64_t total = 0;
@@ -141,15 +141,31 @@ void attn_partials_kernel(AttnArgs a) {
     const int floor_len = (a.chunk / kBalanceSplits + kMinChunk - 1) / kMinChunk * kMinChunk;
     const int cp = (int)min((int64_t)a.chunk,
                             max((int64_t)floor_len, (fit + kMinChunk - 1) / kMinChunk * kMinChunk));
-    const int u = split + S * b;
-    int acc = 0, bi = -1, si = 0;
-    for (int i = 0; i < B && bi < 0; ++i) {
-      const int n = (min(max(a.seq_lens[i], 0), a.max_ctx) + cp - 1) / cp;
-      if (u < acc + n) {
-        bi = i;
-        si = u - acc;
+    // A sequence keeps its first S items on its own workgroups (split < n),
+    // so equal lengths map as without balancing; the items past S of long
+    // sequences go, in order, to the workgroups that short sequences leave
+    // free (split >= n).  The items number at most S * B, so every one has
+    // a workgroup.  (Which K/V rows stream together matters: handing each
+    // sequence's items to the next sequence's workgroups measured 17 %
+    // slower at 128K x b8 with 17 splits.)
+    auto items = [&](int i) { return (min(max(a.seq_lens[i], 0), a.max_ctx) + cp - 1) / cp; };
+    const int nb = items(b);
+    int bi = -1, si = 0;
+    if (split < nb) {
+      bi = b;
+      si = split;
+    } else {
+      int r = split - nb;  // rank among the free workgroups, in (sequence, split) order
+      for (int i = 0; i < b; ++i) r += max(0, S - items(i));
+      int acc = 0;
+      for (int i = 0; i < B && bi < 0; ++i) {
+        const int o = max(0, items(i) - S);
+        if (r < acc + o) {
+          bi = i;
+          si = S + (r - acc);
+        }
+        acc += o;
       }
-      acc += n;
     }
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) a.header[0] = cp;
     if (bi < 0) return;  // more workgroups than items

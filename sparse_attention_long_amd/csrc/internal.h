@@ -24,12 +24,16 @@ constexpr int kTargetWorkgroups = 512;
 // (sequence, kv-head) finishes the softmax itself and writes the output
 // directly (no partials, no combine launch).
 constexpr int kDirectSpan = 1024;
-// Largest chunk of one split.  A workgroup keeps kv-group logits for
+// Chunk of one split, as planned.  A workgroup keeps kv-group logits for
 // kLogitBuf positions in LDS (fp32) and writes them out in bursts of that
 // size (every kLogitBuf positions of a longer chunk).  Longer chunks measured
 // slower at 128K x b8 (one round of 512 workgroups then spans 4 GB of K/V at
 // once; two rounds of 8192-position chunks span 2 GB each).
-constexpr int kMaxChunk = 8192;
+constexpr int kPlanChunk = 8192;
+// Largest chunk: the plan widens its chunks up to this size instead of adding
+// a split for a last sliver of at most kPlanChunk / 8 positions (a capacity
+// a few positions past a multiple of 8192, e.g. headroom for drafted tokens).
+constexpr int kMaxChunk = kPlanChunk + kPlanChunk / 8;
 constexpr int kLogitBuf = 4096;
 // Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.
 constexpr int kMaxRows = 64;
