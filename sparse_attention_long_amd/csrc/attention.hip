@@ -75,10 +75,19 @@ struct Occupancy {
 // Internal emit mode; the layout written is VGSA_LOGITS_KVGROUP_SUM.
 constexpr int kEmitSumColumn = 3;
 
+// Lane moves within 16-lane rows (DPP: VALU only, no LDS crossbar traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                           0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm 1,0,3,2: lane i <- i ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm 2,3,0,1: lane i <- i ^ 2
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <- i ^ 7 (within 8 lanes)
+constexpr int kDppXor8 = 0x128;       // row_ror:8: lane i <- i ^ 8 (within 16 lanes)
+
 __device__ __forceinline__ float swap_adjacent_lanes(float x) {  // lane i <-> lane i ^ 1
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
-                                                           0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF,
-                                                           true));
+  return dpp_move<kDppXor1>(x);
 }
 
 // Lazy rescaling: a row's running max is only raised (and O, l rescaled)
@@ -543,23 +552,27 @@ void attn_partials_kernel(AttnArgs a) {
         }
       // Reduce-scatter over the 16 query-row lanes: after the four steps lane
       // c16 holds the full sum of position pb = bit 3, r = 2*bit 2 + bit 1.
+      // Each step pairs a lane with one whose bit (8, 4, 2, then 1) differs
+      // and whose higher bits agree: lane ^ 8, lane ^ 7 (the mirror within 8
+      // lanes: bit 4 differs, bit 8 agrees), lane ^ 2, lane ^ 1; over the
+      // steps every lane's partner sets join into all 16 lanes.
       const bool h8 = (c16 >> 3) & 1, h4 = (c16 >> 2) & 1, h2 = (c16 >> 1) & 1;
       float v4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float keep = h8 ? v8[4 + i] : v8[i];
         const float give = h8 ? v8[i] : v8[4 + i];
-        v4[i] = keep + __shfl_xor(give, 8);
+        v4[i] = keep + dpp_move<kDppXor8>(give);
       }
       float v2[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float keep = h4 ? v4[2 + i] : v4[i];
         const float give = h4 ? v4[i] : v4[2 + i];
-        v2[i] = keep + __shfl_xor(give, 4);
+        v2[i] = keep + dpp_move<kDppHalfMirror>(give);
       }
-      float v1 = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 2);
-      v1 += __shfl_xor(v1, 1);
+      float v1 = (h2 ? v2[1] : v2[0]) + dpp_move<kDppXor2>(h2 ? v2[0] : v2[1]);
+      v1 += dpp_move<kDppXor1>(v1);
       const int e = (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
       if ((c16 & 1) == 0) slog[ts - lbase + e] = v1;
     }
