@@ -90,6 +90,37 @@ __device__ __forceinline__ float swap_adjacent_lanes(float x) {  // lane i <-> l
   return dpp_move<kDppXor1>(x);
 }
 
+// Lanes i and i ^ 16 (ROWS = true) or i and i ^ 32: both values of the pair,
+// the lower lane's first, in both lanes (gfx950 permlane swaps: VALU, no LDS
+// crossbar traffic).
+template <bool ROWS>
+__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  if constexpr (ROWS) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+}
+
+// Max and sum over lanes i, i ^ 16, i ^ 32, i ^ 48 (one 16-lane column).
+__device__ __forceinline__ float column_max(float x) {
+  float lo, hi;
+  lane_pair<true>(x, lo, hi);
+  lane_pair<false>(fmaxf(lo, hi), lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float column_sum(float x) {
+  float lo, hi;
+  lane_pair<true>(x, lo, hi);
+  lane_pair<false>(lo + hi, lo, hi);
+  return lo + hi;
+}
+
 // Lazy rescaling: a row's running max is only raised (and O, l rescaled)
 // when a tile exceeds it by more than 2^kRescaleLog2; otherwise the stale max
 // is kept, so p <= 2^kRescaleLog2.  The combine uses the same (m, l, O)
@@ -617,8 +648,7 @@ void attn_partials_kernel(AttnArgs a) {
           x[pb][r] = seen ? sacc[pb][qb][r] * a.scale_log2 : kNegInf;
           mx = fmaxf(mx, x[pb][r]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = column_max(mx);
       const bool grow = mx > m_run[qb] + kRescaleLog2;
       if (__any(grow)) {
         const float m_new = grow ? mx : m_run[qb];
@@ -680,8 +710,7 @@ void attn_partials_kernel(AttnArgs a) {
   // Row sums: combine the four 16-lane groups.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    l_run[qb] += __shfl_xor(l_run[qb], 16);
-    l_run[qb] += __shfl_xor(l_run[qb], 32);
+    l_run[qb] = column_sum(l_run[qb]);
   }
   if (kg == 0) {
 #pragma unroll
