@@ -144,17 +144,32 @@ void attn_partials_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t sbuf[WAVES * kTile * VS];
   // Query fragments, already in MFMA operand order: [qb][ks][lane] x 16 B.
   __shared__ __align__(16) u32x4 sq[QB * KS * 64];
-  __shared__ float s_m[WAVES][kMaxRows];
-  __shared__ float s_l[WAVES][kMaxRows];
-  __shared__ float s_inv[kMaxRows];  // 1 / (merged row sum), for the one-split output
   __shared__ int s_idx[WAVES][kTile];           // sparse: positions of the staged tile
   __shared__ uint32_t s_row[WAVES][kTile];      // sparse: cache element offsets of those rows
-  __shared__ int s_blk[SPARSE ? 1 : kMaxChunk / 16];  // paged verify: the chunk's block ids
-  // Kv-group logits of the chunk, written out in bursts of kLogitBuf
-  // positions: contiguous 16-byte stores instead of 128 bytes per tile, which
-  // would interleave small writes with the K/V read stream.
+  // One array, three uses in turn:
+  //  * slog, the kv-group logits of the chunk: held here and written out in
+  //    contiguous bursts, all of a chunk of up to kLogitBufMax positions
+  //    once the loop is done (contiguous caches).  Stores issued while the
+  //    K/V stream runs cost far more than their bytes: one 4096-position
+  //    burst per workgroup in mid-chunk cost 3 % of the verify time;
+  //  * s_blk, the paged verify's block ids of the chunk, in the top
+  //    kMaxChunk / 16 entries (a paged launch holds kLogitBuf positions of
+  //    logits, so the two do not meet);
+  //  * after the loop (logits out, block ids no longer read): the merge's
+  //    per-wavefront row max and sum and the rows' 1 / sum.
   constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || EMIT == kEmitSumColumn;
-  __shared__ __align__(16) float slog[kGroupLogits ? kLogitBuf : 4];
+  constexpr int kBlkIds = SPARSE ? 0 : kMaxChunk / 16;
+  constexpr int kRowStats = 2 * WAVES * kMaxRows + kMaxRows;
+  constexpr int kShared = kGroupLogits ? kLogitBufMax
+                                       : (kBlkIds > kRowStats ? kBlkIds : kRowStats);
+  static_assert(!kGroupLogits || kLogitBuf + kBlkIds <= kLogitBufMax, "logits meet block ids");
+  static_assert(kRowStats <= kShared, "row statistics do not fit");
+  __shared__ __align__(16) float sx[kShared];
+  float* const slog = sx;
+  int* const s_blk = reinterpret_cast<int*>(sx + kShared - kBlkIds);
+  float (*const s_m)[kMaxRows] = reinterpret_cast<float (*)[kMaxRows]>(sx);
+  float (*const s_l)[kMaxRows] = reinterpret_cast<float (*)[kMaxRows]>(sx + WAVES * kMaxRows);
+  float* const s_inv = sx + 2 * WAVES * kMaxRows;  // 1 / (merged row sum), one-split output
   // Per-head logits: each wavefront turns its 16 x 32 tile of one row block
   // around in LDS so that a store instruction writes two rows' 32 positions
   // as contiguous 128-byte runs (any row alignment); s_lrow[m] is the element
@@ -459,6 +474,10 @@ void attn_partials_kernel(AttnArgs a) {
   __syncthreads();  // query fragments staged
 
   int lbase = start;  // first position held in slog
+  // positions of logits slog holds (a multiple of step), and the tile count
+  // at which it is full
+  const int log_cap = a.paged ? kLogitBuf : kLogitBufMax;
+  int flush_tile = log_cap / step;
   auto flush_logits = [&](int n) {  // slog[0, n) -> logits[lbase, lbase + n), nontemporal
     float* lp = a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + lbase;
     int tid = threadIdx.x;
@@ -696,14 +715,15 @@ void attn_partials_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     ++tile_no;
-    if (kGroupLogits && tile_no % (kLogitBuf / step) == 0 &&
+    if (kGroupLogits && tile_no == flush_tile &&
         start + (tile_no - 1) * step + (WAVES - 1) * kTile < end) {
       // the last wavefront has a tile_no-th tile, so every wavefront reaches
       // this point (the condition is the same for all): the buffer is full
       __syncthreads();
-      flush_logits(min(kLogitBuf, end - lbase));
+      flush_logits(min(log_cap, end - lbase));
       __syncthreads();
-      lbase += kLogitBuf;
+      lbase += log_cap;
+      flush_tile += log_cap / step;
     }
   }
 
@@ -711,6 +731,11 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     l_run[qb] = column_sum(l_run[qb]);
+  }
+  __syncthreads();  // every wavefront's logits are in slog; no block id is read again
+  if (kGroupLogits && end > lbase) {
+    flush_logits(end - lbase);  // the rest (read once, later)
+    __syncthreads();            // slog read out: its space takes the row statistics
   }
   if (kg == 0) {
 #pragma unroll
@@ -720,8 +745,6 @@ void attn_partials_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
-
-  if (kGroupLogits && end > lbase) flush_logits(end - lbase);  // the rest (read once, later)
 
   // Merge the wavefronts, relative to each row's workgroup max M, in four
   // rounds of D/4 head-dim columns: every wavefront parks its scaled

@@ -24,9 +24,10 @@ constexpr int kTargetWorkgroups = 512;
 // (sequence, kv-head) finishes the softmax itself and writes the output
 // directly (no partials, no combine launch).
 constexpr int kDirectSpan = 1024;
-// Chunk of one split, as planned.  A workgroup keeps kv-group logits for
-// kLogitBuf positions in LDS (fp32) and writes them out in bursts of that
-// size (every kLogitBuf positions of a longer chunk).  Longer chunks measured
+// Chunk of one split, as planned.  A workgroup keeps the kv-group logits of
+// its chunk in LDS (fp32; kLogitBufMax positions, kLogitBuf for paged caches)
+// and writes them out after its loop (and whenever the buffer is full, in a
+// longer chunk).  Longer chunks measured
 // slower at 128K x b8 (one round of 512 workgroups then spans 4 GB of K/V at
 // once; two rounds of 8192-position chunks span 2 GB each).
 constexpr int kPlanChunk = 8192;
@@ -34,7 +35,8 @@ constexpr int kPlanChunk = 8192;
 // a split for a last sliver of at most kPlanChunk / 8 positions (a capacity
 // a few positions past a multiple of 8192, e.g. headroom for drafted tokens).
 constexpr int kMaxChunk = kPlanChunk + kPlanChunk / 8;
-constexpr int kLogitBuf = 4096;
+constexpr int kLogitBuf = 4096;     // paged caches (the block-id table shares the space)
+constexpr int kLogitBufMax = 8192;  // contiguous caches: a whole planned chunk
 // Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.
 constexpr int kMaxRows = 64;
 
