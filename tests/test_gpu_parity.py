@@ -40,6 +40,12 @@ CASES = {
     "chunk4224_g1t3_d64": W.small("c4224", batch=8, num_q_heads=8, num_kv_heads=8, head_dim=64,
                                   gamma=2, lens=(33000, 20000, 4500, 8300, 12289, 30000, 4097, 16500),
                                   budget=300, n_sink=4, window=32, seed=16),
+    # paged twin with equal lengths: 8 x 8 workgroup rows, items of 4224
+    # positions, so the paged launch's 4096-position logit buffer fills
+    # mid-chunk (contiguous launches hold 8192)
+    "chunk4224_paged_g1t3_d64": W.small("c4224p", batch=8, num_q_heads=8, num_kv_heads=8,
+                                        head_dim=64, gamma=2, ctx=33000, paged=True, budget=300,
+                                        n_sink=4, window=32, seed=17),
 }
 
 
