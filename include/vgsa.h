@@ -138,11 +138,14 @@ size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc);
 
 /* Workspace bytes needed by vgsa_sparse_attention / vgsa_sparse_partials
  * (idx_stride: the list capacity, plus the tail of vgsa_sparse_attention).
- * vgsa_sparse_attention keeps per-(sequence, kv-head) counters in the last
- * ceil(B * Hkv * 4 / 256) * 256 of these bytes: they must be zero when the
- * workspace is first used (allocate it zero-filled), and every call leaves
- * them zero.  Other calls (vgsa_sparse_partials, the verify calls) must not
- * be given that part of the buffer. */
+ * vgsa_sparse_attention keeps per-(sequence, kv-head) counters in the first
+ * ceil(B * Hkv * 4 / 256) * 256 bytes of its workspace, at the same place
+ * whatever the span, so one workspace sized for the largest span serves
+ * every smaller one: they must be zero when the workspace is first used
+ * (allocate it zero-filled, and zero it again before using it with a larger
+ * B * Hkv), and every call leaves them zero.  Other calls
+ * (vgsa_sparse_partials, the verify calls) write a header at the start of
+ * their workspace and must not be given this buffer. */
 size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_stride);
 
 /* ------------------------------------------------------------------------ */
@@ -289,13 +292,18 @@ vgsa_status vgsa_select_topk_hybrid_ws(int32_t batch, int32_t max_ctx, const flo
  *           among equal sums); every position when the blocks of L number at
  *           most k_blocks.
  * n_idx     int32 [B]: positions written
+ * block_sums  nullable fp32 [B][ceil(max_ctx / block)], caller-owned device
+ *           memory: when given, row b receives the block sums the ranking
+ *           compared (float32, members summed in position order) for blocks
+ *           [0, ceil(L / block)); later entries are left untouched.  It lets a
+ *           caller check the sums against an exact sum and rank them itself.
  * Rows are limited to ceil(max_ctx / block) <= 8704 blocks
  * (VGSA_ERR_UNSUPPORTED beyond).
  */
 vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
                                const int32_t* seq_lens, int32_t k_blocks, int32_t block,
                                int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
-                               int32_t* n_idx, void* stream);
+                               int32_t* n_idx, float* block_sums, void* stream);
 
 /* 4. Sparse attention over an index list (page size 1).
  *    (Vegas section 2 step 3 and section 3; Dustin "3.")

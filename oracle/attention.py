@@ -279,22 +279,17 @@ def select_topk_hybrid_batch(target: np.ndarray, draft: np.ndarray, seq_lens: Se
 
 def block_sums(scores: np.ndarray, length: int, block: int) -> np.ndarray:
     """Score of each `block`-position block of [0, L): the sum of its members'
-    scores, accumulated in float32 in position order (the precision and order
-    in which the selection compares them; the last block may be partial)."""
+    scores (the last block may be partial), from the definition: the members
+    widened to float64 and summed exactly (math.fsum, correctly rounded)."""
     L = int(length)
     nb = -(-L // block)
-    out = np.zeros(nb, dtype=np.float32)
-    x = np.asarray(scores[:L], dtype=np.float32)
-    for i in range(nb):
-        s = np.float32(0.0)
-        for j in range(i * block, min(L, (i + 1) * block)):
-            s = np.float32(s + x[j])
-        out[i] = s
-    return out
+    x = np.asarray(scores[:L], dtype=np.float64)
+    return np.array([math.fsum(x[i * block:min(L, (i + 1) * block)].tolist()) for i in range(nb)],
+                    dtype=np.float64)
 
 
 def select_blocks(scores: np.ndarray, length: int, k_blocks: int, block: int, n_sink: int,
-                  window: int) -> np.ndarray:
+                  window: int, sums: Optional[np.ndarray] = None) -> np.ndarray:
     """Block-granular selection (structured block sparsity, the euno.news
     summary of arXiv 2512.21911, "3. sparse verification engine"; Quest's
     page-level selection in Dustin's comparison): whole blocks of `block`
@@ -304,7 +299,12 @@ def select_blocks(scores: np.ndarray, length: int, k_blocks: int, block: int, n_
     first; the rest of the k_blocks go to the largest block sums, lower block
     first among equals.  If k_blocks covers every block all positions are
     kept.  Returns the kept positions ascending (every member of a kept
-    block below L)."""
+    block below L).
+
+    `sums` (optional, one value per block of [0, L)) are the block sums to
+    rank, compared as given: e.g. another implementation's own rounded sums,
+    so that a selection made from them can be checked exactly.  Default: the
+    exact sums of block_sums."""
     L = int(length)
     if L <= 0:
         return np.zeros(0, dtype=np.int64)
@@ -318,7 +318,10 @@ def select_blocks(scores: np.ndarray, length: int, k_blocks: int, block: int, n_
     nf = int(forced.sum())
     if nf > k_blocks:
         raise ValueError("sink and window blocks exceed the block budget")
-    chosen = _top_by(block_sums(scores, L, block), np.flatnonzero(~forced), k_blocks - nf)
+    rank = block_sums(scores, L, block) if sums is None else np.asarray(sums, dtype=np.float64)[:nb]
+    if rank.shape[0] != nb:
+        raise ValueError("one block sum per block of [0, L) is needed")
+    chosen = _top_by(rank, np.flatnonzero(~forced), k_blocks - nf)
     keep = forced.copy()
     keep[chosen] = True
     pos = np.arange(L, dtype=np.int64)
@@ -326,8 +329,10 @@ def select_blocks(scores: np.ndarray, length: int, k_blocks: int, block: int, n_
 
 
 def select_blocks_batch(scores: np.ndarray, seq_lens: Sequence[int], k_blocks: int, block: int,
-                        n_sink: int, window: int) -> List[np.ndarray]:
-    return [select_blocks(scores[b], int(seq_lens[b]), k_blocks, block, n_sink, window)
+                        n_sink: int, window: int,
+                        sums: Optional[np.ndarray] = None) -> List[np.ndarray]:
+    return [select_blocks(scores[b], int(seq_lens[b]), k_blocks, block, n_sink, window,
+                          None if sums is None else sums[b])
             for b in range(scores.shape[0])]
 
 

@@ -53,7 +53,7 @@ SIGNATURES = {
     "vgsa_select_topk_hybrid_ws": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                            c_i32, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_select_blocks": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32,
-                                   c_vp, c_vp]),
+                                   c_vp, c_vp, c_vp]),
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
@@ -240,6 +240,8 @@ def aggregate_scores(logits, seq_lens, num_q_heads: int, num_kv_heads: int, *,
                      layout: str = "kvgroup_sum", scores=None, accumulate: bool = False):
     """vgsa_aggregate_scores.  Returns scores fp32 [B, max_ctx] (added to
     `scores` when accumulating); per-head logits are [B, R, H, max_ctx]."""
+    if accumulate and scores is None:
+        raise ValueError("accumulate needs the scores to add to")
     _need(logits, "logits", torch.float32)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     lay = _LAYOUTS[layout]
@@ -247,8 +249,6 @@ def aggregate_scores(logits, seq_lens, num_q_heads: int, num_kv_heads: int, *,
     n_rows = logits.shape[1] * logits.shape[2] if lay == LOGITS_PER_HEAD and logits.dim() == 4 else 0
     if scores is None:
         scores = torch.empty((B, max_ctx), dtype=torch.float32, device=logits.device)
-    if accumulate and scores is None:
-        raise ValueError("accumulate needs the scores to add to")
     _check(load().vgsa_aggregate_scores(B, num_q_heads, num_kv_heads, max_ctx, lay, n_rows,
                                         int(bool(accumulate)), _p(logits),
                                         _p(seq_lens), _p(scores), _stream(logits.device)),
@@ -314,9 +314,10 @@ def select_topk_hybrid(target_scores, draft_scores, seq_lens, k: int, m: int, n_
 
 
 def select_blocks(scores, seq_lens, k_blocks: int, block: int, n_sink: int, window: int, *,
-                  idx_stride=None, idx=None, n_idx=None):
+                  idx_stride=None, idx=None, n_idx=None, block_sums=None):
     """vgsa_select_blocks.  Returns (idx int32 [B, idx_stride] positions of the
-    kept blocks, n_idx int32 [B])."""
+    kept blocks, n_idx int32 [B]).  `block_sums` (fp32 [B, ceil(max_ctx /
+    block)], optional) receives the block sums the ranking compared."""
     _need(scores, "scores", torch.float32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     B, max_ctx = scores.shape
@@ -325,8 +326,12 @@ def select_blocks(scores, seq_lens, k_blocks: int, block: int, n_sink: int, wind
         idx = torch.empty((B, stride), dtype=torch.int32, device=scores.device)
     if n_idx is None:
         n_idx = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    if block_sums is not None:
+        _need(block_sums, "block_sums", torch.float32, 2)
+        if tuple(block_sums.shape) != (B, -(-max_ctx // block)):
+            raise ValueError(f"block_sums must be [{B}, {-(-max_ctx // block)}]")
     _check(load().vgsa_select_blocks(B, max_ctx, _p(scores), _p(seq_lens), k_blocks, block, n_sink,
-                                     window, _p(idx), idx.shape[1], _p(n_idx),
+                                     window, _p(idx), idx.shape[1], _p(n_idx), _p(block_sums),
                                      _stream(scores.device)), "vgsa_select_blocks")
     return idx, n_idx
 

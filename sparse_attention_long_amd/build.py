@@ -30,7 +30,10 @@ FLAGS = [
     "-shared",
     "-Wall",
     "-Wno-unused-function",
-    # packed fp32 VALU forms are kept out of the generated code
+    # packed fp32 VALU forms (v_pk_{add,mul,fma}_f32) are kept out of the
+    # device code: the gfx950 pass honours this feature switch (the x86 host
+    # pass does not know it and warns, harmlessly).  A CPU test disassembles
+    # the built library and fails if any such opcode appears.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

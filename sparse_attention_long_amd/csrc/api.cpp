@@ -9,7 +9,6 @@
 namespace vgsa {
 
 size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p);
-size_t sparse_sync_offset(const vgsa_attn_desc& d, int32_t idx_stride);
 size_t sparse_sync_bytes(const vgsa_attn_desc& d);
 
 namespace {
@@ -165,12 +164,10 @@ size_t partial_bytes(const vgsa_attn_desc& d, const SplitPlan& p) {
   return kHeaderBytes + (o_bytes + 255) / 256 * 256 + rows * 2 * 4;
 }
 
-// The sparse workspace: the partials, then the fused merge's arrival
-// counters (one int32 per (sequence, kv-head)).
-size_t sparse_sync_offset(const vgsa_attn_desc& d, int32_t idx_stride) {
-  return (partial_bytes(d, make_plan(d.batch, d.num_kv_heads, idx_stride)) + 255) / 256 * 256;
-}
-
+// The one-call sparse workspace: the fused merge's arrival counters (one
+// int32 per (sequence, kv-head)) at its start, then the partials.  The
+// counters' place does not depend on the span, so one zero-filled workspace
+// serves calls whose split plans differ (e.g. draft steps of growing tails).
 size_t sparse_sync_bytes(const vgsa_attn_desc& d) {
   return ((size_t)d.batch * d.num_kv_heads * 4 + 255) / 256 * 256;
 }
@@ -212,7 +209,8 @@ size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc) {
 
 size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_stride) {
   if (check_desc(desc) != VGSA_OK || idx_stride < 1) return 0;
-  return sparse_sync_offset(*desc, idx_stride) + sparse_sync_bytes(*desc);
+  return sparse_sync_bytes(*desc) +
+         partial_bytes(*desc, make_plan(desc->batch, desc->num_kv_heads, idx_stride));
 }
 
 }  // extern "C"
@@ -279,12 +277,13 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   // one split for lists up to kDirectSpan (the output is written directly);
   // longer lists split, and with `fused` the splits merge in the same launch
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, span);
-  const size_t need = fused ? sparse_sync_offset(d, span) + sparse_sync_bytes(d)
-                            : partial_bytes(d, p);
-  st = check_workspace(workspace, workspace_bytes, need);
+  // fused: the counters first, the partials after them
+  const size_t sync_bytes = fused ? sparse_sync_bytes(d) : 0;
+  st = check_workspace(workspace, workspace_bytes, sync_bytes + partial_bytes(d, p));
   if (st != VGSA_OK) return st;
   if (d.batch == 0) return VGSA_OK;
-  AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens, workspace);
+  AttnArgs a = base_args(d, p, q, k_cache, v_cache, block_table, seq_lens,
+                         static_cast<char*>(workspace) + sync_bytes);
   a.idx = idx;
   a.n_idx = n_idx;
   a.idx_stride = idx_stride;
@@ -295,8 +294,7 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   a.direct = (out != nullptr && p.num_splits == 1) ? 1 : 0;
   if (fused && p.num_splits > 1) {
     a.fuse = 1;
-    a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                        sparse_sync_offset(d, span));
+    a.sync = static_cast<int32_t*>(workspace);
   }
   return hip_status(launch_attention_partials(a, true, static_cast<hipStream_t>(stream)));
 }
@@ -535,7 +533,7 @@ vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float*
 vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
                                const int32_t* seq_lens, int32_t k_blocks, int32_t block,
                                int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
-                               int32_t* n_idx, void* stream) {
+                               int32_t* n_idx, float* block_sums, void* stream) {
   if (batch < 0 || max_ctx < 1 || k_blocks < 1 || block < 1 || block > 1024 || n_sink < 0 ||
       window < 0)
     return VGSA_ERR_INVALID_ARG;
@@ -549,7 +547,7 @@ vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scor
   if (((int64_t)max_ctx + block - 1) / block > kMaxSelBlocks) return VGSA_ERR_UNSUPPORTED;
   if (batch == 0) return VGSA_OK;
   return hip_status(launch_select_blocks(batch, max_ctx, scores, seq_lens, k_blocks, block, n_sink,
-                                         window, idx, idx_stride, n_idx,
+                                         window, idx, idx_stride, n_idx, block_sums,
                                          static_cast<hipStream_t>(stream)));
 }
 

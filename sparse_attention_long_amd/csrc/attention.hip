@@ -358,9 +358,11 @@ void attn_partials_kernel(AttnArgs a) {
         sidx[lane] = p;
         uint32_t off = (uint32_t)p * D;
         if (a.paged) {
+          // entries past the list (p = 0) read row 0 of the sequence's own
+          // first block: another block may hold anything, and P = 0 times a
+          // non-finite V is NaN
           int blk = !listed ? btab[p >> 4] : it == 0 ? blk_pre[0] : it == 1 ? blk_pre[1]
                   : it == 2 ? blk_pre[2] : it == 3 ? blk_pre[3] : btab[p >> 4];
-          if (li >= end) blk = 0;  // entries past the list: any in-range row will do
           blk = min(max(blk, 0), a.num_blocks - 1);
           off = (((uint32_t)blk * a.hkv + g) * 16u + (uint32_t)(p & 15)) * D;
         }

@@ -166,6 +166,6 @@ constexpr int kMaxSelBlocks = 8704;
 hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
                                 const int32_t* seq_lens, int32_t k_blocks, int32_t block,
                                 int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
-                                int32_t* n_idx, hipStream_t stream);
+                                int32_t* n_idx, float* block_sums, hipStream_t stream);
 
 }  // namespace vgsa

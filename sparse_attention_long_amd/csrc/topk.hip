@@ -575,31 +575,29 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
 // row go to LDS, one selection stage runs over them (keys in registers: a
 // row has at most kMaxSelBlocks blocks), and the kept blocks are written out
 // expanded to their positions, ascending, so the list feeds the sparse
-// attention call as it is.
+// attention call as it is.  With bsum_out the fp32 block sums the ranking
+// compared are also written out ([B][ceil(max_ctx / block)], blocks below
+// ceil(L / block)), so a caller can check them and rank them itself.
 template <bool VEC>
 __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
     int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     int32_t k_blocks, int32_t block, int32_t n_sink, int32_t window, int32_t* __restrict__ idx,
-    int32_t idx_stride, int32_t* __restrict__ n_idx) {
+    int32_t idx_stride, int32_t* __restrict__ n_idx, float* __restrict__ bsum_out) {
   __shared__ SelectLds sh;
   __shared__ __align__(16) float s_bsum[kMaxSelBlocks];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int L = min(max(seq_lens[b], 0), max_ctx);
   const int nb = (L + block - 1) / block;
   int32_t* out = idx + (size_t)b * idx_stride;
-  if (nb <= k_blocks) {
-    for (int j = tid; j < L; j += kThreadsTk) out[j] = j;
-    if (tid == 0) n_idx[b] = L;
-    return;
-  }
+  const bool keep_all = nb <= k_blocks;
   // forced blocks: [0, s_end) hold the sinks, [w_start, nb) the window
   const int s_end = min((n_sink + block - 1) / block, nb);
   const int w_start = window > 0 ? max(s_end, max(0, L - window) / block) : nb;
-  const int r = k_blocks - (s_end + (nb - w_start));  // >= 0: checked on the host
+  const int r = keep_all ? 0 : k_blocks - (s_end + (nb - w_start));  // >= 0: checked on the host
   const int head_pos = min(L, s_end * block), tail0 = w_start * block;
   const int tail_pos = w_start < nb ? L - tail0 : 0;
 
-  if (r > 0) {
+  if (r > 0 || bsum_out != nullptr) {
     // block sums (members below L only), float32 in position order
     const float* sc = scores + (size_t)b * max_ctx;
     if (VEC && block == 16) {
@@ -647,6 +645,18 @@ __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
         s_bsum[i] = sum;
       }
     }
+    if (bsum_out != nullptr) {
+      // each thread reads back only the sums it wrote itself
+      const int nbs = (max_ctx + block - 1) / block;
+      for (int i = tid; i < nb; i += kThreadsTk) bsum_out[(size_t)b * nbs + i] = s_bsum[i];
+    }
+  }
+  if (keep_all) {
+    for (int j = tid; j < L; j += kThreadsTk) out[j] = j;
+    if (tid == 0) n_idx[b] = L;
+    return;
+  }
+  if (r > 0) {
     sh.taken[tid] = 0u;  // one round: word t holds blocks 32t .. 32t + 31
     sh.in_bin[tid] = 0u;
     select_stage<true, false>(sh, s_bsum, kMaxSelBlocks, 1, s_end, w_start, (uint32_t)r);
@@ -1043,17 +1053,17 @@ hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float*
 hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
                                 const int32_t* seq_lens, int32_t k_blocks, int32_t block,
                                 int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
-                                int32_t* n_idx, hipStream_t stream) {
+                                int32_t* n_idx, float* block_sums, hipStream_t stream) {
   if ((max_ctx + block - 1) / block > kMaxSelBlocks) return hipErrorInvalidValue;
   const bool vec = max_ctx % 4 == 0 && block % 4 == 0 &&
                    (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   const dim3 grid(batch), block_dim(kThreadsTk);
   if (vec)
     hipLaunchKernelGGL(select_blocks_kernel<true>, grid, block_dim, 0, stream, max_ctx, scores,
-                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx);
+                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx, block_sums);
   else
     hipLaunchKernelGGL(select_blocks_kernel<false>, grid, block_dim, 0, stream, max_ctx, scores,
-                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx);
+                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx, block_sums);
   return hipGetLastError();
 }
 

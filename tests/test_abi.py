@@ -202,14 +202,14 @@ def test_aggregate_and_select_argument_checks(lib):
     assert H(2, 100, FAKE, FAKE, FAKE, 0, 0, 0, 0, FAKE, 8, FAKE, None) == INVALID    # k < 1
     assert H(2, 262145, FAKE, FAKE, FAKE, 8, 2, 2, 2, FAKE, 8, FAKE, None) == UNSUPPORTED
     K = lib.vgsa_select_blocks
-    assert K(0, 100, FAKE, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None) == OK        # empty batch
-    assert K(2, 100, FAKE, FAKE, 8, 0, 4, 16, FAKE, 128, FAKE, None) == INVALID     # block < 1
-    assert K(2, 100, FAKE, FAKE, 8, 2048, 4, 16, FAKE, 16384, FAKE, None) == INVALID  # block > 1024
-    assert K(2, 100, FAKE, FAKE, 2, 16, 4, 16, FAKE, 128, FAKE, None) == INVALID    # 1 + 1 + 1 > 2
-    assert K(2, 100, FAKE, FAKE, 3, 16, 4, 16, FAKE, 47, FAKE, None) == INVALID     # idx_stride < 48
-    assert K(2, 100, None, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None) == INVALID
-    assert K(2, 100, FAKE, FAKE, 8, 16, -1, 16, FAKE, 128, FAKE, None) == INVALID
-    assert K(2, 16 * 8704 + 1, FAKE, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None) == UNSUPPORTED
+    assert K(0, 100, FAKE, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None, None) == OK        # empty batch
+    assert K(2, 100, FAKE, FAKE, 8, 0, 4, 16, FAKE, 128, FAKE, None, None) == INVALID     # block < 1
+    assert K(2, 100, FAKE, FAKE, 8, 2048, 4, 16, FAKE, 16384, FAKE, None, None) == INVALID  # block > 1024
+    assert K(2, 100, FAKE, FAKE, 2, 16, 4, 16, FAKE, 128, FAKE, None, None) == INVALID    # 1 + 1 + 1 > 2
+    assert K(2, 100, FAKE, FAKE, 3, 16, 4, 16, FAKE, 47, FAKE, None, None) == INVALID     # idx_stride < 48
+    assert K(2, 100, None, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None, None) == INVALID
+    assert K(2, 100, FAKE, FAKE, 8, 16, -1, 16, FAKE, 128, FAKE, None, None) == INVALID
+    assert K(2, 16 * 8704 + 1, FAKE, FAKE, 8, 16, 4, 16, FAKE, 128, FAKE, None, None) == UNSUPPORTED
 
 
 def test_append_argument_checks(lib):
@@ -274,3 +274,12 @@ def test_select_workspace_sizes_and_validation(lib):
                                           fake, None, 0, None) == 3
     assert lib.vgsa_select_topk_hybrid_ws(4, 131072, fake, None, fake, 512, 100, 4, 64, fake, 512,
                                           fake, fake, ws(4, 131072), None) == 1
+
+
+def test_binding_refuses_accumulate_without_scores():
+    """aggregate_scores(accumulate=True) needs the scores to add to: the
+    binding raises before allocating anything or calling the library."""
+    import torch
+    with pytest.raises(ValueError, match="accumulate"):
+        B.aggregate_scores(torch.zeros(1, 8, 16), torch.zeros(1, dtype=torch.int32), 8, 8,
+                           accumulate=True)

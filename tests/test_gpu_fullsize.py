@@ -6,8 +6,11 @@ verify with the kv-group-summed logit epilogue, aggregate, select, then the
 sparse pass (sparse verify over the T rows and/or single-query draft steps
 whose lists carry the freshly drafted positions).  The oracle checks:
   * selection for every sequence, bit-exact on the GPU's own scores;
-  * outputs, lse, collected logits and scores on a sample of sequences
-    (first and last) and kv-heads (first and last), element by element.
+  * outputs, lse, collected logits and scores of every sequence, element by
+    element, on kv-head b mod Hkv of sequence b (plus the first and last
+    kv-heads for the first and last sequences).  Every sequence matters: the
+    ragged verify hands a long sequence's extra items to the workgroups of
+    other sequences.
 """
 import numpy as np
 import pytest
@@ -56,13 +59,18 @@ def test_fullsize_sampled(name):
             assert np.array_equal(idx_h[b, :n_h[b]], want[b]), f"{name} idx b={b}"
             assert set(x.planted[b].tolist()) <= set(want[b].tolist()), f"planted key dropped b={b}"
 
-        bs = sorted({0, w.batch - 1})
-        gs = sorted({0, w.num_kv_heads - 1})
         G = w.group
-        heads = [h for g in gs for h in range(g * G, (g + 1) * G)]
+
+        def heads_of(b):
+            gs = {b % w.num_kv_heads}
+            if b in (0, w.batch - 1):
+                gs |= {0, w.num_kv_heads - 1}
+            return sorted(gs), [h for g in sorted(gs) for h in range(g * G, (g + 1) * G)]
+
         lg_h = lg.cpu().numpy()
-        for b in bs:
+        for b in range(w.batch):
             say(f"[fullsize] {name} layer {layer}: oracle b={b}")
+            gs, heads = heads_of(b)
             qb, kb, vb = sub(x.q, b), sub(x.k, b), sub(x.v, b)
             o_ref, lse_ref = oracle.verify_attention(qb, kb, vb, lens[b:b + 1], heads=heads)
             assert_out_close(out[b:b + 1, heads], o_ref[:, heads], f"{name} b={b} verify out")
@@ -70,8 +78,8 @@ def test_fullsize_sampled(name):
             l_ref = oracle.collected_logits(qb, kb, lens[b:b + 1], w.collect_rows)
             absl = np.where(np.isneginf(l_ref), 0.0, np.abs(l_ref))
             grp = oracle.kvgroup_sum(l_ref, w.num_kv_heads)
-            assert_logits_close(lg_h[b:b + 1], grp, f"{name} b={b} group logits",
-                                floor=oracle.kvgroup_sum(absl, w.num_kv_heads))
+            assert_logits_close(lg_h[b:b + 1, gs], grp[:, gs], f"{name} b={b} group logits",
+                                floor=oracle.kvgroup_sum(absl, w.num_kv_heads)[:, gs])
             assert_logits_close(sc[b:b + 1], oracle.aggregate_scores(l_ref), f"{name} b={b} scores",
                                 floor=oracle.aggregate_scores(absl))
 
@@ -80,7 +88,8 @@ def test_fullsize_sampled(name):
             so, sl = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n_idx,
                                          block_table=d.block_table, max_ctx=d.max_ctx)
             torch.cuda.synchronize()
-            for b in bs:
+            for b in range(w.batch):
+                heads = heads_of(b)[1]
                 o_ref, lse_ref = oracle.sparse_attention(sub(x.q, b), sub(x.k, b), sub(x.v, b),
                                                          lens[b:b + 1], [want[b]], heads=heads)
                 assert_out_close(so[b:b + 1, heads], o_ref[:, heads], f"{name} b={b} sparse out")
@@ -96,7 +105,8 @@ def test_fullsize_sampled(name):
             so, sl = Bn.sparse_attention(qd, d.k, d.v, dev_i32(lens_s), idx, n_idx, tail=s,
                                          block_table=d.block_table, max_ctx=d.max_ctx)
             torch.cuda.synchronize()
-            for b in bs:
+            for b in range(w.batch):
+                heads = heads_of(b)[1]
                 o_ref, lse_ref = oracle.sparse_attention(sub(x.q_draft[s - 1], b), sub(x.k, b),
                                                          sub(x.v, b), lens_s[b:b + 1], [lists[b]],
                                                          heads=heads)

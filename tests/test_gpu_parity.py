@@ -12,8 +12,8 @@ import torch
 import oracle
 from sparse_attention_long_amd import binding as Bn
 from sparse_attention_long_amd import workloads as W
-from tests.gpu_helpers import (assert_lse_close, assert_logits_close, assert_out_close, dev_i32,
-                               say, to_device)
+from tests.gpu_helpers import (assert_lse_close, assert_logits_close, assert_out_close, dev_bf16,
+                               dev_i32, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,8 +35,9 @@ CASES = {
                               ctx=None, ctx_range=(40, 300), paged=True, budget=48, n_sink=4,
                               window=12, seed=15),
     "ctx2k_b1_h32kv8_d128": W.WORKLOADS["ctx2k_b1_h32kv8_d128"],
-    # 8 x 8 workgroup rows -> 4224-position chunks: a mid-chunk logit flush,
-    # ragged last chunks, chunks shorter than the LDS logit buffer
+    # 8 x 8 workgroup rows -> 4224-position chunks: ragged last chunks and
+    # chunks shorter than the LDS logit buffer (contiguous launches hold 8192
+    # positions, so nothing flushes mid-chunk here; the paged twin does)
     "chunk4224_g1t3_d64": W.small("c4224", batch=8, num_q_heads=8, num_kv_heads=8, head_dim=64,
                                   gamma=2, lens=(33000, 20000, 4500, 8300, 12289, 30000, 4097, 16500),
                                   budget=300, n_sink=4, window=32, seed=16),
@@ -355,14 +356,33 @@ def test_hybrid_select_on_verify_scores(name):
 
 # ------------------------------------------------------------------ block selection
 def _blocks_case(scores_h, lens, kb, block, n_sink, window, stride=None):
-    scores = torch.from_numpy(np.ascontiguousarray(scores_h, dtype=np.float32)).cuda()
+    """Block selection on the GPU against the oracle: the GPU's fp32 block
+    sums against the exact fp64 sums (the scores tolerance, 1e-3 * max(1,
+    sum of |members|); -inf blocks exactly), and the kept positions bit-exact
+    against the oracle's selection ranking the GPU's own block sums (the same
+    values compared on both sides)."""
+    scores_h = np.ascontiguousarray(scores_h, dtype=np.float32)
+    scores = torch.from_numpy(scores_h).cuda()
+    nbs = -(-scores_h.shape[1] // block)
+    sums = torch.full((scores_h.shape[0], nbs), float("nan"), dtype=torch.float32, device="cuda")
     idx, n = Bn.select_blocks(scores, dev_i32(lens), kb, block, n_sink, window,
-                              idx_stride=stride or kb * block)
+                              idx_stride=stride or kb * block, block_sums=sums)
     torch.cuda.synchronize()
-    idx_h, n_h = idx.cpu().numpy(), n.cpu().numpy()
+    idx_h, n_h, sums_h = idx.cpu().numpy(), n.cpu().numpy(), sums.cpu().numpy()
     out = []
     for b, L in enumerate(lens):
-        want = oracle.select_blocks(scores_h[b], int(L), kb, block, n_sink, window)
+        nb = -(-int(L) // block)
+        ref = oracle.block_sums(scores_h[b], int(L), block)
+        got = sums_h[b, :nb].astype(np.float64)
+        inf = np.isinf(ref)
+        assert np.array_equal(got[inf], ref[inf]), (b, L, block, "infinite block sums")
+        mag = np.array([np.abs(scores_h[b, i * block:min(int(L), (i + 1) * block)].astype(np.float64)).sum()
+                        for i in range(nb)])
+        err = np.abs(got[~inf] - ref[~inf])
+        tol = 1e-3 * np.maximum(1.0, mag[~inf])
+        assert np.all(err <= tol), (b, L, block, float(err.max(initial=0.0)))
+        assert np.all(np.isnan(sums_h[b, nb:])), (b, L, block, "sums written past the length")
+        want = oracle.select_blocks(scores_h[b], int(L), kb, block, n_sink, window, sums=got)
         assert n_h[b] == len(want), (b, L, kb, block, n_h[b], len(want))
         assert np.array_equal(idx_h[b, :n_h[b]], want), (b, L, kb, block, n_sink, window)
         out.append(want)
@@ -505,7 +525,7 @@ def test_sparse_one_launch_merge_repeats_and_resets(name):
         o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, x.seq_lens, lists)
         assert_out_close(out, o_ref, f"{name} rep {rep} out")
         assert_lse_close(lse, lse_ref, f"{name} rep {rep} lse")
-        assert int(ws[nbytes - sync_bytes:].count_nonzero()) == 0, "counters not reset"
+        assert int(ws[:sync_bytes].count_nonzero()) == 0, "counters not reset"
     # the two-phase form on its own workspace agrees
     ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     idx_d, n_d = dev_i32(idx), dev_i32(n)
@@ -518,6 +538,75 @@ def test_sparse_one_launch_merge_repeats_and_resets(name):
     np.testing.assert_allclose(o2.float().cpu().numpy(), out.float().cpu().numpy(), atol=8e-3,
                                rtol=1e-2)
     np.testing.assert_allclose(l2.cpu().numpy(), lse.cpu().numpy(), atol=1e-5)
+
+
+@pytest.mark.parametrize("count", [45, 700, 1500])
+def test_sparse_paged_ignores_blocks_it_does_not_own(count):
+    """A paged pool whose blocks outside the sequences' tables hold NaN (as a
+    pool of freed or never-written blocks may): every gathered row, the
+    padding of a list's last partial tile included, comes from a block the
+    sequence owns, so the outputs stay finite and match the oracle.  Block
+    ids are shifted by one so that pool block 0 is one of the NaN blocks."""
+    w = CASES["paged_g8t6_d64"]
+    say(f"[sparse paged NaN pool] count={count}")
+    x = W.make_layer(w)
+    nan_blk = np.full((1,) + x.k_pool.shape[1:], 0x7FC0, dtype=np.uint16)  # bf16 quiet NaN
+    kp = np.concatenate([nan_blk, x.k_pool, nan_blk, nan_blk])
+    vp = np.concatenate([nan_blk, x.v_pool, nan_blk, nan_blk])
+    tab = x.block_table.copy()
+    for b, L in enumerate(x.seq_lens):
+        tab[b, :-(-int(L) // 16)] += 1
+    q = dev_bf16(x.q)
+    k, v, bt, lens = dev_bf16(kp), dev_bf16(vp), dev_i32(tab), dev_i32(x.seq_lens)
+    idx, n = W.index_lists(w.seed + 90 + count, x.seq_lens, count=count, stride=count)
+    for qrows in (w.q_len, 1):
+        out, lse = Bn.sparse_attention(q[:, :, :qrows].contiguous(), k, v, lens, dev_i32(idx),
+                                       dev_i32(n), block_table=bt, max_ctx=w.max_ctx())
+        torch.cuda.synchronize()
+        lists = [idx[b, :n[b]] for b in range(w.batch)]
+        o_ref, lse_ref = oracle.sparse_attention(x.q[:, :, :qrows], x.k, x.v, x.seq_lens, lists)
+        assert_out_close(out, o_ref, f"NaN pool count {count} rows {qrows} out")
+        assert_lse_close(lse, lse_ref, f"NaN pool count {count} rows {qrows} lse")
+    if count == 45:  # the verify pass reads owned blocks only, too
+        out, lse, lg = Bn.verify_attention(q, k, v, lens, block_table=bt, max_ctx=w.max_ctx(),
+                                           collect_rows=w.collect_rows, layout="kvgroup_sum")
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.verify_attention(x.q, x.k, x.v, x.seq_lens)
+        assert_out_close(out, o_ref, "NaN pool verify out")
+        assert_lse_close(lse, lse_ref, "NaN pool verify lse")
+        for b, L in enumerate(x.seq_lens):
+            assert np.all(~np.isnan(lg[b, :, :int(L)].cpu().numpy())), "NaN pool verify logits"
+
+
+def test_sparse_workspace_reused_across_split_plans():
+    """One zero-filled workspace, sized for the longest span, serves draft
+    steps whose split plans differ: with 4093 listed positions the tails 1..6
+    plan different split counts (the span crosses a chunk boundary), then
+    tail 1 again.  Each call matches the oracle and leaves the counters
+    zero."""
+    w = W.small("reuse", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, gamma=0,
+                lens=(6000,), budget=64, n_sink=4, window=16, seed=47)
+    x = W.make_layer(w)
+    d = to_device(x)
+    count = 4093
+    desc = Bn.make_desc(d.q, d.k, None, d.max_ctx)
+    plans = {Bn.split_plan(desc, count + t) for t in range(1, 7)}
+    assert len(plans) > 1, plans  # the case exercises a change of plan
+    ws = torch.zeros(Bn.sparse_workspace_bytes(desc, count + 6), dtype=torch.uint8, device="cuda")
+    sync_bytes = -(-w.batch * w.num_kv_heads * 4 // 256) * 256
+    for tail in (1, 2, 3, 4, 5, 6, 1):
+        say(f"[sparse workspace reuse] tail={tail}")
+        lens = np.array([int(x.seq_lens[0]) - 6], np.int32)
+        idx, n = W.index_lists(w.seed + 3, lens, count=count, stride=count)
+        lens_t = lens + np.int32(tail)
+        out, lse = Bn.sparse_attention(d.q, d.k, d.v, dev_i32(lens_t), dev_i32(idx), dev_i32(n),
+                                       max_ctx=d.max_ctx, tail=tail, workspace=ws)
+        torch.cuda.synchronize()
+        lists = [np.concatenate([idx[0, :n[0]], np.arange(lens_t[0] - tail, lens_t[0])])]
+        o_ref, lse_ref = oracle.sparse_attention(x.q, x.k, x.v, lens_t, lists)
+        assert_out_close(out, o_ref, f"reuse tail {tail} out")
+        assert_lse_close(lse, lse_ref, f"reuse tail {tail} lse")
+        assert int(ws[:sync_bytes].count_nonzero()) == 0, f"counters not reset after tail {tail}"
 
 
 @pytest.mark.parametrize("name", ["g4t5_d64", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])

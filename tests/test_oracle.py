@@ -369,14 +369,31 @@ def test_select_blocks_reductions_and_edges():
     for k, ns, win in [(40, 4, 16), (1, 0, 0), (100, 0, 99)]:
         assert np.array_equal(oracle.select_blocks(sc, L, k, 1, ns, win),
                               oracle.select_topk(sc, L, k, ns, win))
-    # block sums: float32, the partial last block holds positions 32..36 only;
-    # exact on integer scores, within float32 rounding otherwise
-    bs = oracle.block_sums(sc, 37, 16)
-    assert bs.dtype == np.float32 and bs.shape == (3,)
-    np.testing.assert_allclose(bs, [sc[0:16].astype(np.float64).sum(), sc[16:32].astype(np.float64).sum(),
-                                    sc[32:37].astype(np.float64).sum()], rtol=1e-5, atol=1e-5)
+    # block sums: the partial last block holds positions 32..36 only; on
+    # integer scores they equal the integer sums (python ints, exact)
     si = rng.integers(-50, 50, size=37).astype(np.float32)
-    assert list(oracle.block_sums(si, 37, 16)) == [si[0:16].sum(), si[16:32].sum(), si[32:].sum()]
+    bs = oracle.block_sums(si, 37, 16)
+    assert bs.dtype == np.float64 and bs.shape == (3,)
+    ints = [int(x) for x in si]
+    assert list(bs) == [sum(ints[0:16]), sum(ints[16:32]), sum(ints[32:37])]
+    # block 1: every block sum is its one score
+    assert np.array_equal(oracle.block_sums(sc, 37, 1), sc[:37].astype(np.float64))
+    # exact, not float32 in position order: 2^24 + 1 + 1 + 1 + 1 is 2^24 + 4
+    # (a float32 running sum stays at 2^24), and 1e8 - 1e8 + 0.5 keeps the 0.5
+    big = np.array([2.0 ** 24, 1, 1, 1, 1, 1e8, -1e8, 0.5], dtype=np.float32)
+    assert list(oracle.block_sums(big, 8, 5)) == [2.0 ** 24 + 4, 0.5]
+    # the block sums of a row add up to its total (dyadic scores: exact)
+    dy = rng.integers(-1000, 1000, size=500).astype(np.float32) / np.float32(64)
+    assert oracle.block_sums(dy, 500, 16).sum() == float(dy.astype(np.float64).sum())
+    # a -inf member makes its block -inf
+    sinf = np.ones(40, np.float32)
+    sinf[17] = -np.inf
+    assert list(oracle.block_sums(sinf, 40, 16)) == [16.0, -np.inf, 8.0]
+    # ranking given sums: the sums decide, not the scores
+    given = np.array([0.0, 5.0, 1.0, 9.0, 2.0])
+    assert list(oracle.select_blocks(si, 37, 2, 8, 0, 0, sums=given)) == list(range(8, 16)) + list(range(24, 32))
+    with pytest.raises(ValueError):
+        oracle.select_blocks(si, 37, 2, 8, 0, 0, sums=given[:3])
     # k_blocks covering every block keeps everything; L = 0 keeps nothing
     assert list(oracle.select_blocks(sc, 37, 3, 16, 1, 1)) == list(range(37))
     assert list(oracle.select_blocks(sc, 0, 3, 16, 1, 1)) == []
