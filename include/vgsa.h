@@ -75,7 +75,9 @@ typedef enum vgsa_status {
   VGSA_ERR_INVALID_ARG = 1, /* a scalar, shape or pointer is invalid         */
   VGSA_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels implement */
   VGSA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned    */
-  VGSA_ERR_HIP = 4          /* a HIP launch failed                           */
+  VGSA_ERR_HIP = 4,         /* a HIP launch failed                           */
+  VGSA_ERR_TOO_LARGE = 5    /* needs more than the library's static scratch
+                               (vgsa_verify_attention_noalloc only)          */
 } vgsa_status;
 
 /* Layout of the collected pre-softmax logits written by the verify pass.
@@ -184,6 +186,32 @@ vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, con
                                   uint64_t head_mask, vgsa_logit_layout layout, float* logits,
                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/* 1 (no allocation).  For callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it.
+ * The same call as vgsa_verify_attention, same arguments (the caller still
+ * passes q, the caches, logits, out and lse) and bit-identical results, but
+ * without a workspace: the split partials go to a static device array of
+ * vgsa_noalloc_scratch_bytes() bytes (64 MiB) that the library holds on each
+ * GPU it runs on until the process ends.  The call allocates nothing and
+ * frees nothing.
+ *   - VGSA_ERR_TOO_LARGE, with nothing launched, when the desc needs more
+ *     than that (vgsa_verify_workspace_bytes(desc) > the scratch size).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (other streams, other host threads) race and give wrong
+ *     results.  Order them on one stream.  The array keeps the last call's
+ *     contents; nothing in it needs to start at zero (each call writes every
+ *     byte it reads).
+ *   - The array's device address is looked up on the first call made on each
+ *     device (that call must run with the device current).
+ */
+size_t vgsa_noalloc_scratch_bytes(void);
+vgsa_status vgsa_verify_attention_noalloc(const vgsa_attn_desc* desc, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          uint32_t collect_mask, uint64_t head_mask,
+                                          vgsa_logit_layout layout, float* logits, void* out,
+                                          float* lse, void* stream);
 
 /* 2. Aggregate collected logits into one score per position.
  *    (Vegas, "A. aggregated attention-logit selection": the sum over draft

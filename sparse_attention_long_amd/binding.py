@@ -65,6 +65,9 @@ SIGNATURES = {
     "vgsa_verify_finish": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp, c_i32,
                                    c_i32, c_i32, c_vp, c_vp, c_vp]),
     "vgsa_append_positions": (c_i32, [c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]),
+    "vgsa_noalloc_scratch_bytes": (c_sz, []),
+    "vgsa_verify_attention_noalloc": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp,
+                                              c_vp, c_u32, c_u64, c_i32, c_vp, c_vp, c_vp, c_vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -234,6 +237,33 @@ def verify_attention(q, k_cache, v_cache, seq_lens, *, block_table=None, max_ctx
         hmask, lay, _p(logits) if lay != LOGITS_NONE else None, _p(out), _p(lse), _p(ws), ws.numel(),
         _stream(dev)), "vgsa_verify_attention")
     return out, lse, logits
+
+
+def verify_attention_noalloc(q, k_cache, v_cache, seq_lens, out, lse, logits=None, *,
+                             block_table=None, max_ctx=None,
+                             collect_rows: Optional[Sequence[int]] = None,
+                             heads: Optional[Sequence[int]] = None, layout: str = "kvgroup_sum",
+                             scale: float = 0.0):
+    """vgsa_verify_attention_noalloc: vgsa_verify_attention with the library's
+    static scratch as the workspace.  The caller passes every output (out,
+    lse, and logits unless layout is "none"); nothing is allocated here or in
+    the library."""
+    _check_attn(q, k_cache, v_cache, seq_lens, block_table)
+    desc = make_desc(q, k_cache, block_table, max_ctx, scale)
+    lay = _LAYOUTS[layout]
+    T = q.shape[2]
+    mask = row_mask((0, T - 1) if collect_rows is None else collect_rows, T)
+    if lay != LOGITS_NONE and logits is None:
+        raise ValueError("logits must be given unless layout is 'none'")
+    _check(load().vgsa_verify_attention_noalloc(
+        ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens), mask,
+        head_mask(heads, q.shape[1]), lay, _p(logits) if lay != LOGITS_NONE else None, _p(out),
+        _p(lse), _stream(q.device)), "vgsa_verify_attention_noalloc")
+    return out, lse, logits
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().vgsa_noalloc_scratch_bytes())
 
 
 def aggregate_scores(logits, seq_lens, num_q_heads: int, num_kv_heads: int, *,

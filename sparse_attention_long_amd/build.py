@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvgsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "attention.hip", "scores.hip", "topk.hip"]
+SOURCES = ["api.cpp", "attention.hip", "scores.hip", "topk.hip", "noalloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -185,6 +185,7 @@ const char* vgsa_status_string(vgsa_status status) {
     case VGSA_ERR_UNSUPPORTED: return "unsupported configuration";
     case VGSA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case VGSA_ERR_HIP: return "HIP launch failed";
+    case VGSA_ERR_TOO_LARGE: return "request exceeds the library's static scratch";
   }
   return "unknown status";
 }

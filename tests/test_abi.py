@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -283,3 +283,24 @@ def test_binding_refuses_accumulate_without_scores():
     with pytest.raises(ValueError, match="accumulate"):
         B.aggregate_scores(torch.zeros(1, 8, 16), torch.zeros(1, dtype=torch.int32), 8, 8,
                            accumulate=True)
+
+
+def test_noalloc_verify_rejects_requests_beyond_its_scratch(lib):
+    """vgsa_verify_attention_noalloc refuses, before any HIP call, a desc whose
+    split partials exceed the static scratch, and reports an invalid desc as
+    the workspace form does."""
+    scratch = lib.vgsa_noalloc_scratch_bytes()
+    assert scratch == 64 << 20
+    N = lib.vgsa_verify_attention_noalloc
+    # batch 64 x 64 q-heads x 5 rows at 32K: 4 x the headline's partials
+    big = B.AttnDesc(64, 64, 8, 128, 5, 32768, 0, 0, 0, 0.0)
+    assert lib.vgsa_verify_workspace_bytes(ctypes.byref(big)) > scratch
+    assert N(ctypes.byref(big), FAKE, FAKE, FAKE, None, FAKE, 17, B.ALL_HEADS, 2, FAKE, FAKE, FAKE,
+             None) == 5
+    assert B.status_string(5) == "request exceeds the library's static scratch"
+    bad = B.AttnDesc(2, 6, 4, 128, 5, 1000, 0, 0, 0, 0.0)   # Hq not a multiple of Hkv
+    assert N(ctypes.byref(bad), FAKE, FAKE, FAKE, None, FAKE, 17, B.ALL_HEADS, 2, FAKE, FAKE, FAKE,
+             None) == INVALID
+    odd = B.AttnDesc(2, 8, 4, 96, 5, 1000, 0, 0, 0, 0.0)    # head_dim 96
+    assert N(ctypes.byref(odd), FAKE, FAKE, FAKE, None, FAKE, 17, B.ALL_HEADS, 2, FAKE, FAKE, FAKE,
+             None) == UNSUPPORTED
