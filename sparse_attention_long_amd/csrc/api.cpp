@@ -278,7 +278,10 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   // one split for lists up to kDirectSpan (the output is written directly);
   // longer lists split, and with `fused` the splits merge in the same launch
   const SplitPlan p = make_plan(d.batch, d.num_kv_heads, span);
-  // fused: the counters first, the partials after them
+  // fused: the counters first, the partials after them; the fused merge
+  // addresses the partials with 32-bit byte offsets
+  if (fused && p.num_splits > 1 && partial_bytes(d, p) > (size_t)0x7FFFFFFF)
+    return VGSA_ERR_UNSUPPORTED;
   const size_t sync_bytes = fused ? sparse_sync_bytes(d) : 0;
   st = check_workspace(workspace, workspace_bytes, sync_bytes + partial_bytes(d, p));
   if (st != VGSA_OK) return st;

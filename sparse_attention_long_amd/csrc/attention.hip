@@ -788,19 +788,28 @@ void attn_partials_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4*>(obuf + (wave * RP + qb * 16 + c16) * CS + j * 16 + 4 * kg) =
             oacc[r * DBR + j][qb] * scl[qb];
     __syncthreads();
-    for (int e = threadIdx.x; e < rows * DC; e += NT) {
-      const int m = e / DC, dc = e % DC;
-      float acc = 0.f;
+    // four consecutive columns per thread: 16-byte LDS reads, 16-byte partial
+    // stores, 8-byte output stores
+    constexpr int DQ = DC / 4;
+    for (int e = threadIdx.x; e < rows * DQ; e += NT) {
+      const int m = e / DQ, dq = e % DQ;
+      f32x4 acc = *reinterpret_cast<const f32x4*>(obuf + m * CS + dq * 4);
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) acc += obuf[(w * RP + m) * CS + dc];
-      const int d = r * DC + dc;
-      float* dst = a.part_o + ((row_base + m) * S + split) * D + d;
-      if (a.direct)
-        a.out[(row_base + m) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc * s_inv[m]));
-      else if (SPARSE && a.fuse)  // read back in this launch, maybe from another XCD
-        __hip_atomic_store(dst, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else  // written once, read once (next launch)
-        __builtin_nontemporal_store(acc, dst);
+      for (int w = 1; w < WAVES; ++w) acc += *reinterpret_cast<const f32x4*>(obuf + (w * RP + m) * CS + dq * 4);
+      const int d = r * DC + dq * 4;
+      const size_t po = ((row_base + m) * S + split) * D + d;  // partial element offset
+      if (a.direct) {
+        const float inv = s_inv[m];
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv)) |
+                            (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[1] * inv)) << 16;
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)(acc[2] * inv)) |
+                            (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[3] * inv)) << 16;
+        *reinterpret_cast<u32x2*>(a.out + (row_base + m) * D + d) = u32x2{lo, hi};
+      } else if (SPARSE && a.fuse) {  // read back in this launch, maybe from another XCD
+        store4_device(a.part_o, (uint32_t)(po * 4), make_float4(acc[0], acc[1], acc[2], acc[3]));
+      } else {  // written once, read once (next launch)
+        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(a.part_o + po));
+      }
     }
     __syncthreads();
   }
@@ -811,8 +820,7 @@ void attn_partials_kernel(AttnArgs a) {
     } else {
       const size_t prow = (row_base + threadIdx.x) * S + split;
       if (SPARSE && a.fuse) {
-        __hip_atomic_store(a.part_ml + prow * 2 + 0, rowM, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.part_ml + prow * 2 + 1, rowL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store2_device(a.part_ml, (uint32_t)(prow * 8), make_float2(rowM, rowL));
       } else {
         a.part_ml[prow * 2 + 0] = rowM;
         a.part_ml[prow * 2 + 1] = rowL;

@@ -8,6 +8,38 @@ namespace vgsa {
 // Threads of a combine / aggregate workgroup.
 constexpr int kMergeBlock = 256;
 
+// 16- and 8-byte accesses at device scope for partial results exchanged
+// inside one launch: the SC1 cache-policy bit makes a store write through, and
+// a load read past, the issuing XCD's L2, so another XCD sees the data without
+// a cache-wide write-back.  Buffer instructions take a wave-uniform base (the
+// partial array) and a 32-bit byte offset (the host keeps these arrays below
+// 2 GiB); the resource word is the gfx9 raw-buffer one.
+constexpr int kCpolSc1 = 16;
+constexpr int kRawBufferWord3 = 0x00020000;
+typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2m __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t device_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, kRawBufferWord3);
+}
+__device__ __forceinline__ void store4_device(float* base, uint32_t byte_off, float4 v) {
+  const u32x4m u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, device_rsrc(base), byte_off, 0, kCpolSc1);
+}
+__device__ __forceinline__ void store2_device(float* base, uint32_t byte_off, float2 v) {
+  const u32x2m u = {__float_as_uint(v.x), __float_as_uint(v.y)};
+  __builtin_amdgcn_raw_buffer_store_b64(u, device_rsrc(base), byte_off, 0, kCpolSc1);
+}
+__device__ __forceinline__ float4 load4_device(const float* base, uint32_t byte_off) {
+  const u32x4m u = __builtin_amdgcn_raw_buffer_load_b128(device_rsrc(base), byte_off, 0, kCpolSc1);
+  return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                     __uint_as_float(u[3]));
+}
+__device__ __forceinline__ float2 load2_device(const float* base, uint32_t byte_off) {
+  const u32x2m u = __builtin_amdgcn_raw_buffer_load_b64(device_rsrc(base), byte_off, 0, kCpolSc1);
+  return make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
+}
+
 // Splits (or logit rows) whose loads are issued together before any is used:
 // the merge is a chain of dependent HBM round trips otherwise.
 constexpr int kMergeBatch = 8;
@@ -41,14 +73,9 @@ __device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int 
     for (int i = 0; i < kMergeBatch; ++i) {
       if (s0 + i < nvalid) {
         if (COHERENT) {
-          const float* mp = reinterpret_cast<const float*>(ml + s0 + i);
-          const float* op = reinterpret_cast<const float*>(po + (size_t)(s0 + i) * Q);
-          m[i].x = __hip_atomic_load(mp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          m[i].y = __hip_atomic_load(mp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          o[i].x = __hip_atomic_load(op, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          o[i].y = __hip_atomic_load(op + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          o[i].z = __hip_atomic_load(op + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          o[i].w = __hip_atomic_load(op + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const size_t ps = (size_t)row * a.part_splits + s0 + i;  // partial row of split s0 + i
+          m[i] = load2_device(a.part_ml, (uint32_t)(ps * 8));
+          o[i] = load4_device(a.part_o, (uint32_t)((ps * Q + t) * 16));
         } else {
           m[i] = ml[s0 + i];
           o[i] = po[(size_t)(s0 + i) * Q];
