@@ -301,6 +301,10 @@ void attn_partials_kernel(AttnArgs a) {
     }
   }
   const int lim_min = L - T;  // every row sees positions <= L - T
+  // kv-group logits: weight 1 for a collected row of this lane, else 0
+  float rowc_w[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) rowc_w[qb] = rowc[qb] >= 0 ? 1.f : 0.f;
   // per-head logits: the collected rows of block qb, bit c16 (wave-uniform),
   // so blocks and row pairs with nothing to write are skipped
   uint32_t cmask[QB];
@@ -589,18 +593,25 @@ void attn_partials_kernel(AttnArgs a) {
         __builtin_amdgcn_wave_barrier();
       }
     } else if (EMIT == VGSA_LOGITS_KVGROUP_SUM) {
-      // v8[pb*4 + r]: this lane's collected rows summed, at position pb*16 + 4*kg + r.
+      // v8[pb*4 + r]: this lane's collected rows summed, at position pb*16 +
+      // 4*kg + r: a 0/1 weight per row (collected or not) times its S^T
+      // value, so no branch or select per term.  The earliest collected row
+      // sees a prefix of what the later ones see, so a position is hidden
+      // from a collected row iff it is hidden from that one: past its causal
+      // limit (one wave-uniform count per tile) the sum is -inf.  A kv-group
+      // with no collected head sums to 0 at every position.
+      const int row_first = __builtin_ctz(a.row_mask);
+      const int vis0 = (full || gmask == 0ull)
+                           ? kTile : max(0, min(L - T + row_first, ts + n_in - 1) - ts + 1);
       float v8[8];
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float acc = 0.f;
-          const int e = pb * 16 + 4 * kg + r;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            if (rowc[qb] >= 0) acc += (full || e < vis[qb]) ? sacc[pb][qb][r] * a.scale : kNegInf;
-          v8[pb * 4 + r] = acc;
+          for (int qb = 0; qb < QB; ++qb) acc = __builtin_fmaf(rowc_w[qb], sacc[pb][qb][r], acc);
+          v8[pb * 4 + r] = (pb * 16 + 4 * kg + r) < vis0 ? acc * a.scale : kNegInf;
         }
       // Reduce-scatter over the 16 query-row lanes: after the four steps lane
       // c16 holds the full sum of position pb = bit 3, r = 2*bit 2 + bit 1.
