@@ -88,6 +88,7 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
   a.num_blocks = d.num_blocks;
   a.num_splits = p.num_splits;
   a.chunk = p.chunk;
+  a.waves = p.waves;
   a.scale = effective_scale(d);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   const Carve c = carve(d, p, workspace);
@@ -130,31 +131,38 @@ vgsa_status check_attn_pointers(const vgsa_attn_desc& d, const void* q, const vo
 
 }  // namespace
 
-SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span) {
+SplitPlan make_plan(const vgsa_attn_desc& d, int32_t span) {
   if (span < 1) span = 1;  // callers validate; keep the plan total anyway
-  const int64_t bh = (int64_t)(batch > 0 ? batch : 1) * num_kv_heads;
+  const int waves = attention_waves(d);
+  const bool wide = waves == kWavesWide;
+  const int64_t min_chunk = wide ? kMinChunkWide : kMinChunk;
+  const int64_t plan_chunk = wide ? kPlanChunkWide : kPlanChunk;
+  const int64_t max_chunk = wide ? kMaxChunkWide : kMaxChunk;
+  const int64_t target = wide ? kTargetWorkgroupsWide : kTargetWorkgroups;
+  const int64_t bh = (int64_t)(d.batch > 0 ? d.batch : 1) * d.num_kv_heads;
   const int64_t max_splits =
-      span <= kDirectSpan ? 1 : (ceil_div(span, kMinChunk) > 0 ? ceil_div(span, kMinChunk) : 1);
-  int64_t s = ceil_div(kTargetWorkgroups, bh);
+      span <= kDirectSpan ? 1 : (ceil_div(span, min_chunk) > 0 ? ceil_div(span, min_chunk) : 1);
+  int64_t s = ceil_div(target, bh);
   if (s < 1) s = 1;
   if (s > max_splits) s = max_splits;
-  int64_t chunk = ceil_div(ceil_div(span, s), kMinChunk) * kMinChunk;
-  if (chunk > kPlanChunk) {
-    chunk = kPlanChunk;
+  int64_t chunk = ceil_div(ceil_div(span, s), min_chunk) * min_chunk;
+  if (chunk > plan_chunk) {
+    chunk = plan_chunk;
     // A last split of a sliver would add a workgroup to every (sequence,
     // kv-head), and one more split changes which workgroups share a CU and
     // an XCD (17 splits measured 10 % slower than 16 at 128K x b8): the
-    // sliver is spread over the other splits instead (chunk <= kMaxChunk).
-    const int64_t n = ceil_div(span, (int64_t)kPlanChunk);
-    if (n > 1 && span - (n - 1) * kPlanChunk <= kPlanChunk / 8)
-      chunk = ceil_div(ceil_div(span, n - 1), kMinChunk) * kMinChunk;
+    // sliver is spread over the other splits instead (chunk <= max_chunk).
+    const int64_t n = ceil_div(span, plan_chunk);
+    if (n > 1 && span - (n - 1) * plan_chunk <= max_chunk - plan_chunk)
+      chunk = ceil_div(ceil_div(span, n - 1), min_chunk) * min_chunk;
   }
   s = ceil_div(span, chunk);
   SplitPlan p;
   p.num_splits = (int32_t)s;
   p.chunk = (int32_t)chunk;
-  p.part_splits = (s > 1 && batch > 1 && batch <= kMaxBalanceBatch) ? (int32_t)(kBalanceSplits * s)
-                                                                    : (int32_t)s;
+  p.part_splits = (s > 1 && d.batch > 1 && d.batch <= kMaxBalanceBatch)
+                      ? (int32_t)(kBalanceSplits * s) : (int32_t)s;
+  p.waves = waves;
   return p;
 }
 
@@ -197,7 +205,7 @@ vgsa_status vgsa_split_plan(const vgsa_attn_desc* desc, int32_t span, int32_t* n
   const vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   if (span < 1 || num_splits == nullptr || chunk == nullptr) return VGSA_ERR_INVALID_ARG;
-  const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, span);
+  const SplitPlan p = make_plan(*desc, span);
   *num_splits = p.num_splits;
   *chunk = p.chunk;
   return VGSA_OK;
@@ -205,13 +213,13 @@ vgsa_status vgsa_split_plan(const vgsa_attn_desc* desc, int32_t span, int32_t* n
 
 size_t vgsa_verify_workspace_bytes(const vgsa_attn_desc* desc) {
   if (check_desc(desc) != VGSA_OK) return 0;
-  return partial_bytes(*desc, make_plan(desc->batch, desc->num_kv_heads, desc->max_ctx));
+  return partial_bytes(*desc, make_plan(*desc, desc->max_ctx));
 }
 
 size_t vgsa_sparse_workspace_bytes(const vgsa_attn_desc* desc, int32_t idx_stride) {
   if (check_desc(desc) != VGSA_OK || idx_stride < 1) return 0;
   return sparse_sync_bytes(*desc) +
-         partial_bytes(*desc, make_plan(desc->batch, desc->num_kv_heads, idx_stride));
+         partial_bytes(*desc, make_plan(*desc, idx_stride));
 }
 
 }  // extern "C"
@@ -243,7 +251,7 @@ vgsa_status verify_launch(const vgsa_attn_desc* desc, const void* q, const void*
       if (d.num_q_heads < 64 && (head_mask >> d.num_q_heads) != 0ull) return VGSA_ERR_INVALID_ARG;
     }
   }
-  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
+  const SplitPlan p = make_plan(d, d.max_ctx);
   st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
   if (st != VGSA_OK) return st;
   if (d.batch == 0) return VGSA_OK;
@@ -277,7 +285,7 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   const int32_t span = idx_stride + tail;
   // one split for lists up to kDirectSpan (the output is written directly);
   // longer lists split, and with `fused` the splits merge in the same launch
-  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, span);
+  const SplitPlan p = make_plan(d, span);
   // fused: the counters first, the partials after them; the fused merge
   // addresses the partials with 32-bit byte offsets
   if (fused && p.num_splits > 1 && partial_bytes(d, p) > (size_t)0x7FFFFFFF)
@@ -335,7 +343,7 @@ vgsa_status vgsa_combine_partials(const vgsa_attn_desc* desc, int32_t span,
   const vgsa_attn_desc& d = *desc;
   if (span < 1 || lengths == nullptr || out == nullptr || !aligned(out, 16))
     return VGSA_ERR_INVALID_ARG;
-  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, span);
+  const SplitPlan p = make_plan(d, span);
   st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
   if (st != VGSA_OK) return st;
   const int64_t rows = (int64_t)d.batch * d.num_q_heads * d.q_len;
@@ -368,7 +376,7 @@ vgsa_status vgsa_verify_attention(const vgsa_attn_desc* desc, const void* q, con
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   if (out == nullptr || !aligned(out, 16)) return VGSA_ERR_INVALID_ARG;
-  const SplitPlan p = make_plan(desc->batch, desc->num_kv_heads, desc->max_ctx);
+  const SplitPlan p = make_plan(*desc, desc->max_ctx);
   if (p.num_splits == 1) {
     // one split: the partials kernel finishes the softmax and writes out / lse
     return verify_launch(desc, q, k_cache, v_cache, block_table, seq_lens, collect_mask, head_mask,
@@ -411,7 +419,7 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
         (num_rows < 1 || num_rows > (int64_t)d.q_len * d.num_q_heads))
       return VGSA_ERR_INVALID_ARG;
   }
-  const SplitPlan p = make_plan(d.batch, d.num_kv_heads, d.max_ctx);
+  const SplitPlan p = make_plan(d, d.max_ctx);
   st = check_workspace(workspace, workspace_bytes, partial_bytes(d, p));
   if (st != VGSA_OK) return st;
   const int64_t rows = (int64_t)d.batch * d.num_q_heads * d.q_len;

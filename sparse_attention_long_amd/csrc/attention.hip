@@ -148,21 +148,27 @@ void attn_partials_kernel(AttnArgs a) {
   __shared__ uint32_t s_row[WAVES][kTile];      // sparse: cache element offsets of those rows
   // One array, three uses in turn:
   //  * slog, the kv-group logits of the chunk: held here and written out in
-  //    contiguous bursts, all of a chunk of up to kLogitBufMax positions
-  //    once the loop is done (contiguous caches).  Stores issued while the
-  //    K/V stream runs cost far more than their bytes: one 4096-position
-  //    burst per workgroup in mid-chunk cost 3 % of the verify time;
+  //    contiguous bursts once the loop is done.  Stores issued while the K/V
+  //    stream runs cost far more than their bytes: one 4096-position burst
+  //    per workgroup in mid-chunk cost 3 % of the verify time.  Wide
+  //    layouts hold a whole chunk (kMaxChunkWide positions), contiguous or
+  //    paged; narrow ones kLogitBufMax (contiguous) or kLogitBuf (paged)
+  //    positions, flushed whenever full;
   //  * s_blk, the paged verify's block ids of the chunk, in the top
-  //    kMaxChunk / 16 entries (a paged launch holds kLogitBuf positions of
-  //    logits, so the two do not meet);
+  //    kMaxChunk / 16 entries (beyond the logit buffer);
   //  * after the loop (logits out, block ids no longer read): the merge's
   //    per-wavefront row max and sum and the rows' 1 / sum.
+  constexpr bool kWide = WAVES == kWavesWide;
+  constexpr int kChunkMax = kWide ? kMaxChunkWide : kMaxChunk;
+  constexpr int kLogCap = kWide ? kMaxChunkWide : kLogitBufMax;       // contiguous caches
+  constexpr int kLogCapPaged = kWide ? kMaxChunkWide : kLogitBuf;     // paged caches
   constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || EMIT == kEmitSumColumn;
-  constexpr int kBlkIds = SPARSE ? 0 : kMaxChunk / 16;
+  constexpr int kBlkIds = SPARSE ? 0 : kChunkMax / 16;
   constexpr int kRowStats = 2 * WAVES * kMaxRows + kMaxRows;
-  constexpr int kShared = kGroupLogits ? kLogitBufMax
+  constexpr int kShared = kGroupLogits ? (kWide ? kLogCap + kBlkIds : kLogitBufMax)
                                        : (kBlkIds > kRowStats ? kBlkIds : kRowStats);
-  static_assert(!kGroupLogits || kLogitBuf + kBlkIds <= kLogitBufMax, "logits meet block ids");
+  static_assert(!kGroupLogits || kLogCapPaged + kBlkIds <= kShared, "logits meet block ids");
+  static_assert(!kGroupLogits || kLogCap <= kShared, "logit buffer does not fit");
   static_assert(kRowStats <= kShared, "row statistics do not fit");
   __shared__ __align__(16) float sx[kShared];
   float* const slog = sx;
@@ -193,9 +199,9 @@ void attn_partials_kernel(AttnArgs a) {
     int64_t total = 0;
     for (int i = 0; i < B; ++i) total += min(max(a.seq_lens[i], 0), a.max_ctx);
     const int64_t fit = (total + (int64_t)S * B - B - 1) / ((int64_t)S * B - B);  // S > 1 here
-    const int floor_len = (a.chunk / kBalanceSplits + kMinChunk - 1) / kMinChunk * kMinChunk;
-    const int cp = (int)min((int64_t)a.chunk,
-                            max((int64_t)floor_len, (fit + kMinChunk - 1) / kMinChunk * kMinChunk));
+    constexpr int MC = WAVES * kTile;  // one step of every wavefront
+    const int floor_len = (a.chunk / kBalanceSplits + MC - 1) / MC * MC;
+    const int cp = (int)min((int64_t)a.chunk, max((int64_t)floor_len, (fit + MC - 1) / MC * MC));
     // A sequence keeps its first S items on its own workgroups (split < n),
     // so equal lengths map as without balancing; the items past S of long
     // sequences go, in order, to the workgroups that short sequences leave
@@ -402,8 +408,8 @@ void attn_partials_kernel(AttnArgs a) {
   // Paged verify: the chunk's block ids (clamped) go to LDS once, so no load
   // address waits on a block-table read inside the loop.  Their loads go out
   // with the query fragments' below (one round trip for both).
-  constexpr int kBlkPerThread = (kMaxChunk / 16 + NT - 1) / NT;
-  const int nblk = (!SPARSE && a.paged) ? (end - 1 - start) / 16 + 1 : 0;  // <= kMaxChunk / 16
+  constexpr int kBlkPerThread = (kChunkMax / 16 + NT - 1) / NT;
+  const int nblk = (!SPARSE && a.paged) ? (end - 1 - start) / 16 + 1 : 0;  // <= kChunkMax / 16
   int blk_v[kBlkPerThread];
 #pragma unroll
   for (int j = 0; j < kBlkPerThread; ++j) {
@@ -414,6 +420,16 @@ void attn_partials_kernel(AttnArgs a) {
   u32x4 kraw[NI], vraw[NI];
   int ts = start + wave * kTile;
   int tile_no = 0;
+  // Wide verify: after its first tile (wavefront w takes tile w) a wavefront
+  // claims the next unclaimed tile of the chunk from an LDS counter, so the
+  // wavefronts that run faster take more tiles and all finish within about
+  // one tile of each other (two wavefronts share each SIMD, and the arbiter
+  // favours the older one).  The chunk's logits fit the LDS buffer whole
+  // (the plan's chunk is at most kMaxChunkWide), so no mid-chunk flush
+  // assumes a fixed tile order.
+  constexpr bool kClaim = kWide && !SPARSE;
+  __shared__ int s_next_tile;
+  if (kClaim && threadIdx.x == 0) s_next_tile = WAVES;
 
   // Stage the query fragments (B operand of S^T = K Q^T) before the first
   // tile's loads go out: a wavefront's loads complete in issue order, so
@@ -482,7 +498,7 @@ void attn_partials_kernel(AttnArgs a) {
   int lbase = start;  // first position held in slog
   // positions of logits slog holds (a multiple of step), and the tile count
   // at which it is full
-  const int log_cap = a.paged ? kLogitBuf : kLogitBufMax;
+  const int log_cap = a.paged ? kLogCapPaged : kLogCap;
   int flush_tile = log_cap / step;
   auto flush_logits = [&](int n) {  // slog[0, n) -> logits[lbase, lbase + n), nontemporal
     float* lp = a.logits + ((size_t)b * a.hkv + g) * a.max_ctx + lbase;
@@ -497,7 +513,12 @@ void attn_partials_kernel(AttnArgs a) {
       for (int i = tid; i < n; i += NT) __builtin_nontemporal_store(slog[i], lp + i);
     }
   };
-  for (; ts < end; ts += step) {
+  while (ts < end) {
+    int claimed = 0;  // the wavefront's next tile (kClaim)
+    if (kClaim) {
+      if (lane == 0) claimed = atomicAdd(&s_next_tile, 1);
+      claimed = __builtin_amdgcn_readfirstlane(claimed);
+    }
     // Entry e of the tile (e = pb*16 + 4*kg + r for this lane's S^T values)
     // is visible to query row qb iff e < vis[qb]: positions ascend within a
     // tile, so each row sees a prefix.  `full`: every entry visible to all.
@@ -529,7 +550,7 @@ void attn_partials_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       *reinterpret_cast<u32x4*>(vt + (i * RPI + lrow) * VS + lchunk * 8) = kraw[i];
-    const int tn = ts + step;
+    const int tn = kClaim ? start + claimed * kTile : ts + step;
     if (tn < end) {
       stage(tn, tile_no + 1);
       issue(tn, kbase, kraw);
@@ -728,7 +749,7 @@ void attn_partials_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     ++tile_no;
-    if (kGroupLogits && tile_no == flush_tile &&
+    if (!kClaim && kGroupLogits && tile_no == flush_tile &&
         start + (tile_no - 1) * step + (WAVES - 1) * kTile < end) {
       // the last wavefront has a tile_no-th tile, so every wavefront reaches
       // this point (the condition is the same for all): the buffer is full
@@ -738,6 +759,7 @@ void attn_partials_kernel(AttnArgs a) {
       lbase += log_cap;
       flush_tile += log_cap / step;
     }
+    ts = tn;
   }
 
   // Row sums: combine the four 16-lane groups.
@@ -886,49 +908,60 @@ template <int D, bool SPARSE, int EMIT, int WAVES>
 hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int rows = a.group * a.q_len;
   const dim3 block(WAVES * 64);
-  if (rows <= 16) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 1, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
-  } else if (rows <= 32) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 2, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
-  } else if (rows <= 48) {
-    hipLaunchKernelGGL((attn_partials_kernel<D, 3, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+  if constexpr (WAVES == kWaves) {
+    // narrow: only d = 128 with four row blocks (one wavefront per SIMD)
+    if constexpr (D != 128) return hipErrorInvalidValue;
+    else {
+      if (rows <= 48) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+    }
   } else {
-    // four row blocks of d = 128 leave registers for one wavefront per SIMD:
-    // never launched with 8 wavefronts (not even instantiated)
-    if constexpr (D == 128 && WAVES == kWavesWide) return hipErrorInvalidValue;
-    else hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+    if (rows <= 16) {
+      hipLaunchKernelGGL((attn_partials_kernel<D, 1, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+    } else if (rows <= 32) {
+      hipLaunchKernelGGL((attn_partials_kernel<D, 2, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+    } else if (rows <= 48) {
+      hipLaunchKernelGGL((attn_partials_kernel<D, 3, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+    } else {
+      // four row blocks of d = 128 leave registers for one wavefront per
+      // SIMD: the narrow layout (not instantiated wide)
+      if constexpr (D == 128) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((attn_partials_kernel<D, 4, SPARSE, EMIT, WAVES>), grid, block, 0, s, a);
+    }
   }
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_dim(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) {
-  if (sparse) {
-    // one split over a list longer than one round of 4 wavefronts: 8 wavefronts
-    // (not for four query blocks of d = 128, whose registers allow one
-    // wavefront per SIMD only)
-    if (a.num_splits == 1 && a.chunk > kMinChunk && (D == 64 || a.group * a.q_len <= 48))
-      return launch_d<D, true, VGSA_LOGITS_NONE, kWavesWide>(a, grid, s);
-    return launch_d<D, true, VGSA_LOGITS_NONE, kWaves>(a, grid, s);
-  }
+template <int D, int WAVES>
+hipError_t launch_layout(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) {
+  if (sparse) return launch_d<D, true, VGSA_LOGITS_NONE, WAVES>(a, grid, s);
   switch (a.layout) {
-    case VGSA_LOGITS_PER_HEAD: return launch_d<D, false, VGSA_LOGITS_PER_HEAD, kWaves>(a, grid, s);
+    case VGSA_LOGITS_PER_HEAD: return launch_d<D, false, VGSA_LOGITS_PER_HEAD, WAVES>(a, grid, s);
     case VGSA_LOGITS_KVGROUP_SUM: {
       // the summed query fits in the last block's two spare columns
       const int rows = a.group * a.q_len;
       if (rows + 2 <= (rows + 15) / 16 * 16)
-        return launch_d<D, false, kEmitSumColumn, kWaves>(a, grid, s);
-      return launch_d<D, false, VGSA_LOGITS_KVGROUP_SUM, kWaves>(a, grid, s);
+        return launch_d<D, false, kEmitSumColumn, WAVES>(a, grid, s);
+      return launch_d<D, false, VGSA_LOGITS_KVGROUP_SUM, WAVES>(a, grid, s);
     }
-    default: return launch_d<D, false, VGSA_LOGITS_NONE, kWaves>(a, grid, s);
+    default: return launch_d<D, false, VGSA_LOGITS_NONE, WAVES>(a, grid, s);
   }
+}
+
+template <int D>
+hipError_t launch_dim(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t s) {
+  return a.waves == kWavesWide ? launch_layout<D, kWavesWide>(a, sparse, grid, s)
+                               : launch_layout<D, kWaves>(a, sparse, grid, s);
 }
 
 }  // namespace
 
 hipError_t launch_attention_partials(const AttnArgs& a, bool sparse, hipStream_t s) {
   // the split plan never makes these: LDS logit buffer and mid-chunk flush
-  if (a.chunk > kMaxChunk || a.chunk % kMinChunk != 0) return hipErrorInvalidValue;
+  const bool wide = a.waves == kWavesWide;
+  if (!wide && a.waves != kWaves) return hipErrorInvalidValue;
+  if (a.chunk > (wide ? kMaxChunkWide : kMaxChunk) || a.chunk % (wide ? kMinChunkWide : kMinChunk) != 0)
+    return hipErrorInvalidValue;
   const dim3 grid(a.num_splits, a.hkv, a.batch);
   return a.head_dim == 64 ? launch_dim<64>(a, sparse, grid, s) : launch_dim<128>(a, sparse, grid, s);
 }

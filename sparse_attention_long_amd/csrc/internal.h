@@ -10,33 +10,46 @@
 
 namespace vgsa {
 
-// Positions one wavefront processes per step, waves per workgroup, and the
-// smallest chunk a workgroup is given (one step of every wave).
+// Positions one wavefront processes per step.
 constexpr int kTile = 32;
+// Launch layouts of the attention kernels.  Wide: one workgroup of 8
+// wavefronts per CU (two per SIMD), every workgroup the same age on its CU.
+// Two 4-wavefront workgroups sharing a CU ran at different speeds: the SIMD
+// arbiter favours the older wavefronts, so the workgroup dispatched second
+// looped 7-8 % longer and set the verify kernel's end.  Narrow: 4
+// wavefronts, for d = 128 with four 16-row blocks, whose registers allow one
+// wavefront per SIMD.
 constexpr int kWaves = 4;
-constexpr int kWavesWide = 8;  // one-split sparse launches
-constexpr int kThreads = kWaves * 64;
+constexpr int kWavesWide = 8;
+// Smallest chunk a workgroup is given (one step of every wavefront).
 constexpr int kMinChunk = kTile * kWaves;
-// Workgroups aimed for per attention launch: one round of 2 per CU on 256
-// CUs, so each workgroup slot pays its start-up and merge once.
+constexpr int kMinChunkWide = kTile * kWavesWide;
+// Workgroups aimed for per attention launch: one round on 256 CUs (wide: one
+// per CU; narrow: two per CU), so each workgroup slot pays its start-up and
+// merge once.
 constexpr int kTargetWorkgroups = 512;
+constexpr int kTargetWorkgroupsWide = 256;
 // Spans up to this many positions get one split: a single workgroup per
 // (sequence, kv-head) finishes the softmax itself and writes the output
 // directly (no partials, no combine launch).
 constexpr int kDirectSpan = 1024;
 // Chunk of one split, as planned.  A workgroup keeps the kv-group logits of
-// its chunk in LDS (fp32; kLogitBufMax positions, kLogitBuf for paged caches)
-// and writes them out after its loop (and whenever the buffer is full, in a
-// longer chunk).  Longer chunks measured
-// slower at 128K x b8 (one round of 512 workgroups then spans 4 GB of K/V at
-// once; two rounds of 8192-position chunks span 2 GB each).
+// its chunk in LDS (fp32) and writes them out after its loop (narrow paged
+// launches hold kLogitBuf positions and flush whenever the buffer is full).
+// Narrow: 8192 positions (longer chunks measured slower at 128K x b8: one
+// round of 512 workgroups then spans 4 GB of K/V at once).  Wide: 16384, the
+// same bytes per CU.
 constexpr int kPlanChunk = 8192;
+constexpr int kPlanChunkWide = 16384;
 // Largest chunk: the plan widens its chunks up to this size instead of adding
-// a split for a last sliver of at most kPlanChunk / 8 positions (a capacity
-// a few positions past a multiple of 8192, e.g. headroom for drafted tokens).
+// a split for a last sliver (a capacity a few positions past a multiple of
+// the planned chunk, e.g. headroom for drafted tokens): up to kPlanChunk / 8
+// positions (narrow) or one step of every wavefront (wide, whose LDS logit
+// buffer holds exactly this many positions).
 constexpr int kMaxChunk = kPlanChunk + kPlanChunk / 8;
-constexpr int kLogitBuf = 4096;     // paged caches (the block-id table shares the space)
-constexpr int kLogitBufMax = 8192;  // contiguous caches: a whole planned chunk
+constexpr int kMaxChunkWide = kPlanChunkWide + kMinChunkWide;
+constexpr int kLogitBuf = 4096;     // narrow paged caches (the block-id table shares the space)
+constexpr int kLogitBufMax = 8192;  // narrow contiguous caches: a whole planned chunk
 // Largest (Hq/Hkv) * T handled by one workgroup: four 16-row MFMA blocks.
 constexpr int kMaxRows = 64;
 
@@ -45,7 +58,15 @@ struct SplitPlan {
   int32_t chunk;
   int32_t part_splits;  // row stride of the partial arrays: num_splits, or
                         // kBalanceSplits * num_splits when items may shrink
+  int32_t waves;        // kWavesWide, or kWaves for d = 128 with four row blocks
 };
+
+// Wavefronts per attention workgroup for this shape (wide unless d = 128 with
+// more than three 16-row blocks).
+inline int attention_waves(const vgsa_attn_desc& d) {
+  const int64_t rows = (int64_t)(d.num_q_heads / d.num_kv_heads) * d.q_len;
+  return (d.head_dim == 128 && rows > 48) ? kWaves : kWavesWide;
+}
 
 // Ragged batches: a verify launch over several sequences (at most
 // kMaxBalanceBatch) shrinks its items so that the non-empty ones fill the
@@ -54,7 +75,9 @@ struct SplitPlan {
 constexpr int kBalanceSplits = 4;
 constexpr int kMaxBalanceBatch = 256;
 
-SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t span);
+// Split plan of an attention launch over `span` positions (the capacity for
+// verify, the list capacity plus tail for sparse) for this shape.
+SplitPlan make_plan(const vgsa_attn_desc& d, int32_t span);
 
 // Partial results of one attention launch, carved out of the workspace:
 //   header  int32 [64]               [0]: the item length the launch used
@@ -100,6 +123,7 @@ struct AttnArgs {
   int32_t batch, hq, hkv, group, q_len, head_dim;
   int32_t max_ctx, paged, max_blocks, num_blocks;
   int32_t num_splits, chunk;
+  int32_t waves;     // wavefronts per workgroup (the plan's layout)
   float scale;       // natural-log softmax scale
   float scale_log2;  // scale * log2(e)
 };

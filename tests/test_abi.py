@@ -225,29 +225,41 @@ def test_append_argument_checks(lib):
 
 
 def test_split_plan_covers_span(lib):
+    # wide layout (one 8-wavefront workgroup per CU): chunks of 256 .. 16640
     for B_, Hkv, span in [(16, 8, 32768), (1, 8, 32768), (8, 8, 131078), (4, 8, 65536), (1, 1, 5),
                           (16, 8, 512), (1, 8, 2049), (64, 8, 131088), (64, 8, 9216), (64, 8, 9217),
                           (512, 8, 1 << 20)]:
         d = desc(batch=B_, num_kv_heads=Hkv, num_q_heads=Hkv, q_len=1, max_ctx=span)
         s, c = B.split_plan(d, span)
+        assert s >= 1 and c % 256 == 0 and c <= 16640 and s * c >= span and (s - 1) * c < span
+    # narrow layout (d = 128 with four 16-row blocks): chunks of 128 .. 9216
+    for B_, span in [(16, 32768), (1, 32768), (8, 131078), (64, 131088), (2, 5000)]:
+        d = desc(batch=B_, num_kv_heads=8, num_q_heads=64, q_len=8, max_ctx=span)
+        s, c = B.split_plan(d, span)
         assert s >= 1 and c % 128 == 0 and c <= 9216 and s * c >= span and (s - 1) * c < span
-    # one round of 512 workgroups (2 per CU) at the 32K x b16 shape
+    # one round of 256 wide workgroups (one per CU) at the 32K x b16 shape ...
     d = desc(batch=16, num_q_heads=64, num_kv_heads=8, q_len=5, max_ctx=32768)
+    assert B.split_plan(d, 32768) == (2, 16384)
+    # ... of 512 narrow ones (two per CU) with four row blocks
+    d = desc(batch=16, num_q_heads=64, num_kv_heads=8, q_len=8, max_ctx=32768)
     assert B.split_plan(d, 32768) == (4, 8192)
-    # chunks are capped at 8192 positions ...
+    # chunks are capped at 16384 positions ...
     d = desc(batch=1, num_q_heads=8, num_kv_heads=1, q_len=2, head_dim=64, max_ctx=1 << 24)
-    assert B.split_plan(d, 1 << 24) == (2048, 8192)
+    assert B.split_plan(d, 1 << 24) == (1024, 16384)
     d = desc(batch=8, num_q_heads=32, num_kv_heads=8, q_len=7, max_ctx=145000)
-    assert B.split_plan(d, 145000) == (18, 8192)
-    # ... except that a last sliver of at most 1024 positions is spread over
-    # the other splits (chunks of at most 9216)
-    for span in (131078, 131088, 131072 + 1024):
+    assert B.split_plan(d, 145000) == (9, 16384)
+    # ... except that a last sliver of at most 256 positions (one step of
+    # every wavefront) is spread over the other splits (chunks of 16640)
+    for span in (131078, 131088, 131072 + 256):
         d = desc(batch=8, num_q_heads=32, num_kv_heads=8, q_len=7, max_ctx=span)
-        assert B.split_plan(d, span) == (16, 8320)
-    d = desc(batch=8, num_q_heads=32, num_kv_heads=8, q_len=7, max_ctx=131072 + 1025)
-    assert B.split_plan(d, 131072 + 1025) == (17, 8192)
+        assert B.split_plan(d, span) == (8, 16640)
+    d = desc(batch=8, num_q_heads=32, num_kv_heads=8, q_len=7, max_ctx=131072 + 257)
+    assert B.split_plan(d, 131072 + 257) == (9, 16384)
     d = desc(batch=2, num_q_heads=8, num_kv_heads=1, q_len=2, max_ctx=2 * 8192 + 100)
-    assert B.split_plan(d, 2 * 8192 + 100) == (129, 128)   # not capped: no widening
+    assert B.split_plan(d, 2 * 8192 + 100) == (65, 256)   # not capped: no widening
+    # narrow: slivers up to 1024 positions are spread (chunks of at most 9216)
+    d = desc(batch=8, num_q_heads=64, num_kv_heads=8, q_len=8, max_ctx=131088)
+    assert B.split_plan(d, 131088) == (16, 8320)
 
 
 def test_select_workspace_sizes_and_validation(lib):

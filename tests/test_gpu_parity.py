@@ -441,8 +441,15 @@ def test_select_blocks_on_verify_scores_then_sparse(name):
     assert_lse_close(lse, lse_ref, f"{name} block sparse lse")
 
 
-def test_determinism_bitwise():
-    w = CASES["g8t5_d128"]
+@pytest.mark.parametrize("name", ["g8t5_d128", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])
+def test_determinism(name):
+    """Two runs give bitwise identical logits, scores, selected positions and
+    sparse outputs: every position's logit sum is computed by the same
+    arithmetic whichever wavefront takes its tile.  The verify output and lse
+    agree to within fp32 accumulation order (the tiles a wavefront takes are
+    claimed at run time, so its order of accumulation may differ): at most one
+    bf16 unit of the output, 1e-5 in lse."""
+    w = CASES[name]
     x = W.make_layer(w)
     d = to_device(x)
     runs = []
@@ -450,14 +457,20 @@ def test_determinism_bitwise():
         out, lse, lg = run_verify(d, w, "kvgroup_sum")
         sc = Bn.aggregate_scores(lg, d.seq_lens, w.num_q_heads, w.num_kv_heads)
         idx, n = Bn.select_topk(sc, d.seq_lens, w.budget, w.n_sink, w.window)
-        so, sl = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n)
+        so, sl = Bn.sparse_attention(d.q, d.k, d.v, d.seq_lens, idx, n, block_table=d.block_table,
+                                     max_ctx=d.max_ctx)
         torch.cuda.synchronize()
         L = x.seq_lens
         lgv = np.concatenate([lg[b, :, :L[b]].cpu().numpy().ravel() for b in range(w.batch)])
-        runs.append([out.view(torch.int16).cpu().numpy(), lse.cpu().numpy(), lgv,
-                     idx.cpu().numpy(), so.view(torch.int16).cpu().numpy(), sl.cpu().numpy()])
-    for a, b in zip(*runs):
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+        scv = np.concatenate([sc[b, :L[b]].cpu().numpy() for b in range(w.batch)])
+        runs.append(dict(out=out.float().cpu().numpy(), lse=lse.cpu().numpy(), lg=lgv, sc=scv,
+                         idx=np.concatenate([idx[b, :n[b]].cpu().numpy() for b in range(w.batch)]),
+                         so=so.view(torch.int16).cpu().numpy(), sl=sl.cpu().numpy()))
+    a, b = runs
+    for key in ("lg", "sc", "idx", "so", "sl"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+    np.testing.assert_allclose(a["out"], b["out"], atol=8e-3, rtol=1e-2)
+    np.testing.assert_allclose(a["lse"], b["lse"], atol=1e-5, rtol=0)
 
 
 @pytest.mark.parametrize("name", ["g4t5_d64", "ctx2k_b1_h32kv8_d128", "paged_g8t6_d64"])
