@@ -199,9 +199,31 @@ void attn_partials_kernel(AttnArgs a) {
     int64_t total = 0;
     for (int i = 0; i < B; ++i) total += min(max(a.seq_lens[i], 0), a.max_ctx);
     const int64_t fit = (total + (int64_t)S * B - B - 1) / ((int64_t)S * B - B);  // S > 1 here
-    constexpr int MC = WAVES * kTile;  // one step of every wavefront
+    // item granularity: a tile when the wavefronts claim tiles, else one
+    // step of every wavefront
+    constexpr int MC = (kWide && !SPARSE) ? kTile : WAVES * kTile;
     const int floor_len = (a.chunk / kBalanceSplits + MC - 1) / MC * MC;
-    const int cp = (int)min((int64_t)a.chunk, max((int64_t)floor_len, (fit + MC - 1) / MC * MC));
+    int cp = (int)min((int64_t)a.chunk, max((int64_t)floor_len, (fit + MC - 1) / MC * MC));
+    // cp above always fits (the items of a sequence number at most L / cp +
+    // 1); the smallest item length that still gives at most S * B items is
+    // found by bisection in steps of MC.  For lengths 12536, 60439, 51539,
+    // 12189 over 32 workgroups per kv-head it gives 32 items of 4320
+    // positions (an even split is 4272) instead of 29 of 5120.
+    {
+      const int64_t SB = (int64_t)S * B;
+      auto fits = [&](int c) {
+        int64_t n = 0;
+        for (int i = 0; i < B; ++i) n += (min(max(a.seq_lens[i], 0), a.max_ctx) + c - 1) / c;
+        return n <= SB;
+      };
+      int lo = max(floor_len, (int)(((total + SB - 1) / SB + MC - 1) / MC * MC));
+      int hi = cp;
+      while (lo < hi) {
+        const int mid = max(lo, (lo + hi) / 2 / MC * MC);
+        if (fits(mid)) hi = mid; else lo = mid + MC;
+      }
+      cp = hi;
+    }
     // A sequence keeps its first S items on its own workgroups (split < n),
     // so equal lengths map as without balancing; the items past S of long
     // sequences go, in order, to the workgroups that short sequences leave

@@ -118,7 +118,7 @@ __device__ __forceinline__ void combine_block(const CombineArgs& a, int block) {
   const int row = block * (kMergeBlock / Q) + threadIdx.x / Q;
   // the item length the partials were made with (clamped: the header only
   // ever narrows the plan's chunk)
-  const int chunk = min(max(a.header[0], kMinChunk), a.chunk);
+  const int chunk = min(max(a.header[0], kTile), a.chunk);
   if (row < a.rows) combine_quad<D>(a, row, threadIdx.x % Q, chunk);
 }
 
