@@ -14,9 +14,12 @@ verify kernel (the dominant one) against the 8 TB/s HBM peak, timed with HIP
 events on the stream it runs on; `cpu_baseline` is the fp64 oracle on a
 bounded sample of the same workload on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers N]
                     [--logits kvgroup_sum|per_head] [--collect two|all]
-                    [--select plain|hybrid]
+                    [--select plain|hybrid|blocks]
+
+--layers N runs N layers per step, each with its own queries and cache (the
+ragged paged workload defines 24); `value` stays iterations/s per layer.
 
 The defaults are the kv-group-summed layout and the two Collect-2-Query rows;
 the JSON also reports the verify kernel with every row collected and the
@@ -97,17 +100,40 @@ def counter_traffic(workload_name):
     return int(m.group(1))
 
 
-def cpu_baseline(w, x, seconds, rows, heads=None):
+def host_cpu():
+    """Model name and usable core count of this host."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        nproc = os.cpu_count() or 1
+    return model, nproc
+
+
+def cpu_baseline(w, x, seconds, rows, heads=None, gpu_idx=None):
     """The fp64 oracle, as it stands, on whole sequences of the workload until
-    `seconds` have passed; scaled to iterations/s of the full batch."""
+    `seconds` have passed; scaled to iterations/s of the full batch.
+
+    Also reports, for the sequences it ran, how many of the positions the GPU
+    selected from its fp32 scores the oracle selects from its fp64 scores
+    (informational: the parity bar compares selections on the same scores)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        blas_threads = 1
+    model, nproc = host_cpu()
     t0 = time.perf_counter()
     done = 0
+    overlap = []
     for b in range(w.batch):
         sl = slice(b, b + 1)
         lens = x.seq_lens[sl]
@@ -116,6 +142,10 @@ def cpu_baseline(w, x, seconds, rows, heads=None):
         sc = oracle.aggregate_scores(oracle.kvgroup_sum(lg, w.num_kv_heads, heads=heads,
                                                         num_q_heads=w.num_q_heads))
         idx = oracle.select_topk(sc[0], int(lens[0]), w.budget, w.n_sink, w.window)
+        if gpu_idx is not None:
+            g_idx, g_n = gpu_idx
+            mine = set(g_idx[b, :g_n[b]].tolist())
+            overlap.append(len(mine & set(idx.tolist())) / max(1, len(idx)))
         if w.sparse_verify:
             oracle.sparse_attention(x.q[sl], x.k[sl], x.v[sl], lens, [idx])
         for s in range(1, w.draft_steps + 1):
@@ -126,14 +156,24 @@ def cpu_baseline(w, x, seconds, rows, heads=None):
             break
     el = time.perf_counter() - t0
     per_seq = el / done
-    return {
+    out = {
         "value": 1.0 / (per_seq * w.batch),
         "unit": "iters/s",
-        "cores": int(threads),
+        "cores": int(blas_threads),
         "kind": "oracle",
         "sample": f"{done} of {w.batch} sequences (full iteration each: verify, logits, scores, "
                   f"select, sparse) in {el:.1f} s, fp64 numpy; value scaled to the whole batch",
+        "cpu_model": model,
+        "nproc": int(nproc),
+        "threading": f"matrix products on {blas_threads} BLAS threads; the per-row softmax, "
+                     "sums, sort and gathers single-threaded numpy",
     }
+    if overlap:
+        out["selection_overlap_vs_fp64_scores"] = {
+            "sequences": len(overlap), "mean": float(np.mean(overlap)), "min": float(np.min(overlap)),
+            "note": "fraction of the oracle's fp64-score selection that the GPU's fp32-score "
+                    "selection also keeps (layer 0)"}
+    return out
 
 
 def main():
@@ -151,6 +191,9 @@ def main():
     ap.add_argument("--select", choices=("plain", "hybrid", "blocks"), default="plain",
                     help="top-k by the verify scores; hybrid: top-m by a draft-lookahead score "
                          "first (synthetic draft scores); blocks: whole 16-position blocks")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="a step runs this many layers in turn, each with its own cache and queries "
+                         "(up to the workload's layer count); value stays iterations/s per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=0,
                     help="1: capture one step as a HIP graph and time its replays")
@@ -173,6 +216,13 @@ def main():
 
     name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
+    n_layers = args.layers
+    if not 1 <= n_layers <= w.layers:
+        print(f"--layers must be 1..{w.layers} for {name}", file=sys.stderr)
+        sys.exit(2)
+    if n_layers > 1 and args.graph:
+        print("--graph captures one layer's step; use it with --layers 1", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     Bn.load()
@@ -200,16 +250,30 @@ def main():
         bt = torch.from_numpy(x.block_table).to(dev)
     else:
         k, v, bt = d_bf16(x.k), d_bf16(x.v), None
-    # Cold caches: K/V below 512 MiB would stay in the 256 MB Infinity Cache
-    # from one launch to the next, so such workloads rotate through copies of
-    # K/V (same values, other addresses) whose sizes add up to at least
-    # 512 MiB; every launch that reads K/V takes the next copy.
-    kv_bytes = (k.numel() + v.numel()) * 2
-    n_copies = 1 if kv_bytes >= ROTATE_BYTES else min(64, -(-ROTATE_BYTES // kv_bytes))
-    k_copies, v_copies = [k], [v]
-    for _ in range(n_copies - 1):
-        k_copies.append(k.clone())
-        v_copies.append(v.clone())
+    q_layers = [q]
+    if n_layers > 1:
+        # layers 1 .. n-1: their own queries and caches (the block table and
+        # lengths are shared by all layers)
+        k_copies, v_copies = [k], [v]
+        for layer in range(1, n_layers):
+            xl = W.make_layer(w, layer)
+            q_layers.append(d_bf16(xl.q))
+            k_copies.append(d_bf16(xl.k_pool if w.paged else xl.k))
+            v_copies.append(d_bf16(xl.v_pool if w.paged else xl.v))
+            del xl
+        log(f"[bench] {n_layers} layers generated in {time.perf_counter() - t0:.1f}s")
+        n_copies = n_layers
+    else:
+        # Cold caches: K/V below 512 MiB would stay in the 256 MB Infinity
+        # Cache from one launch to the next, so such workloads rotate through
+        # copies of K/V (same values, other addresses) whose sizes add up to at
+        # least 512 MiB; every launch that reads K/V takes the next copy.
+        kv_bytes = (k.numel() + v.numel()) * 2
+        n_copies = 1 if kv_bytes >= ROTATE_BYTES else min(64, -(-ROTATE_BYTES // kv_bytes))
+        k_copies, v_copies = [k], [v]
+        for _ in range(n_copies - 1):
+            k_copies.append(k.clone())
+            v_copies.append(v.clone())
     cur = [0]
 
     def kv():
@@ -256,10 +320,9 @@ def main():
         out_d = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device=dev)
         lse_d = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
 
-    def draft_steps():
+    def draft_steps(k, v):
         # step s attends the kept positions and the s + 1 drafted since (the
         # trailing positions of its length), in one launch
-        k, v = kv()
         for s in range(n_draft):
             Bn.sparse_attention(q_draft[s], k, v, lens_draft[s], idx, n_idx, block_table=bt,
                                 max_ctx=max_ctx, tail=s + 1, out=out_d, lse=lse_d, workspace=ws_d)
@@ -279,17 +342,24 @@ def main():
             Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx,
                            workspace=ws_sel)
 
-    def step():
-        rotate()
-        k, v = kv()
-        Bn.verify_partials(desc, q, k, v, lens, bt, rows, KV, logits, ws_v, heads=heads)
+    def layer_step(ql, k, v):
+        Bn.verify_partials(desc, ql, k, v, lens, bt, rows, KV, logits, ws_v, heads=heads)
         # split combine + score aggregation in one launch
         Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
         select()
         if w.sparse_verify:
-            Bn.sparse_attention(q, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
+            Bn.sparse_attention(ql, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                 out=out_s, lse=lse_s, workspace=ws_s)
-        draft_steps()
+        draft_steps(k, v)
+
+    def step():
+        if n_layers > 1:
+            # every layer in turn, each on its own cache
+            for layer in range(n_layers):
+                layer_step(q_layers[layer], k_copies[layer], v_copies[layer])
+            return
+        rotate()
+        layer_step(q, *kv())
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -367,7 +437,7 @@ def main():
             lambda: Bn.sparse_attention(q, *kv(), lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                         out=out_s, lse=lse_s, workspace=ws_s))
     if n_draft:
-        stages["draft_steps"] = per_launch_us(draft_steps)
+        stages["draft_steps"] = per_launch_us(lambda: draft_steps(*kv()))
     verify_none_us = per_launch_us(
         lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, rows, Bn.LOGITS_NONE, None, ws_v))
     # every verify row collected (the score summed over all T rows), same layout
@@ -397,7 +467,7 @@ def main():
 
     ab = alg_bytes(w, x.seq_lens, args.logits, len(rows), n_heads,
                    k_blocks * BLK if args.select == "blocks" else None)
-    iters = K / wall
+    iters = K * n_layers / wall  # iterations per second per layer
     achieved = ab["verify_kernel"] / (verify_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
@@ -420,7 +490,7 @@ def main():
                    "score_heads": None if heads is None else list(heads),
                    "select": args.select, "draft_m": w.draft_m if args.select == "hybrid" else None,
                    "k_blocks": k_blocks if args.select == "blocks" else None,
-                   "kv_copies": n_copies},
+                   "kv_copies": n_copies if n_layers == 1 else 1, "layers_per_step": n_layers},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
                      "kernel": "attn_partials_kernel (verify)",
@@ -447,7 +517,16 @@ def main():
         result["sparse_roofline"]["frac"] = result["sparse_roofline"]["achieved"] / HBM_PEAK_GBS
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, rows, heads)
+        # the GPU's plain selection of this layer, from its own fp32 scores
+        Bn.verify_attention(q, k_copies[0], v_copies[0], lens, block_table=bt, max_ctx=max_ctx,
+                            collect_rows=rows, heads=heads, layout=args.logits, logits=logits,
+                            out=out, lse=lse)
+        Bn.aggregate_scores(logits, lens, Hq, Hkv, layout=args.logits, scores=scores)
+        Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx,
+                       workspace=ws_sel)
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, rows, heads,
+                                              gpu_idx=(idx.cpu().numpy(), n_idx.cpu().numpy()))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
