@@ -142,6 +142,10 @@ void attn_partials_kernel(AttnArgs a) {
   // Per-wavefront K/V tiles, [position][d]; reused at the end as the fp32
   // merge buffers.
   __shared__ __align__(16) uint16_t sbuf[WAVES * kTile * VS];
+  // Summed collected query (kv-group logits through the MFMA): in the last
+  // block's two spare columns, 14 (bf16 high part) and 15 (low part).
+  constexpr bool kSumQuery = EMIT == kEmitSumColumn;
+  constexpr int kSumCol = 14;
   // Query fragments, already in MFMA operand order: [qb][ks][lane] x 16 B.
   __shared__ __align__(16) u32x4 sq[QB * KS * 64];
   __shared__ int s_idx[WAVES][kTile];           // sparse: positions of the staged tile
@@ -162,7 +166,7 @@ void attn_partials_kernel(AttnArgs a) {
   constexpr int kChunkMax = kWide ? kMaxChunkWide : kMaxChunk;
   constexpr int kLogCap = kWide ? kMaxChunkWide : kLogitBufMax;       // contiguous caches
   constexpr int kLogCapPaged = kWide ? kMaxChunkWide : kLogitBuf;     // paged caches
-  constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || EMIT == kEmitSumColumn;
+  constexpr bool kGroupLogits = EMIT == VGSA_LOGITS_KVGROUP_SUM || kSumQuery;
   constexpr int kBlkIds = SPARSE ? 0 : kChunkMax / 16;
   constexpr int kRowStats = 2 * WAVES * kMaxRows + kMaxRows;
   constexpr int kShared = kGroupLogits ? (kWide ? kLogCap + kBlkIds : kLogitBufMax)
@@ -462,44 +466,8 @@ void attn_partials_kernel(AttnArgs a) {
     const int fl = f & 63, fks = (f >> 6) % KS, fqb = (f >> 6) / KS;
     const int m = fqb * 16 + (fl & 15);
     u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (m < rows) {
+    if (m < rows)
       val = *reinterpret_cast<const u32x4*>(a.q + (row_base + m) * D + fks * 32 + (fl >> 4) * 8);
-    } else if (EMIT == kEmitSumColumn && m >= QB * 16 - 2) {
-      // summed query of the collected rows of the collected heads (heads
-      // ascending, then rows ascending): column QB*16-2 its bf16 rounding,
-      // column QB*16-1 the rest.  Loads go out kSumBatch at a time: one after
-      // another they would be dependent round trips before the first tile.
-      constexpr int kSumBatch = 4;
-      float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const int R = __builtin_popcount(a.row_mask), n_sum = __builtin_popcountll(gmask) * R;
-      for (int k0 = 0; k0 < n_sum; k0 += kSumBatch) {
-        bf16x8 qv[kSumBatch];
-#pragma unroll
-        for (int i = 0; i < kSumBatch; ++i) {
-          // uniform: the (k / R)-th collected head, its (k % R)-th collected row
-          const int k = min(k0 + i, n_sum - 1);
-          uint64_t hm = gmask;
-          for (int c = k / R; c > 0; --c) hm &= hm - 1ull;
-          uint32_t mm = a.row_mask;
-          for (int c = k % R; c > 0; --c) mm &= mm - 1u;
-          const int hh = __builtin_ctzll(hm), t = __builtin_ctz(mm);
-          qv[i] = load16(a.q + (row_base + hh * T + t) * D + fks * 32 + (fl >> 4) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < kSumBatch; ++i)
-          if (k0 + i < n_sum) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) qs[j] += (float)qv[i][j];
-          }
-      }
-      bf16x8 part;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const __bf16 hi = (__bf16)qs[j];
-        part[j] = m == QB * 16 - 2 ? hi : (__bf16)(qs[j] - (float)hi);
-      }
-      val = __builtin_bit_cast(u32x4, part);
-    }
     sq[f] = val;
   }
   if (!SPARSE && a.paged) {
@@ -516,6 +484,33 @@ void attn_partials_kernel(AttnArgs a) {
     issue(ts, vbase, vraw);
   }
   __syncthreads();  // query fragments staged
+  if (kSumQuery) {
+    // The summed query of the collected rows of the collected heads (heads
+    // ascending, then rows ascending), formed from the staged fragments in
+    // LDS (no more HBM round trips before the first tile): thread t < D sums
+    // column d = t in fp32 and writes its bf16 rounding to column kSumCol
+    // and the bf16 rounding of the remainder to kSumCol + 1 (about 16
+    // significant bits together).  A fragment element (row m, column d) sits
+    // in block m / 16, step d / 32, lane ((d % 32) / 8) * 16 + m % 16, slot d % 8.
+    if ((int)threadIdx.x < D) {
+      const int dcol = threadIdx.x, ks = dcol / 32, lq = ((dcol % 32) / 8) * 16, j = dcol % 8;
+      const uint16_t* sqh = reinterpret_cast<const uint16_t*>(sq);
+      float qs = 0.f;
+      for (int hh = 0; hh < G; ++hh) {
+        if (!((gmask >> hh) & 1ull)) continue;
+        for (int t = 0; t < T; ++t) {
+          if (!((a.row_mask >> t) & 1u)) continue;
+          const int m = hh * T + t;
+          qs += __builtin_bit_cast(float, (uint32_t)sqh[(((m >> 4) * KS + ks) * 64 + lq + (m & 15)) * 8 + j] << 16);
+        }
+      }
+      const __bf16 hi = (__bf16)qs, lo = (__bf16)(qs - (float)hi);
+      uint16_t* sqw = reinterpret_cast<uint16_t*>(sq);
+      sqw[(((QB - 1) * KS + ks) * 64 + lq + kSumCol) * 8 + j] = __builtin_bit_cast(uint16_t, hi);
+      sqw[(((QB - 1) * KS + ks) * 64 + lq + kSumCol + 1) * 8 + j] = __builtin_bit_cast(uint16_t, lo);
+    }
+    __syncthreads();  // summed query staged
+  }
 
   int lbase = start;  // first position held in slog
   // positions of logits slog holds (a multiple of step), and the tile count
@@ -683,11 +678,11 @@ void attn_partials_kernel(AttnArgs a) {
       if ((c16 & 1) == 0) slog[ts - lbase + e] = v1;
     }
 
-    if (EMIT == kEmitSumColumn) {
+    if (kSumQuery) {
       // Lanes c16 = 14 / 15 of the last block hold K . (high / low part);
-      // after the exchange both hold the sum.  The earlier collected row sees
-      // a prefix of what the later one sees, so past its causal limit the
-      // sum is -inf.
+      // after the exchange both hold the sum.  The earlier
+      // collected row sees a prefix of what the later one sees, so past its
+      // causal limit the sum is -inf.
       // (a kv-group with no collected head sums to 0 at every position)
       const int row_first = __builtin_ctz(a.row_mask);  // the earliest collected row
       const int vis0 = (full || gmask == 0ull)
@@ -701,7 +696,7 @@ void attn_partials_kernel(AttnArgs a) {
           x += swap_adjacent_lanes(x);
           lv[pb][r] = (pb * 16 + 4 * kg + r) < vis0 ? x * a.scale : kNegInf;
         }
-      if (c16 == 14) {
+      if (c16 == kSumCol) {
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb)
           *reinterpret_cast<f32x4*>(slog + (ts - lbase) + pb * 16 + 4 * kg) = lv[pb];
@@ -960,7 +955,10 @@ hipError_t launch_layout(const AttnArgs& a, bool sparse, dim3 grid, hipStream_t 
   switch (a.layout) {
     case VGSA_LOGITS_PER_HEAD: return launch_d<D, false, VGSA_LOGITS_PER_HEAD, WAVES>(a, grid, s);
     case VGSA_LOGITS_KVGROUP_SUM: {
-      // the summed query fits in the last block's two spare columns
+      // the summed query fits in the last block's two spare columns;
+      // otherwise a lane reduction sums the collected rows (an extra block
+      // entering only S^T measured slower at d = 64 x 48 rows: +11.7 %
+      // against +9.4 %, and +28 % with every row collected)
       const int rows = a.group * a.q_len;
       if (rows + 2 <= (rows + 15) / 16 * 16)
         return launch_d<D, false, kEmitSumColumn, WAVES>(a, grid, s);
