@@ -191,6 +191,9 @@ def main():
     ap.add_argument("--select", choices=("plain", "hybrid", "blocks"), default="plain",
                     help="top-k by the verify scores; hybrid: top-m by a draft-lookahead score "
                          "first (synthetic draft scores); blocks: whole 16-position blocks")
+    ap.add_argument("--finish-select", choices=("fused", "separate"), default="fused",
+                    help="plain selection on rows of up to 65536 positions: the finish and the "
+                         "selection in one launch (fused) or two")
     ap.add_argument("--layers", type=int, default=1,
                     help="a step runs this many layers in turn, each with its own cache and queries "
                          "(up to the workload's layer count); value stays iterations/s per layer")
@@ -332,6 +335,16 @@ def main():
     n_ws_sel = Bn.select_workspace_bytes(B, max_ctx)
     ws_sel = torch.empty(n_ws_sel, dtype=torch.uint8, device=dev) if n_ws_sel else None
 
+    # plain selection on rows of up to 65536 positions: finish (combine +
+    # aggregate) and selection in one launch
+    fused = args.select == "plain" and max_ctx <= 65536 and args.finish_select == "fused"
+    ws_fs = torch.zeros(Bn.finish_select_workspace_bytes(B), dtype=torch.uint8, device=dev) \
+        if fused else None
+
+    def finish_select():
+        Bn.verify_finish_select(desc, lens, ws_v, out, lse, KV, logits, scores, w.budget, w.n_sink,
+                                w.window, idx, n_idx, ws_fs)
+
     def select():
         if args.select == "hybrid":
             Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink, w.window,
@@ -344,9 +357,12 @@ def main():
 
     def layer_step(ql, k, v):
         Bn.verify_partials(desc, ql, k, v, lens, bt, rows, KV, logits, ws_v, heads=heads)
-        # split combine + score aggregation in one launch
-        Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
-        select()
+        if fused:
+            finish_select()
+        else:
+            # split combine + score aggregation in one launch, then the selection
+            Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
+            select()
         if w.sparse_verify:
             Bn.sparse_attention(ql, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                 out=out_s, lse=lse_s, workspace=ws_s)
@@ -426,12 +442,16 @@ def main():
     verify_us = per_launch_us(
         lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, rows, KV, logits, ws_v, heads=heads))
     log(f"[bench] verify kernel {verify_us:.1f} us per launch")
-    stages = {
-        "verify_partials": verify_us,
-        "combine_aggregate": per_launch_us(
-            lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)),
-        "select": per_launch_us(select),
-    }
+    # the finish and the selection as separate launches (the step's form when
+    # they are not fused)
+    finish_us = per_launch_us(lambda: Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores))
+    select_us = per_launch_us(select)
+    stages = {"verify_partials": verify_us}
+    if fused:
+        stages["finish_select"] = per_launch_us(finish_select)
+    else:
+        stages["combine_aggregate"] = finish_us
+        stages["select"] = select_us
     if w.sparse_verify:
         stages["sparse"] = per_launch_us(
             lambda: Bn.sparse_attention(q, *kv(), lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
@@ -490,6 +510,7 @@ def main():
                    "score_heads": None if heads is None else list(heads),
                    "select": args.select, "draft_m": w.draft_m if args.select == "hybrid" else None,
                    "k_blocks": k_blocks if args.select == "blocks" else None,
+                   "finish_select_fused": fused,
                    "kv_copies": n_copies if n_layers == 1 else 1, "layers_per_step": n_layers},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name),
@@ -503,6 +524,8 @@ def main():
         "logit_emit_overhead": stages["verify_partials"] / verify_none_us - 1.0,
         "verify_partials_all_rows_us": verify_all_us,
         "logit_emit_overhead_all_rows": verify_all_us / verify_none_us - 1.0,
+        "combine_aggregate_us": finish_us,
+        "select_us": select_us,
         "select_hybrid_us": select_hybrid_us,
         "select_blocks_us": select_blocks_us,
         "sparse_over_blocks_us": sparse_blocks_us,

@@ -415,6 +415,35 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
                                vgsa_logit_layout layout, int32_t num_rows, int32_t accumulate,
                                const float* logits, float* scores, void* stream);
 
+/* Steps 1 (second phase), 2 and 3 in one launch: vgsa_verify_finish with
+ * scores, then vgsa_select_topk on the scores it wrote, with the same results
+ * as those two calls (identical out, lse, scores, idx and n_idx).
+ *    (Vegas §2 steps 1-2, "A. aggregated attention-logit selection";
+ *    Dustin "1." protected sinks and window.)
+ * The workgroups that sum a sequence's scores also count the leading 12 bits
+ * of their order-preserving keys into a histogram of that sequence; the last
+ * of them to finish selects the sequence's positions in the same launch,
+ * starting from that histogram.  No workgroup waits on another.
+ * desc .. scores  as vgsa_verify_finish; scores must not be NULL
+ * k, n_sink, window, idx, idx_stride, n_idx  as vgsa_select_topk
+ * select_workspace  >= vgsa_finish_select_workspace_bytes(batch) bytes of
+ *          device memory, 256-byte aligned: per-sequence histograms and
+ *          counters.  It must be zero before its first use (e.g. a
+ *          zero-filled allocation); every call leaves it zero again.  Calls
+ *          that share it must not overlap.
+ * Errors: as vgsa_verify_finish and vgsa_select_topk; VGSA_ERR_UNSUPPORTED
+ * for max_ctx > 65536 (make the two calls instead); VGSA_ERR_WORKSPACE for a
+ * missing, small or misaligned select_workspace.
+ */
+size_t vgsa_finish_select_workspace_bytes(int32_t batch);
+vgsa_status vgsa_verify_finish_select(const vgsa_attn_desc* desc, const int32_t* seq_lens,
+                                      const void* workspace, size_t workspace_bytes, void* out,
+                                      float* lse, vgsa_logit_layout layout, int32_t num_rows,
+                                      int32_t accumulate, const float* logits, float* scores,
+                                      int32_t k, int32_t n_sink, int32_t window, int32_t* idx,
+                                      int32_t idx_stride, int32_t* n_idx, void* select_workspace,
+                                      size_t select_workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

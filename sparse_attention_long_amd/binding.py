@@ -64,6 +64,10 @@ SIGNATURES = {
                                       c_vp, c_vp]),
     "vgsa_verify_finish": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp, c_i32,
                                    c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "vgsa_finish_select_workspace_bytes": (c_sz, [c_i32]),
+    "vgsa_verify_finish_select": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp,
+                                          c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                          c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_append_positions": (c_i32, [c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "vgsa_noalloc_scratch_bytes": (c_sz, []),
     "vgsa_verify_attention_noalloc": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp,
@@ -434,3 +438,27 @@ def verify_finish(desc: AttnDesc, seq_lens, workspace, out, lse, layout: int = L
     _check(load().vgsa_verify_finish(
         ctypes.byref(desc), _p(seq_lens), _p(workspace), workspace.numel(), _p(out), _p(lse),
         layout, num_rows, int(bool(accumulate)), _p(logits), _p(scores), _stream(out.device)), "vgsa_verify_finish")
+
+
+def finish_select_workspace_bytes(batch: int) -> int:
+    return int(load().vgsa_finish_select_workspace_bytes(batch))
+
+
+def verify_finish_select(desc: AttnDesc, seq_lens, workspace, out, lse, layout: int, logits,
+                         scores, k: int, n_sink: int, window: int, idx, n_idx, select_workspace,
+                         accumulate: bool = False) -> None:
+    """vgsa_verify_finish_select: verify_finish (with scores) and the top-k
+    selection on those scores in one launch.  `select_workspace` (uint8,
+    finish_select_workspace_bytes(B) bytes) must be zero before its first
+    use; every call leaves it zero.  Per-head logits are [B, R, H, max_ctx]."""
+    _need(idx, "idx", torch.int32, 2)
+    _need(n_idx, "n_idx", torch.int32, 1)
+    _need(select_workspace, "select_workspace", torch.uint8)
+    num_rows = 0
+    if layout == LOGITS_PER_HEAD and logits is not None and logits.dim() == 4:
+        num_rows = logits.shape[1] * logits.shape[2]
+    _check(load().vgsa_verify_finish_select(
+        ctypes.byref(desc), _p(seq_lens), _p(workspace), workspace.numel(), _p(out), _p(lse),
+        layout, num_rows, int(bool(accumulate)), _p(logits), _p(scores), k, n_sink, window,
+        _p(idx), idx.shape[1], _p(n_idx), _p(select_workspace), select_workspace.numel(),
+        _stream(out.device)), "vgsa_verify_finish_select")

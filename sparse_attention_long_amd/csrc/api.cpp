@@ -403,10 +403,15 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
                        tail, workspace, workspace_bytes, out, lse, true, stream);
 }
 
-vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
-                               const void* workspace, size_t workspace_bytes, void* out, float* lse,
-                               vgsa_logit_layout layout, int32_t num_rows, int32_t accumulate,
-                               const float* logits, float* scores, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch arguments of the finish step (combine + aggregate).
+vgsa_status finish_args(const vgsa_attn_desc* desc, const int32_t* seq_lens,
+                        const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                        vgsa_logit_layout layout, int32_t num_rows, int32_t accumulate,
+                        const float* logits, float* scores, CombineArgs& ca, AggregateArgs& ag) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
@@ -424,9 +429,8 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
   if (st != VGSA_OK) return st;
   const int64_t rows = (int64_t)d.batch * d.num_q_heads * d.q_len;
   if (rows > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
-  if (rows == 0) return VGSA_OK;
   const Carve c = carve(d, p, const_cast<void*>(workspace));
-  CombineArgs ca{};
+  ca = CombineArgs{};
   ca.part_o = c.part_o;
   ca.part_ml = c.part_ml;
   ca.lengths = seq_lens;
@@ -440,9 +444,56 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
   ca.header = c.header;
   ca.out = static_cast<uint16_t*>(out);
   ca.lse = lse;
-  AggregateArgs ag{d.batch,  d.num_q_heads,         d.num_kv_heads, d.max_ctx, (int32_t)layout,
-                   num_rows, accumulate ? 1 : 0, logits,          seq_lens,  scores};
+  ag = AggregateArgs{d.batch,  d.num_q_heads,         d.num_kv_heads, d.max_ctx, (int32_t)layout,
+                     num_rows, accumulate ? 1 : 0, logits,          seq_lens,  scores};
+  return VGSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_lens,
+                               const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                               vgsa_logit_layout layout, int32_t num_rows, int32_t accumulate,
+                               const float* logits, float* scores, void* stream) {
+  CombineArgs ca;
+  AggregateArgs ag;
+  const vgsa_status st = finish_args(desc, seq_lens, workspace, workspace_bytes, out, lse, layout,
+                                     num_rows, accumulate, logits, scores, ca, ag);
+  if (st != VGSA_OK) return st;
+  if (ca.rows == 0) return VGSA_OK;
   return hip_status(launch_combine_aggregate(ca, ag, static_cast<hipStream_t>(stream)));
+}
+
+size_t vgsa_finish_select_workspace_bytes(int32_t batch) {
+  if (batch < 1 || batch > kMaxGridYZ) return 0;
+  return finish_select_workspace_bytes(batch);
+}
+
+vgsa_status vgsa_verify_finish_select(const vgsa_attn_desc* desc, const int32_t* seq_lens,
+                                      const void* workspace, size_t workspace_bytes, void* out,
+                                      float* lse, vgsa_logit_layout layout, int32_t num_rows,
+                                      int32_t accumulate, const float* logits, float* scores,
+                                      int32_t k, int32_t n_sink, int32_t window, int32_t* idx,
+                                      int32_t idx_stride, int32_t* n_idx, void* select_workspace,
+                                      size_t select_workspace_bytes, void* stream) {
+  if (scores == nullptr) return VGSA_ERR_INVALID_ARG;
+  if (k < 1 || n_sink < 0 || window < 0 || (int64_t)n_sink + window > k) return VGSA_ERR_INVALID_ARG;
+  if (idx_stride < k || idx == nullptr || n_idx == nullptr) return VGSA_ERR_INVALID_ARG;
+  CombineArgs ca;
+  AggregateArgs ag;
+  vgsa_status st = finish_args(desc, seq_lens, workspace, workspace_bytes, out, lse, layout,
+                               num_rows, accumulate, logits, scores, ca, ag);
+  if (st != VGSA_OK) return st;
+  if (desc->max_ctx > kFinishSelectMaxCtx || desc->batch > kMaxGridYZ) return VGSA_ERR_UNSUPPORTED;
+  if ((int64_t)desc->batch * idx_stride > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
+  if (ca.rows == 0) return VGSA_OK;
+  st = check_workspace(select_workspace, select_workspace_bytes,
+                       finish_select_workspace_bytes(desc->batch));
+  if (st != VGSA_OK) return st;
+  return hip_status(launch_finish_select(ca, ag, k, n_sink, window, idx, idx_stride, n_idx,
+                                         select_workspace, static_cast<hipStream_t>(stream)));
 }
 
 vgsa_status vgsa_aggregate_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -39,6 +39,12 @@ __device__ __forceinline__ float2 load2_device(const float* base, uint32_t byte_
   const u32x2m u = __builtin_amdgcn_raw_buffer_load_b64(device_rsrc(base), byte_off, 0, kCpolSc1);
   return make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
 }
+__device__ __forceinline__ float load1_device(const float* base, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(device_rsrc(base), byte_off, 0, kCpolSc1));
+}
+__device__ __forceinline__ void store1_device(float* base, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), device_rsrc(base), byte_off, 0, kCpolSc1);
+}
 
 // Splits (or logit rows) whose loads are issued together before any is used:
 // the merge is a chain of dependent HBM round trips otherwise.
@@ -127,25 +133,52 @@ constexpr int combine_blocks(int rows) {
   return (rows + kMergeBlock / (D / 4) - 1) / (kMergeBlock / (D / 4));
 }
 
-// Score of position j of sequence b: the collected logits summed in a fixed
-// order (kv-groups ascending, or rows then heads ascending), then added to
-// the score already there when accumulating (e.g. over layers).
+// Score of position j < L of sequence b (returned, not stored): the
+// collected logits summed in a fixed order (kv-groups ascending, or rows then
+// heads ascending), then added to the score already there when accumulating
+// (e.g. over layers).
+// U positions j0 + u * stride at once (those at or past L give 0), their
+// loads issued together.
+template <int U>
+__device__ __forceinline__ void aggregate_values(const AggregateArgs& a, int b, int j0, int stride,
+                                                 int L, float (&res)[U]) {
+  const int n = a.layout == VGSA_LOGITS_KVGROUP_SUM ? a.hkv : a.n_rows;
+  const float* p = a.logits + (size_t)b * n * a.max_ctx;
+  float s[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) s[u] = 0.f;
+  for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
+    float v[U][kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int j = j0 + u * stride;
+        v[u][i] = (r0 + i < n && j < L) ? p[(size_t)(r0 + i) * a.max_ctx + j] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i)
+        if (r0 + i < n) s[u] += v[u][i];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j0 + u * stride;
+    res[u] = (a.accumulate && j < L) ? a.scores[(size_t)b * a.max_ctx + j] + s[u] : s[u];
+  }
+}
+
+__device__ __forceinline__ float aggregate_value(const AggregateArgs& a, int b, int j) {
+  float v[1];
+  aggregate_values<1>(a, b, j, 0, j + 1, v);
+  return v[0];
+}
+
 __device__ __forceinline__ void aggregate_position(const AggregateArgs& a, int b, int j) {
   const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
   if (j >= L) return;
-  const int n = a.layout == VGSA_LOGITS_KVGROUP_SUM ? a.hkv : a.n_rows;
-  const float* p = a.logits + (size_t)b * n * a.max_ctx + j;
-  float s = 0.f;
-  for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
-    float v[kMergeBatch];
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) v[i] = r0 + i < n ? p[(size_t)(r0 + i) * a.max_ctx] : 0.f;
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i)
-      if (r0 + i < n) s += v[i];
-  }
-  float* dst = a.scores + (size_t)b * a.max_ctx + j;
-  *dst = a.accumulate ? *dst + s : s;
+  a.scores[(size_t)b * a.max_ctx + j] = aggregate_value(a, b, j);
 }
 
 }  // namespace vgsa

@@ -33,6 +33,7 @@
 // deterministic: keys above the threshold key, then the lowest positions
 // among keys equal to it.
 #include "internal.h"
+#include "merge_ops.h"
 
 namespace vgsa {
 namespace {
@@ -40,7 +41,7 @@ namespace {
 constexpr int kThreadsTk = 1024;
 constexpr int kWavesTk = kThreadsTk / 64;
 constexpr int kBins = 4096;
-constexpr int kRunMax = 32;      // keys a thread keeps in registers
+constexpr int kRunMax = 16;      // keys a thread holds in registers at once
 constexpr int kCandMax = 4096;   // LDS candidate list capacity
 constexpr int kCandPerThread = kCandMax / kThreadsTk;
 
@@ -68,8 +69,20 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
   return (uint32_t)v;
 }
 
-// Exclusive prefix sum of v over the workgroup; `total` receives the sum.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
+// Lane 8j + 7 of each group of eight lanes receives the OR of the group's x
+// (DPP row shifts by 1, 2, 4 with zero fill; a group never crosses a 16-lane
+// row).  All lanes of the wavefront must be active.
+__device__ __forceinline__ uint32_t or_lanes8(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  return x;
+}
+
+// Exclusive prefix sum of v over the workgroup (.x) and the sum (.y).
+// Results come back by value: a call the compiler keeps out of line then
+// needs no stack slots.
+__device__ uint2 block_scan(uint32_t v, uint32_t* s_wave) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) s_wave[wave] = x;
@@ -82,8 +95,13 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t&
     tot += c;
   }
   __syncthreads();
-  total = tot;
-  return base + x - v;
+  return make_uint2(base + x - v, tot);
+}
+
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
+  const uint2 r = block_scan(v, s_wave);
+  total = r.y;
+  return r.x;
 }
 
 struct Row {
@@ -127,16 +145,16 @@ __device__ __forceinline__ void load_keys(const Row& c, int base, uint32_t (&key
 
 // Finds, among the counted keys, the digit of the `want`-th largest, the rank
 // left inside that digit, and (in s_out[2]) how many keys the digit's bin
-// holds.  hist holds nb bins; all threads call.
-__device__ void find_digit(const uint32_t* hist, uint32_t nb, int shift, uint32_t& prefix,
-                           uint32_t& want, uint32_t* s_wave, uint32_t* s_out) {
+// holds.  hist holds nb bins; all threads call.  Returns (prefix, want) by
+// value (an out-of-line call then needs no stack slots).
+__device__ uint2 find_digit_v(const uint32_t* hist, uint32_t nb, int shift, uint32_t prefix,
+                              uint32_t want, uint32_t* s_wave, uint32_t* s_out) {
   const int tid = threadIdx.x;
   uint32_t cnt[4];
   const int top = (int)nb - 1 - 4 * tid;  // thread t owns bins top .. top-3 (descending)
 #pragma unroll
   for (int q = 0; q < 4; ++q) cnt[q] = (top - q >= 0) ? hist[top - q] : 0u;
-  uint32_t tot;
-  uint32_t above = block_exclusive_scan(cnt[0] + cnt[1] + cnt[2] + cnt[3], s_wave, tot);
+  uint32_t above = block_scan(cnt[0] + cnt[1] + cnt[2] + cnt[3], s_wave).x;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (top - q >= 0 && above < want && want <= above + cnt[q]) {
@@ -147,9 +165,17 @@ __device__ void find_digit(const uint32_t* hist, uint32_t nb, int shift, uint32_
     above += cnt[q];
   }
   __syncthreads();
-  prefix = s_out[0];
-  want = s_out[1];
+  const uint2 r = make_uint2(s_out[0], s_out[1]);
   __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nb, int shift,
+                                           uint32_t& prefix, uint32_t& want, uint32_t* s_wave,
+                                           uint32_t* s_out) {
+  const uint2 r = find_digit_v(hist, nb, shift, prefix, want, s_wave, s_out);
+  prefix = r.x;
+  want = r.y;
 }
 
 __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
@@ -218,9 +244,11 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
   uint32_t ctotal;
   const uint32_t cbase = block_exclusive_scan(ccount, s_wave, ctotal);
 
-  const int shifts[2] = {8, 0};
-  const uint32_t masks[2] = {0xFFF00000u, 0xFFFFFF00u};
-  const uint32_t nbs[2] = {4096u, 256u};
+  // passes 2 and 3: 12 then 8 key bits (selects, not arrays indexed at run
+  // time, which would live in scratch memory)
+  const auto pass_shift = [](int pass) { return pass == 0 ? 8 : 0; };
+  const auto pass_mask = [](int pass) { return pass == 0 ? 0xFFF00000u : 0xFFFFFF00u; };
+  const auto pass_bins = [](int pass) { return pass == 0 ? 4096u : 256u; };
   if (ctotal <= (uint32_t)kCandMax) {
     // ---------------- fast path: resolve and emit from the candidate list
     uint32_t o = cbase;
@@ -241,10 +269,10 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
       __syncthreads();
       for (int q = tid; q < (int)ctotal; q += kThreadsTk) {
         const uint32_t kk = cand_key[q];
-        if ((kk & masks[pass]) == prefix) atomicAdd(&hist[(kk >> shifts[pass]) & (nbs[pass] - 1u)], 1u);
+        if ((kk & pass_mask(pass)) == prefix) atomicAdd(&hist[(kk >> pass_shift(pass)) & (pass_bins(pass) - 1u)], 1u);
       }
       __syncthreads();
-      find_digit(hist, nbs[pass], shifts[pass], prefix, want, s_wave, s_out);
+      find_digit(hist, pass_bins(pass), pass_shift(pass), prefix, want, s_wave, s_out);
     }
     const uint32_t thr = prefix, need_eq = want;
     // ordered emit: thread t owns list entries [4t, 4t+4)
@@ -281,11 +309,11 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_large_kernel(
       if (!resident) load_keys(c, base, key, n);
 #pragma unroll
       for (int i = 0; i < kRunMax; ++i)
-        if (i < n && key[i] != 0u && (key[i] & masks[pass]) == prefix)
-          atomicAdd(&hist[(key[i] >> shifts[pass]) & (nbs[pass] - 1u)], 1u);
+        if (i < n && key[i] != 0u && (key[i] & pass_mask(pass)) == prefix)
+          atomicAdd(&hist[(key[i] >> pass_shift(pass)) & (pass_bins(pass) - 1u)], 1u);
     }
     __syncthreads();
-    find_digit(hist, nbs[pass], shifts[pass], prefix, want, s_wave, s_out);
+    find_digit(hist, pass_bins(pass), pass_shift(pass), prefix, want, s_wave, s_out);
   }
   const uint32_t thr = prefix, need_eq = want;
   uint32_t ceq = 0u;
@@ -342,24 +370,27 @@ constexpr int kBinCapOne = 252;    // bin members ranked directly: one round
 constexpr int kBinCapMany = 764;   // ... reloaded rounds
 constexpr int kBinCap = kBinCapMany;
 
-// LDS of the one-workgroup selection.
-struct SelectLds {
+// LDS of the one-workgroup selection, for rows of up to RM rounds.
+template <int RM>
+struct SelectLdsT {
   uint32_t hist[kBins];
   uint32_t s_wave[kWavesTk];
   uint32_t s_out[4];
-  uint32_t taken[kMaxRounds * kThreadsTk];   // positions selected (above the bin, or ranked in)
-  uint32_t in_bin[kMaxRounds * kThreadsTk];  // bin members, when they are all equal
+  uint32_t taken[RM * kThreadsTk];   // positions selected (above the bin, or ranked in)
+  uint32_t in_bin[RM * kThreadsTk];  // bin members, when they are all equal
   // bin members as (key << 32 | ~position): larger means ranked first
   __align__(16) uint64_t bin_rank_key[kBinCap + 4];
   uint32_t count;
 };
+using SelectLds = SelectLdsT<kMaxRounds>;
 
 // The threshold bin: sh.bin_rank_key[0, nbin) holds its members (not
 // exact), or sh.in_bin marks them (exact: their keys are all equal).  The
 // best `want` of them join sh.taken: larger key, then lower position.
 // Starts with a workgroup barrier (after the members were written) and ends
 // with one.
-__device__ void resolve_bin(SelectLds& sh, uint32_t nbin, uint32_t want, bool exact, int R) {
+template <class Lds>
+__device__ void resolve_bin(Lds& sh, uint32_t nbin, uint32_t want, bool exact, int R) {
   const int tid = threadIdx.x;
   if (!exact && tid < 4) sh.bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
   __syncthreads();
@@ -402,11 +433,18 @@ __device__ void resolve_bin(SelectLds& sh, uint32_t nbin, uint32_t want, bool ex
 // [s_end, w_start) of highest score in row `sc` (lower position first among
 // equal keys).  EXCL: positions already marked are no candidates; a thread
 // only marks positions whose keys it has already read, so the marks it reads
-// are the earlier stage's.  Starts and ends with a workgroup barrier.
-template <bool VEC, bool EXCL>
-__device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restrict__ sc,
+// are the earlier stage's.  COHERENT: the scores were written in this launch
+// by other workgroups (possibly on another XCD): they are read with
+// device-scope loads.  PREHIST: ghist holds the first pass's histogram (top
+// 12 key bits of the stage's candidates, kBins counts, written in this launch:
+// read with device-scope loads, together with the first round's keys).
+// Starts and ends with a workgroup barrier.
+template <bool VEC, bool EXCL, bool COHERENT = false, bool PREHIST = false, class Lds>
+__device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ sc,
                                              int max_ctx, int R, int s_end, int w_start,
-                                             uint32_t want_stage) {
+                                             uint32_t want_stage,
+                                             const uint32_t* __restrict__ ghist = nullptr) {
+  static_assert(!(PREHIST && EXCL), "a precomputed histogram has no exclusions");
   const int tid = threadIdx.x;
   const bool reload = R > 1;
   // Keys of round `rd`; 0 outside M = [s_end, w_start) (and for excluded
@@ -420,11 +458,16 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
     for (int c = 0; c < kSmallChunks; ++c) {
       const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
       if (VEC) {
-        const float4 x = *reinterpret_cast<const float4*>(sc + min(p0, max_ctx - 4));
+        const int o = min(p0, max_ctx - 4);
+        const float4 x = COHERENT ? load4_device(sc, (uint32_t)o * 4u)
+                                  : *reinterpret_cast<const float4*>(sc + o);
         v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[c][e] = sc[min(p0 + e, max_ctx - 1)];
+        for (int e = 0; e < 4; ++e) {
+          const int o = min(p0 + e, max_ctx - 1);
+          v[c][e] = COHERENT ? load1_device(sc, (uint32_t)o * 4u) : sc[o];
+        }
       }
     }
 #pragma unroll
@@ -438,9 +481,27 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
       }
     }
   };
-  if (tid == 0) sh.count = 0u;
-  __syncthreads();  // earlier marks complete
-  if (!reload) load_round(0);
+  bool have0 = false;  // key[] holds round 0
+  if (PREHIST) {
+    uint32_t h[kBins / kThreadsTk];
+#pragma unroll
+    for (int q = 0; q < kBins / kThreadsTk; ++q)
+      h[q] = __float_as_uint(
+          load1_device(reinterpret_cast<const float*>(ghist), (uint32_t)(tid + q * kThreadsTk) * 4u));
+    load_round(0);
+    have0 = true;
+#pragma unroll
+    for (int q = 0; q < kBins / kThreadsTk; ++q) sh.hist[tid + q * kThreadsTk] = h[q];
+    if (tid == 0) sh.count = 0u;
+    __syncthreads();
+  } else {
+    if (tid == 0) sh.count = 0u;
+    __syncthreads();  // earlier marks complete
+    if (!reload) {
+      load_round(0);
+      have0 = true;
+    }
+  }
 
   // Radix passes: after each, keys whose masked value exceeds `prefix` are
   // taken and `want` more come from the bin (masked value == prefix).
@@ -450,19 +511,22 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
   for (; level < 3; ++level) {
     const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
     const uint32_t nb = level == 2 ? 256u : (uint32_t)kBins;
-    for (int i = tid; i < (int)nb; i += kThreadsTk) sh.hist[i] = 0u;
-    __syncthreads();
+    if (!PREHIST || level > 0) {
+      for (int i = tid; i < (int)nb; i += kThreadsTk) sh.hist[i] = 0u;
+      __syncthreads();
 #pragma unroll 1
-    for (int rd = 0; rd < R; ++rd) {
-      if (reload) load_round(rd);
+      for (int rd = 0; rd < R; ++rd) {
+        if (reload && !(rd == 0 && have0)) load_round(rd);
 #pragma unroll
-      for (int c = 0; c < kSmallChunks; ++c)
+        for (int c = 0; c < kSmallChunks; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
-            atomicAdd(&sh.hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
+          for (int e = 0; e < 4; ++e)
+            if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
+              atomicAdd(&sh.hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
+      }
+      if (reload) have0 = false;  // key[] ends on the last round
+      __syncthreads();
     }
-    __syncthreads();
     find_digit(sh.hist, nb, shift, prefix, want, sh.s_wave, sh.s_out);
     nbin = sh.s_out[2];
     mask |= (nb - 1u) << shift;
@@ -470,10 +534,13 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
   }
   const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
 
-  // Mark keys above the bin; collect (or mark) the bin's members.
+  // Mark keys above the bin; collect (or mark) the bin's members.  The
+  // eight lanes whose positions share a bitmap word OR their bits together
+  // (DPP) and the last of them stores the word: one LDS write per word
+  // instead of eight atomics on it.
 #pragma unroll 1
   for (int rd = 0; rd < R; ++rd) {
-    if (reload) load_round(rd);
+    if (reload && !(rd == 0 && have0)) load_round(rd);
 #pragma unroll
     for (int c = 0; c < kSmallChunks; ++c) {
       uint32_t above = 0u, inb = 0u;
@@ -484,7 +551,9 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
         inb |= (key[c][e] != 0u && mk == prefix) ? (1u << e) : 0u;
       }
       const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
-      if (above != 0u) atomicOr(&sh.taken[p0 >> 5], above << (p0 & 31));
+      // lanes 8j .. 8j + 7 hold the 32 positions of word p0 >> 5, at bits 4 (t & 7)
+      const uint32_t word = or_lanes8(above << (p0 & 31));
+      if ((tid & 7) == 7 && word != 0u) sh.taken[p0 >> 5] |= word;  // its only writer here
       if (inb != 0u) {
         if (exact) {
           atomicOr(&sh.in_bin[p0 >> 5], inb << (p0 & 31));
@@ -504,7 +573,8 @@ __device__ __forceinline__ void select_stage(SelectLds& sh, const float* __restr
 
 // Ordered emit: [0, s_end) ++ the positions marked in sh.taken ++ [w_start, L)
 // (r of them marked).  Thread t owns words R*t .. R*t + R - 1.
-__device__ void emit_taken(SelectLds& sh, int R, int s_end, int w_start, int L, int r,
+template <class Lds>
+__device__ void emit_taken(Lds& sh, int R, int s_end, int w_start, int L, int r,
                            int32_t* __restrict__ out, int32_t idx_stride) {
   const int tid = threadIdx.x;
   const uint32_t* my = sh.taken + R * tid;
@@ -959,6 +1029,115 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
   if (tid == 0) n_idx[b] = k;
 }
 
+// ---------------------------------------------------------------------------
+// Finish and select in one launch, for rows of up to two rounds.
+//   * Workgroups [0, B * pieces) aggregate: workgroup (b, piece) sums the
+//     collected logits of positions piece * 4096 .. + 4095 below L_b into
+//     the scores (aggregate_values: the arithmetic of the aggregation
+//     kernel), stores them with device scope, and counts the top 12 key bits
+//     of those in M = [s_end, w_start) into an LDS histogram, which it then
+//     adds into the row's histogram in the workspace (device-scope atomics,
+//     non-empty bins only).  It counts itself in once all of that is out;
+//     the last of the row's pieces to do so selects the row: it moves the
+//     histogram to LDS (leaving zeros for the next call) and runs the
+//     one-workgroup selection from the threshold scan on, reading the scores
+//     with device-scope loads.  No workgroup waits on another.  A row whose
+//     output does not depend on the scores (L <= k, or the forced positions
+//     fill the budget) is written by its piece 0.
+//   * The workgroups after them combine the split partials, kThreadsTk / (D
+//     / 4) rows each (combine_quad, as the combine kernel).
+// Aggregation comes first in the grid: its workgroups are dispatched first,
+// and the selections start while the combine runs.
+constexpr int kAggPos = 4 * kThreadsTk;  // positions per aggregation workgroup
+constexpr int kFusedRounds = 2;
+
+struct FinishSelectArgs {
+  int32_t k, n_sink, window;
+  int32_t* idx;
+  int32_t idx_stride;
+  int32_t* n_idx;
+  uint32_t* hist;   // [B][kBins] key histograms; zero between calls
+  int32_t* arrive;  // [B] pieces counted in; zero between calls
+  int32_t pieces;   // aggregation workgroups per sequence
+  int32_t n_agg;    // B * pieces
+};
+
+template <int D, bool VEC>
+__global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c, AggregateArgs ag,
+                                                                   FinishSelectArgs f) {
+  __shared__ SelectLdsT<kFusedRounds> sh;
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= f.n_agg) {
+    constexpr int Q = D / 4;
+    const int row = ((int)blockIdx.x - f.n_agg) * (kThreadsTk / Q) + tid / Q;
+    const int chunk = min(max(c.header[0], kTile), c.chunk);
+    if (row < c.rows) combine_quad<D>(c, row, tid % Q, chunk);
+    return;
+  }
+  const int b = (int)blockIdx.x / f.pieces, piece = (int)blockIdx.x % f.pieces;
+  const SelRow s = sel_row(b, ag.max_ctx, ag.seq_lens, f.k, f.n_sink, f.window);
+  int32_t* out = f.idx + (size_t)b * f.idx_stride;
+  if (s.trivial && piece == 0) {
+    if (s.L <= f.k) {
+      for (int j = tid; j < s.L; j += kThreadsTk) out[j] = j;
+      if (tid == 0) f.n_idx[b] = s.L;
+    } else {
+      for (int i = tid; i < s.s_end; i += kThreadsTk) out[i] = i;
+      for (int i = tid; i < s.L - s.w_start; i += kThreadsTk) out[s.s_end + i] = s.w_start + i;
+      if (tid == 0) f.n_idx[b] = f.k;
+    }
+  }
+  const int j0 = piece * kAggPos;
+  if (j0 >= s.L) return;  // no position here (and not counted in)
+
+  if (!s.trivial)
+    for (int i = tid; i < kBins; i += kThreadsTk) sh.hist[i] = 0u;
+  __syncthreads();
+  float* srow = ag.scores + (size_t)b * ag.max_ctx;
+  float val[4];
+  aggregate_values<4>(ag, b, j0 + tid, kThreadsTk, s.L, val);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = j0 + tid + u * kThreadsTk;
+    if (j < s.L) {
+      store1_device(srow, (uint32_t)j * 4u, val[u]);
+      if (!s.trivial && j >= s.s_end && j < s.w_start) atomicAdd(&sh.hist[order_key(val[u]) >> 20], 1u);
+    }
+  }
+  if (s.trivial) return;
+  __syncthreads();
+  uint32_t* gh = f.hist + (size_t)b * kBins;
+  for (int i = tid; i < kBins; i += kThreadsTk) {
+    const uint32_t h = sh.hist[i];
+    if (h != 0u) atomicAdd(gh + i, h);
+  }
+  // every store and histogram add of this workgroup has completed before it
+  // counts itself in
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int n_pieces = (s.L + kAggPos - 1) / kAggPos;
+    const int done = atomicAdd(f.arrive + b, 1) + 1;
+    s_last = done == n_pieces;
+    if (done == n_pieces) atomicExch(f.arrive + b, 0);  // ready for the next call
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // select from the row's histogram (every piece has added to it), then
+  // leave it zero for the next call
+  for (int i = tid; i < s.R * kThreadsTk; i += kThreadsTk) {
+    sh.taken[i] = 0u;
+    sh.in_bin[i] = 0u;
+  }
+  select_stage<VEC, false, true, true>(sh, srow, ag.max_ctx, s.R, s.s_end, s.w_start, (uint32_t)s.r,
+                                       gh);
+  emit_taken(sh, s.R, s.s_end, s.w_start, s.L, s.r, out, f.idx_stride);
+  if (tid == 0) f.n_idx[b] = f.k;
+  for (int i = tid; i < kBins; i += kThreadsTk) store1_device(reinterpret_cast<float*>(gh), (uint32_t)i * 4u, 0.f);
+}
+
 }  // namespace
 
 hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* scores,
@@ -1064,6 +1243,41 @@ hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* sco
   else
     hipLaunchKernelGGL(select_blocks_kernel<false>, grid, block_dim, 0, stream, max_ctx, scores,
                        seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx, block_sums);
+  return hipGetLastError();
+}
+
+size_t finish_select_workspace_bytes(int32_t batch) {
+  const size_t hist = ((size_t)batch * kBins * 4 + 255) / 256 * 256;
+  return hist + ((size_t)batch * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, int32_t k,
+                                int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
+                                int32_t* n_idx, void* workspace, hipStream_t stream) {
+  if (ag.max_ctx > kFusedRounds * kRoundLen || ag.scores == nullptr) return hipErrorInvalidValue;
+  FinishSelectArgs f;
+  f.k = k;
+  f.n_sink = n_sink;
+  f.window = window;
+  f.idx = idx;
+  f.idx_stride = idx_stride;
+  f.n_idx = n_idx;
+  f.hist = static_cast<uint32_t*>(workspace);
+  f.arrive = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                        ((size_t)ag.batch * kBins * 4 + 255) / 256 * 256);
+  f.pieces = (ag.max_ctx + kAggPos - 1) / kAggPos;
+  f.n_agg = ag.batch * f.pieces;
+  const int q = c.head_dim / 4;
+  const int n_comb = (c.rows + kThreadsTk / q - 1) / (kThreadsTk / q);
+  const dim3 grid((unsigned)(f.n_agg + n_comb)), block(kThreadsTk);
+  const bool vec = ag.max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(ag.scores) & 15) == 0;
+  if (c.head_dim == 64) {
+    if (vec) hipLaunchKernelGGL((finish_select_kernel<64, true>), grid, block, 0, stream, c, ag, f);
+    else hipLaunchKernelGGL((finish_select_kernel<64, false>), grid, block, 0, stream, c, ag, f);
+  } else {
+    if (vec) hipLaunchKernelGGL((finish_select_kernel<128, true>), grid, block, 0, stream, c, ag, f);
+    else hipLaunchKernelGGL((finish_select_kernel<128, false>), grid, block, 0, stream, c, ag, f);
+  }
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -286,6 +286,49 @@ def test_select_workspace_sizes_and_validation(lib):
                                           fake, None, 0, None) == 3
     assert lib.vgsa_select_topk_hybrid_ws(4, 131072, fake, None, fake, 512, 100, 4, 64, fake, 512,
                                           fake, fake, ws(4, 131072), None) == 1
+
+
+def test_finish_select_argument_checks(lib):
+    """vgsa_verify_finish_select validates as vgsa_verify_finish plus
+    vgsa_select_topk, refuses rows past 65536 positions, and checks its
+    selection workspace; all before any launch."""
+    d = desc()
+    dp = ctypes.byref(d)
+    ws = lib.vgsa_verify_workspace_bytes(dp)
+    sws = lib.vgsa_finish_select_workspace_bytes(2)
+    assert sws >= 2 * 4096 * 4 + 2 * 4 and sws % 256 == 0
+    assert lib.vgsa_finish_select_workspace_bytes(0) == 0
+    F = lib.vgsa_verify_finish_select
+
+    def call(**kw):
+        a = dict(d=dp, lens=FAKE, ws=FAKE, ws_bytes=ws, out=FAKE, lse=None, layout=2, rows=0, acc=0,
+                 logits=FAKE, scores=FAKE, k=64, sink=4, window=16, idx=FAKE, stride=64, n_idx=FAKE,
+                 sws=FAKE, sws_bytes=sws)
+        a.update(kw)
+        return F(a["d"], a["lens"], a["ws"], a["ws_bytes"], a["out"], a["lse"], a["layout"],
+                 a["rows"], a["acc"], a["logits"], a["scores"], a["k"], a["sink"], a["window"],
+                 a["idx"], a["stride"], a["n_idx"], a["sws"], a["sws_bytes"], None)
+
+    assert call(scores=None) == INVALID      # the scores are required
+    assert call(logits=None) == INVALID
+    assert call(layout=0) == INVALID         # no logits layout
+    assert call(k=0) == INVALID
+    assert call(sink=50, window=20) == INVALID  # forced positions exceed the budget
+    assert call(stride=63) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(n_idx=None) == INVALID
+    assert call(lens=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=ws - 1) == WORKSPACE
+    assert call(sws=None) == WORKSPACE
+    assert call(sws_bytes=sws - 1) == WORKSPACE
+    assert call(sws=ctypes.c_void_p(0x1010)) == WORKSPACE
+    big = desc(max_ctx=65537)
+    assert F(ctypes.byref(big), FAKE, FAKE, lib.vgsa_verify_workspace_bytes(ctypes.byref(big)), FAKE,
+             None, 2, 0, 0, FAKE, FAKE, 64, 4, 16, FAKE, 64, FAKE, FAKE, sws, None) == UNSUPPORTED
+    bad = desc(head_dim=96)
+    assert F(ctypes.byref(bad), FAKE, FAKE, 1 << 40, FAKE, None, 2, 0, 0, FAKE, FAKE, 64, 4, 16, FAKE,
+             64, FAKE, FAKE, sws, None) == UNSUPPORTED
 
 
 def test_binding_refuses_accumulate_without_scores():
