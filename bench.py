@@ -308,6 +308,10 @@ def main():
     stride = k_blocks * BLK if args.select == "blocks" else w.budget
     idx = torch.empty((B, stride), dtype=torch.int32, device=dev)
     n_idx = torch.empty((B,), dtype=torch.int32, device=dev)
+    # block mode: the kept blocks' ids (the gathers expand them themselves)
+    blocks = args.select == "blocks"
+    blk_ids = torch.empty((B, k_blocks), dtype=torch.int32, device=dev)
+    n_ids = torch.empty((B,), dtype=torch.int32, device=dev)
     ws_s = torch.zeros(Bn.sparse_workspace_bytes(desc, stride), dtype=torch.uint8, device=dev)
     out_s = torch.empty_like(out)
     lse_s = torch.empty_like(lse)
@@ -327,8 +331,13 @@ def main():
         # step s attends the kept positions and the s + 1 drafted since (the
         # trailing positions of its length), in one launch
         for s in range(n_draft):
-            Bn.sparse_attention(q_draft[s], k, v, lens_draft[s], idx, n_idx, block_table=bt,
-                                max_ctx=max_ctx, tail=s + 1, out=out_d, lse=lse_d, workspace=ws_d)
+            if blocks:
+                Bn.sparse_attention_blocks(q_draft[s], k, v, lens_draft[s], blk_ids, n_ids, BLK,
+                                           block_table=bt, max_ctx=max_ctx, tail=s + 1, out=out_d,
+                                           lse=lse_d, workspace=ws_d)
+            else:
+                Bn.sparse_attention(q_draft[s], k, v, lens_draft[s], idx, n_idx, block_table=bt,
+                                    max_ctx=max_ctx, tail=s + 1, out=out_d, lse=lse_d, workspace=ws_d)
 
     draft_sc = torch.from_numpy(W.draft_scores(w)).to(dev)
     # rows of several 32768-position rounds: selection spread over one workgroup per round
@@ -349,8 +358,9 @@ def main():
         if args.select == "hybrid":
             Bn.select_topk_hybrid(scores, draft_sc, lens, w.budget, w.draft_m, w.n_sink, w.window,
                                   idx=idx, n_idx=n_idx, workspace=ws_sel)
-        elif args.select == "blocks":
-            Bn.select_blocks(scores, lens, k_blocks, BLK, w.n_sink, w.window, idx=idx, n_idx=n_idx)
+        elif blocks:
+            Bn.select_block_ids(scores, lens, k_blocks, BLK, w.n_sink, w.window, ids=blk_ids,
+                                n_ids=n_ids)
         else:
             Bn.select_topk(scores, lens, w.budget, w.n_sink, w.window, idx=idx, n_idx=n_idx,
                            workspace=ws_sel)
@@ -364,9 +374,16 @@ def main():
             Bn.verify_finish(desc, lens, ws_v, out, lse, KV, logits, scores)
             select()
         if w.sparse_verify:
+            sparse_pass(ql, k, v)
+        draft_steps(k, v)
+
+    def sparse_pass(ql, k, v):
+        if blocks:
+            Bn.sparse_attention_blocks(ql, k, v, lens, blk_ids, n_ids, BLK, block_table=bt,
+                                       max_ctx=max_ctx, out=out_s, lse=lse_s, workspace=ws_s)
+        else:
             Bn.sparse_attention(ql, k, v, lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
                                 out=out_s, lse=lse_s, workspace=ws_s)
-        draft_steps(k, v)
 
     def step():
         if n_layers > 1:
@@ -453,9 +470,7 @@ def main():
         stages["combine_aggregate"] = finish_us
         stages["select"] = select_us
     if w.sparse_verify:
-        stages["sparse"] = per_launch_us(
-            lambda: Bn.sparse_attention(q, *kv(), lens, idx, n_idx, block_table=bt, max_ctx=max_ctx,
-                                        out=out_s, lse=lse_s, workspace=ws_s))
+        stages["sparse"] = per_launch_us(lambda: sparse_pass(q, *kv()))
     if n_draft:
         stages["draft_steps"] = per_launch_us(lambda: draft_steps(*kv()))
     verify_none_us = per_launch_us(
@@ -478,12 +493,21 @@ def main():
     n_b = torch.empty((B,), dtype=torch.int32, device=dev)
     select_blocks_us = per_launch_us(
         lambda: Bn.select_blocks(scores, lens, k_blocks, BLK, w.n_sink, w.window, idx=idx_b, n_idx=n_b))
-    sparse_blocks_us = None
+    # ... and as block ids, with the gather over the block lists
+    ids_b = torch.empty((B, k_blocks), dtype=torch.int32, device=dev)
+    nid_b = torch.empty((B,), dtype=torch.int32, device=dev)
+    select_block_ids_us = per_launch_us(
+        lambda: Bn.select_block_ids(scores, lens, k_blocks, BLK, w.n_sink, w.window, ids=ids_b,
+                                    n_ids=nid_b))
+    sparse_blocks_us = sparse_block_ids_us = None
     if w.sparse_verify:
         ws_b = torch.zeros(Bn.sparse_workspace_bytes(desc, k_blocks * BLK), dtype=torch.uint8, device=dev)
         sparse_blocks_us = per_launch_us(
             lambda: Bn.sparse_attention(q, *kv(), lens, idx_b, n_b, block_table=bt, max_ctx=max_ctx,
                                         out=out_s, lse=lse_s, workspace=ws_b))
+        sparse_block_ids_us = per_launch_us(
+            lambda: Bn.sparse_attention_blocks(q, *kv(), lens, ids_b, nid_b, BLK, block_table=bt,
+                                               max_ctx=max_ctx, out=out_s, lse=lse_s, workspace=ws_b))
 
     ab = alg_bytes(w, x.seq_lens, args.logits, len(rows), n_heads,
                    k_blocks * BLK if args.select == "blocks" else None)
@@ -529,6 +553,8 @@ def main():
         "select_hybrid_us": select_hybrid_us,
         "select_blocks_us": select_blocks_us,
         "sparse_over_blocks_us": sparse_blocks_us,
+        "select_block_ids_us": select_block_ids_us,
+        "sparse_over_block_ids_us": sparse_block_ids_us,
     }
     if w.sparse_verify and stages.get("sparse"):
         sb = ab["sparse_kernel_kv"]

@@ -333,6 +333,22 @@ vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scor
                                int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
                                int32_t* n_idx, float* block_sums, void* stream);
 
+/* 3'' (block ids).  The same selection as vgsa_select_blocks, written as
+ * the kept blocks' ids instead of their positions, for the block-list gather
+ * (vgsa_sparse_attention_blocks).
+ * block_ids  int32 [B][ids_stride], ids_stride >= k_blocks.  Row b receives
+ *          the kept blocks ascending (block i covers positions
+ *          [i * block, (i + 1) * block)); every block of [0, L) when they
+ *          number at most k_blocks.
+ * n_ids    int32 [B]: blocks written
+ * Other arguments, limits and errors as vgsa_select_blocks.
+ */
+vgsa_status vgsa_select_block_ids(int32_t batch, int32_t max_ctx, const float* scores,
+                                  const int32_t* seq_lens, int32_t k_blocks, int32_t block,
+                                  int32_t n_sink, int32_t window, int32_t* block_ids,
+                                  int32_t ids_stride, int32_t* n_ids, float* block_sums,
+                                  void* stream);
+
 /* 4. Sparse attention over an index list (page size 1).
  *    (Vegas section 2 step 3 and section 3; Dustin "3.")
  * desc->q_len is T' (1 for a draft step, gamma + 1 for a sparse verify).
@@ -357,6 +373,35 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
                                   const int32_t* n_idx, int32_t idx_stride, int32_t tail,
                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/* 4 (block lists).  Sparse attention over whole blocks of positions
+ *    (structured block sparsity: the euno.news summary of arXiv 2512.21911,
+ *    "3. sparse verification engine"; with block = 16 on a paged cache each
+ *    listed block is one page, Vegas section 3).  The same attention as
+ *    vgsa_sparse_attention over the position list that the blocks expand
+ *    to, without that list being written out.
+ * block_ids, n_ids, ids_stride  int32 [B][ids_stride] ascending distinct
+ *          block ids as written by vgsa_select_block_ids, n_ids[b] of them
+ *          (0 .. ids_stride); block i stands for positions [i * block,
+ *          (i + 1) * block) clipped to [0, L'_b - tail): only the last
+ *          listed block may reach past L'_b - tail, and ids must be below
+ *          ceil((L'_b - tail) / block).
+ * block    positions per block, 1 .. 1024
+ * tail     as in vgsa_sparse_attention (the positions L'_b - tail .. L'_b - 1
+ *          follow the blocks' positions)
+ * workspace  >= vgsa_sparse_workspace_bytes(desc, ids_stride * block + tail)
+ *          bytes, its counter part zero on first use (as for
+ *          vgsa_sparse_attention, which it may share).
+ * Other arguments and errors as vgsa_sparse_attention; VGSA_ERR_INVALID_ARG
+ * for a block outside 1 .. 1024.
+ */
+vgsa_status vgsa_sparse_attention_blocks(const vgsa_attn_desc* desc, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         const int32_t* block_ids, const int32_t* n_ids,
+                                         int32_t ids_stride, int32_t block, int32_t tail, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream);
 
 /* Draft steps: append consecutive positions to index lists.
  *    (Vegas section 2 step 3: each drafting step attends over the selected

@@ -2,6 +2,7 @@
 from .attention import (  # noqa: F401
     aggregate_scores,
     attend,
+    block_positions,
     block_sums,
     collected_logits,
     default_scale,

@@ -328,6 +328,15 @@ def select_blocks(scores: np.ndarray, length: int, k_blocks: int, block: int, n_
     return pos[keep[pos // block]]
 
 
+def block_positions(ids: Sequence[int], block: int, length: int) -> np.ndarray:
+    """The positions a list of block ids stands for (structured block
+    sparsity: block i is positions [i * block, (i + 1) * block)), clipped to
+    [0, length), in list order.  Returns int64 positions."""
+    L = int(length)
+    out = [p for i in ids for p in range(int(i) * block, min((int(i) + 1) * block, L))]
+    return np.asarray(out, dtype=np.int64)
+
+
 def select_blocks_batch(scores: np.ndarray, seq_lens: Sequence[int], k_blocks: int, block: int,
                         n_sink: int, window: int,
                         sums: Optional[np.ndarray] = None) -> List[np.ndarray]:

@@ -56,6 +56,11 @@ SIGNATURES = {
                                    c_vp, c_vp, c_vp]),
     "vgsa_sparse_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "vgsa_select_block_ids": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp,
+                                      c_i32, c_vp, c_vp, c_vp]),
+    "vgsa_sparse_attention_blocks": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp,
+                                             c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                             c_sz, c_vp]),
     "vgsa_verify_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_u32,
                                      c_u64, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "vgsa_sparse_partials": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -368,6 +373,52 @@ def select_blocks(scores, seq_lens, k_blocks: int, block: int, n_sink: int, wind
                                      window, _p(idx), idx.shape[1], _p(n_idx), _p(block_sums),
                                      _stream(scores.device)), "vgsa_select_blocks")
     return idx, n_idx
+
+
+def select_block_ids(scores, seq_lens, k_blocks: int, block: int, n_sink: int, window: int, *,
+                     ids_stride=None, ids=None, n_ids=None, block_sums=None):
+    """vgsa_select_block_ids.  Returns (ids int32 [B, ids_stride] kept block
+    ids ascending, n_ids int32 [B])."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, max_ctx = scores.shape
+    stride = k_blocks if ids_stride is None else ids_stride
+    if ids is None:
+        ids = torch.empty((B, stride), dtype=torch.int32, device=scores.device)
+    if n_ids is None:
+        n_ids = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    if block_sums is not None:
+        _need(block_sums, "block_sums", torch.float32, 2)
+        if tuple(block_sums.shape) != (B, -(-max_ctx // block)):
+            raise ValueError(f"block_sums must be [{B}, {-(-max_ctx // block)}]")
+    _check(load().vgsa_select_block_ids(B, max_ctx, _p(scores), _p(seq_lens), k_blocks, block,
+                                        n_sink, window, _p(ids), ids.shape[1], _p(n_ids),
+                                        _p(block_sums), _stream(scores.device)),
+           "vgsa_select_block_ids")
+    return ids, n_ids
+
+
+def sparse_attention_blocks(q, k_cache, v_cache, seq_lens, ids, n_ids, block: int, *,
+                            block_table=None, max_ctx=None, tail: int = 0, out=None, lse=None,
+                            workspace=None, scale: float = 0.0):
+    """vgsa_sparse_attention_blocks: sparse attention over whole blocks of
+    `block` positions (ids ascending).  Returns (out, lse) as sparse_attention."""
+    _check_attn(q, k_cache, v_cache, seq_lens, block_table)
+    _need(ids, "ids", torch.int32, 2)
+    _need(n_ids, "n_ids", torch.int32, 1)
+    desc = make_desc(q, k_cache, block_table, max_ctx, scale)
+    B, Hq, T, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = _workspace(sparse_workspace_bytes(desc, ids.shape[1] * block + tail), dev, workspace)
+    _check(load().vgsa_sparse_attention_blocks(
+        ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(block_table), _p(seq_lens), _p(ids),
+        _p(n_ids), ids.shape[1], block, tail, _p(out), _p(lse), _p(ws), ws.numel(), _stream(dev)),
+        "vgsa_sparse_attention_blocks")
+    return out, lse
 
 
 def sparse_attention(q, k_cache, v_cache, seq_lens, idx, n_idx, *, block_table=None, max_ctx=None,

@@ -14,6 +14,8 @@ size_t sparse_sync_bytes(const vgsa_attn_desc& d);
 namespace {
 
 constexpr int64_t kMaxGridYZ = 65535;
+// Largest block of a block list (positions per entry), as in block selection.
+constexpr int32_t kMaxIdBlock = 1024;
 constexpr int64_t kMaxOffset = 0x7FFFFFFFLL;  // elements: byte offsets stay within 32 bits
 constexpr uintptr_t kWorkspaceAlign = 256;
 
@@ -105,6 +107,7 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
   a.out = nullptr;
   a.lse = nullptr;
   a.direct = 0;
+  a.id_block = 1;
   return a;
 }
 
@@ -273,16 +276,17 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
                           const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                           const int32_t* idx, const int32_t* n_idx, int32_t idx_stride,
                           int32_t tail, void* workspace, size_t workspace_bytes, void* out,
-                          float* lse, bool fused, void* stream) {
+                          float* lse, bool fused, void* stream, int32_t id_block = 1) {
   vgsa_status st = check_desc(desc);
   if (st != VGSA_OK) return st;
   const vgsa_attn_desc& d = *desc;
   st = check_attn_pointers(d, q, k_cache, v_cache, block_table, seq_lens);
   if (st != VGSA_OK) return st;
   if (idx == nullptr || n_idx == nullptr || idx_stride < 1 || tail < 0) return VGSA_ERR_INVALID_ARG;
-  if ((int64_t)idx_stride + tail > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
-  // entries: up to idx_stride listed, then the trailing positions
-  const int32_t span = idx_stride + tail;
+  if ((int64_t)idx_stride * id_block + tail > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
+  // entries: up to idx_stride listed (times the block size for block lists),
+  // then the trailing positions
+  const int32_t span = idx_stride * id_block + tail;
   // one split for lists up to kDirectSpan (the output is written directly);
   // longer lists split, and with `fused` the splits merge in the same launch
   const SplitPlan p = make_plan(d, span);
@@ -300,6 +304,7 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   a.n_idx = n_idx;
   a.idx_stride = idx_stride;
   a.tail = tail;
+  a.id_block = id_block;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   // one call: a single split writes the output itself, several merge in the launch
@@ -401,6 +406,21 @@ vgsa_status vgsa_sparse_attention(const vgsa_attn_desc* desc, const void* q, con
   // one launch: the splits of a (sequence, kv-head) merge in the same kernel
   return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, idx, n_idx, idx_stride,
                        tail, workspace, workspace_bytes, out, lse, true, stream);
+}
+
+vgsa_status vgsa_sparse_attention_blocks(const vgsa_attn_desc* desc, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         const int32_t* block_ids, const int32_t* n_ids,
+                                         int32_t ids_stride, int32_t block, int32_t tail, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  vgsa_status st = check_desc(desc);
+  if (st != VGSA_OK) return st;
+  if (out == nullptr || !aligned(out, 16) || ids_stride < 1 || block < 1 || block > kMaxIdBlock)
+    return VGSA_ERR_INVALID_ARG;
+  return sparse_launch(desc, q, k_cache, v_cache, block_table, seq_lens, block_ids, n_ids,
+                       ids_stride, tail, workspace, workspace_bytes, out, lse, true, stream, block);
 }
 
 }  // extern "C"
@@ -593,25 +613,50 @@ vgsa_status vgsa_select_topk_hybrid(int32_t batch, int32_t max_ctx, const float*
                                        static_cast<hipStream_t>(stream)));
 }
 
-vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
+}  // extern "C"
+
+namespace {
+
+vgsa_status select_blocks_call(int32_t batch, int32_t max_ctx, const float* scores,
                                const int32_t* seq_lens, int32_t k_blocks, int32_t block,
-                               int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
-                               int32_t* n_idx, float* block_sums, void* stream) {
-  if (batch < 0 || max_ctx < 1 || k_blocks < 1 || block < 1 || block > 1024 || n_sink < 0 ||
+                               int32_t n_sink, int32_t window, int32_t* out, int32_t out_stride,
+                               int32_t* n_out, float* block_sums, bool ids, void* stream) {
+  if (batch < 0 || max_ctx < 1 || k_blocks < 1 || block < 1 || block > kMaxIdBlock || n_sink < 0 ||
       window < 0)
     return VGSA_ERR_INVALID_ARG;
   // the sink blocks and (at most ceil(window / block) + 1) window blocks fit the budget
   const int64_t forced = ((int64_t)n_sink + block - 1) / block +
                          (window > 0 ? ((int64_t)window + block - 1) / block + 1 : 0);
   if (forced > k_blocks) return VGSA_ERR_INVALID_ARG;
-  if ((int64_t)idx_stride < (int64_t)k_blocks * block) return VGSA_ERR_INVALID_ARG;
-  if (scores == nullptr || seq_lens == nullptr || idx == nullptr || n_idx == nullptr)
+  if ((int64_t)out_stride < (int64_t)k_blocks * (ids ? 1 : block)) return VGSA_ERR_INVALID_ARG;
+  if (scores == nullptr || seq_lens == nullptr || out == nullptr || n_out == nullptr)
     return VGSA_ERR_INVALID_ARG;
   if (((int64_t)max_ctx + block - 1) / block > kMaxSelBlocks) return VGSA_ERR_UNSUPPORTED;
   if (batch == 0) return VGSA_OK;
   return hip_status(launch_select_blocks(batch, max_ctx, scores, seq_lens, k_blocks, block, n_sink,
-                                         window, idx, idx_stride, n_idx, block_sums,
+                                         window, out, out_stride, n_out, block_sums, ids,
                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+vgsa_status vgsa_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
+                               const int32_t* seq_lens, int32_t k_blocks, int32_t block,
+                               int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
+                               int32_t* n_idx, float* block_sums, void* stream) {
+  return select_blocks_call(batch, max_ctx, scores, seq_lens, k_blocks, block, n_sink, window, idx,
+                            idx_stride, n_idx, block_sums, false, stream);
+}
+
+vgsa_status vgsa_select_block_ids(int32_t batch, int32_t max_ctx, const float* scores,
+                                  const int32_t* seq_lens, int32_t k_blocks, int32_t block,
+                                  int32_t n_sink, int32_t window, int32_t* block_ids,
+                                  int32_t ids_stride, int32_t* n_ids, float* block_sums,
+                                  void* stream) {
+  return select_blocks_call(batch, max_ctx, scores, seq_lens, k_blocks, block, n_sink, window,
+                            block_ids, ids_stride, n_ids, block_sums, true, stream);
 }
 
 vgsa_status vgsa_append_positions(int32_t batch, const int32_t* base, int32_t first, int32_t count,

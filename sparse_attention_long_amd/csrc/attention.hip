@@ -268,14 +268,23 @@ void attn_partials_kernel(AttnArgs a) {
   // Sparse: the list entries of this wavefront's first kPreTiles tiles are
   // loaded (clamped in bounds) together with the lengths, so those tiles
   // need no index round trip of their own.
+  // Block lists (id_block = B > 1): entry e of the position list is
+  // position ids[e / B] * B + e % B.
   constexpr int kPreTiles = 4;
+  const int B_id = SPARSE ? a.id_block : 1;
   int idx_pre[kPreTiles];
 #pragma unroll
   for (int i = 0; i < kPreTiles; ++i) {
     idx_pre[i] = 0;
-    if (SPARSE && lane < kTile)
-      idx_pre[i] = a.idx[(size_t)b * a.idx_stride +
-                         min(start + (i * WAVES + wave) * kTile + lane, a.idx_stride - 1)];
+    if (SPARSE && lane < kTile) {
+      const int e = start + (i * WAVES + wave) * kTile + lane;
+      if (B_id == 1) {
+        idx_pre[i] = a.idx[(size_t)b * a.idx_stride + min(e, a.idx_stride - 1)];
+      } else {
+        const int blk_e = min(e / B_id, a.idx_stride - 1);
+        idx_pre[i] = a.idx[(size_t)b * a.idx_stride + blk_e] * B_id + (e - blk_e * B_id);
+      }
+    }
   }
   const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int32_t* btab = a.paged ? a.block_table + (size_t)b * a.max_blocks : nullptr;
@@ -289,8 +298,16 @@ void attn_partials_kernel(AttnArgs a) {
   }
   // sparse: the listed entries, then (virtually) the last `tail` positions
   // below L, e.g. the tokens drafted since the selection
-  const int nlist = SPARSE ? min(max(a.n_idx[b], 0), a.idx_stride) : 0;
   const int tail = SPARSE ? min(a.tail, L) : 0;
+  int nlist = SPARSE ? min(max(a.n_idx[b], 0), a.idx_stride) : 0;
+  if (SPARSE && B_id > 1 && nlist > 0) {
+    // every position of the listed blocks below L - tail (only the last
+    // listed block can reach past it)
+    const int last = a.idx[(size_t)b * a.idx_stride + nlist - 1];
+    nlist = (nlist - 1) * B_id + min(B_id, max(0, L - tail - last * B_id));
+  } else if (SPARSE && B_id > 1) {
+    nlist = 0;
+  }
   const int count = SPARSE ? nlist + tail : L;
   const int G = a.group, T = a.q_len, rows = G * T;
   // Rows [B][Hq][T] of this kv-group are contiguous: row m = hh*T + t of the
@@ -385,8 +402,14 @@ void attn_partials_kernel(AttnArgs a) {
         const bool listed = li < nlist;
         int p = 0;
         if (listed) {
-          p = it == 0 ? idx_pre[0] : it == 1 ? idx_pre[1] : it == 2 ? idx_pre[2]
-            : it == 3 ? idx_pre[3] : a.idx[(size_t)b * a.idx_stride + li];
+          if (it < kPreTiles) {
+            p = it == 0 ? idx_pre[0] : it == 1 ? idx_pre[1] : it == 2 ? idx_pre[2] : idx_pre[3];
+          } else if (B_id == 1) {
+            p = a.idx[(size_t)b * a.idx_stride + li];
+          } else {
+            const int q_ = li / B_id;
+            p = a.idx[(size_t)b * a.idx_stride + q_] * B_id + (li - q_ * B_id);
+          }
         } else if (li < end) {
           p = L - tail + (li - nlist);  // a trailing position
         }
@@ -910,7 +933,7 @@ void attn_partials_kernel(AttnArgs a) {
       c.lse = a.lse;
       constexpr int Q = D / 4;
       for (int e = threadIdx.x; e < rows * Q; e += NT)
-        combine_quad<D, true>(c, (int)row_base + e / Q, e % Q, chunk);
+        combine_quad<D, true>(c, (int)row_base + e / Q, e % Q, chunk, count);
     }
   }
 }

@@ -100,6 +100,8 @@ struct AttnArgs {
   const int32_t* n_idx;  // sparse only
   int32_t idx_stride;
   int32_t tail;          // sparse: the last `tail` positions below the length follow the list
+  int32_t id_block;      // sparse: positions per list entry (1: positions; B > 1: block ids,
+                         // entry i covering positions B*i .. B*i + B - 1)
   float* logits;         // verify only, may be null
   int32_t layout;
   uint32_t row_mask;  // collected rows: bit t set for query row t
@@ -198,6 +200,6 @@ hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, i
 hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
                                 const int32_t* seq_lens, int32_t k_blocks, int32_t block,
                                 int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
-                                int32_t* n_idx, float* block_sums, hipStream_t stream);
+                                int32_t* n_idx, float* block_sums, bool ids, hipStream_t stream);
 
 }  // namespace vgsa

@@ -61,12 +61,15 @@ constexpr int kMergeBatch = 8;
 // partials were written in the same launch by other workgroups (possibly on
 // another XCD, whose L2 this one's does not see): read them with device-scope
 // loads, which bypass stale cache lines.
+// `entries` >= 0: the number of entries the partials cover (given by a caller
+// that has it); otherwise min(lengths[b], span) + tail.
 template <int D, bool COHERENT = false>
-__device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int t, int chunk) {
+__device__ __forceinline__ void combine_quad(const CombineArgs& a, int row, int t, int chunk,
+                                             int entries = -1) {
   constexpr float kNegInf = -__builtin_huge_valf();
   constexpr int Q = D / 4;
   const int b = row / a.rows_per_seq;
-  const int len = min(max(a.lengths[b], 0), a.span) + a.tail;
+  const int len = entries >= 0 ? entries : min(max(a.lengths[b], 0), a.span) + a.tail;
   const int nvalid = min((len + chunk - 1) / chunk, a.part_splits);
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)row * a.part_splits;
   const float4* po = reinterpret_cast<const float4*>(a.part_o) + (size_t)row * a.part_splits * Q + t;

@@ -648,7 +648,9 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
 // attention call as it is.  With bsum_out the fp32 block sums the ranking
 // compared are also written out ([B][ceil(max_ctx / block)], blocks below
 // ceil(L / block)), so a caller can check them and rank them itself.
-template <bool VEC>
+// IDS: the kept blocks' ids are written instead (ascending, n_idx[b] of
+// them), for a gather over block lists.
+template <bool VEC, bool IDS>
 __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
     int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     int32_t k_blocks, int32_t block, int32_t n_sink, int32_t window, int32_t* __restrict__ idx,
@@ -722,8 +724,9 @@ __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
     }
   }
   if (keep_all) {
-    for (int j = tid; j < L; j += kThreadsTk) out[j] = j;
-    if (tid == 0) n_idx[b] = L;
+    const int n_all = IDS ? nb : L;
+    for (int j = tid; j < n_all; j += kThreadsTk) out[j] = j;
+    if (tid == 0) n_idx[b] = n_all;
     return;
   }
   if (r > 0) {
@@ -736,8 +739,19 @@ __global__ __launch_bounds__(kThreadsTk) void select_blocks_kernel(
   }
 
   // Ordered emit: sink positions ++ the chosen middle blocks' positions ++
-  // window positions.  Thread t owns the 32 blocks of bitmap word t.
+  // window positions (IDS: the blocks themselves).  Thread t owns the 32
+  // blocks of bitmap word t.
   const uint32_t word = sh.taken[tid];
+  if (IDS) {
+    uint32_t mid;
+    uint32_t o = block_exclusive_scan((uint32_t)__builtin_popcount(word), sh.s_wave, mid) +
+                 (uint32_t)s_end;
+    for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) out[o++] = 32 * tid + __builtin_ctz(bits);
+    for (int i = tid; i < s_end; i += kThreadsTk) out[i] = i;
+    for (int i = tid; i < nb - w_start; i += kThreadsTk) out[s_end + (int)mid + i] = w_start + i;
+    if (tid == 0) n_idx[b] = s_end + (int)mid + (nb - w_start);
+    return;
+  }
   uint32_t n_mine = 0u, mid_total;
   for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
     const int blk = 32 * tid + __builtin_ctz(bits);
@@ -1232,17 +1246,20 @@ hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float*
 hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* scores,
                                 const int32_t* seq_lens, int32_t k_blocks, int32_t block,
                                 int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
-                                int32_t* n_idx, float* block_sums, hipStream_t stream) {
+                                int32_t* n_idx, float* block_sums, bool ids, hipStream_t stream) {
   if ((max_ctx + block - 1) / block > kMaxSelBlocks) return hipErrorInvalidValue;
   const bool vec = max_ctx % 4 == 0 && block % 4 == 0 &&
                    (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   const dim3 grid(batch), block_dim(kThreadsTk);
-  if (vec)
-    hipLaunchKernelGGL(select_blocks_kernel<true>, grid, block_dim, 0, stream, max_ctx, scores,
-                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx, block_sums);
-  else
-    hipLaunchKernelGGL(select_blocks_kernel<false>, grid, block_dim, 0, stream, max_ctx, scores,
-                       seq_lens, k_blocks, block, n_sink, window, idx, idx_stride, n_idx, block_sums);
+  const auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block_dim, 0, stream, max_ctx, scores, seq_lens, k_blocks,
+                       block, n_sink, window, idx, idx_stride, n_idx, block_sums);
+  };
+  if (ids) {
+    if (vec) go(select_blocks_kernel<true, true>); else go(select_blocks_kernel<false, true>);
+  } else {
+    if (vec) go(select_blocks_kernel<true, false>); else go(select_blocks_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 

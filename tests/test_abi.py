@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -329,6 +329,38 @@ def test_finish_select_argument_checks(lib):
     bad = desc(head_dim=96)
     assert F(ctypes.byref(bad), FAKE, FAKE, 1 << 40, FAKE, None, 2, 0, 0, FAKE, FAKE, 64, 4, 16, FAKE,
              64, FAKE, FAKE, sws, None) == UNSUPPORTED
+
+
+def test_block_list_argument_checks(lib):
+    """vgsa_select_block_ids validates as vgsa_select_blocks but needs only
+    k_blocks entries per row; vgsa_sparse_attention_blocks refuses a block
+    outside 1 .. 1024 and checks its workspace against ids_stride * block +
+    tail entries."""
+    S = lib.vgsa_select_block_ids
+    assert S(2, 1000, FAKE, FAKE, 8, 16, 4, 16, FAKE, 7, FAKE, None, None) == INVALID   # stride < k
+    assert S(2, 1000, FAKE, FAKE, 8, 0, 4, 16, FAKE, 8, FAKE, None, None) == INVALID    # block 0
+    assert S(2, 1000, FAKE, FAKE, 8, 1025, 4, 16, FAKE, 8, FAKE, None, None) == INVALID
+    assert S(2, 1000, FAKE, FAKE, 2, 16, 4, 40, FAKE, 8, FAKE, None, None) == INVALID   # forced > k
+    assert S(2, 1000, None, FAKE, 8, 16, 4, 16, FAKE, 8, FAKE, None, None) == INVALID
+    assert S(2, 1 << 20, FAKE, FAKE, 8, 16, 4, 16, FAKE, 8, FAKE, None, None) == UNSUPPORTED
+    assert S(0, 1000, FAKE, FAKE, 8, 16, 4, 16, FAKE, 8, FAKE, None, None) == OK      # nothing to do
+    d = desc()
+    dp = ctypes.byref(d)
+    SA = lib.vgsa_sparse_attention_blocks
+    ws = lib.vgsa_sparse_workspace_bytes(dp, 8 * 16 + 3)
+    assert SA(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 0, 3, FAKE, None, FAKE, ws, None) == INVALID
+    assert SA(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 1025, 3, FAKE, None, FAKE, ws,
+              None) == INVALID
+    assert SA(dp, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 8, 16, 3, FAKE, None, FAKE, ws,
+              None) == INVALID
+    assert SA(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 16, -1, FAKE, None, FAKE, ws,
+              None) == INVALID
+    assert SA(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 16, 3, None, None, FAKE, ws,
+              None) == INVALID
+    assert SA(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 16, 3, FAKE, None, FAKE, ws - 1,
+              None) == WORKSPACE
+    assert SA(dp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 22, 1024, 3, FAKE, None, FAKE,
+              1 << 40, None) == UNSUPPORTED  # ids_stride * block past int32
 
 
 def test_binding_refuses_accumulate_without_scores():

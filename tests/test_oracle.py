@@ -467,3 +467,20 @@ def test_widen_bf16_exact():
     got = oracle.widen_bf16(bits)
     assert list(got) == want
     assert math.copysign(1.0, got[3]) == -1.0
+
+
+def test_block_positions_expands_block_lists():
+    """Block lists stand for whole blocks of positions, clipped to the length
+    (closed forms), and the positions block selection keeps are exactly the
+    expansion of the blocks they fall in."""
+    assert list(oracle.block_positions([0, 2], 16, 40)) == list(range(16)) + list(range(32, 40))
+    assert list(oracle.block_positions([1, 3], 5, 100)) == [5, 6, 7, 8, 9, 15, 16, 17, 18, 19]
+    assert list(oracle.block_positions([], 16, 40)) == []
+    assert list(oracle.block_positions([2], 16, 32)) == []          # a block wholly past the length
+    assert list(oracle.block_positions([0, 1, 2], 1, 3)) == [0, 1, 2]  # block 1: the ids themselves
+    rng = np.random.default_rng(4)
+    for L, kb, block, ns, win in [(500, 7, 16, 4, 40), (37, 2, 8, 0, 0), (1000, 30, 5, 3, 17)]:
+        sc = rng.standard_normal(L).astype(np.float32)
+        pos = oracle.select_blocks(sc, L, kb, block, ns, win)
+        ids = np.unique(pos // block)
+        assert np.array_equal(oracle.block_positions(ids, block, L), pos)
