@@ -345,7 +345,10 @@ def main():
     ws_sel = torch.empty(n_ws_sel, dtype=torch.uint8, device=dev) if n_ws_sel else None
 
     # plain selection on rows of up to 65536 positions: finish (combine +
-    # aggregate) and selection in one launch
+    # aggregate) and selection in one launch.  Longer rows keep the separate
+    # launches: one workgroup per 32768-position round selects them faster
+    # than the one selecting workgroup of the fused launch (128K x b8: 41 us
+    # against 52 us)
     fused = args.select == "plain" and max_ctx <= 65536 and args.finish_select == "fused"
     ws_fs = torch.zeros(Bn.finish_select_workspace_bytes(B), dtype=torch.uint8, device=dev) \
         if fused else None

@@ -468,7 +468,10 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
  * The workgroups that sum a sequence's scores also count the leading 12 bits
  * of their order-preserving keys into a histogram of that sequence; the last
  * of them to finish selects the sequence's positions in the same launch,
- * starting from that histogram.  No workgroup waits on another.
+ * starting from that histogram.  No workgroup waits on another.  One
+ * workgroup selects each sequence, so rows of more than two 32768-position
+ * rounds select faster with the two calls (vgsa_select_topk_ws spreads a
+ * row over one workgroup per round).
  * desc .. scores  as vgsa_verify_finish; scores must not be NULL
  * k, n_sink, window, idx, idx_stride, n_idx  as vgsa_select_topk
  * select_workspace  >= vgsa_finish_select_workspace_bytes(batch) bytes of
@@ -477,7 +480,7 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
  *          zero-filled allocation); every call leaves it zero again.  Calls
  *          that share it must not overlap.
  * Errors: as vgsa_verify_finish and vgsa_select_topk; VGSA_ERR_UNSUPPORTED
- * for max_ctx > 65536 (make the two calls instead); VGSA_ERR_WORKSPACE for a
+ * for max_ctx > 262144 (make the two calls instead); VGSA_ERR_WORKSPACE for a
  * missing, small or misaligned select_workspace.
  */
 size_t vgsa_finish_select_workspace_bytes(int32_t batch);

@@ -189,10 +189,10 @@ hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float*
 constexpr int kMaxHybridRow = 8 * 32768;
 // Block-granular selection: blocks per row (their sums live in LDS).
 constexpr int kMaxSelBlocks = 8704;
-// Combine + aggregate + select in one launch (rows of max_ctx <= 65536; the
+// Combine + aggregate + select in one launch (rows of max_ctx <= 262144; the
 // workspace holds per-row key histograms and arrival counts, zero between
 // calls).
-constexpr int kFinishSelectMaxCtx = 65536;
+constexpr int kFinishSelectMaxCtx = 262144;
 size_t finish_select_workspace_bytes(int32_t batch);
 hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, int32_t k,
                                 int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,

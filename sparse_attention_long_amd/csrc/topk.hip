@@ -1044,7 +1044,8 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Finish and select in one launch, for rows of up to two rounds.
+// Finish and select in one launch, for rows of up to eight rounds (262144
+// positions).
 //   * Workgroups [0, B * pieces) aggregate: workgroup (b, piece) sums the
 //     collected logits of positions piece * 4096 .. + 4095 below L_b into
 //     the scores (aggregate_values: the arithmetic of the aggregation
@@ -1063,7 +1064,7 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
 // Aggregation comes first in the grid: its workgroups are dispatched first,
 // and the selections start while the combine runs.
 constexpr int kAggPos = 4 * kThreadsTk;  // positions per aggregation workgroup
-constexpr int kFusedRounds = 2;
+constexpr int kFusedRoundsShort = 2;  // LDS of the selection for rows of up to 65536 positions
 
 struct FinishSelectArgs {
   int32_t k, n_sink, window;
@@ -1076,10 +1077,11 @@ struct FinishSelectArgs {
   int32_t n_agg;    // B * pieces
 };
 
-template <int D, bool VEC>
+// RM: rounds the LDS bitmaps hold (max_ctx <= RM * 32768).
+template <int D, bool VEC, int RM>
 __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c, AggregateArgs ag,
                                                                    FinishSelectArgs f) {
-  __shared__ SelectLdsT<kFusedRounds> sh;
+  __shared__ SelectLdsT<RM> sh;
   __shared__ int s_last;
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= f.n_agg) {
@@ -1271,7 +1273,7 @@ size_t finish_select_workspace_bytes(int32_t batch) {
 hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, int32_t k,
                                 int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
                                 int32_t* n_idx, void* workspace, hipStream_t stream) {
-  if (ag.max_ctx > kFusedRounds * kRoundLen || ag.scores == nullptr) return hipErrorInvalidValue;
+  if (ag.max_ctx > kMaxRounds * kRoundLen || ag.scores == nullptr) return hipErrorInvalidValue;
   FinishSelectArgs f;
   f.k = k;
   f.n_sink = n_sink;
@@ -1288,12 +1290,26 @@ hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, i
   const int n_comb = (c.rows + kThreadsTk / q - 1) / (kThreadsTk / q);
   const dim3 grid((unsigned)(f.n_agg + n_comb)), block(kThreadsTk);
   const bool vec = ag.max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(ag.scores) & 15) == 0;
+  const bool short_rows = ag.max_ctx <= kFusedRoundsShort * kRoundLen;
+  const auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, c, ag, f);
+  };
   if (c.head_dim == 64) {
-    if (vec) hipLaunchKernelGGL((finish_select_kernel<64, true>), grid, block, 0, stream, c, ag, f);
-    else hipLaunchKernelGGL((finish_select_kernel<64, false>), grid, block, 0, stream, c, ag, f);
+    if (short_rows) {
+      if (vec) go(finish_select_kernel<64, true, kFusedRoundsShort>);
+      else go(finish_select_kernel<64, false, kFusedRoundsShort>);
+    } else {
+      if (vec) go(finish_select_kernel<64, true, kMaxRounds>);
+      else go(finish_select_kernel<64, false, kMaxRounds>);
+    }
   } else {
-    if (vec) hipLaunchKernelGGL((finish_select_kernel<128, true>), grid, block, 0, stream, c, ag, f);
-    else hipLaunchKernelGGL((finish_select_kernel<128, false>), grid, block, 0, stream, c, ag, f);
+    if (short_rows) {
+      if (vec) go(finish_select_kernel<128, true, kFusedRoundsShort>);
+      else go(finish_select_kernel<128, false, kFusedRoundsShort>);
+    } else {
+      if (vec) go(finish_select_kernel<128, true, kMaxRounds>);
+      else go(finish_select_kernel<128, false, kMaxRounds>);
+    }
   }
   return hipGetLastError();
 }

@@ -290,7 +290,7 @@ def test_select_workspace_sizes_and_validation(lib):
 
 def test_finish_select_argument_checks(lib):
     """vgsa_verify_finish_select validates as vgsa_verify_finish plus
-    vgsa_select_topk, refuses rows past 65536 positions, and checks its
+    vgsa_select_topk, refuses rows past 262144 positions, and checks its
     selection workspace; all before any launch."""
     d = desc()
     dp = ctypes.byref(d)
@@ -323,7 +323,7 @@ def test_finish_select_argument_checks(lib):
     assert call(sws=None) == WORKSPACE
     assert call(sws_bytes=sws - 1) == WORKSPACE
     assert call(sws=ctypes.c_void_p(0x1010)) == WORKSPACE
-    big = desc(max_ctx=65537)
+    big = desc(max_ctx=262145)
     assert F(ctypes.byref(big), FAKE, FAKE, lib.vgsa_verify_workspace_bytes(ctypes.byref(big)), FAKE,
              None, 2, 0, 0, FAKE, FAKE, 64, 4, 16, FAKE, 64, FAKE, FAKE, sws, None) == UNSUPPORTED
     bad = desc(head_dim=96)

@@ -167,3 +167,30 @@ def test_finish_select_crafted_scores(kind):
             fus = _finish_fused(desc, dv, ws, Bn.LOGITS_KVGROUP_SUM, lg, k, n_sink, window, k + 1,
                                 sws, scores0=acc)
             _assert_same(sep, fus, lens, k, n_sink, window, sws, what)
+
+
+@pytest.mark.parametrize("M,lens", [
+    (131088, [131088, 100001, 65537, 700]),   # five rounds (16-byte loads)
+    (131078, [131078, 99999, 32768]),          # unaligned capacity (4-byte loads)
+    (262144, [262144, 200000]),                # eight rounds
+])
+def test_finish_select_long_rows(M, lens):
+    """Rows of up to eight rounds of 32768 positions: the selecting workgroup
+    reloads the row per pass; threshold bins above the reloaded-row cap take
+    further radix passes."""
+    dv = _Dev(5, lens, M, hq=4, hkv=1, d=64, T=2)
+    desc = Bn.make_desc(dv.q, dv.k, None, M)
+    ws = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    lg0 = torch.empty((len(lens), 1, M), dtype=torch.float32, device="cuda")
+    Bn.verify_partials(desc, dv.q, dv.k, dv.v, dv.seq_lens, None, (0, 1), Bn.LOGITS_KVGROUP_SUM,
+                       lg0, ws)
+    sws = torch.zeros(Bn.finish_select_workspace_bytes(len(lens)), dtype=torch.uint8, device="cuda")
+    for kind in ("normal", "integer_ties", "threshold_bin"):
+        rng = np.random.default_rng(KINDS.index(kind) + 7)
+        lg = torch.from_numpy(_crafted_logits(kind, rng, len(lens), 1, M, lens)).cuda()
+        for k, n_sink, window in [(6554, 4, 256), (512, 4, 64)]:
+            what = f"M={M} {kind} k={k}"
+            say(f"[finish+select long rows] {what}")
+            sep = _finish_separately(desc, dv, ws, Bn.LOGITS_KVGROUP_SUM, lg, k, n_sink, window, k)
+            fus = _finish_fused(desc, dv, ws, Bn.LOGITS_KVGROUP_SUM, lg, k, n_sink, window, k, sws)
+            _assert_same(sep, fus, lens, k, n_sink, window, sws, what)
