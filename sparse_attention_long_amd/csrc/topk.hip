@@ -69,16 +69,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
   return (uint32_t)v;
 }
 
-// Lane 8j + 7 of each group of eight lanes receives the OR of the group's x
-// (DPP row shifts by 1, 2, 4 with zero fill; a group never crosses a 16-lane
-// row).  All lanes of the wavefront must be active.
-__device__ __forceinline__ uint32_t or_lanes8(uint32_t x) {
-  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
-  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
-  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
-  return x;
-}
-
 // Exclusive prefix sum of v over the workgroup (.x) and the sum (.y).
 // Results come back by value: a call the compiler keeps out of line then
 // needs no stack slots.
@@ -534,10 +524,9 @@ __device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ 
   }
   const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
 
-  // Mark keys above the bin; collect (or mark) the bin's members.  The
-  // eight lanes whose positions share a bitmap word OR their bits together
-  // (DPP) and the last of them stores the word: one LDS write per word
-  // instead of eight atomics on it.
+  // Mark keys above the bin; collect (or mark) the bin's members.  (Bitmap
+  // words assembled with DPP ORs over the eight lanes that share a word and
+  // stored once measured slower than the eight lanes' LDS atomics.)
 #pragma unroll 1
   for (int rd = 0; rd < R; ++rd) {
     if (reload && !(rd == 0 && have0)) load_round(rd);
@@ -551,9 +540,7 @@ __device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ 
         inb |= (key[c][e] != 0u && mk == prefix) ? (1u << e) : 0u;
       }
       const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
-      // lanes 8j .. 8j + 7 hold the 32 positions of word p0 >> 5, at bits 4 (t & 7)
-      const uint32_t word = or_lanes8(above << (p0 & 31));
-      if ((tid & 7) == 7 && word != 0u) sh.taken[p0 >> 5] |= word;  // its only writer here
+      if (above != 0u) atomicOr(&sh.taken[p0 >> 5], above << (p0 & 31));
       if (inb != 0u) {
         if (exact) {
           atomicOr(&sh.in_bin[p0 >> 5], inb << (p0 & 31));
