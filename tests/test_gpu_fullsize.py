@@ -6,6 +6,9 @@ verify with the kv-group-summed logit epilogue, aggregate, select, then the
 sparse pass (sparse verify over the T rows and/or single-query draft steps
 whose lists carry the freshly drafted positions).  The oracle checks:
   * selection for every sequence, bit-exact on the GPU's own scores;
+  * for rows of up to 65536 positions, the benchmark's form (verify partials,
+    then combine + aggregate + select in one launch) gives the same scores and
+    selection bit for bit, and outputs within the oracle bar;
   * outputs, lse, collected logits and scores of every sequence, element by
     element, on kv-head b mod Hkv of sequence b (plus the first and last
     kv-heads for the first and last sequences).  Every sequence matters: the
@@ -59,6 +62,32 @@ def test_fullsize_sampled(name):
             assert np.array_equal(idx_h[b, :n_h[b]], want[b]), f"{name} idx b={b}"
             assert set(x.planted[b].tolist()) <= set(want[b].tolist()), f"planted key dropped b={b}"
 
+        # the benchmark's form for rows of up to 65536 positions: verify partials,
+        # then the split combine, the score aggregation and the selection in one
+        # launch (vgsa_verify_finish_select)
+        out_f = lse_f = None
+        if d.max_ctx <= 65536:
+            say(f"[fullsize] {name} layer {layer}: verify partials + finish-select")
+            desc = Bn.make_desc(d.q, d.k, d.block_table, d.max_ctx)
+            ws = torch.empty(Bn.verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+            lg_f = torch.empty_like(lg)
+            Bn.verify_partials(desc, d.q, d.k, d.v, d.seq_lens, d.block_table, w.collect_rows,
+                               Bn.LOGITS_KVGROUP_SUM, lg_f, ws)
+            out_f, lse_f = torch.empty_like(out), torch.empty_like(lse)
+            sc_f = torch.empty_like(scores)
+            idx_f = torch.full_like(idx, -1)
+            n_f = torch.empty_like(n_idx)
+            sws = torch.zeros(Bn.finish_select_workspace_bytes(w.batch), dtype=torch.uint8,
+                              device="cuda")
+            Bn.verify_finish_select(desc, d.seq_lens, ws, out_f, lse_f, Bn.LOGITS_KVGROUP_SUM, lg_f,
+                                    sc_f, w.budget, w.n_sink, w.window, idx_f, n_f, sws)
+            torch.cuda.synchronize()
+            for b in range(w.batch):
+                L = lens[b]
+                assert torch.equal(sc_f[b, :L], scores[b, :L]), f"{name} b={b} fused scores"
+                assert int(n_f[b]) == n_h[b], f"{name} b={b} fused count"
+                assert torch.equal(idx_f[b, :n_h[b]], idx[b, :n_h[b]]), f"{name} b={b} fused idx"
+
         G = w.group
 
         def heads_of(b):
@@ -75,6 +104,9 @@ def test_fullsize_sampled(name):
             o_ref, lse_ref = oracle.verify_attention(qb, kb, vb, lens[b:b + 1], heads=heads)
             assert_out_close(out[b:b + 1, heads], o_ref[:, heads], f"{name} b={b} verify out")
             assert_lse_close(lse[b:b + 1, heads], lse_ref[:, heads], f"{name} b={b} verify lse")
+            if out_f is not None:
+                assert_out_close(out_f[b:b + 1, heads], o_ref[:, heads], f"{name} b={b} fused out")
+                assert_lse_close(lse_f[b:b + 1, heads], lse_ref[:, heads], f"{name} b={b} fused lse")
             l_ref = oracle.collected_logits(qb, kb, lens[b:b + 1], w.collect_rows)
             absl = np.where(np.isneginf(l_ref), 0.0, np.abs(l_ref))
             grp = oracle.kvgroup_sum(l_ref, w.num_kv_heads)
