@@ -350,10 +350,10 @@ void attn_partials_kernel(AttnArgs a) {
     }
   }
   const int lim_min = L - T;  // every row sees positions <= L - T
-  // kv-group logits: weight 1 for a collected row of this lane, else 0
+  // kv-group logits: the softmax scale for a collected row of this lane, else 0
   float rowc_w[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) rowc_w[qb] = rowc[qb] >= 0 ? 1.f : 0.f;
+  for (int qb = 0; qb < QB; ++qb) rowc_w[qb] = rowc[qb] >= 0 ? a.scale : 0.f;
   // per-head logits: the collected rows of block qb, bit c16 (wave-uniform),
   // so blocks and row pairs with nothing to write are skipped
   uint32_t cmask[QB];
@@ -655,12 +655,14 @@ void attn_partials_kernel(AttnArgs a) {
       }
     } else if (EMIT == VGSA_LOGITS_KVGROUP_SUM) {
       // v8[pb*4 + r]: this lane's collected rows summed, at position pb*16 +
-      // 4*kg + r: a 0/1 weight per row (collected or not) times its S^T
-      // value, so no branch or select per term.  The earliest collected row
-      // sees a prefix of what the later ones see, so a position is hidden
-      // from a collected row iff it is hidden from that one: past its causal
-      // limit (one wave-uniform count per tile) the sum is -inf.  A kv-group
-      // with no collected head sums to 0 at every position.
+      // 4*kg + r: a weight per row (the softmax scale when collected, else 0)
+      // times its S^T value, so no branch or select per term.  The earliest
+      // collected row sees a prefix of what the later ones see, so a
+      // position is hidden from a collected row iff it is hidden from that
+      // one: past its causal limit (one wave-uniform count per tile) the sum
+      // is -inf, applied once to the reduced sum (the terms summed there are
+      // finite products either way).  A kv-group with no collected head sums
+      // to 0 at every position.
       const int row_first = __builtin_ctz(a.row_mask);
       const int vis0 = (full || gmask == 0ull)
                            ? kTile : max(0, min(L - T + row_first, ts + n_in - 1) - ts + 1);
@@ -672,7 +674,7 @@ void attn_partials_kernel(AttnArgs a) {
           float acc = 0.f;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) acc = __builtin_fmaf(rowc_w[qb], sacc[pb][qb][r], acc);
-          v8[pb * 4 + r] = (pb * 16 + 4 * kg + r) < vis0 ? acc * a.scale : kNegInf;
+          v8[pb * 4 + r] = acc;
         }
       // Reduce-scatter over the 16 query-row lanes: after the four steps lane
       // c16 holds the full sum of position pb = bit 3, r = 2*bit 2 + bit 1.
@@ -698,7 +700,7 @@ void attn_partials_kernel(AttnArgs a) {
       float v1 = (h2 ? v2[1] : v2[0]) + dpp_move<kDppXor2>(h2 ? v2[0] : v2[1]);
       v1 += dpp_move<kDppXor1>(v1);
       const int e = (h8 ? 16 : 0) + 4 * kg + 2 * h4 + h2;
-      if ((c16 & 1) == 0) slog[ts - lbase + e] = v1;
+      if ((c16 & 1) == 0) slog[ts - lbase + e] = e < vis0 ? v1 : kNegInf;
     }
 
     if (kSumQuery) {
