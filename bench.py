@@ -30,6 +30,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -40,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify+topk+sparse-attn iters/s per layer at 32K, b16; % of HBM peak BW"
 HBM_PEAK_GBS = 8000.0
+OVERHEAD_ROUNDS = 6  # alternating rounds of the logit-overhead measurement
 # K/V smaller than this rotate through copies (twice the 256 MB Infinity Cache)
 ROTATE_BYTES = 512 << 20
 
@@ -445,17 +447,18 @@ def main():
     # ---- stage breakdown and logit-emit overhead (outside the timed region):
     # each stage launched K times back to back between one pair of events, so
     # the figure is its pipelined per-launch time (no queue drain per launch)
-    def per_launch_us(fn):
+    def per_launch_us(fn, n=None):
+        n = K if n is None else n
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
         torch.cuda.synchronize()
         e0.record()
-        for _ in range(K):
+        for _ in range(n):
             rotate()  # the next K/V copy (the launches below read it through kv())
             fn()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / K
+        return e0.elapsed_time(e1) * 1e3 / n
 
     # the verify kernel's launch duration for the roofline: K launches of the
     # timed configuration back to back on the launch stream
@@ -476,16 +479,28 @@ def main():
         stages["sparse"] = per_launch_us(lambda: sparse_pass(q, *kv()))
     if n_draft:
         stages["draft_steps"] = per_launch_us(lambda: draft_steps(*kv()))
-    verify_none_us = per_launch_us(
-        lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, rows, Bn.LOGITS_NONE, None, ws_v))
-    # every verify row collected (the score summed over all T rows), same layout
+    # Logit-collection overhead: the collecting kernel (the step's rows, and
+    # every verify row: the score summed over all T rows, same layout) against
+    # the same kernel with collection off, in alternating rounds, medians over
+    # the rounds.  One back-to-back sample of each drifts by a few per cent
+    # over a run: as much as the overhead itself at the short ragged workload.
     all_rows = tuple(range(T))
     logits_all = logits
     if KV == Bn.LOGITS_PER_HEAD and len(rows) != T:
         logits_all = torch.empty((B, T, n_heads, max_ctx), dtype=torch.float32, device=dev)
-    verify_all_us = per_launch_us(
-        lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, all_rows, KV, logits_all, ws_v,
-                                   heads=heads))
+    ovh_fns = {
+        "none": lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, rows, Bn.LOGITS_NONE, None, ws_v),
+        "rows": lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, rows, KV, logits, ws_v,
+                                           heads=heads),
+        "all": lambda: Bn.verify_partials(desc, q, *kv(), lens, bt, all_rows, KV, logits_all, ws_v,
+                                          heads=heads),
+    }
+    ovh_samples = {key: [] for key in ovh_fns}
+    for _ in range(OVERHEAD_ROUNDS):
+        for key, fn in ovh_fns.items():
+            ovh_samples[key].append(per_launch_us(fn, max(4, K // 2)))
+    ovh = {key: statistics.median(v_) for key, v_ in ovh_samples.items()}
+    verify_none_us, verify_all_us = ovh["none"], ovh["all"]
     del logits_all
     # hybrid selection (draft signal first) on the same scores, for comparison
     select_hybrid_us = per_launch_us(
@@ -548,9 +563,12 @@ def main():
         "gpu_ms_per_step": gpu_ms / K,
         "stages_us": stages,
         "verify_partials_no_logits_us": verify_none_us,
-        "logit_emit_overhead": stages["verify_partials"] / verify_none_us - 1.0,
+        "verify_partials_collect_us": ovh["rows"],
+        "logit_emit_overhead": ovh["rows"] / verify_none_us - 1.0,
         "verify_partials_all_rows_us": verify_all_us,
         "logit_emit_overhead_all_rows": verify_all_us / verify_none_us - 1.0,
+        "logit_overhead_method": f"medians of {OVERHEAD_ROUNDS} alternating rounds of "
+                                 f"{max(4, K // 2)} launches per kernel form",
         "combine_aggregate_us": finish_us,
         "select_us": select_us,
         "select_hybrid_us": select_hybrid_us,
