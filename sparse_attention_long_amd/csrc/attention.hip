@@ -730,20 +730,33 @@ void attn_partials_kernel(AttnArgs a) {
 
     // Online softmax (log2 units, lazily rescaled) and the P fragments
     // (B operand of O^T = V^T P^T).
+    // x holds the unscaled S values (-inf where hidden); the scale is applied
+    // to the row maximum (rounding is monotonic, so that is the maximum of the
+    // scaled values) and inside the exponent's fused multiply-add.  Tiles that
+    // every row sees in full skip the mask (one wave-uniform branch).
     bf16x8 pf[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float x[2][4];
       float mx = kNegInf;
+      if (full) {
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
+        for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool seen = full || (pb * 16 + 4 * kg + r) < vis[qb];
-          x[pb][r] = seen ? sacc[pb][qb][r] * a.scale_log2 : kNegInf;
-          mx = fmaxf(mx, x[pb][r]);
-        }
-      mx = column_max(mx);
+          for (int r = 0; r < 4; ++r) {
+            x[pb][r] = sacc[pb][qb][r];
+            mx = fmaxf(mx, x[pb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[pb][r] = (pb * 16 + 4 * kg + r) < vis[qb] ? sacc[pb][qb][r] : kNegInf;
+            mx = fmaxf(mx, x[pb][r]);
+          }
+      }
+      mx = column_max(mx) * a.scale_log2;
       const bool grow = mx > m_run[qb] + kRescaleLog2;
       if (__any(grow)) {
         const float m_new = grow ? mx : m_run[qb];
@@ -761,7 +774,7 @@ void attn_partials_kernel(AttnArgs a) {
       for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pv = fast_exp2(x[pb][r] - m_use);
+          const float pv = fast_exp2(__builtin_fmaf(x[pb][r], a.scale_log2, -m_use));
           pf[qb][pb * 4 + r] = (__bf16)pv;
           psum += pv;
         }
