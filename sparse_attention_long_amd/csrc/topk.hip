@@ -69,21 +69,31 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
   return (uint32_t)v;
 }
 
-// Exclusive prefix sum of v over the workgroup (.x) and the sum (.y).
-// Results come back by value: a call the compiler keeps out of line then
-// needs no stack slots.
+// Sum of x over lanes 0..15 (DPP row scan; lane 15 holds the total), the
+// same value in every lane.
+__device__ __forceinline__ uint32_t row0_sum(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  return (uint32_t)__builtin_amdgcn_readlane(v, 15);
+}
+
+// Exclusive prefix sum of v over the workgroup (.x) and the sum (.y).  Lane w
+// of every wave reads wave w's total, so the waves before this one and all
+// waves are two 16-lane sums rather than a loop over the totals.  Results
+// come back by value: a call the compiler keeps out of line then needs no
+// stack slots.
 __device__ uint2 block_scan(uint32_t v, uint32_t* s_wave) {
+  static_assert(kWavesTk == 16, "one DPP row of wave totals");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWavesTk; ++w) {
-    const uint32_t c = s_wave[w];
-    base += (w < wave) ? c : 0u;
-    tot += c;
-  }
+  const uint32_t c = lane < kWavesTk ? s_wave[lane] : 0u;
+  const uint32_t tot = row0_sum(c);
+  const uint32_t base = row0_sum(lane < wave ? c : 0u);
   __syncthreads();
   return make_uint2(base + x - v, tot);
 }
@@ -366,10 +376,11 @@ struct SelectLdsT {
   uint32_t hist[kBins];
   uint32_t s_wave[kWavesTk];
   uint32_t s_out[4];
-  uint32_t taken[RM * kThreadsTk];   // positions selected (above the bin, or ranked in)
-  uint32_t in_bin[RM * kThreadsTk];  // bin members, when they are all equal
+  __align__(16) uint32_t taken[RM * kThreadsTk];   // positions selected (above the bin, or ranked in)
+  __align__(16) uint32_t in_bin[RM * kThreadsTk];  // bin members, when they are all equal
   // bin members as (key << 32 | ~position): larger means ranked first
   __align__(16) uint64_t bin_rank_key[kBinCap + 4];
+  uint32_t rank[kBinCap];  // members ranked before each one
   uint32_t count;
 };
 using SelectLds = SelectLdsT<kMaxRounds>;
@@ -382,24 +393,39 @@ using SelectLds = SelectLdsT<kMaxRounds>;
 template <class Lds>
 __device__ void resolve_bin(Lds& sh, uint32_t nbin, uint32_t want, bool exact, int R) {
   const int tid = threadIdx.x;
-  if (!exact && tid < 4) sh.bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
+  if (!exact) {
+    if (tid < 4) sh.bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
+    for (int q = tid; q < (int)nbin; q += kThreadsTk) sh.rank[q] = 0u;
+  }
   __syncthreads();
   if (!exact) {
-    // rank = members with a larger key, or an equal key at a lower position
+    // rank = members with a larger key, or an equal key at a lower position.
+    // Members go 64 to a wave (lane = member), and the waves left over split
+    // the list to compare against into shares: every lane of a wave reads the
+    // same entries, and the partial counts meet in sh.rank.
+    const int lane = tid & 63, wave = tid >> 6;
     const int n4 = (int)(nbin + 3u) / 4;
-    for (int q = tid; q < (int)nbin; q += kThreadsTk) {
-      const uint64_t cq = sh.bin_rank_key[q];
-      uint32_t rank = 0u;
-      for (int f = 0; f < n4; ++f) {
+    const int blocks = (int)(nbin + 63u) / 64;  // <= kWavesTk: nbin <= kBinCap
+    const int shares = max(1, kWavesTk / blocks);
+    const int mb = wave / shares, sh_i = wave % shares;
+    if (mb < blocks) {
+      const int q = mb * 64 + lane;
+      const uint64_t cq = q < (int)nbin ? sh.bin_rank_key[q] : ~0ull;
+      const int f1 = (sh_i + 1) * n4 / shares;
+      uint32_t cnt = 0u;
+      for (int f = sh_i * n4 / shares; f < f1; ++f) {
         const uint64_t* c4 = sh.bin_rank_key + 4 * f;
-        rank += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
-                (c4[3] > cq ? 1u : 0u);
+        cnt += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
+               (c4[3] > cq ? 1u : 0u);
       }
-      if (rank < want) {
-        const int pq = (int)~(uint32_t)cq;
+      if (q < (int)nbin && cnt != 0u) atomicAdd(&sh.rank[q], cnt);
+    }
+    __syncthreads();
+    for (int q = tid; q < (int)nbin; q += kThreadsTk)
+      if (sh.rank[q] < want) {
+        const int pq = (int)~(uint32_t)sh.bin_rank_key[q];
         atomicOr(&sh.taken[pq >> 5], 1u << (pq & 31));
       }
-    }
   } else {
     // the first `want` bin members in position order join the taken set;
     // thread t owns words R*t .. R*t + R - 1
@@ -419,55 +445,85 @@ __device__ void resolve_bin(Lds& sh, uint32_t nbin, uint32_t want, bool exact, i
   __syncthreads();
 }
 
+// Lanes 0..7 of the result: the 32-bit halves of four 64-bit wave-uniform
+// masks, b[j / 2] >> 32 (j % 2) in lane j (other lanes 0).  v_writelane
+// takes the scalar operand directly, one instruction per lane (a register
+// move; the asm touches no memory).
+__device__ __forceinline__ uint32_t words8(const uint64_t (&b)[4]) {
+  uint32_t w = 0u;
+#define VGSA_WL(J, X) asm("v_writelane_b32 %0, %1, " #J : "+v"(w) : "s"(X))
+  VGSA_WL(0, (uint32_t)b[0]);
+  VGSA_WL(1, (uint32_t)(b[0] >> 32));
+  VGSA_WL(2, (uint32_t)b[1]);
+  VGSA_WL(3, (uint32_t)(b[1] >> 32));
+  VGSA_WL(4, (uint32_t)b[2]);
+  VGSA_WL(5, (uint32_t)(b[2] >> 32));
+  VGSA_WL(6, (uint32_t)b[3]);
+  VGSA_WL(7, (uint32_t)(b[3] >> 32));
+#undef VGSA_WL
+  return w;
+}
+
 // One selection stage: marks in sh.taken the `want_stage` middle positions
 // [s_end, w_start) of highest score in row `sc` (lower position first among
-// equal keys).  EXCL: positions already marked are no candidates; a thread
-// only marks positions whose keys it has already read, so the marks it reads
-// are the earlier stage's.  COHERENT: the scores were written in this launch
-// by other workgroups (possibly on another XCD): they are read with
-// device-scope loads.  PREHIST: ghist holds the first pass's histogram (top
-// 12 key bits of the stage's candidates, kBins counts, written in this launch:
-// read with device-scope loads, together with the first round's keys).
+// equal keys).  FROM_LDS: `sc` is an LDS array (else global memory, read as a
+// buffer bounded by the row, whose loads past the row return 0).  EXCL:
+// positions already marked are no candidates; a thread only marks positions
+// whose keys it has already read, so the marks it reads are the earlier
+// stage's.  COHERENT: the scores were written in this launch by other
+// workgroups (possibly on another XCD): they are read with device-scope
+// loads.  PREHIST: ghist holds the first pass's histogram (top 12 key bits of
+// the stage's candidates, kBins counts, written in this launch: read with
+// device-scope loads, together with the first round's keys).
+// Slot (c, e) of a thread holds position rd * kRoundLen + c * 4 * kThreadsTk +
+// 256 * wave + 64 * e + lane: one slot of a wave is 64 consecutive positions,
+// two whole bitmap words, which a ballot over the slot gives at once.
 // Starts and ends with a workgroup barrier.
-template <bool VEC, bool EXCL, bool COHERENT = false, bool PREHIST = false, class Lds>
+template <bool FROM_LDS, bool EXCL, bool COHERENT = false, bool PREHIST = false, class Lds>
 __device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ sc,
                                              int max_ctx, int R, int s_end, int w_start,
                                              uint32_t want_stage,
                                              const uint32_t* __restrict__ ghist = nullptr) {
   static_assert(!(PREHIST && EXCL), "a precomputed histogram has no exclusions");
-  const int tid = threadIdx.x;
+  static_assert(!(FROM_LDS && COHERENT), "device-scope loads read global memory");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool reload = R > 1;
+  // (unused when FROM_LDS)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), 0, max_ctx * 4, kRawBufferWord3);
   // Keys of round `rd`; 0 outside M = [s_end, w_start) (and for excluded
-  // positions).  Addresses are clamped into the row rather than branched on,
-  // so all loads are in flight together (a clamped load only serves
-  // positions at or past the row end, which are masked).
+  // positions).  A wave whose 256 positions of a chunk all lie in M (and no
+  // exclusions) skips the per-position tests.
   uint32_t key[kSmallChunks][4];
   auto load_round = [&](int rd) {
     float v[kSmallChunks][4];
+    const int p_lane = rd * kRoundLen + 256 * wave + lane;
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = p_lane + c * 4 * kThreadsTk + 64 * e;
+        if constexpr (FROM_LDS)
+          v[c][e] = sc[min(p, max_ctx - 1)];
+        else
+          v[c][e] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)p * 4u, 0, COHERENT ? kCpolSc1 : 0));
+      }
 #pragma unroll
     for (int c = 0; c < kSmallChunks; ++c) {
-      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;
-      if (VEC) {
-        const int o = min(p0, max_ctx - 4);
-        const float4 x = COHERENT ? load4_device(sc, (uint32_t)o * 4u)
-                                  : *reinterpret_cast<const float4*>(sc + o);
-        v[c][0] = x.x; v[c][1] = x.y; v[c][2] = x.z; v[c][3] = x.w;
+      const int b0 = rd * kRoundLen + c * 4 * kThreadsTk + 256 * wave;  // wave-uniform
+      if (!EXCL && b0 >= s_end && b0 + 256 <= w_start) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[c][e] = order_key(v[c][e]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int o = min(p0 + e, max_ctx - 1);
-          v[c][e] = COHERENT ? load1_device(sc, (uint32_t)o * 4u) : sc[o];
+          const int p = b0 + 64 * e + lane;
+          bool in = p >= s_end && p < w_start;
+          if (EXCL) in = in && ((sh.taken[p >> 5] >> (p & 31)) & 1u) == 0u;
+          key[c][e] = in ? order_key(v[c][e]) : 0u;
         }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kSmallChunks; ++c) {
-      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
-      const uint32_t gone = EXCL ? (sh.taken[p0 >> 5] >> (p0 & 31)) : 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = p0 + e;
-        key[c][e] = (p >= s_end && p < w_start && ((gone >> e) & 1u) == 0u) ? order_key(v[c][e]) : 0u;
       }
     }
   };
@@ -494,7 +550,10 @@ __device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ 
   }
 
   // Radix passes: after each, keys whose masked value exceeds `prefix` are
-  // taken and `want` more come from the bin (masked value == prefix).
+  // taken and `want` more come from the bin (masked value == prefix).  Real
+  // keys are >= 1 and the bin holds one at least, so with hi = prefix | ~mask
+  // and lo = max(prefix, 1) a key is above the bin iff key > hi and in it iff
+  // key - lo <= hi - lo (unsigned; key 0 is neither).
   uint32_t prefix = 0u, mask = 0u, want = want_stage, nbin = 0u;
   int level = 0;
 #pragma unroll 1
@@ -502,6 +561,7 @@ __device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ 
     const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
     const uint32_t nb = level == 2 ? 256u : (uint32_t)kBins;
     if (!PREHIST || level > 0) {
+      const uint32_t lo = prefix > 1u ? prefix : 1u, span = (prefix | ~mask) - lo;
       for (int i = tid; i < (int)nb; i += kThreadsTk) sh.hist[i] = 0u;
       __syncthreads();
 #pragma unroll 1
@@ -511,8 +571,7 @@ __device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ 
         for (int c = 0; c < kSmallChunks; ++c)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (key[c][e] != 0u && (key[c][e] & mask) == prefix)
-              atomicAdd(&sh.hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
+            if (key[c][e] - lo <= span) atomicAdd(&sh.hist[(key[c][e] >> shift) & (nb - 1u)], 1u);
       }
       if (reload) have0 = false;  // key[] ends on the last round
       __syncthreads();
@@ -523,38 +582,55 @@ __device__ __forceinline__ void select_stage(Lds& sh, const float* __restrict__ 
     if (nbin <= (uint32_t)(reload ? kBinCapMany : kBinCapOne)) break;
   }
   const bool exact = level == 3;  // the bin's keys are all equal: lowest positions first
+  const uint32_t hi = prefix | ~mask, lo = prefix > 1u ? prefix : 1u;
 
-  // Mark keys above the bin; collect (or mark) the bin's members.  (Bitmap
-  // words assembled with DPP ORs over the eight lanes that share a word and
-  // stored once measured slower than the eight lanes' LDS atomics.)
+  // Mark keys above the bin; collect (or mark) the bin's members.  A chunk's
+  // four slots are eight bitmap words that only this wave writes: their
+  // ballots go into lanes 0..7 (lane 2e + h holds half h of slot e) and
+  // those lanes OR them in with one LDS instruction.  Ranked bin members
+  // (few) take list slots with one LDS atomic per chunk that has any.
+  const int wlane = lane < 8 ? lane : 7;
+  const auto mark = [&](auto exact_c) {
+    constexpr bool EXACT = decltype(exact_c)::value;
 #pragma unroll 1
-  for (int rd = 0; rd < R; ++rd) {
-    if (reload && !(rd == 0 && have0)) load_round(rd);
+    for (int rd = 0; rd < R; ++rd) {
+      if (reload && !(rd == 0 && have0)) load_round(rd);
 #pragma unroll
-    for (int c = 0; c < kSmallChunks; ++c) {
-      uint32_t above = 0u, inb = 0u;
+      for (int c = 0; c < kSmallChunks; ++c) {
+        const int b0 = rd * kRoundLen + c * 4 * kThreadsTk + 256 * wave;  // wave-uniform
+        uint64_t up[4], in[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t mk = key[c][e] & mask;
-        above |= (key[c][e] != 0u && mk > prefix) ? (1u << e) : 0u;
-        inb |= (key[c][e] != 0u && mk == prefix) ? (1u << e) : 0u;
-      }
-      const int p0 = rd * kRoundLen + c * 4 * kThreadsTk + 4 * tid;  // 4-aligned: one word
-      if (above != 0u) atomicOr(&sh.taken[p0 >> 5], above << (p0 & 31));
-      if (inb != 0u) {
-        if (exact) {
-          atomicOr(&sh.in_bin[p0 >> 5], inb << (p0 & 31));
-        } else {
+        for (int e = 0; e < 4; ++e) {
+          up[e] = __ballot(key[c][e] > hi);
+          in[e] = __ballot(key[c][e] >= lo) & ~up[e];  // lo <= key <= hi
+        }
+        if (lane < 8) atomicOr(&sh.taken[(b0 >> 5) + wlane], words8(up));
+        if constexpr (EXACT) {
+          if (lane < 8) atomicOr(&sh.in_bin[(b0 >> 5) + wlane], words8(in));
+        } else if ((in[0] | in[1] | in[2] | in[3]) != 0u) {
+          const uint32_t n =
+              (uint32_t)(__popcll(in[0]) + __popcll(in[1]) + __popcll(in[2]) + __popcll(in[3]));
+          uint32_t slot = 0u;
+          if (lane == 0) slot = atomicAdd(&sh.count, n);  // total < nbin <= kBinCap
+          slot = __builtin_amdgcn_readfirstlane(slot);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if ((inb >> e) & 1u) {
-              const uint32_t slot = atomicAdd(&sh.count, 1u);  // < nbin <= kBinCap
-              sh.bin_rank_key[slot] = ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(p0 + e);
+          for (int e = 0; e < 4; ++e) {
+            if ((in[e] >> lane) & 1u) {
+              const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                  (uint32_t)(in[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)in[e], 0u));
+              sh.bin_rank_key[slot + below] =
+                  ((uint64_t)key[c][e] << 32) | (uint32_t)~(uint32_t)(b0 + 64 * e + lane);
             }
+            slot += (uint32_t)__popcll(in[e]);
+          }
         }
       }
     }
-  }
+  };
+  if (exact)
+    mark(std::true_type{});
+  else
+    mark(std::false_type{});
   resolve_bin(sh, nbin, want, exact, R);
 }
 
@@ -613,10 +689,10 @@ __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
   }
   const int m_first = HYBRID ? min(max(m, 0), r) : 0;
   if (HYBRID && m_first > 0)
-    select_stage<VEC, false>(sh, first + (size_t)b * max_ctx, max_ctx, R, s_end, w_start,
+    select_stage<false, false>(sh, first + (size_t)b * max_ctx, max_ctx, R, s_end, w_start,
                              (uint32_t)m_first);
   if (r > m_first)
-    select_stage<VEC, HYBRID>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s_end, w_start,
+    select_stage<false, HYBRID>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s_end, w_start,
                               (uint32_t)(r - m_first));
 
   emit_taken(sh, R, s_end, w_start, L, r, out, idx_stride);
@@ -966,10 +1042,10 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
     // the bin is too big for the list (massive ties): one-workgroup selection
     for (int i = tid; i < R * kThreadsTk; i += kThreadsTk) sh.taken[i] = after_first ? first_row[i] : 0u;
     if (after_first)
-      select_stage<VEC, true>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
+      select_stage<false, true>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
                               (uint32_t)want_stage);
     else
-      select_stage<VEC, false>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
+      select_stage<false, false>(sh, scores + (size_t)b * max_ctx, max_ctx, R, s.s_end, s.w_start,
                                (uint32_t)want_stage);
   } else {
     const uint32_t prefix0 = ws.meta[(size_t)b * 4 + 0];
@@ -1134,7 +1210,7 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
     sh.taken[i] = 0u;
     sh.in_bin[i] = 0u;
   }
-  select_stage<VEC, false, true, true>(sh, srow, ag.max_ctx, s.R, s.s_end, s.w_start, (uint32_t)s.r,
+  select_stage<false, false, true, true>(sh, srow, ag.max_ctx, s.R, s.s_end, s.w_start, (uint32_t)s.r,
                                        gh);
   emit_taken(sh, s.R, s.s_end, s.w_start, s.L, s.r, out, f.idx_stride);
   if (tid == 0) f.n_idx[b] = f.k;
