@@ -60,6 +60,20 @@ __device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Inclusive prefix sum over the 64 lanes (DPP row shifts by 1, 2, 4, 8 within
+// each 16-lane row, then row broadcasts 15 and 31 carry rows 0 and 1 on);
+// lane 63 holds the total.
+__device__ __forceinline__ int wave_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ int wave_total(int x) { return __builtin_amdgcn_readlane(wave_scan(x), 63); }
+
 // Waves per SIMD the register budget is sized for: two (<= 256 registers per
 // wave) unless four query blocks of d = 128 need more.
 template <int D, int QB>
@@ -193,12 +207,71 @@ void attn_partials_kernel(AttnArgs a) {
   int split = blockIdx.x, b = blockIdx.z, chunk = a.chunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, kg = lane >> 4;
+  // Ragged verify batches of up to 64 sequences: lane i holds sequence i's
+  // length (a buffer load bounded by the array: lanes past it read 0) and
+  // the item is derived across the lanes (below).
+  const bool lane_lens = !SPARSE && a.balance && a.batch <= 64;
+  int len_lane = 0;
+  if (lane_lens)
+    len_lane = min(max((int)__builtin_amdgcn_raw_buffer_load_b32(
+                           __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.seq_lens), 0, a.batch * 4,
+                                                             kRawBufferWord3),
+                           (uint32_t)lane * 4u, 0, 0),
+                       0),
+                   a.max_ctx);
 
   // Ragged batches (verify): every workgroup derives the same item length
   // from the lengths, short enough that the non-empty items of a kv-head fill
   // its S * B workgroups, and takes one of them (below): the longest
   // workgroup then has about the mean work, not the longest row's.
-  if (!SPARSE && a.balance) {
+  int L_item = -1;  // the item's sequence length, when the lanes hold it
+  if (lane_lens) {
+    // The same item lengths and mapping as below, with lane i standing for
+    // sequence i: a count over the sequences is one division per lane and a
+    // wave sum.
+    const int S = a.num_splits, B = a.batch;
+    const int64_t total = ((int64_t)wave_total(len_lane >> 16) << 16) + wave_total(len_lane & 0xFFFF);
+    const int64_t fit = (total + (int64_t)S * B - B - 1) / ((int64_t)S * B - B);  // S > 1 here
+    constexpr int MC = (kWide && !SPARSE) ? kTile : WAVES * kTile;
+    const int floor_len = (a.chunk / kBalanceSplits + MC - 1) / MC * MC;
+    int cp = (int)min((int64_t)a.chunk, max((int64_t)floor_len, (fit + MC - 1) / MC * MC));
+    const int SB = S * B;
+    // items of this lane's sequence at item length c, capped (the sum then fits 32 bits)
+    auto n_items = [&](int c) { return min((len_lane + c - 1) / c, SB + 1); };
+    {
+      int lo = max(floor_len, (int)(((total + SB - 1) / SB + MC - 1) / MC * MC));
+      int hi = cp;
+      while (lo < hi) {
+        const int mid = max(lo, (lo + hi) / 2 / MC * MC);
+        if (wave_total(n_items(mid)) <= SB) hi = mid; else lo = mid + MC;
+      }
+      cp = hi;
+    }
+    const int it = (len_lane + cp - 1) / cp;  // items of sequence `lane` (0 past the batch)
+    const int nb = __builtin_amdgcn_readlane(it, b);
+    int bi = -1, si = 0;
+    if (split < nb) {
+      bi = b;
+      si = split;
+    } else {
+      // rank among the free workgroups, then the sequence whose items past S
+      // hold that rank (in sequence order)
+      const int r = split - nb + wave_total(lane < b ? max(0, S - it) : 0);
+      const int o = max(0, it - S);
+      const int pre = wave_scan(o);  // items past S of sequences 0 .. lane
+      const uint64_t hit = __ballot(r < pre);
+      if (hit != 0ull) {
+        bi = __builtin_ctzll(hit);
+        si = S + (r - (__builtin_amdgcn_readlane(pre, bi) - __builtin_amdgcn_readlane(o, bi)));
+      }
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) a.header[0] = cp;
+    if (bi < 0) return;  // more workgroups than items
+    L_item = __builtin_amdgcn_readlane(len_lane, bi);
+    b = bi;
+    split = si;
+    chunk = cp;
+  } else if (!SPARSE && a.balance) {
     const int S = a.num_splits, B = a.batch;
     int64_t total = 0;
     for (int i = 0; i < B; ++i) total += min(max(a.seq_lens[i], 0), a.max_ctx);
@@ -286,7 +359,7 @@ void attn_partials_kernel(AttnArgs a) {
       }
     }
   }
-  const int L = min(max(a.seq_lens[b], 0), a.max_ctx);
+  const int L = L_item >= 0 ? L_item : min(max(a.seq_lens[b], 0), a.max_ctx);
   const int32_t* btab = a.paged ? a.block_table + (size_t)b * a.max_blocks : nullptr;
   // Paged sparse: block ids of the preloaded entries, fetched together.
   int blk_pre[kPreTiles];
@@ -484,14 +557,17 @@ void attn_partials_kernel(AttnArgs a) {
   // tile's loads go out: a wavefront's loads complete in issue order, so
   // query loads issued after the first K/V tile would wait for it.
   // Fragment (qb, ks, lane) holds row m = qb*16 + lane%16,
-  // d = ks*32 + (lane/16)*8 .. +8.
-  for (int f = threadIdx.x; f < QB * KS * 64; f += NT) {
-    const int fl = f & 63, fks = (f >> 6) % KS, fqb = (f >> 6) / KS;
-    const int m = fqb * 16 + (fl & 15);
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (m < rows)
-      val = *reinterpret_cast<const u32x4*>(a.q + (row_base + m) * D + fks * 32 + (fl >> 4) * 8);
-    sq[f] = val;
+  // d = ks*32 + (lane/16)*8 .. +8; a buffer load bounded by the group's rows
+  // (rows past them read 0).
+  {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.q + row_base * D), 0, rows * D * 2, kRawBufferWord3);
+    for (int f = threadIdx.x; f < QB * KS * 64; f += NT) {
+      const int fl = f & 63, fks = (f >> 6) % KS, fqb = (f >> 6) / KS;
+      const int m = fqb * 16 + (fl & 15);
+      sq[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            qr, (uint32_t)((m * D + fks * 32 + (fl >> 4) * 8) * 2), 0, 0));
+    }
   }
   if (!SPARSE && a.paged) {
 #pragma unroll
@@ -515,18 +591,23 @@ void attn_partials_kernel(AttnArgs a) {
     // and the bf16 rounding of the remainder to kSumCol + 1 (about 16
     // significant bits together).  A fragment element (row m, column d) sits
     // in block m / 16, step d / 32, lane ((d % 32) / 8) * 16 + m % 16, slot d % 8.
+    // Rows are taken in ascending order m = hh*T + t; every candidate row's
+    // element is read at once (independent LDS reads) and the rows not
+    // collected add exact zeros.
     if ((int)threadIdx.x < D) {
       const int dcol = threadIdx.x, ks = dcol / 32, lq = ((dcol % 32) / 8) * 16, j = dcol % 8;
       const uint16_t* sqh = reinterpret_cast<const uint16_t*>(sq);
+      uint64_t take = 0ull;  // bit m: row m is a collected row of a collected head (m < rows <= 64)
+      for (int hh = 0; hh < G; ++hh)
+        if ((gmask >> hh) & 1ull) take |= (uint64_t)a.row_mask << (hh * T);
+      float term[QB * 16];
+#pragma unroll
+      for (int m = 0; m < QB * 16; ++m)
+        term[m] = __builtin_bit_cast(float, (uint32_t)sqh[(((m >> 4) * KS + ks) * 64 + lq + (m & 15)) * 8 + j] << 16);
       float qs = 0.f;
-      for (int hh = 0; hh < G; ++hh) {
-        if (!((gmask >> hh) & 1ull)) continue;
-        for (int t = 0; t < T; ++t) {
-          if (!((a.row_mask >> t) & 1u)) continue;
-          const int m = hh * T + t;
-          qs += __builtin_bit_cast(float, (uint32_t)sqh[(((m >> 4) * KS + ks) * 64 + lq + (m & 15)) * 8 + j] << 16);
-        }
-      }
+#pragma unroll
+      for (int m = 0; m < QB * 16; ++m)
+        if ((take >> m) & 1ull) qs += term[m];
       const __bf16 hi = (__bf16)qs, lo = (__bf16)(qs - (float)hi);
       uint16_t* sqw = reinterpret_cast<uint16_t*>(sq);
       sqw[(((QB - 1) * KS + ks) * 64 + lq + kSumCol) * 8 + j] = __builtin_bit_cast(uint16_t, hi);
