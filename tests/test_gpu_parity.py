@@ -17,6 +17,19 @@ from tests.gpu_helpers import (assert_lse_close, assert_logits_close, assert_out
 
 pytestmark = pytest.mark.gpu
 
+
+def _ragged_lens(n, seed):
+    """n lengths: one in eight long (900-1299), the rest short (2-199).  With
+    5 splits of 256 positions the balanced item length drops to 64, so each
+    long sequence has about 20 items and its items past the 5th are handed to
+    the short sequences' free workgroups."""
+    rng = np.random.default_rng(seed)
+    n_long = max(1, n // 8)
+    lens = np.concatenate([rng.integers(900, 1300, size=n_long), rng.integers(2, 200, size=n - n_long)])
+    rng.shuffle(lens)
+    return tuple(int(x) for x in lens)
+
+
 CASES = {
     # name: workload (G*T query rows -> MFMA row blocks)
     # capacities 301 and 257 (cap_align=1): logit and score rows not 16-byte aligned
@@ -47,6 +60,15 @@ CASES = {
     "chunk4224_paged_g1t3_d64": W.small("c4224p", batch=8, num_q_heads=8, num_kv_heads=8,
                                         head_dim=64, gamma=2, ctx=33000, paged=True, budget=300,
                                         n_sink=4, window=32, seed=17),
+    # balanced items over many sequences: 64 sequences (the lengths held one
+    # per lane) and 72 (over 64: the lengths read in a loop), items of long
+    # sequences handed to other sequences' workgroups
+    "b64_balance_g2t2_d64": W.small("b64", batch=64, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                                    gamma=1, lens=_ragged_lens(64, 21), budget=40, n_sink=2,
+                                    window=8, seed=21),
+    "b72_balance_paged_g2t2_d128": W.small("b72", batch=72, num_q_heads=4, num_kv_heads=2,
+                                           head_dim=128, gamma=1, lens=_ragged_lens(72, 22),
+                                           paged=True, budget=40, n_sink=2, window=8, seed=22),
 }
 
 
