@@ -352,7 +352,7 @@ def main():
     # than the one selecting workgroup of the fused launch (128K x b8: 41 us
     # against 52 us)
     fused = args.select == "plain" and max_ctx <= 65536 and args.finish_select == "fused"
-    ws_fs = torch.zeros(Bn.finish_select_workspace_bytes(B), dtype=torch.uint8, device=dev) \
+    ws_fs = torch.zeros(Bn.finish_select_workspace_bytes(B, max_ctx), dtype=torch.uint8, device=dev) \
         if fused else None
 
     def finish_select():

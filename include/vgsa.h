@@ -466,24 +466,29 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
  *    (Vegas §2 steps 1-2, "A. aggregated attention-logit selection";
  *    Dustin "1." protected sinks and window.)
  * The workgroups that sum a sequence's scores also count the leading 12 bits
- * of their order-preserving keys into a histogram of that sequence; the last
- * of them to finish selects the sequence's positions in the same launch,
- * starting from that histogram.  No workgroup waits on another.  One
+ * of their order-preserving keys into a histogram of that sequence and list
+ * their candidates (the keys at or above their own threshold bin); the last
+ * of them to finish selects the sequence's positions in the same launch from
+ * that histogram and those lists.  No workgroup waits on another.  One
  * workgroup selects each sequence, so rows of more than two 32768-position
  * rounds select faster with the two calls (vgsa_select_topk_ws spreads a
  * row over one workgroup per round).
  * desc .. scores  as vgsa_verify_finish; scores must not be NULL
  * k, n_sink, window, idx, idx_stride, n_idx  as vgsa_select_topk
- * select_workspace  >= vgsa_finish_select_workspace_bytes(batch) bytes of
- *          device memory, 256-byte aligned: per-sequence histograms and
- *          counters.  It must be zero before its first use (e.g. a
- *          zero-filled allocation); every call leaves it zero again.  Calls
- *          that share it must not overlap.
+ * select_workspace  >= vgsa_finish_select_workspace_bytes(batch, max_ctx)
+ *          bytes of device memory, 256-byte aligned: per-sequence histograms
+ *          and counters, then the candidate lists (scratch, 8 bytes per
+ *          position).  It must be zero before its first use (e.g. a
+ *          zero-filled allocation); every call leaves it ready for the next
+ *          (the histograms and counters zero again).  Calls that share it
+ *          must not overlap.
  * Errors: as vgsa_verify_finish and vgsa_select_topk; VGSA_ERR_UNSUPPORTED
  * for max_ctx > 262144 (make the two calls instead); VGSA_ERR_WORKSPACE for a
  * missing, small or misaligned select_workspace.
  */
-size_t vgsa_finish_select_workspace_bytes(int32_t batch);
+/* Bytes of select_workspace for batch sequences of capacity max_ctx; 0 for
+ * batch outside 1..65535 or max_ctx outside 1..262144. */
+size_t vgsa_finish_select_workspace_bytes(int32_t batch, int32_t max_ctx);
 vgsa_status vgsa_verify_finish_select(const vgsa_attn_desc* desc, const int32_t* seq_lens,
                                       const void* workspace, size_t workspace_bytes, void* out,
                                       float* lse, vgsa_logit_layout layout, int32_t num_rows,

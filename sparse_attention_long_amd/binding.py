@@ -69,7 +69,7 @@ SIGNATURES = {
                                       c_vp, c_vp]),
     "vgsa_verify_finish": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp, c_i32,
                                    c_i32, c_i32, c_vp, c_vp, c_vp]),
-    "vgsa_finish_select_workspace_bytes": (c_sz, [c_i32]),
+    "vgsa_finish_select_workspace_bytes": (c_sz, [c_i32, c_i32]),
     "vgsa_verify_finish_select": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_sz, c_vp, c_vp,
                                           c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                                           c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
@@ -491,8 +491,8 @@ def verify_finish(desc: AttnDesc, seq_lens, workspace, out, lse, layout: int = L
         layout, num_rows, int(bool(accumulate)), _p(logits), _p(scores), _stream(out.device)), "vgsa_verify_finish")
 
 
-def finish_select_workspace_bytes(batch: int) -> int:
-    return int(load().vgsa_finish_select_workspace_bytes(batch))
+def finish_select_workspace_bytes(batch: int, max_ctx: int) -> int:
+    return int(load().vgsa_finish_select_workspace_bytes(batch, max_ctx))
 
 
 def verify_finish_select(desc: AttnDesc, seq_lens, workspace, out, lse, layout: int, logits,
@@ -500,8 +500,9 @@ def verify_finish_select(desc: AttnDesc, seq_lens, workspace, out, lse, layout: 
                          accumulate: bool = False) -> None:
     """vgsa_verify_finish_select: verify_finish (with scores) and the top-k
     selection on those scores in one launch.  `select_workspace` (uint8,
-    finish_select_workspace_bytes(B) bytes) must be zero before its first
-    use; every call leaves it zero.  Per-head logits are [B, R, H, max_ctx]."""
+    finish_select_workspace_bytes(B, max_ctx) bytes) must be zero before its
+    first use; every call leaves it ready for the next.  Per-head logits are
+    [B, R, H, max_ctx]."""
     _need(idx, "idx", torch.int32, 2)
     _need(n_idx, "n_idx", torch.int32, 1)
     _need(select_workspace, "select_workspace", torch.uint8)

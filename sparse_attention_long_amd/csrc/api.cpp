@@ -486,9 +486,9 @@ vgsa_status vgsa_verify_finish(const vgsa_attn_desc* desc, const int32_t* seq_le
   return hip_status(launch_combine_aggregate(ca, ag, static_cast<hipStream_t>(stream)));
 }
 
-size_t vgsa_finish_select_workspace_bytes(int32_t batch) {
-  if (batch < 1 || batch > kMaxGridYZ) return 0;
-  return finish_select_workspace_bytes(batch);
+size_t vgsa_finish_select_workspace_bytes(int32_t batch, int32_t max_ctx) {
+  if (batch < 1 || batch > kMaxGridYZ || max_ctx < 1 || max_ctx > kFinishSelectMaxCtx) return 0;
+  return finish_select_workspace_bytes(batch, max_ctx);
 }
 
 vgsa_status vgsa_verify_finish_select(const vgsa_attn_desc* desc, const int32_t* seq_lens,
@@ -510,7 +510,7 @@ vgsa_status vgsa_verify_finish_select(const vgsa_attn_desc* desc, const int32_t*
   if ((int64_t)desc->batch * idx_stride > 0x7fffffff) return VGSA_ERR_UNSUPPORTED;
   if (ca.rows == 0) return VGSA_OK;
   st = check_workspace(select_workspace, select_workspace_bytes,
-                       finish_select_workspace_bytes(desc->batch));
+                       finish_select_workspace_bytes(desc->batch, desc->max_ctx));
   if (st != VGSA_OK) return st;
   return hip_status(launch_finish_select(ca, ag, k, n_sink, window, idx, idx_stride, n_idx,
                                          select_workspace, static_cast<hipStream_t>(stream)));

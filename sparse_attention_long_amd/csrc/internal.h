@@ -193,7 +193,7 @@ constexpr int kMaxSelBlocks = 8704;
 // workspace holds per-row key histograms and arrival counts, zero between
 // calls).
 constexpr int kFinishSelectMaxCtx = 262144;
-size_t finish_select_workspace_bytes(int32_t batch);
+size_t finish_select_workspace_bytes(int32_t batch, int32_t max_ctx);
 hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, int32_t k,
                                 int32_t n_sink, int32_t window, int32_t* idx, int32_t idx_stride,
                                 int32_t* n_idx, void* workspace, hipStream_t stream);

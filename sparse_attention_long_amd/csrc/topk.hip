@@ -1115,13 +1115,17 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
 //     kernel), stores them with device scope, and counts the top 12 key bits
 //     of those in M = [s_end, w_start) into an LDS histogram, which it then
 //     adds into the row's histogram in the workspace (device-scope atomics,
-//     non-empty bins only).  It counts itself in once all of that is out;
-//     the last of the row's pieces to do so selects the row: it moves the
-//     histogram to LDS (leaving zeros for the next call) and runs the
-//     one-workgroup selection from the threshold scan on, reading the scores
-//     with device-scope loads.  No workgroup waits on another.  A row whose
-//     output does not depend on the scores (L <= k, or the forced positions
-//     fill the budget) is written by its piece 0.
+//     non-empty bins only).  From its own histogram it finds its threshold
+//     bin for r and lists its candidates, the keys at or above that bin, in
+//     the workspace.  It counts itself in once all of that is out; the last
+//     of the row's pieces to do so selects the row: it loads the row's
+//     histogram (leaving zeros for the next call) and the pieces' counts,
+//     finds the threshold bin, then reads the candidate lists, marking the
+//     candidates above the bin and ranking those in it.  A bin too large to
+//     rank directly (heavy ties) takes the one-workgroup selection over every
+//     score instead.  No workgroup waits on another.  A row whose output does
+//     not depend on the scores (L <= k, or the forced positions fill the
+//     budget) is written by its piece 0.
 //   * The workgroups after them combine the split partials, kThreadsTk / (D
 //     / 4) rows each (combine_quad, as the combine kernel).
 // Aggregation comes first in the grid: its workgroups are dispatched first,
@@ -1136,9 +1140,12 @@ struct FinishSelectArgs {
   int32_t* n_idx;
   uint32_t* hist;   // [B][kBins] key histograms; zero between calls
   int32_t* arrive;  // [B] pieces counted in; zero between calls
+  uint32_t* counts; // [B][pieces] candidates each piece listed
+  uint64_t* lists;  // [B][pieces][kAggPos] the pieces' candidates
   int32_t pieces;   // aggregation workgroups per sequence
   int32_t n_agg;    // B * pieces
 };
+constexpr int kMaxPieces = kMaxRounds * kRoundLen / kAggPos;
 
 // RM: rounds the LDS bitmaps hold (max_ctx <= RM * 32768).
 template <int D, bool VEC, int RM>
@@ -1146,6 +1153,7 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
                                                                    FinishSelectArgs f) {
   __shared__ SelectLdsT<RM> sh;
   __shared__ int s_last;
+  __shared__ uint32_t s_cnt[kMaxPieces];
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= f.n_agg) {
     constexpr int Q = D / 4;
@@ -1191,6 +1199,35 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
     const uint32_t h = sh.hist[i];
     if (h != 0u) atomicAdd(gh + i, h);
   }
+  // The piece's candidates: its eligible keys at or above its own threshold
+  // bin for r (a key of a lower bin has r keys of this piece above it, so it
+  // is never selected; every key when the piece holds fewer than r), listed
+  // as key << 32 | ~position in thread order.  The selecting workgroup reads
+  // these lists instead of every score of the row.
+  if (tid == 0) sh.s_out[0] = 0u;
+  const uint32_t floor_bin =
+      find_digit_v(sh.hist, kBins, 20, 0u, (uint32_t)s.r, sh.s_wave, sh.s_out).x >> 20;
+  {
+    uint32_t key[4], cand = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + tid + u * kThreadsTk;
+      key[u] = order_key(val[u]);
+      if (j < s.L && j >= s.s_end && j < s.w_start && (key[u] >> 20) >= floor_bin) cand |= 1u << u;
+    }
+    const uint2 sc = block_scan((uint32_t)__builtin_popcount(cand), sh.s_wave);
+    float* lst = reinterpret_cast<float*>(f.lists + ((size_t)b * f.pieces + piece) * kAggPos);
+    uint32_t o = sc.x;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if ((cand >> u) & 1u) {
+        const uint64_t e = ((uint64_t)key[u] << 32) | (uint32_t)~(uint32_t)(j0 + tid + u * kThreadsTk);
+        store2_device(lst, o++ * 8u, __builtin_bit_cast(float2, e));
+      }
+    if (tid == 0)
+      store1_device(reinterpret_cast<float*>(f.counts), (uint32_t)(b * f.pieces + piece) * 4u,
+                    __uint_as_float(sc.y));
+  }
   // every store and histogram add of this workgroup has completed before it
   // counts itself in
   __builtin_amdgcn_s_waitcnt(0);
@@ -1210,8 +1247,67 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
     sh.taken[i] = 0u;
     sh.in_bin[i] = 0u;
   }
-  select_stage<false, false, true, true>(sh, srow, ag.max_ctx, s.R, s.s_end, s.w_start, (uint32_t)s.r,
-                                       gh);
+  // The histogram and the pieces' candidate counts, loaded together; the
+  // threshold bin from the histogram.
+  const int np = (s.L + kAggPos - 1) / kAggPos;  // <= kMaxPieces
+  {
+    uint32_t h[kBins / kThreadsTk];
+#pragma unroll
+    for (int q = 0; q < kBins / kThreadsTk; ++q)
+      h[q] = __float_as_uint(load1_device(reinterpret_cast<const float*>(gh), (uint32_t)(tid + q * kThreadsTk) * 4u));
+    const uint32_t cn = tid < np ? __float_as_uint(load1_device(reinterpret_cast<const float*>(f.counts),
+                                                                (uint32_t)(b * f.pieces + tid) * 4u))
+                                 : 0u;
+#pragma unroll
+    for (int q = 0; q < kBins / kThreadsTk; ++q) sh.hist[tid + q * kThreadsTk] = h[q];
+    if (tid < np) s_cnt[tid] = cn;
+    if (tid == 0) sh.count = 0u;
+    __syncthreads();
+  }
+  uint32_t prefix = 0u, want = (uint32_t)s.r;
+  find_digit(sh.hist, kBins, 20, prefix, want, sh.s_wave, sh.s_out);
+  if (sh.s_out[2] <= (uint32_t)kBinCapMany) {
+    // Candidates above the threshold bin are taken; the bin's are ranked.
+    // Every selected position is a candidate of its piece, and so is every
+    // member of the bin that ranks among the `want` best, so ranking the
+    // listed members decides the bin.  Piece p goes to the wavefronts w with
+    // w mod np = p (or w to pieces w, w + 16, .. when np > 16), eight loads
+    // per lane in flight.
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t tb = prefix >> 20;
+    for (int p = wave % np; p < np; p += kWavesTk) {
+      const int kw = np <= kWavesTk ? (kWavesTk - 1 - p) / np + 1 : 1;  // wavefronts on piece p
+      const int k0 = np <= kWavesTk ? wave / np : 0;
+      const uint32_t n = s_cnt[p];
+      const float* lst = reinterpret_cast<const float*>(f.lists + ((size_t)b * f.pieces + p) * kAggPos);
+      const uint32_t stride = (uint32_t)kw * 64u;
+      for (uint32_t e0 = (uint32_t)k0 * 64u + lane; e0 < n; e0 += 8u * stride) {
+        uint64_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t e = min(e0 + i * stride, n - 1u);
+          v[i] = __builtin_bit_cast(uint64_t, load2_device(lst, e * 8u));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (e0 + i * stride >= n) break;
+          const uint32_t key = (uint32_t)(v[i] >> 32), pos = ~(uint32_t)v[i];
+          if ((key >> 20) > tb) {
+            atomicOr(&sh.taken[pos >> 5], 1u << (pos & 31));
+          } else if ((key >> 20) == tb) {
+            const uint32_t slot = atomicAdd(&sh.count, 1u);  // < the bin's size <= kBinCap
+            sh.bin_rank_key[slot] = v[i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    resolve_bin(sh, sh.count, want, false, s.R);
+  } else {
+    // a bin too large to rank directly (heavy ties): every score of the row
+    select_stage<false, false, true, true>(sh, srow, ag.max_ctx, s.R, s.s_end, s.w_start,
+                                           (uint32_t)s.r, gh);
+  }
   emit_taken(sh, s.R, s.s_end, s.w_start, s.L, s.r, out, f.idx_stride);
   if (tid == 0) f.n_idx[b] = f.k;
   for (int i = tid; i < kBins; i += kThreadsTk) store1_device(reinterpret_cast<float*>(gh), (uint32_t)i * 4u, 0.f);
@@ -1328,9 +1424,13 @@ hipError_t launch_select_blocks(int32_t batch, int32_t max_ctx, const float* sco
   return hipGetLastError();
 }
 
-size_t finish_select_workspace_bytes(int32_t batch) {
-  const size_t hist = ((size_t)batch * kBins * 4 + 255) / 256 * 256;
-  return hist + ((size_t)batch * 4 + 255) / 256 * 256;
+// [B][kBins] histograms, [B] arrival counters, [B][pieces] candidate
+// counts, [B][pieces][kAggPos] candidates; 256-byte aligned parts.
+size_t finish_select_workspace_bytes(int32_t batch, int32_t max_ctx) {
+  const size_t pieces = ((size_t)max_ctx + kAggPos - 1) / kAggPos;
+  const auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  return al((size_t)batch * kBins * 4) + al((size_t)batch * 4) + al((size_t)batch * pieces * 4) +
+         al((size_t)batch * pieces * kAggPos * 8);
 }
 
 hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, int32_t k,
@@ -1344,10 +1444,16 @@ hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, i
   f.idx = idx;
   f.idx_stride = idx_stride;
   f.n_idx = n_idx;
-  f.hist = static_cast<uint32_t*>(workspace);
-  f.arrive = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                        ((size_t)ag.batch * kBins * 4 + 255) / 256 * 256);
   f.pieces = (ag.max_ctx + kAggPos - 1) / kAggPos;
+  const auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  char* w = static_cast<char*>(workspace);
+  f.hist = reinterpret_cast<uint32_t*>(w);
+  w += al((size_t)ag.batch * kBins * 4);
+  f.arrive = reinterpret_cast<int32_t*>(w);
+  w += al((size_t)ag.batch * 4);
+  f.counts = reinterpret_cast<uint32_t*>(w);
+  w += al((size_t)ag.batch * f.pieces * 4);
+  f.lists = reinterpret_cast<uint64_t*>(w);
   f.n_agg = ag.batch * f.pieces;
   const int q = c.head_dim / 4;
   const int n_comb = (c.rows + kThreadsTk / q - 1) / (kThreadsTk / q);

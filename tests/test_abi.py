@@ -295,9 +295,12 @@ def test_finish_select_argument_checks(lib):
     d = desc()
     dp = ctypes.byref(d)
     ws = lib.vgsa_verify_workspace_bytes(dp)
-    sws = lib.vgsa_finish_select_workspace_bytes(2)
-    assert sws >= 2 * 4096 * 4 + 2 * 4 and sws % 256 == 0
-    assert lib.vgsa_finish_select_workspace_bytes(0) == 0
+    sws = lib.vgsa_finish_select_workspace_bytes(2, d.max_ctx)
+    pieces = -(-d.max_ctx // 4096)
+    assert sws >= 2 * 4096 * 4 + 2 * 4 + 2 * pieces * (4 + 4096 * 8) and sws % 256 == 0
+    assert lib.vgsa_finish_select_workspace_bytes(0, d.max_ctx) == 0
+    assert lib.vgsa_finish_select_workspace_bytes(2, 0) == 0
+    assert lib.vgsa_finish_select_workspace_bytes(2, 262145) == 0
     F = lib.vgsa_verify_finish_select
 
     def call(**kw):

@@ -77,7 +77,7 @@ def test_fullsize_sampled(name):
             sc_f = torch.empty_like(scores)
             idx_f = torch.full_like(idx, -1)
             n_f = torch.empty_like(n_idx)
-            sws = torch.zeros(Bn.finish_select_workspace_bytes(w.batch), dtype=torch.uint8,
+            sws = torch.zeros(Bn.finish_select_workspace_bytes(w.batch, d.max_ctx), dtype=torch.uint8,
                               device="cuda")
             Bn.verify_finish_select(desc, d.seq_lens, ws, out_f, lse_f, Bn.LOGITS_KVGROUP_SUM, lg_f,
                                     sc_f, w.budget, w.n_sink, w.window, idx_f, n_f, sws)
