@@ -393,6 +393,8 @@ using SelectLds = SelectLdsT<kMaxRounds>;
 template <class Lds>
 __device__ void resolve_bin(Lds& sh, uint32_t nbin, uint32_t want, bool exact, int R) {
   const int tid = threadIdx.x;
+  nbin = __builtin_amdgcn_readfirstlane(nbin);  // the same in every lane (read from LDS)
+  want = __builtin_amdgcn_readfirstlane(want);
   if (!exact) {
     if (tid < 4) sh.bin_rank_key[nbin + tid] = 0u;  // padding to a multiple of 4; ranks last
     for (int q = tid; q < (int)nbin; q += kThreadsTk) sh.rank[q] = 0u;
@@ -413,6 +415,7 @@ __device__ void resolve_bin(Lds& sh, uint32_t nbin, uint32_t want, bool exact, i
       const uint64_t cq = q < (int)nbin ? sh.bin_rank_key[q] : ~0ull;
       const int f1 = (sh_i + 1) * n4 / shares;
       uint32_t cnt = 0u;
+#pragma unroll 4
       for (int f = sh_i * n4 / shares; f < f1; ++f) {
         const uint64_t* c4 = sh.bin_rank_key + 4 * f;
         cnt += (c4[0] > cq ? 1u : 0u) + (c4[1] > cq ? 1u : 0u) + (c4[2] > cq ? 1u : 0u) +
