@@ -1120,7 +1120,8 @@ __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
 //     adds into the row's histogram in the workspace (device-scope atomics,
 //     non-empty bins only).  From its own histogram it finds its threshold
 //     bin for r and lists its candidates, the keys at or above that bin, in
-//     the workspace.  It counts itself in once all of that is out; the last
+//     the workspace (rows with r <= kListMaxR; the others select from every
+//     score).  It counts itself in once all of that is out; the last
 //     of the row's pieces to do so selects the row: it loads the row's
 //     histogram (leaving zeros for the next call) and the pieces' counts,
 //     finds the threshold bin, then reads the candidate lists, marking the
@@ -1149,6 +1150,10 @@ struct FinishSelectArgs {
   int32_t n_agg;    // B * pieces
 };
 constexpr int kMaxPieces = kMaxRounds * kRoundLen / kAggPos;
+// Rows list candidates when r is at most a quarter of a piece: a piece then
+// lists about r / kAggPos of its positions; with a larger r the lists cost
+// more to write and read than the scores they replace.
+constexpr int kListMaxR = kAggPos / 4;
 
 // RM: rounds the LDS bitmaps hold (max_ctx <= RM * 32768).
 template <int D, bool VEC, int RM>
@@ -1207,10 +1212,11 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
   // is never selected; every key when the piece holds fewer than r), listed
   // as key << 32 | ~position in thread order.  The selecting workgroup reads
   // these lists instead of every score of the row.
-  if (tid == 0) sh.s_out[0] = 0u;
-  const uint32_t floor_bin =
-      find_digit_v(sh.hist, kBins, 20, 0u, (uint32_t)s.r, sh.s_wave, sh.s_out).x >> 20;
-  {
+  const bool lists = s.r <= kListMaxR;
+  if (lists) {
+    if (tid == 0) sh.s_out[0] = 0u;
+    const uint32_t floor_bin =
+        find_digit_v(sh.hist, kBins, 20, 0u, (uint32_t)s.r, sh.s_wave, sh.s_out).x >> 20;
     uint32_t key[4], cand = 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1253,7 +1259,7 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
   // The histogram and the pieces' candidate counts, loaded together; the
   // threshold bin from the histogram.
   const int np = (s.L + kAggPos - 1) / kAggPos;  // <= kMaxPieces
-  {
+  if (lists) {
     uint32_t h[kBins / kThreadsTk];
 #pragma unroll
     for (int q = 0; q < kBins / kThreadsTk; ++q)
@@ -1268,8 +1274,8 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
     __syncthreads();
   }
   uint32_t prefix = 0u, want = (uint32_t)s.r;
-  find_digit(sh.hist, kBins, 20, prefix, want, sh.s_wave, sh.s_out);
-  if (sh.s_out[2] <= (uint32_t)kBinCapMany) {
+  if (lists) find_digit(sh.hist, kBins, 20, prefix, want, sh.s_wave, sh.s_out);
+  if (lists && sh.s_out[2] <= (uint32_t)kBinCapMany) {
     // Candidates above the threshold bin are taken; the bin's are ranked.
     // Every selected position is a candidate of its piece, and so is every
     // member of the bin that ranks among the `want` best, so ranking the
@@ -1307,7 +1313,8 @@ __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c
     __syncthreads();
     resolve_bin(sh, sh.count, want, false, s.R);
   } else {
-    // a bin too large to rank directly (heavy ties): every score of the row
+    // no lists (r above kListMaxR), or a bin too large to rank directly
+    // (heavy ties): every score of the row
     select_stage<false, false, true, true>(sh, srow, ag.max_ctx, s.R, s.s_end, s.w_start,
                                            (uint32_t)s.r, gh);
   }
