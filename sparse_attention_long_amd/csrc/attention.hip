@@ -60,20 +60,6 @@ __device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Inclusive prefix sum over the 64 lanes (DPP row shifts by 1, 2, 4, 8 within
-// each 16-lane row, then row broadcasts 15 and 31 carry rows 0 and 1 on);
-// lane 63 holds the total.
-__device__ __forceinline__ int wave_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return x;
-}
-__device__ __forceinline__ int wave_total(int x) { return __builtin_amdgcn_readlane(wave_scan(x), 63); }
-
 // Waves per SIMD the register budget is sized for: two (<= 256 registers per
 // wave) unless four query blocks of d = 128 need more.
 template <int D, int QB>
@@ -230,7 +216,9 @@ void attn_partials_kernel(AttnArgs a) {
     // sequence i: a count over the sequences is one division per lane and a
     // wave sum.
     const int S = a.num_splits, B = a.batch;
-    const int64_t total = ((int64_t)wave_total(len_lane >> 16) << 16) + wave_total(len_lane & 0xFFFF);
+    // (the sum in two 16-bit halves: each half's wave sum fits 32 bits)
+    const uint32_t len_u = (uint32_t)len_lane;
+    const int64_t total = ((int64_t)wave_total(len_u >> 16) << 16) + (int64_t)wave_total(len_u & 0xFFFFu);
     const int64_t fit = (total + (int64_t)S * B - B - 1) / ((int64_t)S * B - B);  // S > 1 here
     constexpr int MC = (kWide && !SPARSE) ? kTile : WAVES * kTile;
     const int floor_len = (a.chunk / kBalanceSplits + MC - 1) / MC * MC;
@@ -243,7 +231,7 @@ void attn_partials_kernel(AttnArgs a) {
       int hi = cp;
       while (lo < hi) {
         const int mid = max(lo, (lo + hi) / 2 / MC * MC);
-        if (wave_total(n_items(mid)) <= SB) hi = mid; else lo = mid + MC;
+        if ((int)wave_total((uint32_t)n_items(mid)) <= SB) hi = mid; else lo = mid + MC;
       }
       cp = hi;
     }
@@ -256,9 +244,9 @@ void attn_partials_kernel(AttnArgs a) {
     } else {
       // rank among the free workgroups, then the sequence whose items past S
       // hold that rank (in sequence order)
-      const int r = split - nb + wave_total(lane < b ? max(0, S - it) : 0);
+      const int r = split - nb + (int)wave_total(lane < b ? (uint32_t)max(0, S - it) : 0u);
       const int o = max(0, it - S);
-      const int pre = wave_scan(o);  // items past S of sequences 0 .. lane
+      const int pre = (int)wave_inclusive_scan((uint32_t)o);  // items past S of sequences 0 .. lane
       const uint64_t hit = __ballot(r < pre);
       if (hit != 0ull) {
         bi = __builtin_ctzll(hit);

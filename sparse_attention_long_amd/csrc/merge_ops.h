@@ -5,6 +5,25 @@
 
 namespace vgsa {
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves: row
+// shifts by 1, 2, 4, 8 (zero fill) scan each 16-lane row, then the last lane
+// of row 0 / row 2 is added to row 1 / row 3 and the last lane of row 1 to
+// rows 2 and 3; lane 63 holds the total.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return (uint32_t)v;
+}
+// Sum of x over the 64 lanes, the same value in every lane.
+__device__ __forceinline__ uint32_t wave_total(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(x), 63);
+}
+
 // Threads of a combine / aggregate workgroup.
 constexpr int kMergeBlock = 256;
 

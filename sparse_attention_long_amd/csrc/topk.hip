@@ -54,21 +54,6 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return key > 1u ? key : 1u;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves: row
-// shifts by 1, 2, 4, 8 (zero fill) scan each 16-lane row, then the last lane
-// of row 0 / row 2 is added to row 1 / row 3 and the last lane of row 1 to
-// rows 2 and 3.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  int v = (int)x;
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return (uint32_t)v;
-}
-
 // Sum of x over lanes 0..15 (DPP row scan; lane 15 holds the total), the
 // same value in every lane.
 __device__ __forceinline__ uint32_t row0_sum(uint32_t x) {
@@ -654,13 +639,12 @@ __device__ void emit_taken(Lds& sh, int R, int s_end, int w_start, int L, int r,
   for (int i = tid; i < L - w_start; i += kThreadsTk) out[s_end + r + i] = w_start + i;
 }
 
-// VEC: 16-byte score loads (rows 16-byte aligned).
 // HYBRID: two stages (Dustin, "1. hybrid attention aggregation"): the first
 // picks min(m, r) free positions by `first` (the draft-lookahead scores), the
 // second the other r - min(m, r) by `scores` (the target-historical scores)
 // among the positions the first stage left free.  Without HYBRID only the
 // second stage runs, picking all r by `scores`.
-template <bool VEC, bool HYBRID>
+template <bool HYBRID>
 __global__ __launch_bounds__(kThreadsTk) void select_topk_kernel(
     int32_t max_ctx, const float* __restrict__ scores, const float* __restrict__ first,
     const int32_t* __restrict__ seq_lens, int32_t k, int32_t m, int32_t n_sink, int32_t window,
@@ -1009,7 +993,6 @@ __global__ __launch_bounds__(kThreadsTk) void select_round_mark_kernel(
   }
 }
 
-template <bool VEC>
 __global__ __launch_bounds__(kThreadsTk) void select_final_kernel(
     int32_t max_ctx, const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     int32_t k, int32_t n_sink, int32_t window, int32_t* __restrict__ idx, int32_t idx_stride,
@@ -1156,7 +1139,7 @@ constexpr int kMaxPieces = kMaxRounds * kRoundLen / kAggPos;
 constexpr int kListMaxR = kAggPos / 4;
 
 // RM: rounds the LDS bitmaps hold (max_ctx <= RM * 32768).
-template <int D, bool VEC, int RM>
+template <int D, int RM>
 __global__ __launch_bounds__(kThreadsTk) void finish_select_kernel(CombineArgs c, AggregateArgs ag,
                                                                    FinishSelectArgs f) {
   __shared__ SelectLdsT<RM> sh;
@@ -1329,9 +1312,7 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
                               const float* draft_scores, const int32_t* seq_lens, int32_t k,
                               int32_t m, int32_t n_sink, int32_t window, int32_t* idx,
                               int32_t idx_stride, int32_t* n_idx, hipStream_t stream) {
-  const auto al16 = [](const float* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool hybrid = draft_scores != nullptr;
-  const bool vec = max_ctx % 4 == 0 && al16(scores) && (!hybrid || al16(draft_scores));
   const int rounds = (max_ctx + kRoundLen - 1) / kRoundLen;
   const dim3 grid(batch), block(kThreadsTk);
   const auto args = [&](auto kernel) {
@@ -1339,11 +1320,7 @@ hipError_t launch_select_topk(int32_t batch, int32_t max_ctx, const float* score
                        m, n_sink, window, idx, idx_stride, n_idx);
   };
   if (rounds <= kMaxRounds) {
-    if (hybrid) {
-      if (vec) args(select_topk_kernel<true, true>); else args(select_topk_kernel<false, true>);
-    } else {
-      if (vec) args(select_topk_kernel<true, false>); else args(select_topk_kernel<false, false>);
-    }
+    if (hybrid) args(select_topk_kernel<true>); else args(select_topk_kernel<false>);
   } else {
     if (hybrid) return hipErrorInvalidValue;  // rows past kMaxRounds rounds: plain selection only
     hipLaunchKernelGGL(select_topk_large_kernel, grid, block, 0, stream, max_ctx, scores, seq_lens,
@@ -1400,16 +1377,14 @@ hipError_t launch_select_topk_split(int32_t batch, int32_t max_ctx, const float*
                          seq_lens, k, n_sink, window, ws);
       hipLaunchKernelGGL(select_round_mark_kernel<true>, grid_r, block, 0, stream, max_ctx, sc,
                          seq_lens, k, n_sink, window, ws);
-      hipLaunchKernelGGL(select_final_kernel<true>, grid_b, block, 0, stream, max_ctx, sc,
-                         seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
     } else {
       hipLaunchKernelGGL(select_round_hist_kernel<false>, grid_r, block, 0, stream, max_ctx, sc,
                          seq_lens, k, n_sink, window, ws);
       hipLaunchKernelGGL(select_round_mark_kernel<false>, grid_r, block, 0, stream, max_ctx, sc,
                          seq_lens, k, n_sink, window, ws);
-      hipLaunchKernelGGL(select_final_kernel<false>, grid_b, block, 0, stream, max_ctx, sc,
-                         seq_lens, k, n_sink, window, idx, idx_stride, n_idx, ws);
     }
+    hipLaunchKernelGGL(select_final_kernel, grid_b, block, 0, stream, max_ctx, sc, seq_lens, k,
+                       n_sink, window, idx, idx_stride, n_idx, ws);
   }
   return hipGetLastError();
 }
@@ -1468,27 +1443,16 @@ hipError_t launch_finish_select(const CombineArgs& c, const AggregateArgs& ag, i
   const int q = c.head_dim / 4;
   const int n_comb = (c.rows + kThreadsTk / q - 1) / (kThreadsTk / q);
   const dim3 grid((unsigned)(f.n_agg + n_comb)), block(kThreadsTk);
-  const bool vec = ag.max_ctx % 4 == 0 && (reinterpret_cast<uintptr_t>(ag.scores) & 15) == 0;
   const bool short_rows = ag.max_ctx <= kFusedRoundsShort * kRoundLen;
   const auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, c, ag, f);
   };
   if (c.head_dim == 64) {
-    if (short_rows) {
-      if (vec) go(finish_select_kernel<64, true, kFusedRoundsShort>);
-      else go(finish_select_kernel<64, false, kFusedRoundsShort>);
-    } else {
-      if (vec) go(finish_select_kernel<64, true, kMaxRounds>);
-      else go(finish_select_kernel<64, false, kMaxRounds>);
-    }
+    if (short_rows) go(finish_select_kernel<64, kFusedRoundsShort>);
+    else go(finish_select_kernel<64, kMaxRounds>);
   } else {
-    if (short_rows) {
-      if (vec) go(finish_select_kernel<128, true, kFusedRoundsShort>);
-      else go(finish_select_kernel<128, false, kFusedRoundsShort>);
-    } else {
-      if (vec) go(finish_select_kernel<128, true, kMaxRounds>);
-      else go(finish_select_kernel<128, false, kMaxRounds>);
-    }
+    if (short_rows) go(finish_select_kernel<128, kFusedRoundsShort>);
+    else go(finish_select_kernel<128, kMaxRounds>);
   }
   return hipGetLastError();
 }
