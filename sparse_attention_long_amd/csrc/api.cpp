@@ -73,6 +73,7 @@ AttnArgs base_args(const vgsa_attn_desc& d, const SplitPlan& p, const void* q, c
                    const void* v, const int32_t* block_table, const int32_t* seq_lens,
                    void* workspace) {
   AttnArgs a{};
+  a.row_split = 1;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -309,6 +310,10 @@ vgsa_status sparse_launch(const vgsa_attn_desc* desc, const void* q, const void*
   a.lse = lse;
   // one call: a single split writes the output itself, several merge in the launch
   a.direct = (out != nullptr && p.num_splits == 1) ? 1 : 0;
+  // a single split of more than one 16-row block: two workgroups share the
+  // rows (all 256 CUs work, each workgroup runs fewer MFMA blocks and merges
+  // fewer rows; the pair's gathers cost one HBM read)
+  a.row_split = (a.direct && p.waves == kWavesWide && a.group * a.q_len > 16) ? 2 : 1;
   if (fused && p.num_splits > 1) {
     a.fuse = 1;
     a.sync = static_cast<int32_t*>(workspace);

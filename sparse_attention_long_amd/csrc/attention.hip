@@ -11,10 +11,13 @@
 //   * section 2 step 3 and section 3: the sparse pass attends only over listed
 //     positions, the list acting as a page-size-1 page table.
 //
-// Layout of the work: one workgroup per (split, kv-head, sequence); its four
-// wavefronts take 32-position tiles of the split in turn.  All G*T query rows
-// that share the kv-head live in one wavefront as 16-row MFMA blocks, so every
-// K/V byte is read from HBM once.  Per tile a wavefront:
+// Layout of the work: one workgroup per (split, kv-head, sequence); its
+// wavefronts (four or eight) take 32-position tiles of the split in turn.  All
+// G*T query rows that share the kv-head live in one wavefront as 16-row MFMA
+// blocks, so every K/V byte is read from HBM once.  (A sparse pass with one
+// split shares the rows between two workgroups on one XCD instead: both
+// gather every listed row, the second read coming from that XCD's L2.)  Per
+// tile a wavefront:
 //   1. loads 32 K rows and 32 V rows with 16-byte loads (prefetched one tile
 //      ahead in registers),
 //   2. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (positions are the
@@ -27,8 +30,9 @@
 //   4. runs an online softmax in log2 units per query row,
 //   5. accumulates O^T += V^T P^T with the same MFMA; P comes straight from
 //      the S^T accumulators, V^T is read from a per-wavefront LDS tile.
-// The four wavefronts are merged through LDS at the end and the workgroup
-// writes its un-normalised partial (o, m, l) for the combine kernel.
+// The wavefronts are merged through LDS at the end and the workgroup writes
+// its un-normalised partial (o, m, l) for the combine kernel, or with one
+// split the normalised output itself.
 #include "internal.h"
 #include "merge_ops.h"
 
@@ -189,8 +193,20 @@ void attn_partials_kernel(AttnArgs a) {
   __shared__ __align__(16) float shl[kHeadLogits ? WAVES * 16 * kHS : 4];
   __shared__ int64_t s_lrow[kHeadLogits ? QB * 16 : 1];
 
-  const int g = blockIdx.y;
-  int split = blockIdx.x, b = blockIdx.z, chunk = a.chunk;
+  int g = blockIdx.y, split = blockIdx.x, b = blockIdx.z, chunk = a.chunk;
+  // Row-split sparse launch (one split): a 1-D grid whose linear ids x + 8*(2j)
+  // and x + 8*(2j + 1) (one XCD: ids are dealt to the XCDs in turn) take the
+  // two halves of the query rows of (sequence, kv-head) pair x + 8*j; the
+  // grid is rounded up to whole rounds of 16, and ids past the pairs leave.
+  int half = 0;
+  if (SPARSE && a.row_split > 1) {
+    const int id = blockIdx.x, pair = (id & 7) + 8 * (id >> 4);
+    if (pair >= a.batch * a.hkv) return;
+    half = (id >> 3) & 1;
+    b = pair / a.hkv;
+    g = pair % a.hkv;
+    split = 0;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, kg = lane >> 4;
   // Ragged verify batches of up to 64 sequences: lane i holds sequence i's
@@ -370,10 +386,16 @@ void attn_partials_kernel(AttnArgs a) {
     nlist = 0;
   }
   const int count = SPARSE ? nlist + tail : L;
-  const int G = a.group, T = a.q_len, rows = G * T;
-  // Rows [B][Hq][T] of this kv-group are contiguous: row m = hh*T + t of the
-  // group (q-head g*G + hh, query t) is row row_base + m.
-  const size_t row_base = ((size_t)b * a.hq + (size_t)g * G) * T;
+  const int G = a.group, T = a.q_len;
+  // This workgroup's query rows: the group's G*T, or (row-split sparse) one
+  // half of them, from the group's row r0.
+  const bool halves = SPARSE && a.row_split > 1;
+  const int rows_half = (G * T + 1) / 2;
+  const int r0 = halves ? half * rows_half : 0;
+  const int rows = halves ? min(G * T - r0, rows_half) : G * T;
+  // Rows [B][Hq][T] of this kv-group are contiguous: row r0 + m = hh*T + t of
+  // the group (q-head g*G + hh, query t) is row row_base + m.
+  const size_t row_base = ((size_t)b * a.hq + (size_t)g * G) * T + r0;
   if (start >= count) {  // whole workgroup: nothing in this split
     // the only split, or (fused merge) an empty list that no workgroup
     // merges: the rows see nothing -> o = 0, lse = -inf
@@ -396,7 +418,7 @@ void attn_partials_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int m = qb * 16 + c16;
     const bool ok = m < rows;
-    const int hh = ok ? m / T : 0, t = ok ? m % T : 0;
+    const int hh = ok ? (r0 + m) / T : 0, t = ok ? (r0 + m) % T : 0;
     lim[qb] = ok ? L - T + t : 0x7fffffff;  // row t sees positions <= L - T + t
     // collected row of a collected head: its rank among the collected rows
     rowc[qb] = (EMIT != VGSA_LOGITS_NONE && ok && ((a.row_mask >> t) & 1u) && ((gmask >> hh) & 1ull))
@@ -1030,7 +1052,8 @@ __global__ __launch_bounds__(kMergeBlock) void combine_kernel(CombineArgs a) {
 
 template <int D, bool SPARSE, int EMIT, int WAVES>
 hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  const int rows = a.group * a.q_len;
+  // rows of one workgroup
+  const int rows = (SPARSE && a.row_split > 1) ? (a.group * a.q_len + 1) / 2 : a.group * a.q_len;
   const dim3 block(WAVES * 64);
   if constexpr (WAVES == kWaves) {
     // narrow: only d = 128 with four row blocks (one wavefront per SIMD)
@@ -1089,7 +1112,11 @@ hipError_t launch_attention_partials(const AttnArgs& a, bool sparse, hipStream_t
   if (!wide && a.waves != kWaves) return hipErrorInvalidValue;
   if (a.chunk > (wide ? kMaxChunkWide : kMaxChunk) || a.chunk % (wide ? kMinChunkWide : kMinChunk) != 0)
     return hipErrorInvalidValue;
-  const dim3 grid(a.num_splits, a.hkv, a.batch);
+  if (a.row_split > 1 && (!sparse || !wide || a.num_splits != 1 || !a.direct)) return hipErrorInvalidValue;
+  // row split: two workgroups per (sequence, kv-head), in whole rounds of 16
+  const int pairs = a.batch * a.hkv;
+  const dim3 grid = a.row_split > 1 ? dim3((unsigned)((pairs + 7) / 8 * 16))
+                                    : dim3(a.num_splits, a.hkv, a.batch);
   return a.head_dim == 64 ? launch_dim<64>(a, sparse, grid, s) : launch_dim<128>(a, sparse, grid, s);
 }
 

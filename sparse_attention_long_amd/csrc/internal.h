@@ -126,6 +126,11 @@ struct AttnArgs {
   int32_t max_ctx, paged, max_blocks, num_blocks;
   int32_t num_splits, chunk;
   int32_t waves;     // wavefronts per workgroup (the plan's layout)
+  // Sparse, one split: the G*T query rows of a (sequence, kv-head) are shared
+  // by this many workgroups (1 or 2), each gathering every listed K/V row.
+  // The two run on one XCD (linear ids x + 8*(2j) and x + 8*(2j + 1)), so the
+  // second read of a row is served by that XCD's L2.
+  int32_t row_split;
   float scale;       // natural-log softmax scale
   float scale_log2;  // scale * log2(e)
 };
