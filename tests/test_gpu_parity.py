@@ -42,6 +42,10 @@ CASES = {
                          lens=(700, 129), budget=64, n_sink=4, window=16, seed=12),
     "g8t8_d64": W.small("g8t8", batch=1, num_q_heads=32, num_kv_heads=4, head_dim=64, gamma=7,
                         lens=(513,), budget=100, n_sink=4, window=32, seed=13),
+    # 21 rows: the one-split sparse pass shares them unevenly (11 + 10) between
+    # two workgroups; 4 (sequence, kv-head) pairs leave padding workgroups
+    "g3t7_d64": W.small("g3t7", batch=2, num_q_heads=6, num_kv_heads=2, head_dim=64, gamma=6,
+                        lens=(520, 90), budget=44, n_sink=3, window=10, seed=18, cap_align=1),
     "g1t2_d128": W.small("g1t2", batch=2, num_q_heads=4, num_kv_heads=4, head_dim=128, gamma=1,
                          lens=(1000, 2), budget=50, n_sink=1, window=3, seed=14),
     "paged_g8t6_d64": W.small("pg", batch=3, num_q_heads=16, num_kv_heads=2, head_dim=64, gamma=5,
