@@ -927,13 +927,16 @@ void attn_partials_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Merge the wavefronts, relative to each row's workgroup max M, in four
-  // rounds of D/4 head-dim columns: every wavefront parks its scaled
-  // accumulators for those columns in LDS (the K/V tiles are free now), then
-  // all threads sum the wavefronts element by element and write the result.
-  constexpr int DC = D / 4;        // columns per round
-  constexpr int DBR = DB / 4;      // 16-wide column blocks per round
+  // Merge the wavefronts, relative to each row's workgroup max M, in rounds
+  // of D/kRounds head-dim columns (two when the parked blocks of half the
+  // columns fit in the K/V tiles, which are free now, else four): every
+  // wavefront parks its scaled accumulators for those columns of the real
+  // rows in LDS, then all threads sum the wavefronts element by element and
+  // write the result.
   constexpr int RP = QB * 16;      // rows held by the accumulators
+  constexpr int kRounds = WAVES * RP * (D / 2 + 4) * 4 <= (int)sizeof(sbuf) ? 2 : 4;
+  constexpr int DC = D / kRounds;  // columns per round
+  constexpr int DBR = DB / kRounds;  // 16-wide column blocks per round
   constexpr int CS = DC + 4;       // row stride of a parked block (floats)
   static_assert(WAVES * RP * CS * 4 <= (int)sizeof(sbuf), "merge rounds must fit in the K/V tiles");
   float* obuf = reinterpret_cast<float*>(sbuf);  // [WAVES][RP][CS]
@@ -959,13 +962,14 @@ void attn_partials_kernel(AttnArgs a) {
   }
   const int S = a.part_splits;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < kRounds; ++r) {
 #pragma unroll
     for (int j = 0; j < DBR; ++j)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        *reinterpret_cast<f32x4*>(obuf + (wave * RP + qb * 16 + c16) * CS + j * 16 + 4 * kg) =
-            oacc[r * DBR + j][qb] * scl[qb];
+        if (qb < QB - 1 || qb * 16 + c16 < rows)  // rows past the real ones are never read
+          *reinterpret_cast<f32x4*>(obuf + (wave * RP + qb * 16 + c16) * CS + j * 16 + 4 * kg) =
+              oacc[r * DBR + j][qb] * scl[qb];
     __syncthreads();
     // four consecutive columns per thread: 16-byte LDS reads, 16-byte partial
     // stores, 8-byte output stores
