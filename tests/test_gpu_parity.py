@@ -83,7 +83,41 @@ def run_verify(d, w, layout):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_verify_logits_scores_select_sparse(name):
-    w = CASES[name]
+    _check_pipeline(name, CASES[name])
+
+
+def _random_workload(seed: int):
+    """A seeded random small shape: batch 1-4, 1/2/4 kv-heads, 1-8 q-heads per
+    kv-head, T = 2..8 rows (G*T <= 64), d = 64 or 128, contiguous or paged,
+    ragged lengths 1..1600, budget, sinks and window drawn too."""
+    rng = np.random.default_rng([2026, seed])
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 6, 8], p=[0.1, 0.1, 0.15, 0.2, 0.2, 0.25]))
+    t = int(rng.integers(2, min(8, 64 // g) + 1))
+    b = int(rng.integers(1, 5))
+    lens = tuple(int(v) for v in rng.integers(1, 1601, size=b))
+    k = int(rng.integers(8, 200))
+    n_sink = int(rng.integers(0, 5))
+    window = int(rng.integers(0, min(32, k - n_sink) + 1))  # the call needs n_sink + window <= k
+    return W.small(f"rnd{seed}", batch=b, num_q_heads=g * hkv, num_kv_heads=hkv,
+                   head_dim=int(rng.choice([64, 128])), gamma=t - 1, lens=lens,
+                   budget=k, n_sink=n_sink, window=window, paged=bool(rng.integers(0, 2)),
+                   cap_align=int(rng.choice([1, 16])), seed=1000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    """The whole path on seeded random small shapes (the same checks as the
+    named cases)."""
+    w = _random_workload(seed)
+    say(f"[random shape] seed={seed} B={w.batch} Hq/Hkv={w.num_q_heads}/{w.num_kv_heads} "
+        f"T={w.q_len} d={w.head_dim} paged={w.paged} lens={w.lens} k={w.budget}")
+    # (planted keys are not checked: whether they win is a property of the
+    # named workloads' data, not of the selection, which is compared exactly)
+    _check_pipeline(f"rnd{seed}", w, planted=False)
+
+
+def _check_pipeline(name, w, planted=True):
     say(f"[verify pipeline] {name}")
     x = W.make_layer(w)
     d = to_device(x)
@@ -118,7 +152,7 @@ def test_verify_logits_scores_select_sparse(name):
         for b in range(w.batch):
             assert n_h[b] == len(want[b])
             assert np.array_equal(idx_h[b, :n_h[b]], want[b]), f"{name}/{layout} idx b={b}"
-        for b, pos in enumerate(x.planted):
+        for b, pos in enumerate(x.planted if planted else []):
             if w.budget < int(x.seq_lens[b]):
                 assert set(pos.tolist()) <= set(want[b].tolist()), f"planted key dropped b={b}"
 
