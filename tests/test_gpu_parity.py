@@ -117,6 +117,41 @@ def test_random_shapes(seed):
     _check_pipeline(f"rnd{seed}", w, planted=False)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_long_lists(seed):
+    """Seeded random long lists (1025-5000 entries: several splits merged in
+    the launch), with T' = 1 or all T rows, a tail of 0-6 trailing positions
+    after the list, contiguous or paged, d = 64 or 128."""
+    rng = np.random.default_rng([2027, seed])
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    t = int(rng.integers(2, min(8, 64 // g) + 1))
+    b = int(rng.integers(1, 4))
+    lens = tuple(int(v) for v in rng.integers(1300, 6001, size=b))
+    w = W.small(f"rl{seed}", batch=b, num_q_heads=g * hkv, num_kv_heads=hkv,
+                head_dim=int(rng.choice([64, 128])), gamma=t - 1, lens=lens, budget=64, n_sink=4,
+                window=16, paged=bool(rng.integers(0, 2)), seed=3000 + seed)
+    tail = int(rng.integers(0, 7))
+    one_row = bool(rng.integers(0, 2))
+    count = int(rng.integers(1025, min(5000, min(lens) - tail) + 1))
+    say(f"[random long lists] seed={seed} B={b} Hq/Hkv={w.num_q_heads}/{hkv} T={t} d={w.head_dim} "
+        f"paged={w.paged} count={count} tail={tail} one_row={one_row}")
+    x = W.make_layer(w)
+    d = to_device(x)
+    below = np.array([int(L) - tail for L in x.seq_lens], np.int32)  # listed positions stay below L - tail
+    idx, n = W.index_lists(w.seed + 1, below, count=count, stride=count)
+    qd = d.q[:, :, -1:].contiguous() if one_row else d.q
+    qh = x.q[:, :, -1:] if one_row else x.q
+    out, lse = Bn.sparse_attention(qd, d.k, d.v, d.seq_lens, dev_i32(idx), dev_i32(n),
+                                   block_table=d.block_table, max_ctx=d.max_ctx, tail=tail)
+    torch.cuda.synchronize()
+    lists = [np.concatenate([idx[i, :n[i]], np.arange(int(x.seq_lens[i]) - tail, int(x.seq_lens[i]))])
+             for i in range(b)]
+    o_ref, lse_ref = oracle.sparse_attention(qh, x.k, x.v, x.seq_lens, lists)
+    assert_out_close(out, o_ref, f"random long lists seed {seed} out")
+    assert_lse_close(lse, lse_ref, f"random long lists seed {seed} lse")
+
+
 def _check_pipeline(name, w, planted=True):
     say(f"[verify pipeline] {name}")
     x = W.make_layer(w)
